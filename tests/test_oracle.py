@@ -1,0 +1,342 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test is chosen so that a plausible slip in the oracle (a dropped term, a
+wrong sign, index or axis, a transposed operand, gate and up swapped) fails at
+least one of them. None of them calls the HIP library.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+from scipy.special import softmax as scipy_softmax
+
+import moe_synth
+from moe_synth import BlockShape
+import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SMALL = BlockShape(hidden=256, num_experts=8, top_k=3, expert_inter=64, dense_inter=128)
+
+
+def _w64(w):
+    """Weights dict with every bf16 tensor widened to float64 (for torch)."""
+    return {k: (oracle.bf16_to_f64(v) if isinstance(v, np.ndarray) and v.dtype == np.uint16 else v)
+            for k, v in w.items()}
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    return moe_synth.make_inputs("tiny")
+
+
+# ---------------------------------------------------------------- GELU
+def test_gelu_matches_torch_tanh_gelu():
+    z = torch.linspace(-12, 12, 20001, dtype=torch.float64)
+    ref = F.gelu(z, approximate="tanh").numpy()
+    np.testing.assert_allclose(oracle.gelu_tanh(z.numpy()), ref, rtol=0, atol=1e-14)
+
+
+def test_gelu_closed_forms():
+    z = np.linspace(-5, 5, 1001)
+    # 0.5 z (1 + t) - (-0.5 z (1 - t)) = z: the odd part of GELU is z / 2
+    np.testing.assert_allclose(oracle.gelu_tanh(z) - oracle.gelu_tanh(-z), z, atol=1e-13)
+    assert oracle.gelu_tanh(0.0) == 0.0
+    assert abs(oracle.gelu_tanh(20.0) - 20.0) < 1e-12
+    assert abs(oracle.gelu_tanh(-20.0)) < 1e-12
+    c = math.sqrt(2 / math.pi)
+    assert abs(oracle.gelu_tanh(1.0) - 0.5 * (1 + math.tanh(c * 1.044715))) < 1e-15
+
+
+# ---------------------------------------------------------------- RMSNorm
+def test_rmsnorm_identity():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((7, 300)) * 3
+    eps = 1e-6
+    r = oracle.rms_normalise(x, eps)
+    ms = np.mean(x * x, axis=1)
+    np.testing.assert_allclose(np.mean(r * r, axis=1), ms / (ms + eps), rtol=1e-13)
+
+
+# ---------------------------------------------------------------- router
+def test_router_logits_closed_form():
+    # one-hot router rows pick coordinates of v = x / rms(x) * s * H^-0.5
+    H, E = 16, 4
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((3, H))
+    s = 1 + 0.1 * rng.standard_normal(H)
+    Wr = np.zeros((E, H))
+    cols = [3, 0, 11, 7]
+    for e, c in enumerate(cols):
+        Wr[e, c] = 1.0
+    got = oracle.router_logits(x, s, Wr, eps=0.0)
+    rms = np.sqrt(np.mean(x * x, axis=1))
+    want = np.stack([x[:, c] / rms * s[c] / math.sqrt(H) for c in cols], axis=1)
+    np.testing.assert_allclose(got, want.astype(np.float32), rtol=1e-7)
+
+
+def test_router_is_scale_free():
+    _, w, x = moe_synth.make_inputs("tiny")
+    x64 = oracle.bf16_to_f64(x)
+    a = oracle.route(x64, w["router_scale"], w["router_w"], w["per_expert_scale"], 4, 0.0)
+    b = oracle.route(4.0 * x64, w["router_scale"], w["router_w"], w["per_expert_scale"], 4, 0.0)
+    np.testing.assert_array_equal(a["topk_idx"], b["topk_idx"])
+    np.testing.assert_allclose(a["topk_w"], b["topk_w"], rtol=1e-12)
+
+
+def test_router_renormalised_weights_sum_to_one(tiny):
+    wl, w, x = tiny
+    r = oracle.route(x, w["router_scale"], w["router_w"], w["per_expert_scale"], 4, 1e-6)
+    np.testing.assert_allclose(r["renorm"].sum(axis=1), 1.0, atol=1e-12)
+    pes = w["per_expert_scale"].astype(np.float64)[r["topk_idx"]]
+    np.testing.assert_allclose((r["topk_w"] / pes).sum(axis=1), 1.0, atol=1e-12)
+    # the per-expert scale multiplies the renormalised weight
+    np.testing.assert_allclose(r["topk_w"], r["renorm"] * pes, rtol=1e-15)
+
+
+def test_router_k_equals_e_is_full_softmax(tiny):
+    wl, w, x = tiny
+    E = w["router_w"].shape[0]
+    r = oracle.route(x, w["router_scale"], w["router_w"], w["per_expert_scale"], E, 1e-6)
+    full = scipy_softmax(r["logits"], axis=1)
+    np.testing.assert_allclose(np.take_along_axis(full, r["topk_idx"].astype(np.int64), 1),
+                               r["renorm"], rtol=1e-12)
+    # every expert appears once
+    np.testing.assert_array_equal(np.sort(r["topk_idx"], axis=1), np.tile(np.arange(E), (x.shape[0], 1)))
+
+
+def test_router_selection_matches_library_topk(tiny):
+    wl, w, x = tiny
+    r = oracle.route(x, w["router_scale"], w["router_w"], w["per_expert_scale"], 4, 1e-6)
+    assert not r["boundary_tie"].any() and not r["order_tie"].any()
+    vals, idx = torch.topk(torch.from_numpy(r["logits"]), 4, dim=1, largest=True, sorted=True)
+    np.testing.assert_array_equal(r["topk_idx"], idx.numpy())
+    # softmax is monotone: selecting on probabilities gives the same set
+    np.testing.assert_array_equal(np.sort(r["topk_idx"], 1),
+                                  np.sort(np.argsort(-r["probs"], 1)[:, :4], 1))
+
+
+def test_router_tie_goes_to_lower_index():
+    H, E = 8, 6
+    x = np.ones((1, H))
+    Wr = np.zeros((E, H))
+    Wr[[1, 2, 4, 5], 0] = 1.0           # experts 1, 2, 4, 5 tie; 0 and 3 lower
+    Wr[3, 0] = -1.0
+    r = oracle.route(x, np.ones(H), Wr, np.ones(E), 3, 0.0)
+    np.testing.assert_array_equal(r["topk_idx"][0], [1, 2, 4])
+    assert r["boundary_tie"][0] and r["order_tie"][0]
+    np.testing.assert_allclose(r["renorm"][0], [1 / 3] * 3, rtol=1e-15)
+
+
+def test_router_bias_is_added_to_logits():
+    _, w, x = moe_synth.make_inputs("tiny")
+    E = w["router_w"].shape[0]
+    bias = np.zeros(E, dtype=np.float32)
+    bias[5] = 100.0                      # forces expert 5 first for every token
+    r = oracle.route(x, w["router_scale"], w["router_w"], w["per_expert_scale"], 4, 1e-6, bias)
+    assert (r["topk_idx"][:, 0] == 5).all()
+    r0 = oracle.route(x, w["router_scale"], w["router_w"], w["per_expert_scale"], 4, 1e-6)
+    np.testing.assert_allclose(r["logits"][:, 5], (r0["logits"][:, 5] + 100.0).astype(np.float32),
+                               rtol=1e-6)
+
+
+# ---------------------------------------------------------------- permutation
+def test_permutation_properties(tiny):
+    wl, w, x = tiny
+    r = oracle.route(x, w["router_scale"], w["router_w"], w["per_expert_scale"], 4, 1e-6)
+    idx = r["topk_idx"]
+    T, K = idx.shape
+    E = 16
+    p = oracle.permute_pairs(idx, E)
+    assert p["counts"].sum() == T * K
+    assert p["offsets"][0] == 0 and p["offsets"][-1] == T * K
+    assert (np.diff(p["offsets"]) == p["counts"]).all()
+    # bijection onto all pairs
+    pairs = set(zip(p["perm_token"].tolist(), p["perm_slot"].tolist()))
+    assert len(pairs) == T * K
+    for e in range(E):
+        a, b = p["offsets"][e], p["offsets"][e + 1]
+        seg_t = p["perm_token"][a:b]
+        assert (np.diff(seg_t) > 0).all()          # strictly increasing tokens
+        assert (idx[seg_t, p["perm_slot"][a:b]] == e).all()
+        # brute force: the tokens that picked e, in order
+        want = [t for t in range(T) if e in idx[t]]
+        assert seg_t.tolist() == want
+    # inv_row is the inverse permutation
+    rows = p["inv_row"]
+    np.testing.assert_array_equal(p["perm_token"][rows], np.repeat(np.arange(T), K))
+    np.testing.assert_array_equal(p["perm_slot"][rows], np.tile(np.arange(K), T))
+    # a token never repeats an expert
+    assert all(len(set(row)) == K for row in idx.tolist())
+
+
+# ---------------------------------------------------------------- block
+def test_masked_dense_equals_sparse_tiny(tiny):
+    wl, w, x = tiny
+    y_s, r = oracle.moe_block(x, w, 4, 1e-6)
+    y_d, _ = oracle.masked_dense_block(x, w, 4, 1e-6, routing=r)
+    np.testing.assert_allclose(y_d, y_s, rtol=1e-10, atol=1e-12)
+
+
+def test_masked_dense_equals_sparse_real_width():
+    # real hidden / intermediate widths, fewer experts to keep it fast
+    shp = BlockShape(hidden=2816, num_experts=12, top_k=8, expert_inter=704, dense_inter=2112)
+    w = moe_synth.make_weights(shp, 11)
+    x = moe_synth.make_tokens(shp, 11, 6)
+    y_s, r = oracle.moe_block(x, w, 8, 1e-6)
+    y_d, _ = oracle.masked_dense_block(x, w, 8, 1e-6, routing=r)
+    np.testing.assert_allclose(y_d, y_s, rtol=1e-9, atol=1e-12)
+
+
+def test_single_expert_top1_reduces_to_dense_geglu():
+    shp = BlockShape(hidden=128, num_experts=1, top_k=1, expert_inter=32, dense_inter=64)
+    w = moe_synth.make_weights(shp, 3)
+    x = moe_synth.make_tokens(shp, 3, 9)
+    y, r = oracle.moe_block(x, w, 1, 1e-6)
+    assert (r["topk_idx"] == 0).all()
+    np.testing.assert_allclose(r["topk_w"][:, 0], w["per_expert_scale"][0], rtol=1e-15)
+    # library reference: torch linear + tanh GELU (float64, CPU)
+    w64 = _w64(w)
+    xt = torch.from_numpy(oracle.bf16_to_f64(x))
+
+    def geglu(gu, dn):
+        gu = torch.from_numpy(gu)
+        I = gu.shape[0] // 2
+        h = F.gelu(F.linear(xt, gu[:I]), approximate="tanh") * F.linear(xt, gu[I:])
+        return F.linear(h, torch.from_numpy(dn))
+
+    want = float(w["per_expert_scale"][0]) * geglu(w64["expert_gate_up"][0], w64["expert_down"][0]) \
+        + geglu(w64["dense_gate_up"], w64["dense_down"])
+    np.testing.assert_allclose(y, want.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_dense_mlp_matches_torch():
+    w = moe_synth.make_weights(SMALL, 4)
+    x = moe_synth.make_tokens(SMALL, 4, 5)
+    w64 = _w64(w)
+    xt = torch.from_numpy(oracle.bf16_to_f64(x))
+    gu = torch.from_numpy(w64["dense_gate_up"])
+    Id = SMALL.dense_inter
+    want = F.linear(F.gelu(F.linear(xt, gu[:Id]), approximate="tanh") * F.linear(xt, gu[Id:]),
+                    torch.from_numpy(w64["dense_down"]))
+    np.testing.assert_allclose(oracle.dense_mlp(x, w["dense_gate_up"], w["dense_down"]),
+                               want.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_brute_force_loops_agree(tiny):
+    wl, w, x = tiny
+    toks = [0, 17, 63]
+    y, _ = oracle.moe_block(x, w, 4, 1e-6)
+    bf = oracle.brute_force_block(x, w, 4, 1e-6, toks)
+    np.testing.assert_allclose(bf, y[toks], rtol=1e-10, atol=1e-12)
+
+
+def test_tokens_are_independent(tiny):
+    wl, w, x = tiny
+    y, _ = oracle.moe_block(x, w, 4, 1e-6)
+    for t in (0, 31, 63):
+        yt, _ = oracle.moe_block(x[t:t + 1], w, 4, 1e-6)
+        np.testing.assert_allclose(yt[0], y[t], rtol=1e-12, atol=1e-14)
+
+
+def test_expert_relabelling_leaves_output_unchanged(tiny):
+    wl, w, x = tiny
+    y, r = oracle.moe_block(x, w, 4, 1e-6)
+    assert not r["boundary_tie"].any()
+    perm = np.random.default_rng(9).permutation(16)
+    w2 = dict(w)
+    for k in ("router_w", "per_expert_scale", "expert_gate_up", "expert_down"):
+        w2[k] = w[k][perm]
+    y2, r2 = oracle.moe_block(x, w2, 4, 1e-6)
+    np.testing.assert_array_equal(perm[r2["topk_idx"]], r["topk_idx"])
+    np.testing.assert_allclose(y2, y, rtol=1e-12, atol=1e-14)
+
+
+def test_worked_example_closed_form():
+    with open(os.path.join(HERE, "golden", "worked_example.json")) as f:
+        ex = json.load(f)
+    w = {k: np.array(ex[k], dtype=np.float64) for k in
+         ("router_scale", "router_w", "per_expert_scale", "expert_gate_up", "expert_down",
+          "dense_gate_up", "dense_down")}
+    w["logit_bias"] = None
+    x = np.array(ex["x"])
+
+    def g(z):
+        return 0.5 * z * (1 + math.tanh(math.sqrt(2 / math.pi) * (z + 0.044715 * z ** 3)))
+
+    s1 = 1 / (1 + math.exp(-1))
+    y1, r1 = oracle.moe_block(x, w, 1, ex["rms_eps"])
+    np.testing.assert_array_equal(r1["topk_idx"], [[0]])
+    np.testing.assert_allclose(r1["logits"], [[0.5, -0.5]], rtol=0)
+    np.testing.assert_allclose(y1[0], [4 * g(1), -g(-1), 0, -4 * g(1)], rtol=1e-14, atol=1e-15)
+    y2, r2 = oracle.moe_block(x, w, 2, ex["rms_eps"])
+    np.testing.assert_array_equal(r2["topk_idx"], [[0, 1]])
+    np.testing.assert_allclose(r2["topk_w"][0], [2 * s1, 3 * (1 - s1)], rtol=1e-14)
+    want = (2 * s1 * np.array([2 * g(1), 0, 0, -2 * g(1)])
+            + 3 * (1 - s1) * g(-1) * np.ones(4) + np.array([0, -g(-1), 0, 0]))
+    np.testing.assert_allclose(y2[0], want, rtol=1e-14, atol=1e-15)
+
+
+# ---------------------------------------------------------------- int8
+def test_int8_quantisation_bounds():
+    w = moe_synth.make_weights(SMALL, 6)
+    q, s = oracle.quantize_int8(w["expert_gate_up"])
+    assert q.dtype == np.int8 and s.dtype == np.float32
+    wf = oracle.bf16_to_f64(w["expert_gate_up"])
+    err = np.abs(wf - oracle.dequantize_int8(q, s))
+    # nearest level: at most half a step, plus the rounding of the fp32 quotient
+    # (half an ulp of a value below 128, i.e. 2^-18 of a step)
+    assert (err <= s.astype(np.float64)[..., None] * (0.5 + 2.0 ** -18 + 1e-9)).all()
+    assert (np.abs(q).max(axis=-1) == 127).all()
+    assert (q != -128).all()
+
+
+def test_int8_rounding_golden():
+    # hand-picked row: max 127 -> scale 1; halves round to even; negative side symmetric
+    row = np.array([[127.0, 2.5, 3.5, -2.5, -0.5, 0.49, 126.5, -127.0]], dtype=np.float32)
+    q, s = oracle.quantize_int8(row)
+    assert s[0] == np.float32(1.0)
+    np.testing.assert_array_equal(q[0], [127, 2, 4, -2, 0, 0, 126, -127])
+    zq, zs = oracle.quantize_int8(np.zeros((2, 5), dtype=np.float32))
+    assert (zs == 0).all() and (zq == 0).all()
+
+
+def test_int8_block_equals_block_on_dequantised_weights(tiny):
+    wl, w, x = tiny
+    wq = dict(w)
+    wq["expert_gate_up_q"], wq["expert_gate_up_scale"] = oracle.quantize_int8(w["expert_gate_up"])
+    wq["expert_down_q"], wq["expert_down_scale"] = oracle.quantize_int8(w["expert_down"])
+    y8, r = oracle.moe_block(x, wq, 4, 1e-6, expert_dtype="int8")
+    wd = dict(w)
+    wd["expert_gate_up"] = oracle.dequantize_int8(wq["expert_gate_up_q"], wq["expert_gate_up_scale"])
+    wd["expert_down"] = oracle.dequantize_int8(wq["expert_down_q"], wq["expert_down_scale"])
+    yd, _ = oracle.moe_block(x, wd, 4, 1e-6, routing=r)
+    np.testing.assert_allclose(y8, yd, rtol=1e-12, atol=1e-14)
+    # and it stays close to the bf16 block (per-channel int8 loses little)
+    yb, _ = oracle.moe_block(x, w, 4, 1e-6, routing=r)
+    rel = np.linalg.norm(y8 - yb) / np.linalg.norm(yb)
+    assert rel < 2e-2
+
+
+# ---------------------------------------------------------------- accumulation
+def test_fp16_accumulation_loses_accuracy_at_real_hidden():
+    """Negative control for the ONNX export card, "MoE dispatch: why this
+    export uses the vectorized unfused path": accumulating the expert products
+    in fp16 at hidden 2816 is far less accurate than accumulating in fp32."""
+    shp = BlockShape(hidden=2816, num_experts=1, top_k=1, expert_inter=64, dense_inter=64)
+    w = moe_synth.make_weights(shp, 8)
+    x = oracle.bf16_to_f64(moe_synth.make_tokens(shp, 8, 4))
+    gate = oracle.bf16_to_f64(w["expert_gate_up"][0][:64])
+    exact = x @ gate.T
+    prod16 = (x[:, None, :] * gate[None, :, :]).astype(np.float16)
+    acc16 = np.zeros(exact.shape, dtype=np.float16)
+    acc32 = np.zeros(exact.shape, dtype=np.float32)
+    for h in range(2816):                        # sequential accumulation
+        acc16 = (acc16 + prod16[:, :, h]).astype(np.float16)
+        acc32 = (acc32 + prod16[:, :, h].astype(np.float32)).astype(np.float32)
+    e16 = np.linalg.norm(acc16 - exact) / np.linalg.norm(exact)
+    e32 = np.linalg.norm(acc32 - exact) / np.linalg.norm(exact)
+    assert e16 > 10 * e32
