@@ -1,0 +1,174 @@
+/*
+ * moe.h -- C ABI of libmoe_ffn.so, the MI355X (gfx950) hybrid MoE FFN block.
+ *
+ * The block is the feed-forward part of a Gemma-4 26B-A4B layer: a 128-expert
+ * top-8 mixture of GeGLU experts running in parallel with a shared dense MLP.
+ * Pages that define it (titles as printed on them):
+ *   [INF2] "Gemma-4 26B-A4B (MoE) on AWS Inferentia2 -- Tensor-Parallel (TP=8)"
+ *          sections "The architecture (a dual-path FFN)", "How it works (the recipe)"
+ *   [INT8] "Gemma-4 26B-A4B (MoE, int8 experts) on AWS Inferentia2 -- TP=8"
+ *          intro and "How it works"
+ *   [TT]   "Gemma-4-26B-A4B-it -- Tenstorrent Blackhole (vLLM bundle)"
+ *          "Configurable knobs" (gathered expert prefill)
+ *   [ONNX] "Gemma-4 26B-A4B-it -- ONNX MoE text decoder (fp16, CUDA) with
+ *          canonical inference metadata", table "Truthful graph contracts"
+ *          (rows "Mixture of Experts", "MoE topology", "Router") and
+ *          "MoE dispatch: why this export uses the vectorized unfused path"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is a DEVICE pointer owned by the caller, contiguous,
+ *   row-major and 16-byte aligned. bf16 tensors hold bfloat16 bit patterns.
+ * - `ws` is caller-owned device scratch of at least moe_workspace_bytes(d, T)
+ *   bytes, 256-byte aligned. Its contents on entry do not matter; calls that
+ *   share one workspace must not overlap in time.
+ * - Work is enqueued on `stream` (0 = the null stream) and the call returns
+ *   without waiting for it; there is no host synchronisation, no allocation
+ *   and no global device state. Device faults surface at the caller's next
+ *   synchronisation.
+ * - Every call checks its arguments before it launches anything. On error it
+ *   returns a negative status, launches nothing and leaves a message for
+ *   moe_last_error(); there is no fallback to another implementation.
+ * - T == 0 is a valid empty batch: the call returns MOE_OK and launches nothing;
+ *   the activation, output and workspace pointers may then be NULL.
+ *
+ * Shape limits: hidden % 256 == 0; expert_inter % 64 == 0; dense_inter % 64 == 0;
+ * 1 <= top_k <= 8; top_k <= num_experts <= 256; 0 <= T <= MOE_MAX_TOKENS.
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MOE_OK               0
+#define MOE_ERR_NULL        -1  /* a required pointer is NULL */
+#define MOE_ERR_SHAPE       -2  /* T < 0 or > MOE_MAX_TOKENS, or a dimension breaks the limits above */
+#define MOE_ERR_UNSUPPORTED -3  /* top_k > 8, num_experts > 256, unknown dtype or path */
+#define MOE_ERR_WORKSPACE   -4  /* ws_bytes smaller than moe_workspace_bytes() */
+#define MOE_ERR_HIP         -5  /* a HIP launch or copy failed; the message names it */
+#define MOE_ERR_ALIGN       -6  /* a tensor is not 16-byte aligned, or ws not 256-byte aligned */
+
+#define MOE_MAX_TOKENS   (1 << 22)
+#define MOE_MAX_EXPERTS  256
+#define MOE_MAX_TOPK     8
+
+/* expert weight storage */
+#define MOE_DTYPE_BF16 0
+#define MOE_DTYPE_INT8 1  /* [INT8]: per-output-channel symmetric int8 + fp32 scale */
+
+/* how moe_block computes the routed experts */
+#define MOE_PATH_AUTO    0  /* streaming when T <= the streaming limit, else grouped */
+#define MOE_PATH_STREAM  1  /* weight-streaming kernels, each weight row read once (small T) */
+#define MOE_PATH_GROUPED 2  /* grouped MFMA GEMMs over the gathered (token, expert) rows */
+
+/* Largest T the streaming path accepts (its per-block staging is sized for it). */
+#define MOE_STREAM_MAX_TOKENS 64
+
+/* Block dimensions. [INF2] "The architecture (a dual-path FFN)": hidden 2816,
+ * 128 experts, top 8, expert intermediate 704, dense intermediate 2112.
+ * rms_eps: the router's RMSNorm epsilon (added to mean(x^2) inside the root). */
+typedef struct moe_dims {
+    int32_t hidden;        /* H  */
+    int32_t num_experts;   /* E  */
+    int32_t top_k;         /* K  */
+    int32_t expert_inter;  /* I  */
+    int32_t dense_inter;   /* Id */
+    float   rms_eps;
+} moe_dims;
+
+/* One layer's weights (all device pointers).
+ * Router, [ONNX] row "Router": logits = (x / rms(x)) * router_scale * H^-0.5 @ router_w^T
+ *   (+ logit_bias), softmax in fp32, top-k, renormalise, * per_expert_scale.
+ * Experts, [INF2] "How it works (the recipe)" and [ONNX] row "Mixture of Experts":
+ *   out = down @ (gelu_tanh(gate @ x) * (up @ x)); gate_up rows [0,I) are gate,
+ *   rows [I,2I) are up. Dense MLP ([ONNX] row "MoE topology") has the same form
+ *   with Id. */
+typedef struct moe_weights {
+    const void*  router_scale;      /* [H]      bf16 */
+    const void*  router_w;          /* [E, H]   bf16 */
+    const float* per_expert_scale;  /* [E]      fp32 */
+    const float* logit_bias;        /* [E]      fp32, or NULL for none */
+    const void*  expert_gate_up;    /* [E, 2I, H]  bf16, or int8 if expert_dtype == INT8 */
+    const void*  expert_down;       /* [E, H, I]   bf16, or int8 */
+    int32_t      expert_dtype;      /* MOE_DTYPE_* */
+    const float* gate_up_scale;     /* [E, 2I] fp32 per-row scales (INT8 only; else ignored) */
+    const float* down_scale;        /* [E, H]  fp32 per-row scales (INT8 only; else ignored) */
+    const void*  dense_gate_up;     /* [2Id, H] bf16 */
+    const void*  dense_down;        /* [H, Id]  bf16 */
+} moe_weights;
+
+#define MOE_MAX_STAGES 8
+
+/* Optional parity / timing hooks for moe_block (pass NULL for none).
+ * Every output pointer is a device pointer or NULL (then it is skipped); the
+ * library copies into them on `stream` after the block has been computed. */
+typedef struct moe_debug {
+    int32_t  path;             /* in:  MOE_PATH_* */
+    int32_t* topk_idx;         /* out: [T, K] selected experts, descending logit, ties -> lower index */
+    float*   topk_w;           /* out: [T, K] renormalised weights times per_expert_scale */
+    int32_t* counts;           /* out: [E]    rows per expert */
+    int32_t* offsets;          /* out: [E+1]  exclusive prefix sum of counts */
+    int32_t* perm_token;       /* out: [T*K]  token of each grouped row (ascending expert, then token) */
+    int32_t* inv_row;          /* out: [T*K]  grouped row of pair (t, k), at index t*K + k */
+    hipEvent_t stage_event[MOE_MAX_STAGES + 1]; /* in: if non-NULL, event i is recorded on `stream`
+                                   before stage i and event n_stages after the last one */
+    int32_t  path_taken;       /* out (host): the path used */
+    int32_t  n_stages;         /* out (host): stages launched; each stage is one kernel launch */
+    const char* stage_name[MOE_MAX_STAGES]; /* out (host): kernel of each stage (static strings) */
+} moe_debug;
+
+/* Exact device bytes moe_block, moe_route and dense_mlp need at this T
+ * (router logits, routing, grouping tables, intermediates). 0 if the
+ * dimensions are invalid (moe_last_error() says why). */
+size_t moe_workspace_bytes(const moe_dims* d, int32_t T);
+
+/* Router alone. [ONNX] "Truthful graph contracts", row "Router".
+ * x [T, H] bf16 -> topk_idx [T, K] int32 (descending logit; equal logits go to
+ * the lower expert index), topk_w [T, K] fp32 (renormalised softmax weights of
+ * the selected experts times per_expert_scale). The router runs in fp32
+ * throughout: RMSNorm, scale, logits, softmax. */
+int moe_route(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
+              int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The whole block. y [T, H] bf16 = dense(x) + sum_k topk_w[t,k] * expert_{topk_idx[t,k]}(x_t)
+ * ([ONNX] row "MoE topology": dense MLP in parallel with the MoE; [INF2] "How it
+ * works": sparse top-k, equal to all-experts-dense with zero weight on unselected
+ * experts). Only the routed (token, expert) pairs are computed ([TT] "Configurable
+ * knobs", gathered expert prefill). GEMMs accumulate in fp32 ([ONNX] "MoE
+ * dispatch": fp16 accumulation loses accuracy at hidden 2816); the GeGLU
+ * intermediates are rounded to bf16 before the down projections. The result is
+ * deterministic: no floating-point atomics, fixed summation order over k.
+ * dbg may be NULL. */
+int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T, void* y,
+              moe_debug* dbg, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The shared dense MLP alone ([ONNX] row "MoE topology"): y [T, H] bf16 =
+ * dense_down @ (gelu_tanh(gate @ x) * (up @ x)), with dense_gate_up [2Id, H]
+ * (gate rows first) and dense_down [H, Id], all bf16. Uses d->hidden and
+ * d->dense_inter; the expert fields of d must still be valid. */
+int dense_mlp(const moe_dims* d, const void* dense_gate_up, const void* dense_down,
+              const void* x, int32_t T, void* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Per-row symmetric int8 quantisation of a bf16 matrix [rows, cols], as the
+ * int8 build quantises the fused expert weights when it loads them ([INT8]
+ * "How it works"): scale[r] = max_c |w[r,c]| / 127 (fp32), q[r,c] =
+ * round-half-even(w[r,c] / scale[r]) clamped to [-127, 127]; an all-zero row
+ * gets scale 0 and q 0. cols % 8 == 0, rows >= 0. Writes q [rows, cols] int8
+ * and scale [rows] fp32. */
+int moe_quantize_int8(const void* w_bf16, int64_t rows, int32_t cols, int8_t* q, float* scale,
+                      hipStream_t stream);
+
+/* Message for the last non-zero status returned on this thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_FFN_H */

@@ -1,0 +1,9 @@
+"""MI355X-native hybrid MoE FFN block (Gemma-4 26B-A4B shape) on gfx950.
+
+The compute lives in ``libmoe_ffn.so`` (hand-written HIP kernels behind the C
+ABI of ``include/moe.h``); this package only marshals torch tensors to it.
+"""
+from ._abi import (MOE_DTYPE_BF16, MOE_DTYPE_INT8, MOE_PATH_AUTO, MOE_PATH_GROUPED,  # noqa: F401
+                   MOE_PATH_STREAM, MOE_STREAM_MAX_TOKENS, load_library)
+from .ops import (BlockDims, LayerWeights, MoEError, dense_mlp, moe_block, moe_quantize_int8,  # noqa: F401
+                  moe_route, moe_workspace_bytes, new_debug)

@@ -1,0 +1,73 @@
+// Device helpers shared by the gfx950 kernels of the MoE FFN block.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+constexpr int kWave = 64;
+
+// bfloat16 <-> fp32. Widening is exact; narrowing rounds to nearest even
+// (finite inputs only: the block never produces inf/nan from finite weights).
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// 8 bf16 held in a uint4 -> 8 floats
+__device__ __forceinline__ void unpack8(const uint4& v, float* f) {
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+    f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+    f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+// 8 int8 held in a uint2 -> 8 floats (exact)
+__device__ __forceinline__ void unpack8_i8(const uint2& v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = (float)(int8_t)((v.x >> (8 * i)) & 0xFF);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[4 + i] = (float)(int8_t)((v.y >> (8 * i)) & 0xFF);
+}
+
+// GELU, tanh approximation ("gelu_pytorch_tanh"):
+// 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))), evaluated in fp32.
+__device__ __forceinline__ float gelu_tanh(float z) {
+    const float c = 0.7978845608028654f;  // sqrt(2/pi)
+    float inner = c * (z + 0.044715f * z * z * z);
+    return 0.5f * z * (1.0f + tanhf(inner));
+}
+
+// Butterfly reductions over the lanes [base, base + width) of a wavefront.
+// The order of the additions is fixed, so results are bitwise reproducible.
+template <int WIDTH>
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = WIDTH / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+template <int WIDTH>
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = WIDTH / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+// Make global writes of this workgroup visible to its other waves (the
+// writers release, the barrier orders, the readers acquire).
+__device__ __forceinline__ void block_sync_global() {
+    __threadfence();
+    __syncthreads();
+    __threadfence();
+}
+
+}  // namespace moe

@@ -1,0 +1,384 @@
+// Host side of libmoe_ffn.so: argument checks, workspace carving, path
+// selection and kernel launches for the C ABI declared in include/moe.h.
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+#define HIP_TRY(expr, what)                                                                     \
+    do {                                                                                        \
+        hipError_t e_ = (expr);                                                                 \
+        if (e_ != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e_)); \
+    } while (0)
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t up256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// Workspace layout at a given T (byte offsets into ws).
+struct Layout {
+    size_t logits, topk_idx, topk_w, tile_counts, counts, offsets, active, n_active;
+    size_t perm_token, perm_w, inv_row, mtile_group, mtile_row0, n_mtiles, h, hd, rows, total;
+    int max_mtiles;
+};
+
+Layout make_layout(const moe_dims& d, int64_t T) {
+    Layout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += up256(bytes);
+        return o;
+    };
+    const int64_t E = d.num_experts, K = d.top_k, TK = T * K;
+    const int64_t n_tiles = (T + 63) / 64;
+    const int64_t BM = moe::kGemmBM;
+    L.max_mtiles = (int)((TK + BM - 1) / BM + (E < TK ? E : TK));
+    L.logits = take(T * E * 4);
+    L.topk_idx = take(TK * 4);
+    L.topk_w = take(TK * 4);
+    L.tile_counts = take(n_tiles * E * 4);
+    L.counts = take(E * 4);
+    L.offsets = take((E + 1) * 4);
+    L.active = take(E * 4);
+    L.n_active = take(4);
+    L.perm_token = take(TK * 4);
+    L.perm_w = take(TK * 4);
+    L.inv_row = take(TK * 4);
+    L.mtile_group = take((size_t)L.max_mtiles * 4);
+    L.mtile_row0 = take((size_t)L.max_mtiles * 4);
+    L.n_mtiles = take(4);
+    L.h = take(TK * d.expert_inter * 2);
+    L.hd = take(T * d.dense_inter * 2);
+    L.rows = take(TK * d.hidden * 2);
+    L.total = off;
+    return L;
+}
+
+int check_dims(const moe_dims* d) {
+    if (!d) return fail(MOE_ERR_NULL, "dims is NULL");
+    if (d->top_k > MOE_MAX_TOPK)
+        return fail(MOE_ERR_UNSUPPORTED, "top_k=%d > %d", d->top_k, MOE_MAX_TOPK);
+    if (d->num_experts > MOE_MAX_EXPERTS)
+        return fail(MOE_ERR_UNSUPPORTED, "num_experts=%d > %d", d->num_experts, MOE_MAX_EXPERTS);
+    if (d->hidden <= 0 || d->hidden % 256)
+        return fail(MOE_ERR_SHAPE, "hidden=%d must be a positive multiple of 256", d->hidden);
+    if (d->expert_inter <= 0 || d->expert_inter % 64)
+        return fail(MOE_ERR_SHAPE, "expert_inter=%d must be a positive multiple of 64", d->expert_inter);
+    if (d->dense_inter <= 0 || d->dense_inter % 64)
+        return fail(MOE_ERR_SHAPE, "dense_inter=%d must be a positive multiple of 64", d->dense_inter);
+    if (d->top_k < 1 || d->num_experts < d->top_k)
+        return fail(MOE_ERR_SHAPE, "need 1 <= top_k (%d) <= num_experts (%d)", d->top_k, d->num_experts);
+    if (!(d->rms_eps >= 0.f) || d->rms_eps > 1.f)
+        return fail(MOE_ERR_SHAPE, "rms_eps=%g must be in [0, 1]", (double)d->rms_eps);
+    return MOE_OK;
+}
+
+int check_T(int32_t T) {
+    if (T < 0 || T > MOE_MAX_TOKENS) return fail(MOE_ERR_SHAPE, "T=%d outside [0, %d]", T, MOE_MAX_TOKENS);
+    return MOE_OK;
+}
+
+int check_ws(const moe_dims* d, int32_t T, void* ws, size_t ws_bytes) {
+    if (!ws) return fail(MOE_ERR_NULL, "workspace is NULL");
+    if (!aligned(ws, 256)) return fail(MOE_ERR_ALIGN, "workspace must be 256-byte aligned");
+    const size_t need = make_layout(*d, T).total;
+    if (ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed at T=%d", ws_bytes, need, T);
+    return MOE_OK;
+}
+
+#define CHECK_PTR(p, name, al)                                                       \
+    do {                                                                             \
+        if (!(p)) return fail(MOE_ERR_NULL, "%s is NULL", name);                     \
+        if (!aligned((p), (al))) return fail(MOE_ERR_ALIGN, "%s is not %d-byte aligned", name, (al)); \
+    } while (0)
+
+int check_weights(const moe_weights* w) {
+    if (!w) return fail(MOE_ERR_NULL, "weights is NULL");
+    CHECK_PTR(w->router_scale, "router_scale", 16);
+    CHECK_PTR(w->router_w, "router_w", 16);
+    CHECK_PTR(w->per_expert_scale, "per_expert_scale", 4);
+    if (w->logit_bias && !aligned(w->logit_bias, 4)) return fail(MOE_ERR_ALIGN, "logit_bias misaligned");
+    CHECK_PTR(w->expert_gate_up, "expert_gate_up", 16);
+    CHECK_PTR(w->expert_down, "expert_down", 16);
+    if (w->expert_dtype != MOE_DTYPE_BF16 && w->expert_dtype != MOE_DTYPE_INT8)
+        return fail(MOE_ERR_UNSUPPORTED, "expert_dtype=%d", w->expert_dtype);
+    if (w->expert_dtype == MOE_DTYPE_INT8) {
+        CHECK_PTR(w->gate_up_scale, "gate_up_scale", 4);
+        CHECK_PTR(w->down_scale, "down_scale", 4);
+    }
+    CHECK_PTR(w->dense_gate_up, "dense_gate_up", 16);
+    CHECK_PTR(w->dense_down, "dense_down", 16);
+    return MOE_OK;
+}
+
+// Largest T routed to the streaming path by MOE_PATH_AUTO (env MOE_STREAM_MAX_T overrides).
+int stream_limit() {
+    int lim = 32;
+    if (const char* s = std::getenv("MOE_STREAM_MAX_T")) {
+        const int v = std::atoi(s);
+        if (v >= 0) lim = v;
+    }
+    return lim < MOE_STREAM_MAX_TOKENS ? lim : MOE_STREAM_MAX_TOKENS;
+}
+
+bool stream_fits(const moe_dims& d) { return d.expert_inter <= 1024 && d.dense_inter <= 4096; }
+
+// Records the stage events of a debug struct around each launch.
+struct Stages {
+    moe_debug* dbg;
+    hipStream_t s;
+    int n = 0;
+    hipError_t begin(const char* name) {
+        if (!dbg) return hipSuccess;
+        if (n < MOE_MAX_STAGES) dbg->stage_name[n] = name;
+        hipError_t e = hipSuccess;
+        if (n <= MOE_MAX_STAGES && dbg->stage_event[n]) e = hipEventRecord(dbg->stage_event[n], s);
+        ++n;
+        return e;
+    }
+    hipError_t end() {
+        if (!dbg) return hipSuccess;
+        dbg->n_stages = n;
+        if (n <= MOE_MAX_STAGES && dbg->stage_event[n]) return hipEventRecord(dbg->stage_event[n], s);
+        return hipSuccess;
+    }
+};
+
+template <typename T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err; }
+
+size_t moe_workspace_bytes(const moe_dims* d, int32_t T) {
+    if (check_dims(d) != MOE_OK || check_T(T) != MOE_OK) return 0;
+    return make_layout(*d, T).total;
+}
+
+int moe_route(const moe_dims* d, const moe_weights* w, const void* x, int32_t T, int32_t* topk_idx,
+              float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int rc;
+    if ((rc = check_dims(d)) || (rc = check_T(T)) || (rc = check_weights(w))) return rc;
+    g_err[0] = 0;
+    if (T == 0) return MOE_OK;  // empty batch: tensors may be NULL, nothing is launched
+    CHECK_PTR(x, "x", 16);
+    CHECK_PTR(topk_idx, "topk_idx", 4);
+    CHECK_PTR(topk_w, "topk_w", 4);
+    if ((rc = check_ws(d, T, ws, ws_bytes))) return rc;
+    const Layout L = make_layout(*d, T);
+    float* logits = at<float>(ws, L.logits);
+    HIP_TRY(moe::launch_router_logits((const uint16_t*)x, (const uint16_t*)w->router_scale,
+                                      (const uint16_t*)w->router_w, w->logit_bias, T, d->hidden,
+                                      d->num_experts, d->rms_eps, logits, stream),
+            "router_logits launch");
+    HIP_TRY(moe::launch_router_topk(logits, w->per_expert_scale, T, d->num_experts, d->top_k,
+                                    topk_idx, topk_w, stream),
+            "router_topk launch");
+    return MOE_OK;
+}
+
+int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T, void* y,
+              moe_debug* dbg, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int rc;
+    if ((rc = check_dims(d)) || (rc = check_T(T)) || (rc = check_weights(w))) return rc;
+    if (T > 0) {  // empty batch: x, y and ws may be NULL
+        CHECK_PTR(x, "x", 16);
+        CHECK_PTR(y, "y", 16);
+        if ((rc = check_ws(d, T, ws, ws_bytes))) return rc;
+    }
+    int path = dbg ? dbg->path : MOE_PATH_AUTO;
+    if (path != MOE_PATH_AUTO && path != MOE_PATH_STREAM && path != MOE_PATH_GROUPED)
+        return fail(MOE_ERR_UNSUPPORTED, "unknown path %d", path);
+    if (path == MOE_PATH_AUTO)
+        path = (T <= stream_limit() && stream_fits(*d)) ? MOE_PATH_STREAM : MOE_PATH_GROUPED;
+    if (path == MOE_PATH_STREAM && (T > MOE_STREAM_MAX_TOKENS || !stream_fits(*d)))
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "streaming path needs T <= %d, expert_inter <= 1024, dense_inter <= 4096",
+                    MOE_STREAM_MAX_TOKENS);
+    g_err[0] = 0;
+    if (dbg) {
+        dbg->path_taken = path;
+        dbg->n_stages = 0;
+    }
+    if (T == 0) return MOE_OK;
+
+    const Layout L = make_layout(*d, T);
+    const bool int8 = w->expert_dtype == MOE_DTYPE_INT8;
+    const int H = d->hidden, E = d->num_experts, K = d->top_k, I = d->expert_inter, Id = d->dense_inter;
+    float* logits = at<float>(ws, L.logits);
+    int32_t* topk_idx = at<int32_t>(ws, L.topk_idx);
+    float* topk_w = at<float>(ws, L.topk_w);
+    moe::PermuteOut po;
+    po.tile_counts = at<int32_t>(ws, L.tile_counts);
+    po.counts = at<int32_t>(ws, L.counts);
+    po.offsets = at<int32_t>(ws, L.offsets);
+    po.perm_token = at<int32_t>(ws, L.perm_token);
+    po.perm_w = at<float>(ws, L.perm_w);
+    po.inv_row = at<int32_t>(ws, L.inv_row);
+    po.active = at<int32_t>(ws, L.active);
+    po.n_active = at<int32_t>(ws, L.n_active);
+    po.mtile_group = at<int32_t>(ws, L.mtile_group);
+    po.mtile_row0 = at<int32_t>(ws, L.mtile_row0);
+    po.n_mtiles = at<int32_t>(ws, L.n_mtiles);
+    uint16_t* h = at<uint16_t>(ws, L.h);
+    uint16_t* hd = at<uint16_t>(ws, L.hd);
+    uint16_t* rows = at<uint16_t>(ws, L.rows);
+    const uint16_t* xb = (const uint16_t*)x;
+
+    Stages st{dbg, stream};
+    HIP_TRY(st.begin("router_logits"), "event record");
+    HIP_TRY(moe::launch_router_logits(xb, (const uint16_t*)w->router_scale,
+                                      (const uint16_t*)w->router_w, w->logit_bias, T, H, E,
+                                      d->rms_eps, logits, stream),
+            "router_logits launch");
+    if (path == MOE_PATH_STREAM) {
+        HIP_TRY(st.begin("topk_permute"), "event record");
+        HIP_TRY(moe::launch_permute(logits, w->per_expert_scale, topk_idx, topk_w, T, K, E,
+                                    moe::kGemmBM, po, stream),
+                "permute launch");
+        moe::StreamArgs sa{};
+        sa.T = T; sa.H = H; sa.I = I; sa.Id = Id; sa.K = K; sa.E = E;
+        sa.x = xb;
+        sa.gu = w->expert_gate_up; sa.gu_scale = w->gate_up_scale;
+        sa.dw = w->expert_down; sa.dw_scale = w->down_scale;
+        sa.active = po.active; sa.n_active = po.n_active; sa.offsets = po.offsets;
+        sa.perm_token = po.perm_token; sa.perm_w = po.perm_w; sa.inv_row = po.inv_row;
+        sa.max_active = T * K < E ? T * K : E;
+        sa.dgu = (const uint16_t*)w->dense_gate_up; sa.ddw = (const uint16_t*)w->dense_down;
+        sa.h = h; sa.hd = hd; sa.y = (uint16_t*)y;
+        HIP_TRY(st.begin("stream_gateup"), "event record");
+        HIP_TRY(moe::launch_stream_gateup(sa, int8, stream), "stream_gateup launch");
+        HIP_TRY(st.begin("stream_down_combine"), "event record");
+        HIP_TRY(moe::launch_stream_down(sa, int8, stream), "stream_down launch");
+    } else {
+        HIP_TRY(st.begin("router_topk"), "event record");
+        HIP_TRY(moe::launch_router_topk(logits, w->per_expert_scale, T, E, K, topk_idx, topk_w, stream),
+                "router_topk launch");
+        HIP_TRY(st.begin("permute"), "event record");
+        HIP_TRY(moe::launch_permute(nullptr, nullptr, topk_idx, topk_w, T, K, E, moe::kGemmBM, po, stream),
+                "permute launch");
+        moe::GemmArgs g{};
+        // experts gate/up + GELU: gathered rows of x
+        g.A = xb; g.lda = H; g.a_rows = po.perm_token;
+        g.B = w->expert_gate_up; g.b_group_stride = (int64_t)2 * I * H; g.ldb = H;
+        g.b_scale = int8 ? w->gate_up_scale : nullptr; g.scale_group_stride = 2 * I;
+        g.K = H; g.n_out = I; g.up_off = I;
+        g.mtile_group = po.mtile_group; g.mtile_row0 = po.mtile_row0; g.n_mtiles = po.n_mtiles;
+        g.group_end = po.offsets; g.max_mtiles = L.max_mtiles;
+        g.C = h; g.ldc = I;
+        HIP_TRY(st.begin("gemm_gateup_experts"), "event record");
+        HIP_TRY(moe::launch_gemm_gateup(g, int8, stream), "gemm_gateup launch");
+        // dense gate/up + GELU
+        moe::GemmArgs gd{};
+        gd.A = xb; gd.lda = H; gd.B = w->dense_gate_up; gd.ldb = H; gd.K = H;
+        gd.n_out = Id; gd.up_off = Id; gd.M_dense = T; gd.C = hd; gd.ldc = Id;
+        HIP_TRY(st.begin("gemm_gateup_dense"), "event record");
+        HIP_TRY(moe::launch_gemm_gateup(gd, false, stream), "gemm_gateup dense launch");
+        // experts down, weighted rows
+        moe::GemmArgs gw{};
+        gw.A = h; gw.lda = I; gw.B = w->expert_down; gw.b_group_stride = (int64_t)H * I; gw.ldb = I;
+        gw.b_scale = int8 ? w->down_scale : nullptr; gw.scale_group_stride = H;
+        gw.K = I; gw.n_out = H;
+        gw.mtile_group = po.mtile_group; gw.mtile_row0 = po.mtile_row0; gw.n_mtiles = po.n_mtiles;
+        gw.group_end = po.offsets; gw.max_mtiles = L.max_mtiles;
+        gw.C = rows; gw.ldc = H; gw.row_w = po.perm_w;
+        HIP_TRY(st.begin("gemm_down_experts"), "event record");
+        HIP_TRY(moe::launch_gemm_down(gw, int8, stream), "gemm_down launch");
+        // dense down + combine
+        moe::GemmArgs gc{};
+        gc.A = hd; gc.lda = Id; gc.B = w->dense_down; gc.ldb = Id; gc.K = Id; gc.n_out = H;
+        gc.M_dense = T; gc.C = (uint16_t*)y; gc.ldc = H;
+        gc.comb = rows; gc.inv_row = po.inv_row; gc.topk = K;
+        HIP_TRY(st.begin("gemm_dense_down_combine"), "event record");
+        HIP_TRY(moe::launch_gemm_combine(gc, stream), "gemm_combine launch");
+    }
+    HIP_TRY(st.end(), "event record");
+
+    if (dbg) {
+        const int64_t TK = (int64_t)T * K;
+        struct { void* dst; const void* src; size_t bytes; } cp[] = {
+            {dbg->topk_idx, topk_idx, (size_t)TK * 4},
+            {dbg->topk_w, topk_w, (size_t)TK * 4},
+            {dbg->counts, po.counts, (size_t)E * 4},
+            {dbg->offsets, po.offsets, (size_t)(E + 1) * 4},
+            {dbg->perm_token, po.perm_token, (size_t)TK * 4},
+            {dbg->inv_row, po.inv_row, (size_t)TK * 4},
+        };
+        for (auto& c : cp)
+            if (c.dst) HIP_TRY(hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyDeviceToDevice, stream),
+                               "debug copy");
+    }
+    return MOE_OK;
+}
+
+int dense_mlp(const moe_dims* d, const void* dense_gate_up, const void* dense_down, const void* x,
+              int32_t T, void* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int rc;
+    if ((rc = check_dims(d)) || (rc = check_T(T))) return rc;
+    CHECK_PTR(dense_gate_up, "dense_gate_up", 16);
+    CHECK_PTR(dense_down, "dense_down", 16);
+    g_err[0] = 0;
+    if (T == 0) return MOE_OK;  // empty batch: x, y and ws may be NULL
+    CHECK_PTR(x, "x", 16);
+    CHECK_PTR(y, "y", 16);
+    if ((rc = check_ws(d, T, ws, ws_bytes))) return rc;
+    const Layout L = make_layout(*d, T);
+    const int H = d->hidden, Id = d->dense_inter;
+    uint16_t* hd = at<uint16_t>(ws, L.hd);
+    if (T <= stream_limit() && stream_fits(*d)) {
+        moe::StreamArgs sa{};
+        sa.T = T; sa.H = H; sa.I = d->expert_inter; sa.Id = Id; sa.K = d->top_k; sa.E = d->num_experts;
+        sa.x = (const uint16_t*)x; sa.max_active = 0;
+        sa.dgu = (const uint16_t*)dense_gate_up; sa.ddw = (const uint16_t*)dense_down;
+        sa.hd = hd; sa.y = (uint16_t*)y;
+        HIP_TRY(moe::launch_stream_gateup(sa, false, stream), "stream_gateup launch");
+        HIP_TRY(moe::launch_stream_down(sa, false, stream), "stream_down launch");
+    } else {
+        moe::GemmArgs gd{};
+        gd.A = (const uint16_t*)x; gd.lda = H; gd.B = dense_gate_up; gd.ldb = H; gd.K = H;
+        gd.n_out = Id; gd.up_off = Id; gd.M_dense = T; gd.C = hd; gd.ldc = Id;
+        HIP_TRY(moe::launch_gemm_gateup(gd, false, stream), "gemm_gateup dense launch");
+        moe::GemmArgs gc{};
+        gc.A = hd; gc.lda = Id; gc.B = dense_down; gc.ldb = Id; gc.K = Id; gc.n_out = H;
+        gc.M_dense = T; gc.C = (uint16_t*)y; gc.ldc = H;
+        HIP_TRY(moe::launch_gemm_combine(gc, stream), "gemm_combine launch");
+    }
+    return MOE_OK;
+}
+
+int moe_quantize_int8(const void* w_bf16, int64_t rows, int32_t cols, int8_t* q, float* scale,
+                      hipStream_t stream) {
+    if (rows < 0 || rows > ((int64_t)1 << 32) || cols <= 0 || cols % 8)
+        return fail(MOE_ERR_SHAPE, "rows=%lld cols=%d (need rows >= 0, cols > 0, cols %% 8 == 0)",
+                    (long long)rows, cols);
+    CHECK_PTR(w_bf16, "w", 16);
+    CHECK_PTR(q, "q", 16);
+    CHECK_PTR(scale, "scale", 4);
+    g_err[0] = 0;
+    if (rows == 0) return MOE_OK;
+    HIP_TRY(moe::launch_quantize_int8((const uint16_t*)w_bf16, rows, cols, q, scale, stream),
+            "quantize launch");
+    return MOE_OK;
+}
+
+}  // extern "C"

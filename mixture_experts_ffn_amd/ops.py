@@ -1,0 +1,174 @@
+"""Python binding of libmoe_ffn.so: the entry points of include/moe.h with the
+same names, taking torch tensors for device memory and the current HIP stream.
+
+Argument marshalling only: every step of the block runs in the HIP kernels of
+the library. There is no CPU or PyTorch fallback; a missing library or a bad
+argument raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Optional
+
+import torch
+
+from . import _abi
+from ._abi import MoeDebug, MoeDims, MoeWeights
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, where: str, msg: str):
+        super().__init__(f"{where}: {_abi.STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+@dataclasses.dataclass
+class BlockDims:
+    hidden: int
+    num_experts: int
+    top_k: int
+    expert_inter: int
+    dense_inter: int
+    rms_eps: float = 1e-6
+
+    def c(self) -> MoeDims:
+        return MoeDims(self.hidden, self.num_experts, self.top_k, self.expert_inter,
+                       self.dense_inter, self.rms_eps)
+
+
+@dataclasses.dataclass
+class LayerWeights:
+    """Device tensors of one layer (layouts as in include/moe.h)."""
+    router_scale: torch.Tensor            # [H] bf16
+    router_w: torch.Tensor                # [E, H] bf16
+    per_expert_scale: torch.Tensor        # [E] fp32
+    expert_gate_up: torch.Tensor          # [E, 2I, H] bf16 or int8
+    expert_down: torch.Tensor             # [E, H, I] bf16 or int8
+    dense_gate_up: torch.Tensor           # [2Id, H] bf16
+    dense_down: torch.Tensor              # [H, Id] bf16
+    logit_bias: Optional[torch.Tensor] = None   # [E] fp32
+    gate_up_scale: Optional[torch.Tensor] = None  # [E, 2I] fp32 (int8)
+    down_scale: Optional[torch.Tensor] = None     # [E, H] fp32 (int8)
+
+    @property
+    def expert_dtype(self) -> int:
+        return _abi.MOE_DTYPE_INT8 if self.expert_gate_up.dtype == torch.int8 else _abi.MOE_DTYPE_BF16
+
+    def c(self) -> MoeWeights:
+        def ptr(t):
+            return None if t is None else _dev(t, "weight").data_ptr()
+        return MoeWeights(ptr(self.router_scale), ptr(self.router_w), ptr(self.per_expert_scale),
+                          ptr(self.logit_bias), ptr(self.expert_gate_up), ptr(self.expert_down),
+                          self.expert_dtype, ptr(self.gate_up_scale), ptr(self.down_scale),
+                          ptr(self.dense_gate_up), ptr(self.dense_down))
+
+
+def _lib():
+    return _abi.load_library()
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(rc: int, where: str):
+    if rc != _abi.MOE_OK:
+        raise MoEError(rc, where, _lib().moe_last_error().decode())
+
+
+def moe_workspace_bytes(dims: BlockDims, T: int) -> int:
+    n = _lib().moe_workspace_bytes(ctypes.byref(dims.c()), int(T))
+    if n == 0:
+        raise MoEError(_abi.MOE_ERR_SHAPE, "moe_workspace_bytes", _lib().moe_last_error().decode())
+    return int(n)
+
+
+def _workspace(dims, T, device, workspace):
+    need = moe_workspace_bytes(dims, T)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return _dev(workspace, "workspace"), need
+
+
+def moe_route(dims: BlockDims, weights: LayerWeights, x: torch.Tensor, topk_idx=None,
+              topk_w=None, workspace=None, stream=None):
+    """Router alone: returns (topk_idx [T,K] int32, topk_w [T,K] fp32)."""
+    x = _dev(x, "x")
+    T = x.shape[0]
+    if topk_idx is None:
+        topk_idx = torch.empty((T, dims.top_k), dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, dims.top_k), dtype=torch.float32, device=x.device)
+    ws, _ = _workspace(dims, T, x.device, workspace)
+    rc = _lib().moe_route(ctypes.byref(dims.c()), ctypes.byref(weights.c()), x.data_ptr(), T,
+                          _dev(topk_idx, "topk_idx").data_ptr(), _dev(topk_w, "topk_w").data_ptr(),
+                          ws.data_ptr(), ws.numel(), _stream(stream))
+    _check(rc, "moe_route")
+    return topk_idx, topk_w
+
+
+def moe_block(dims: BlockDims, weights: LayerWeights, x: torch.Tensor, y=None,
+              debug: Optional[MoeDebug] = None, workspace=None, stream=None) -> torch.Tensor:
+    """The whole block: y = dense(x) + sum_k w_k expert_k(x) (bf16 [T, H])."""
+    x = _dev(x, "x")
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, dims.hidden), dtype=torch.bfloat16, device=x.device)
+    ws, _ = _workspace(dims, T, x.device, workspace)
+    rc = _lib().moe_block(ctypes.byref(dims.c()), ctypes.byref(weights.c()), x.data_ptr(), T,
+                          _dev(y, "y").data_ptr(), ctypes.byref(debug) if debug is not None else None,
+                          ws.data_ptr(), ws.numel(), _stream(stream))
+    _check(rc, "moe_block")
+    return y
+
+
+def dense_mlp(dims: BlockDims, dense_gate_up: torch.Tensor, dense_down: torch.Tensor,
+              x: torch.Tensor, y=None, workspace=None, stream=None) -> torch.Tensor:
+    """The shared dense MLP alone (bf16 [T, H])."""
+    x = _dev(x, "x")
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, dims.hidden), dtype=torch.bfloat16, device=x.device)
+    ws, _ = _workspace(dims, T, x.device, workspace)
+    rc = _lib().dense_mlp(ctypes.byref(dims.c()), _dev(dense_gate_up, "dense_gate_up").data_ptr(),
+                          _dev(dense_down, "dense_down").data_ptr(), x.data_ptr(), T,
+                          _dev(y, "y").data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream))
+    _check(rc, "dense_mlp")
+    return y
+
+
+def moe_quantize_int8(w: torch.Tensor, q=None, scale=None, stream=None):
+    """Per-row symmetric int8 of a bf16 tensor [..., cols]: returns (q int8, scale fp32 [...])."""
+    w = _dev(w, "w")
+    cols = w.shape[-1]
+    rows = w.numel() // cols
+    if q is None:
+        q = torch.empty(w.shape, dtype=torch.int8, device=w.device)
+    if scale is None:
+        scale = torch.empty(w.shape[:-1], dtype=torch.float32, device=w.device)
+    rc = _lib().moe_quantize_int8(w.data_ptr(), rows, cols, _dev(q, "q").data_ptr(),
+                                  _dev(scale, "scale").data_ptr(), _stream(stream))
+    _check(rc, "moe_quantize_int8")
+    return q, scale
+
+
+def new_debug(path: int = _abi.MOE_PATH_AUTO, **outputs) -> MoeDebug:
+    """A moe_debug struct; keyword arguments name device tensors for its outputs."""
+    d = MoeDebug()
+    d.path = path
+    for k, t in outputs.items():
+        setattr(d, k, _dev(t, k).data_ptr())
+    return d

@@ -12,16 +12,18 @@ hidden 2816, 128 experts, top-8, expert intermediate 704, dense intermediate
 
 Recipe (per workload seed ``s``):
 
-* ``SeedSequence(s).spawn(2)`` gives two independent PCG64 streams: stream 0
-  draws the weights, stream 1 the activations. The weights of a workload thus
-  do not depend on how many tokens are drawn.
+* ``SeedSequence(s).spawn(3)`` gives three independent PCG64 streams: stream 0
+  draws the weights, stream 1 the activations, stream 2 the skew permutation.
+  The weights of a workload thus do not depend on how many tokens are drawn,
+  and the router weights can be drawn without the experts.
 * Weight stream, in this order, all drawn as float32 and then rounded to
   bfloat16 with round-to-nearest-even unless noted:
   router scale ``1 + 0.1*N(0,1)`` [H]; router weight ``0.02*N`` [E,H];
   per-expert scale ``U(0.5,1.5)`` [E] (kept float32); expert gate_up
   ``0.02*N`` [E,2I,H] drawn expert by expert; expert down ``0.02*N`` [E,H,I]
   expert by expert; dense gate_up ``0.02*N`` [2Id,H]; dense down ``0.02*N``
-  [H,Id]; for the skewed workload only, ``perm = permutation(E)`` and a logit
+  [H,Id].
+* Skew stream (skewed workload only): ``perm = permutation(E)`` and a logit
   bias ``-1.2*ln(perm+1)`` (float32), i.e. the log-probability of a Zipf law
   with exponent 1.2 over a random rank order.
 * Activation stream: ``x = N(0,1)`` [T,H], rounded to bfloat16.
@@ -91,9 +93,7 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def _streams(seed: int):
-    ss = np.random.SeedSequence(seed)
-    w, a = ss.spawn(2)
-    return np.random.Generator(np.random.PCG64(w)), np.random.Generator(np.random.PCG64(a))
+    return [np.random.Generator(np.random.PCG64(c)) for c in np.random.SeedSequence(seed).spawn(3)]
 
 
 def _normal_bf16(rng, shape, std, mean=0.0):
@@ -104,14 +104,23 @@ def _normal_bf16(rng, shape, std, mean=0.0):
     return f32_to_bf16_bits(z)
 
 
-def make_weights(shape: BlockShape, seed: int, skew: bool = False) -> dict:
-    """Draw one layer's weights (see the module docstring for the recipe)."""
-    rng, _ = _streams(seed)
+def make_weights(shape: BlockShape, seed: int, skew: bool = False, router_only: bool = False) -> dict:
+    """Draw one layer's weights (see the module docstring for the recipe).
+
+    ``router_only`` stops after the router tensors (and the skew bias)."""
+    rng, _, rng_skew = _streams(seed)
     H, E, I, Id = shape.hidden, shape.num_experts, shape.expert_inter, shape.dense_inter
     w = {}
     w["router_scale"] = _normal_bf16(rng, (H,), 0.1, mean=1.0)
     w["router_w"] = _normal_bf16(rng, (E, H), 0.02)
     w["per_expert_scale"] = rng.uniform(0.5, 1.5, size=(E,)).astype(np.float32)
+    if skew:
+        perm = rng_skew.permutation(E)
+        w["logit_bias"] = (-1.2 * np.log(perm.astype(np.float64) + 1.0)).astype(np.float32)
+    else:
+        w["logit_bias"] = None
+    if router_only:
+        return w
     gu = np.empty((E, 2 * I, H), dtype=np.uint16)
     for e in range(E):
         gu[e] = _normal_bf16(rng, (2 * I, H), 0.02)
@@ -122,17 +131,12 @@ def make_weights(shape: BlockShape, seed: int, skew: bool = False) -> dict:
     w["expert_down"] = dn
     w["dense_gate_up"] = _normal_bf16(rng, (2 * Id, H), 0.02)
     w["dense_down"] = _normal_bf16(rng, (H, Id), 0.02)
-    if skew:
-        perm = rng.permutation(E)
-        w["logit_bias"] = (-1.2 * np.log(perm.astype(np.float64) + 1.0)).astype(np.float32)
-    else:
-        w["logit_bias"] = None
     return w
 
 
 def make_tokens(shape: BlockShape, seed: int, tokens: int) -> np.ndarray:
     """Draw the activations x [T, H] as bfloat16 bits."""
-    _, rng = _streams(seed)
+    rng = _streams(seed)[1]
     return _normal_bf16(rng, (tokens, shape.hidden), 1.0)
 
 

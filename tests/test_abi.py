@@ -1,0 +1,140 @@
+"""The C-ABI library: it loads, exports every declared symbol, sizes its
+workspace, and rejects bad arguments before launching anything.
+
+No test here launches a kernel: argument checks run on the host before any
+HIP call, so they work without a GPU.
+"""
+import ctypes
+import re
+
+import pytest
+
+from mixture_experts_ffn_amd import _abi
+
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _abi.load_library()
+
+
+def _declared_functions():
+    src = open(_abi.HEADER_PATH).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if not n.startswith("MOE_") and n not in ("if", "defined")))
+
+
+def test_header_declares_the_boundary():
+    assert set(_declared_functions()) == set(_abi.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def _real():
+    return _abi.MoeDims(2816, 128, 8, 704, 2112, 1e-6)
+
+
+def test_workspace_bytes(L):
+    d = _real()
+    n8 = L.moe_workspace_bytes(ctypes.byref(d), 8)
+    n2048 = L.moe_workspace_bytes(ctypes.byref(d), 2048)
+    assert 0 < n8 < n2048
+    assert n8 % 256 == 0 and n2048 % 256 == 0
+    # grouped rows [T*K, H] bf16 dominate at large T
+    assert n2048 >= 2048 * 8 * 2816 * 2 + 2048 * 8 * 704 * 2
+    assert L.moe_workspace_bytes(ctypes.byref(d), 0) > 0
+    assert L.moe_workspace_bytes(ctypes.byref(d), -1) == 0
+    bad = _abi.MoeDims(2816, 128, 9, 704, 2112, 1e-6)
+    assert L.moe_workspace_bytes(ctypes.byref(bad), 8) == 0
+    assert b"top_k" in L.moe_last_error()
+
+
+FAKE = 0x7F0000000000  # 256-aligned host-side value; never dereferenced
+
+
+def _weights(**over):
+    w = _abi.MoeWeights(FAKE, FAKE, FAKE, None, FAKE, FAKE, _abi.MOE_DTYPE_BF16, None, None, FAKE, FAKE)
+    for k, v in over.items():
+        setattr(w, k, v)
+    return w
+
+
+@pytest.mark.parametrize("dims,code", [
+    ((2816, 128, 8, 704, 2112), 0),
+    ((2816, 128, 9, 704, 2112), _abi.MOE_ERR_UNSUPPORTED),
+    ((2816, 300, 8, 704, 2112), _abi.MOE_ERR_UNSUPPORTED),
+    ((2800, 128, 8, 704, 2112), _abi.MOE_ERR_SHAPE),
+    ((2816, 128, 8, 700, 2112), _abi.MOE_ERR_SHAPE),
+    ((2816, 128, 8, 704, 2100), _abi.MOE_ERR_SHAPE),
+    ((2816, 4, 8, 704, 2112), _abi.MOE_ERR_SHAPE),
+    ((2816, 128, 0, 704, 2112), _abi.MOE_ERR_SHAPE),
+])
+def test_dims_validation(L, dims, code):
+    d = _abi.MoeDims(*dims, 1e-6)
+    n = L.moe_workspace_bytes(ctypes.byref(d), 16)
+    assert (n > 0) == (code == 0)
+    if code:
+        w = _weights()
+        rc = L.moe_block(ctypes.byref(d), ctypes.byref(w), FAKE, 16, FAKE, None, FAKE, 1 << 40, None)
+        assert rc == code, L.moe_last_error()
+
+
+def test_block_argument_errors(L):
+    d = _real()
+    ws = L.moe_workspace_bytes(ctypes.byref(d), 8)
+    ok = dict(x=FAKE, T=8, y=FAKE, ws=FAKE, ws_bytes=ws)
+
+    def call(w=None, **kw):
+        a = dict(ok, **kw)
+        w = w or _weights()
+        return L.moe_block(ctypes.byref(d), ctypes.byref(w), a["x"], a["T"], a["y"], None,
+                           a["ws"], a["ws_bytes"], None)
+
+    assert call(x=None) == _abi.MOE_ERR_NULL
+    assert call(y=None) == _abi.MOE_ERR_NULL
+    assert call(ws=None) == _abi.MOE_ERR_NULL
+    assert call(x=FAKE + 8) == _abi.MOE_ERR_ALIGN
+    assert call(ws=FAKE + 16) == _abi.MOE_ERR_ALIGN
+    assert call(ws_bytes=ws - 1) == _abi.MOE_ERR_WORKSPACE
+    assert call(T=-1) == _abi.MOE_ERR_SHAPE
+    assert call(T=_abi.MOE_MAX_TOKENS + 1) == _abi.MOE_ERR_SHAPE
+    assert call(w=_weights(router_w=None)) == _abi.MOE_ERR_NULL
+    assert call(w=_weights(expert_dtype=7)) == _abi.MOE_ERR_UNSUPPORTED
+    # int8 experts need their scales
+    assert call(w=_weights(expert_dtype=_abi.MOE_DTYPE_INT8)) == _abi.MOE_ERR_NULL
+    assert b"gate_up_scale" in L.moe_last_error()
+    # an empty batch is a valid no-op (nothing is launched)
+    assert call(T=0, ws_bytes=L.moe_workspace_bytes(ctypes.byref(d), 0)) == _abi.MOE_OK
+    assert call(T=0, x=None, y=None, ws=None, ws_bytes=0) == _abi.MOE_OK
+
+
+def test_stream_path_limits(L):
+    d = _real()
+    T = _abi.MOE_STREAM_MAX_TOKENS + 1
+    ws = L.moe_workspace_bytes(ctypes.byref(d), T)
+    dbg = _abi.MoeDebug()
+    dbg.path = _abi.MOE_PATH_STREAM
+    w = _weights()
+    rc = L.moe_block(ctypes.byref(d), ctypes.byref(w), FAKE, T, FAKE, ctypes.byref(dbg), FAKE, ws, None)
+    assert rc == _abi.MOE_ERR_UNSUPPORTED
+    dbg.path = 9
+    rc = L.moe_block(ctypes.byref(d), ctypes.byref(w), FAKE, 8, FAKE, ctypes.byref(dbg), FAKE, ws, None)
+    assert rc == _abi.MOE_ERR_UNSUPPORTED
+
+
+def test_route_dense_quant_argument_errors(L):
+    d = _real()
+    ws = L.moe_workspace_bytes(ctypes.byref(d), 8)
+    w = _weights()
+    assert L.moe_route(ctypes.byref(d), ctypes.byref(w), FAKE, 8, None, FAKE, FAKE, ws, None) == _abi.MOE_ERR_NULL
+    assert L.moe_route(ctypes.byref(d), ctypes.byref(w), FAKE, 8, FAKE, FAKE, FAKE, 16, None) == _abi.MOE_ERR_WORKSPACE
+    assert L.dense_mlp(ctypes.byref(d), None, FAKE, FAKE, 8, FAKE, FAKE, ws, None) == _abi.MOE_ERR_NULL
+    assert L.dense_mlp(ctypes.byref(d), FAKE, FAKE, FAKE, 0, FAKE, FAKE, ws, None) == _abi.MOE_OK
+    assert L.moe_quantize_int8(FAKE, 10, 12, FAKE, FAKE, None) == _abi.MOE_ERR_SHAPE
+    assert L.moe_quantize_int8(FAKE, -1, 16, FAKE, FAKE, None) == _abi.MOE_ERR_SHAPE
+    assert L.moe_quantize_int8(FAKE, 0, 16, FAKE, FAKE, None) == _abi.MOE_OK
+    assert L.moe_quantize_int8(FAKE + 4, 4, 16, FAKE, FAKE, None) == _abi.MOE_ERR_ALIGN

@@ -1,0 +1,248 @@
+"""GPU parity of the HIP path against the CPU oracle (through the C ABI).
+
+Integer results (top-k indices, counts, offsets, grouped order, inverse rows,
+int8 codes) must match bit for bit; near-ties of the router (logit gap under
+1e-6) are flagged and then checked for validity instead. The block output must
+reach cosine >= 0.9999 and relative L2 <= 1e-2 (bf16) or 2e-2 (int8 experts).
+Real-shape workloads are checked at their full sizes, in the configuration
+the bench times, on sampled tokens (the block is token-independent).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+import oracle
+from mixture_experts_ffn_amd import (MOE_PATH_GROUPED, MOE_PATH_STREAM, MoEError, dense_mlp,
+                                     moe_block, moe_quantize_int8, moe_route, new_debug)
+from gpu_util import (REL_BF16, REL_INT8, bf16_dev, check_routing, compare_y, dims_of,
+                      oracle_int8_weights, routing_for, to_np, upload, y_f64)
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    return torch.device("cuda:0")
+
+
+def inputs(name, dev, tokens=None):
+    key = (name, tokens)
+    if key not in _CACHE:
+        wl, w, x = moe_synth.make_inputs(name, tokens)
+        lw = upload(w, dev, int8=wl.int8)
+        _CACHE[key] = (wl, w, x, lw, bf16_dev(x, dev))
+    return _CACHE[key]
+
+
+def oracle_route(wl, w, x):
+    s = wl.shape
+    return oracle.route(x, w["router_scale"], w["router_w"], w["per_expert_scale"], s.top_k,
+                        s.rms_eps, w.get("logit_bias"))
+
+
+def sample_tokens(T, n=24, seed=0):
+    if T <= 64:
+        return np.arange(T)
+    rng = np.random.default_rng(seed)
+    s = set(rng.choice(T, size=n - 2, replace=False).tolist()) | {0, T - 1}
+    return np.array(sorted(s))
+
+
+def run_block(wl, lw, xd, path):
+    s = wl.shape
+    T = xd.shape[0]
+    K, E = s.top_k, s.num_experts
+    out = dict(topk_idx=torch.empty((T, K), dtype=torch.int32, device=xd.device),
+               topk_w=torch.empty((T, K), dtype=torch.float32, device=xd.device),
+               counts=torch.empty(E, dtype=torch.int32, device=xd.device),
+               offsets=torch.empty(E + 1, dtype=torch.int32, device=xd.device),
+               perm_token=torch.empty(T * K, dtype=torch.int32, device=xd.device),
+               inv_row=torch.empty(T * K, dtype=torch.int32, device=xd.device))
+    dbg = new_debug(path, **out)
+    y = moe_block(dims_of(s), lw, xd, debug=dbg)
+    torch.cuda.synchronize()
+    assert dbg.path_taken == path
+    return y, {k: to_np(v) for k, v in out.items()}
+
+
+# ----------------------------------------------------------------------------
+def test_quantize_int8_bit_exact(dev):
+    say("case: int8 quantiser, real-shape expert weights (seed 4)")
+    wl, w, x, lw, xd = inputs("int8_decode", dev)
+    q_ref, s_ref = oracle.quantize_int8(w["expert_gate_up"][:16])
+    gu = bf16_dev(w["expert_gate_up"][:16], dev)
+    q, s = moe_quantize_int8(gu)
+    np.testing.assert_array_equal(to_np(q), q_ref)
+    np.testing.assert_array_equal(to_np(s).view(np.uint32), s_ref.view(np.uint32))
+    # the full layer as uploaded for the block
+    qd_ref, sd_ref = oracle.quantize_int8(w["expert_down"])
+    np.testing.assert_array_equal(to_np(lw.expert_down), qd_ref)
+    np.testing.assert_array_equal(to_np(lw.down_scale).view(np.uint32), sd_ref.view(np.uint32))
+    # zero rows and halfway cases
+    row = np.array([[127.0, 2.5, 3.5, -2.5, -0.5, 0.49, 126.5, -127.0]], dtype=np.float32)
+    rb = moe_synth.f32_to_bf16_bits(np.concatenate([row, np.zeros_like(row)]))
+    q2, s2 = moe_quantize_int8(bf16_dev(rb, dev))
+    np.testing.assert_array_equal(to_np(q2)[0], [127, 2, 4, -2, 0, 0, 126, -127])
+    assert to_np(s2)[1] == 0 and (to_np(q2)[1] == 0).all()
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "skew", "int8_prefill"])
+def test_route_parity(dev, name):
+    wl, w, x, lw, xd = inputs(name, dev)
+    say(f"case: moe_route {name} T={x.shape[0]}")
+    idx, wt = moe_route(dims_of(wl.shape), lw, xd)
+    torch.cuda.synchronize()
+    ref = oracle_route(wl, w, x)
+    n_flag = check_routing(to_np(idx), to_np(wt), ref, w["per_expert_scale"])
+    say(f"  flagged near-ties: {n_flag} of {x.shape[0]}")
+
+
+PATH_CASES = [("tiny", MOE_PATH_STREAM), ("tiny", MOE_PATH_GROUPED),
+              ("decode", MOE_PATH_STREAM), ("decode", MOE_PATH_GROUPED),
+              ("prefill", MOE_PATH_GROUPED), ("skew", MOE_PATH_GROUPED),
+              ("int8_decode", MOE_PATH_STREAM), ("int8_decode", MOE_PATH_GROUPED),
+              ("int8_prefill", MOE_PATH_GROUPED)]
+
+
+@pytest.mark.parametrize("name,path", PATH_CASES)
+def test_block_parity(dev, name, path):
+    wl, w, x, lw, xd = inputs(name, dev)
+    s = wl.shape
+    T = x.shape[0]
+    say(f"case: moe_block {name} T={T} path={path}")
+    y, dbg = run_block(wl, lw, xd, path)
+    ref = oracle_route(wl, w, x)
+    check_routing(dbg["topk_idx"], dbg["topk_w"], ref, w["per_expert_scale"])
+    # grouping: exact integer work on the GPU's own indices
+    p = oracle.permute_pairs(dbg["topk_idx"], s.num_experts)
+    for k in ("counts", "offsets", "perm_token", "inv_row"):
+        np.testing.assert_array_equal(dbg[k], p[k], err_msg=k)
+    # block output on sampled tokens
+    toks = sample_tokens(T)
+    r = routing_for(dbg["topk_idx"][toks], {k: v[toks] for k, v in ref.items()}, w["per_expert_scale"])
+    ow = oracle_int8_weights(w) if wl.int8 else w
+    y_ref, _ = oracle.moe_block(x[toks], ow, s.top_k, s.rms_eps,
+                                expert_dtype="int8" if wl.int8 else "bf16", routing=r)
+    cos, rel = compare_y(y_f64(y)[toks], y_ref, REL_INT8 if wl.int8 else REL_BF16)
+    say(f"  tokens checked {len(toks)}  cos {cos:.7f}  rel-L2 {rel:.3e}")
+
+
+def test_skew_routing_collapses_to_few_experts(dev):
+    wl, w, x, lw, xd = inputs("skew", dev)
+    say("case: skew load imbalance")
+    y, dbg = run_block(wl, lw, xd, MOE_PATH_GROUPED)
+    counts = dbg["counts"]
+    assert counts.sum() == x.shape[0] * wl.shape.top_k
+    say(f"  experts with rows: {(counts > 0).sum()}, max rows {counts.max()}")
+    assert counts.max() > 8 * x.shape[0] * wl.shape.top_k / wl.shape.num_experts
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "int8_decode"])
+def test_stream_and_grouped_paths_agree(dev, name):
+    wl, w, x, lw, xd = inputs(name, dev)
+    say(f"case: paths agree {name}")
+    y1, d1 = run_block(wl, lw, xd, MOE_PATH_STREAM)
+    y2, d2 = run_block(wl, lw, xd, MOE_PATH_GROUPED)
+    np.testing.assert_array_equal(d1["topk_idx"], d2["topk_idx"])
+    np.testing.assert_array_equal(d1["perm_token"], d2["perm_token"])
+    a, b = y_f64(y1), y_f64(y2)
+    rel = np.linalg.norm(a - b) / np.linalg.norm(b)
+    assert rel < 5e-3, rel
+
+
+@pytest.mark.parametrize("name,path", [("prefill", MOE_PATH_GROUPED), ("decode", MOE_PATH_STREAM)])
+def test_block_is_deterministic(dev, name, path):
+    wl, w, x, lw, xd = inputs(name, dev)
+    say(f"case: determinism {name} path={path}")
+    y1, _ = run_block(wl, lw, xd, path)
+    y2, _ = run_block(wl, lw, xd, path)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_tokens_are_independent(dev):
+    wl, w, x, lw, xd = inputs("prefill", dev)
+    say("case: batch vs decode slices")
+    y_all, _ = run_block(wl, lw, xd, MOE_PATH_GROUPED)
+    for t0 in (0, 1000, 2040):
+        y8, _ = run_block(wl, lw, xd[t0:t0 + 8].contiguous(), MOE_PATH_STREAM)
+        a, b = y_f64(y8), y_f64(y_all[t0:t0 + 8])
+        assert np.linalg.norm(a - b) / np.linalg.norm(b) < 5e-3
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 64), ("decode", 8), ("prefill", 300)])
+def test_dense_mlp_parity(dev, name, T):
+    wl, w, x, lw, xd = inputs(name, dev)
+    say(f"case: dense_mlp {name} T={T}")
+    xs = xd[:T].contiguous()
+    y = dense_mlp(dims_of(wl.shape), lw.dense_gate_up, lw.dense_down, xs)
+    torch.cuda.synchronize()
+    toks = sample_tokens(T)
+    y_ref = oracle.dense_mlp(x[:T][toks], w["dense_gate_up"], w["dense_down"])
+    compare_y(y_f64(y)[toks], y_ref, REL_BF16)
+
+
+EDGE = {
+    "e1k1": moe_synth.BlockShape(hidden=256, num_experts=1, top_k=1, expert_inter=64, dense_inter=64),
+    "k_eq_e": moe_synth.BlockShape(hidden=512, num_experts=8, top_k=8, expert_inter=128, dense_inter=128),
+    "e256": moe_synth.BlockShape(hidden=256, num_experts=256, top_k=8, expert_inter=64, dense_inter=192),
+}
+
+
+@pytest.mark.parametrize("shape", sorted(EDGE))
+@pytest.mark.parametrize("T,path", [(1, MOE_PATH_STREAM), (1, MOE_PATH_GROUPED), (64, MOE_PATH_STREAM),
+                                    (200, MOE_PATH_GROUPED)])
+def test_edge_shapes(dev, shape, T, path):
+    s = EDGE[shape]
+    say(f"case: edge {shape} T={T} path={path}")
+    wl = moe_synth.Workload(shape, s, T, 21)
+    w = moe_synth.make_weights(s, 21)
+    x = moe_synth.make_tokens(s, 21, T)
+    lw = upload(w, dev)
+    y, dbg = run_block(wl, lw, bf16_dev(x, dev), path)
+    ref = oracle_route(wl, w, x)
+    check_routing(dbg["topk_idx"], dbg["topk_w"], ref, w["per_expert_scale"])
+    p = oracle.permute_pairs(dbg["topk_idx"], s.num_experts)
+    for k in ("counts", "offsets", "perm_token", "inv_row"):
+        np.testing.assert_array_equal(dbg[k], p[k], err_msg=k)
+    r = routing_for(dbg["topk_idx"], ref, w["per_expert_scale"])
+    y_ref, _ = oracle.moe_block(x, w, s.top_k, s.rms_eps, routing=r)
+    compare_y(y_f64(y), y_ref, REL_BF16)
+
+
+@pytest.mark.parametrize("T", [65, 129, 1000])
+def test_ragged_real_shape(dev, T):
+    wl, w, x, lw, xd = inputs("prefill", dev)
+    say(f"case: ragged real shape T={T}")
+    xs = xd[:T].contiguous()
+    y, dbg = run_block(wl, lw, xs, MOE_PATH_GROUPED)
+    ref = oracle_route(wl, w, x[:T])
+    check_routing(dbg["topk_idx"], dbg["topk_w"], ref, w["per_expert_scale"])
+    toks = sample_tokens(T, n=12, seed=T)
+    r = routing_for(dbg["topk_idx"][toks], {k: v[toks] for k, v in ref.items()}, w["per_expert_scale"])
+    y_ref, _ = oracle.moe_block(x[:T][toks], w, 8, 1e-6, routing=r)
+    compare_y(y_f64(y)[toks], y_ref, REL_BF16)
+
+
+def test_empty_batch_and_errors(dev):
+    wl, w, x, lw, xd = inputs("tiny", dev)
+    say("case: empty batch, workspace and path errors")
+    d = dims_of(wl.shape)
+    y = moe_block(d, lw, xd[:0].contiguous())
+    assert y.shape == (0, wl.shape.hidden)
+    small = torch.empty(256, dtype=torch.uint8, device=dev)
+    with pytest.raises(MoEError, match="WORKSPACE"):
+        moe_block(d, lw, xd, workspace=small)
+    with pytest.raises(MoEError, match="UNSUPPORTED"):
+        wl2, w2, x2, lw2, xd2 = inputs("prefill", dev)
+        moe_block(dims_of(wl2.shape), lw2, xd2[:100].contiguous(), debug=new_debug(MOE_PATH_STREAM))

@@ -59,3 +59,12 @@ def test_skew_bias_is_zipf_log_rank():
     b = w["logit_bias"].astype(np.float64)
     ranks = np.sort(np.exp(-b / 1.2))
     np.testing.assert_allclose(ranks, np.arange(1, 129), rtol=1e-5)
+
+
+def test_router_only_draw_matches_full_draw():
+    shp = moe_synth.BlockShape(hidden=256, num_experts=16, top_k=4, expert_inter=64, dense_inter=64)
+    full = moe_synth.make_weights(shp, 7, skew=True)
+    ro = moe_synth.make_weights(shp, 7, skew=True, router_only=True)
+    for k in ("router_scale", "router_w", "per_expert_scale", "logit_bias"):
+        np.testing.assert_array_equal(full[k], ro[k])
+    assert "expert_gate_up" not in ro
