@@ -1,0 +1,385 @@
+#!/usr/bin/env python3
+"""Benchmark of the hybrid MoE FFN block on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+
+A step is one pass of the whole block (router, grouping, experts, dense MLP,
+combine) over one batch of seeded synthetic tokens, on one layer's weights.
+Consecutive steps cycle through several distinct copies of the layer's
+weights (``--layers``, default 4, i.e. > 6 GB), as consecutive layers of a
+model would, so no step finds the previous step's weights in the 256 MB
+last-level cache. Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line. ``value`` is tokens/s of the primary workload (decode,
+T=8, by default); the dominant kernel's roofline is measured live with HIP
+events recorded on the library's stream around that kernel in every timed
+step. The prefill (T=2048) numbers the metric also names are reported under
+``prefill``. ``cpu_baseline`` times the CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import moe_synth  # noqa: E402
+
+METRIC = "MoE FFN layer tokens/s: decode T=8 (HBM GB/s), prefill T=2048 (MFMA %)"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+
+# the pages' whole-model figures (context only, other hardware)
+PAGE_CONTEXT = [
+    {"figure": "prefill 77 ms (whole model, one-line prompt)", "hardware": "AWS inf2.24xlarge, 8 NeuronCores, TP=8, bf16",
+     "page": "Gemma-4 26B-A4B (MoE) on AWS Inferentia2 -- Tensor-Parallel (TP=8), intro"},
+    {"figure": "prefill 84 ms, decode 12.8 tok/s (whole model, 19-token prompt)",
+     "hardware": "NVIDIA H200, onnxruntime-gpu 1.29, fp16",
+     "page": "Gemma-4 26B-A4B-it -- ONNX MoE text decoder (fp16, CUDA), Numerical parity section"},
+]
+
+
+# ---------------------------------------------------------------- HIP events
+class HipEvents:
+    """hipEvent_t through the HIP runtime the process already uses."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7", mode=ctypes.RTLD_GLOBAL)
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> int:
+        ev = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return ev.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        self.hip.hipEventSynchronize(ctypes.c_void_p(b))
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+
+def _sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+# ---------------------------------------------------------------- algorithmic work
+def algorithmic(shape: moe_synth.BlockShape, T: int, n_active: int, int8: bool):
+    """Bytes and FLOPs of the routed block (only the touched experts' weights,
+    each read once; x read and y written once; intermediates not counted)."""
+    H, E, K, I, Id = shape.hidden, shape.num_experts, shape.top_k, shape.expert_inter, shape.dense_inter
+    wb = 1 if int8 else 2
+    gu_expert = 2 * I * H * wb + (2 * I * 4 if int8 else 0)
+    dn_expert = H * I * wb + (H * 4 if int8 else 0)
+    dense = (2 * Id * H + H * Id) * 2
+    router = E * H * 2 + H * 2 + E * 4
+    bytes_total = n_active * (gu_expert + dn_expert) + dense + router + 2 * T * H * 2
+    flops = T * (2 * E * H + K * (2 * H * 2 * I + 2 * I * H) + 2 * H * 2 * Id + 2 * Id * H)
+    return {"bytes": bytes_total, "flops": flops, "gu_expert": gu_expert, "dn_expert": dn_expert}
+
+
+def stage_work(stage: str, shape, T, n_active, int8):
+    """Algorithmic bytes and FLOPs of one launch of a stage's kernel, with the
+    units it processes (weights of the touched experts read once, activations
+    and outputs once; no re-reads, no padding)."""
+    H, E, K, I, Id = shape.hidden, shape.num_experts, shape.top_k, shape.expert_inter, shape.dense_inter
+    TK = T * K
+    wb = 1 if int8 else 2
+    gu_w = 2 * I * H * wb + (2 * I * 4 if int8 else 0)
+    dn_w = H * I * wb + (H * 4 if int8 else 0)
+    router_w = E * H * 2 + H * 2
+    x, y = T * H * 2, T * H * 2
+    table = {
+        "decode_front": (router_w + 2 * Id * H * 2 + x + T * E * 4 + T * Id * 2,
+                         2 * T * E * H + 2 * T * H * 2 * Id,
+                         "router weights + dense gate_up + x + logits + hd"),
+        "decode_route": (T * E * 4 + E * 4 + TK * 20, 0, "logits + routing tables"),
+        "decode_experts_gateup": (n_active * gu_w + x + TK * I * 2, 2 * TK * H * 2 * I,
+                                  f"{n_active} experts' gate_up ({gu_w} B each) + x + h"),
+        "decode_down": (n_active * dn_w + H * Id * 2 + TK * I * 2 + T * Id * 2,
+                        2 * TK * I * H + 2 * T * Id * H,
+                        f"{n_active} experts' down ({dn_w} B each) + dense down + h + hd"),
+        "decode_combine": ((TK + T) * H * 4 + y, 2 * TK * H, "fp32 partial rows + y"),
+        "router_logits": (router_w + x + T * E * 4, 2 * T * E * H, "router weights + x + logits"),
+        "router_topk": (T * E * 4 + E * 4 + TK * 8, 0, "logits + top-k"),
+        "permute": (TK * 8 + TK * 12 + E * 8, 0, "top-k + grouping tables"),
+        "gemm_gateup_experts": (n_active * gu_w + x + TK * I * 2, 2 * TK * H * 2 * I,
+                                f"{n_active} experts' gate_up ({gu_w} B each) + x + h"),
+        "gemm_gateup_dense": (2 * Id * H * 2 + x + T * Id * 2, 2 * T * H * 2 * Id,
+                              "dense gate_up + x + hd"),
+        "gemm_down_experts": (n_active * dn_w + TK * I * 2 + TK * H * 2, 2 * TK * I * H,
+                              f"{n_active} experts' down ({dn_w} B each) + h + rows"),
+        "gemm_dense_down_combine": (H * Id * 2 + T * Id * 2 + TK * H * 2 + y, 2 * T * Id * H,
+                                    "dense down + hd + expert rows + y"),
+    }
+    return table[stage]
+
+
+# ---------------------------------------------------------------- workloads
+def run_workload(name, steps, warmup, layers, dev, ev: HipEvents, log):
+    import torch
+    from mixture_experts_ffn_amd import BlockCall, moe_quantize_int8, new_debug, _abi
+    from mixture_experts_ffn_amd.ops import BlockDims, LayerWeights
+
+    wl = moe_synth.WORKLOADS[name]
+    s = wl.shape
+    T = wl.tokens
+    t0 = time.time()
+    w = moe_synth.make_weights(s, wl.seed, wl.skew)
+    x = moe_synth.make_tokens(s, wl.seed, T)
+    log(f"[bench] {name}: generated inputs in {time.time() - t0:.1f}s")
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def f32(a):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+
+    base = LayerWeights(router_scale=bf(w["router_scale"]), router_w=bf(w["router_w"]),
+                        per_expert_scale=f32(w["per_expert_scale"]),
+                        expert_gate_up=bf(w["expert_gate_up"]), expert_down=bf(w["expert_down"]),
+                        dense_gate_up=bf(w["dense_gate_up"]), dense_down=bf(w["dense_down"]),
+                        logit_bias=f32(w["logit_bias"]))
+    del w
+    if wl.int8:
+        base.expert_gate_up, base.gate_up_scale = moe_quantize_int8(base.expert_gate_up)
+        base.expert_down, base.down_scale = moe_quantize_int8(base.expert_down)
+    copies = [base]
+    for _ in range(layers - 1):
+        copies.append(LayerWeights(**{k: (None if v is None else v.clone())
+                                      for k, v in vars(base).items()}))
+    dims = BlockDims(s.hidden, s.num_experts, s.top_k, s.expert_inter, s.dense_inter, s.rms_eps)
+    xd = bf(x)
+    y = torch.empty((T, s.hidden), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, __import__("mixture_experts_ffn_amd").moe_workspace_bytes(dims, T)),
+                     dtype=torch.uint8, device=dev)
+    calls = [BlockCall(dims, c, xd, y=y, workspace=ws) for c in copies]
+    torch.cuda.synchronize()
+
+    # one call with the parity outputs: routing statistics and the stage list
+    counts = torch.empty(s.num_experts, dtype=torch.int32, device=dev)
+    dbg = new_debug(counts=counts)
+    stage_ev = [ev.create() for _ in range(_abi.MOE_MAX_STAGES + 1)]
+    for i, e in enumerate(stage_ev):
+        dbg.stage_event[i] = e
+    calls[0](dbg)
+    torch.cuda.synchronize()
+    n_stages = dbg.n_stages
+    stage_names = [dbg.stage_name[i].decode() for i in range(n_stages)]
+    path = dbg.path_taken
+    cnt = counts.cpu().numpy()
+    n_active = int((cnt > 0).sum())
+
+    # per-stage breakdown (all stage events), outside the timed region
+    per_stage = np.zeros(n_stages)
+    n_brk = 10
+    for i in range(n_brk):
+        calls[i % layers](dbg)
+        torch.cuda.synchronize()
+        for j in range(n_stages):
+            per_stage[j] += ev.elapsed_ms(stage_ev[j], stage_ev[j + 1])
+    per_stage /= n_brk
+    dom = int(np.argmax(per_stage))
+    dom_name = stage_names[dom]
+
+    # timed region: the whole block, nothing else on the stream
+    for i in range(warmup):
+        calls[i % layers]()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(steps):
+        calls[i % layers]()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_step = elapsed * 1e3 / steps
+
+    # dominant kernel: HIP events on the library's stream around that kernel in
+    # every step of a second timed run (an event marker costs a few us of
+    # stream time, so it is kept out of the run above)
+    pairs = [(ev.create(), ev.create()) for _ in range(steps)]
+    dbgs = []
+    for a, b in pairs:
+        d = new_debug()
+        d.stage_event[dom] = a
+        d.stage_event[dom + 1] = b
+        dbgs.append(d)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        calls[i % layers](dbgs[i])
+    torch.cuda.synchronize()
+    dom_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs]))
+
+    work = algorithmic(s, T, n_active, wl.int8)
+    dbytes, dflops, dunits = stage_work(dom_name, s, T, n_active, wl.int8)
+    res = {
+        "workload": name, "T": T, "path": {1: "stream", 2: "grouped"}.get(path, path),
+        "ms_per_step": ms_step, "tokens_per_s": T / (ms_step * 1e-3),
+        "experts_touched": n_active, "max_rows_per_expert": int(cnt.max()),
+        "block_bytes": work["bytes"], "block_flops": work["flops"],
+        "block_gbs": work["bytes"] / (ms_step * 1e-3) / 1e9,
+        "block_tflops": work["flops"] / (ms_step * 1e-3) / 1e12,
+        "stages_us": {n: round(float(t) * 1e3, 2) for n, t in zip(stage_names, per_stage)},
+        "stages_gbs": {n: round(stage_work(n, s, T, n_active, wl.int8)[0] / (float(t) * 1e-3) / 1e9, 1)
+                       for n, t in zip(stage_names, per_stage)},
+        "dominant": {"kernel": dom_name, "avg_us": dom_ms * 1e3, "bytes": dbytes, "flops": dflops,
+                     "units": dunits},
+    }
+    res["block_hbm_frac"] = res["block_gbs"] / HBM_PEAK_GBS
+    res["block_mfma_frac"] = res["block_tflops"] / MFMA_BF16_PEAK_TFLOPS
+    log(f"[bench] {name}: {ms_step * 1e3:.1f} us/step, {res['tokens_per_s']:.0f} tok/s, "
+        f"{res['block_gbs']:.0f} GB/s, dominant {dom_name} {dom_ms * 1e3:.1f} us, stages {res['stages_us']} "
+        f"GB/s {res['stages_gbs']}")
+    del calls, copies, base
+    torch.cuda.empty_cache()
+    return res
+
+
+def roofline_for(res, bound):
+    d = res["dominant"]
+    sec = d["avg_us"] * 1e-6
+    if bound == "hbm":
+        ach = d["bytes"] / sec / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": ach / HBM_PEAK_GBS}
+    else:
+        ach = d["flops"] / sec / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / MFMA_BF16_PEAK_TFLOPS}
+    roof["kernel"] = d["kernel"]
+    roof["traffic"] = measured_traffic(d["kernel"], res["workload"])
+    return roof
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current source of that kernel (else null)."""
+    try:
+        rec = json.load(open(PROFILE_TRAFFIC))
+    except (OSError, ValueError):
+        return None
+    for r in rec.get("kernels", []):
+        if r.get("kernel") == kernel and r.get("workload") == workload:
+            src = os.path.join(ROOT, r["source"])
+            if os.path.exists(src) and _sha(src) == r.get("source_sha"):
+                return r.get("bytes_per_launch")
+    return None
+
+
+def cpu_baseline(name, budget_s, log):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle
+    from threadpoolctl import threadpool_info, threadpool_limits
+    wl = moe_synth.WORKLOADS[name]
+    s = wl.shape
+    T = min(wl.tokens, 8)
+    w = moe_synth.make_weights(s, wl.seed, wl.skew)
+    x = moe_synth.make_tokens(s, wl.seed, wl.tokens)[:T]
+    cores = min(os.cpu_count() or 1, 16)   # the machine's CPU share for one GPU
+    with threadpool_limits(limits=cores):
+        used = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.moe_block(x, w, s.top_k, s.rms_eps)
+            n += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+    v = n * T / dt
+    log(f"[bench] cpu oracle: {n} calls x {T} tokens in {dt:.1f}s -> {v:.2f} tok/s on {used} threads")
+    return {"value": v, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+            "sample": f"{n} oracle calls of the {name} workload's first {T} tokens (fp64 numpy, "
+                      f"same seeded weights), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode", choices=sorted(moe_synth.WORKLOADS))
+    ap.add_argument("--layers", type=int, default=4, help="distinct weight copies cycled per step")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the T=2048 secondary line")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0 = skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (the block is measured on one MI355X); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    from mixture_experts_ffn_amd import load_library
+    load_library()
+    dev = torch.device("cuda:0")
+    ev = HipEvents()
+
+    primary = run_workload(args.workload, args.steps, args.warmup, args.layers, dev, ev, log)
+    bound = "hbm" if primary["path"] == "stream" or primary["workload"] in ("prefill",) else "mfma"
+    roof = roofline_for(primary, bound)
+    out = {
+        "metric": METRIC,
+        "value": primary["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": primary["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if primary["path"] == "stream" else "bf16",
+        "data": "synthetic: seeded random tokens and random-init weights of the real block shape",
+        "config": {"workload": f"{args.workload}: {moe_synth.WORKLOADS[args.workload].note}",
+                   "T": primary["T"], "hidden": 2816 if args.workload != "tiny" else 512,
+                   "experts": moe_synth.WORKLOADS[args.workload].shape.num_experts,
+                   "top_k": moe_synth.WORKLOADS[args.workload].shape.top_k,
+                   "expert_inter": moe_synth.WORKLOADS[args.workload].shape.expert_inter,
+                   "dense_inter": moe_synth.WORKLOADS[args.workload].shape.dense_inter,
+                   "seed": moe_synth.WORKLOADS[args.workload].seed,
+                   "layers_cycled": args.layers, "path": primary["path"]},
+        "roofline": roof,
+        "block": {k: primary[k] for k in ("block_bytes", "block_gbs", "block_hbm_frac", "block_flops",
+                                          "block_tflops", "block_mfma_frac", "experts_touched",
+                                          "stages_us", "stages_gbs", "dominant")},
+    }
+    if args.workload == "decode" and not args.no_prefill:
+        pre = run_workload("prefill", max(10, args.steps // 4), max(3, args.warmup // 4), args.layers,
+                           dev, ev, log)
+        out["prefill"] = {k: pre[k] for k in ("T", "path", "ms_per_step", "tokens_per_s", "block_gbs",
+                                              "block_hbm_frac", "block_tflops", "block_mfma_frac",
+                                              "experts_touched", "stages_us", "stages_gbs", "dominant")}
+        out["prefill"]["roofline"] = roofline_for(pre, "hbm")
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds, log)
+    else:
+        out["cpu_baseline"] = None
+    out["context"] = PAGE_CONTEXT
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -5,5 +5,6 @@ ABI of ``include/moe.h``); this package only marshals torch tensors to it.
 """
 from ._abi import (MOE_DTYPE_BF16, MOE_DTYPE_INT8, MOE_PATH_AUTO, MOE_PATH_GROUPED,  # noqa: F401
                    MOE_PATH_STREAM, MOE_STREAM_MAX_TOKENS, load_library)
-from .ops import (BlockDims, LayerWeights, MoEError, dense_mlp, moe_block, moe_quantize_int8,  # noqa: F401
+from .ops import (BlockCall, BlockDims, LayerWeights, MoEError, dense_mlp, moe_block,  # noqa: F401
+                  moe_quantize_int8,
                   moe_route, moe_workspace_bytes, new_debug)

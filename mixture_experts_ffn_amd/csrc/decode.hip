@@ -1,0 +1,571 @@
+// Small-batch (decode) path of the MoE FFN block on gfx950.
+//
+// With a handful of tokens per expert the block is bound by reading the
+// touched experts' weights from HBM once. Four launches, each filling the chip:
+//
+//   K1 decode_front: router logits (two experts per wavefront) side by side
+//      with the dense MLP's gate/up rows; both only need x.
+//   K2 decode_route: one workgroup: softmax/top-k of every token (ONNX export
+//      card, "Truthful graph contracts", row "Router") and the grouping of the
+//      routed pairs by expert (counts, offsets, grouped rows, inverse rows,
+//      list of touched experts).
+//   K3 decode_experts_gateup: 8 gate rows (+ the 8 matching up rows) of one
+//      touched expert per workgroup; every weight row is read exactly once
+//      with wide non-temporal loads issued before anything waits, then dotted
+//      with the expert's tokens staged in LDS.
+//   K4 decode_down: output-stationary. A workgroup owns 8 output features and
+//      reads those rows of every touched expert's down matrix (double-buffered
+//      in registers) and of the dense down matrix, then forms
+//      y = dense + sum_k w_k * expert_k in k order (row "MoE topology") without
+//      a rows buffer and without atomics.
+// int8 experts (int8 experts card, "How it works") are read as int8, widened
+// exactly in registers, and their per-row scale multiplies the dot product.
+#include "common.h"
+#include "kernels.h"
+#include "topk.h"
+#include "../../include/moe.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kGURows = 8;         // gate rows per gate/up work item: 2 per wavefront
+constexpr int kPass = 4;           // tokens staged per pass
+constexpr int kRouterExperts = 8;  // experts per router work item: 2 per wavefront
+constexpr int kRouteThreads = 1024;
+constexpr int kMaxPairs = MOE_STREAM_MAX_TOKENS * MOE_MAX_TOPK;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 ld_nt16(const void* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_nt8(const void* p) {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    return make_uint2(v.x, v.y);
+}
+// 8 weights at element offset `col` of a weight matrix: 16 bytes of bf16, or
+// 8 bytes of int8 kept in .x/.y
+template <bool INT8>
+__device__ __forceinline__ uint4 load_w8(const void* w, int64_t col) {
+    if (INT8) {
+        const uint2 v = ld_nt8(reinterpret_cast<const int8_t*>(w) + col);
+        return make_uint4(v.x, v.y, 0u, 0u);
+    }
+    return ld_nt16(reinterpret_cast<const uint16_t*>(w) + col);
+}
+template <bool INT8>
+__device__ __forceinline__ void unpack_w8(const uint4& v, float* f) {
+    if (INT8) unpack8_i8(make_uint2(v.x, v.y), f);
+    else unpack8(v, f);
+}
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+
+// acc + a.lo*b.lo + a.hi*b.hi on packed bf16 pairs (v_dot2c_f32_bf16, fp32
+// accumulation; no unpacking of either operand)
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+__device__ __forceinline__ float dot8_bf16(const uint4& a, const uint4& b, float acc) {
+    acc = dot2(a.x, b.x, acc);
+    acc = dot2(a.y, b.y, acc);
+    acc = dot2(a.z, b.z, acc);
+    return dot2(a.w, b.w, acc);
+}
+// 8 int8 (in .x/.y) -> 8 bf16 (exact: |q| <= 127 fits the bf16 significand)
+__device__ __forceinline__ uint4 i8x8_to_bf16(const uint4& v) {
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t word = q < 2 ? v.x : v.y;
+        const int sh = (q & 1) * 16;
+        const float lo = (float)(int8_t)((word >> sh) & 0xFF);
+        const float hi = (float)(int8_t)((word >> (sh + 8)) & 0xFF);
+        o[q] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+// weights as packed bf16, whatever their storage
+template <bool INT8>
+__device__ __forceinline__ uint4 as_bf16(const uint4& v) {
+    if (INT8) return i8x8_to_bf16(v);
+    return v;
+}
+
+__device__ __forceinline__ float dot8(const float* a, const float* b) {
+    float s = a[0] * b[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) s += a[i] * b[i];
+    return s;
+}
+
+// Stage x rows tok(pass .. pass+nt) into LDS as [kPass][H/8] 16-byte chunks.
+// Every load is unconditional (indices clamped into range) so that all of them
+// are in flight together; only the LDS stores are predicated.
+template <int NJ>
+__device__ __forceinline__ void stage_x(const uint16_t* __restrict__ x, int H, const int32_t* toks,
+                                        int pass, int nt, uint4* xs) {
+    const int hc8 = H >> 3;
+    const int n = nt * hc8;
+    constexpr int kPer = (kPass * 32 * NJ + kThreads - 1) / kThreads;  // chunks per thread
+    int64_t tok[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int i = min((int)threadIdx.x + q * kThreads, n - 1);
+        const int r = i / hc8;
+        tok[q] = toks ? (int64_t)toks[pass + r] : (int64_t)(pass + r);
+    }
+    uint4 v[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int i = min((int)threadIdx.x + q * kThreads, n - 1);
+        const int c = i - (i / hc8) * hc8;
+        v[q] = reinterpret_cast<const uint4*>(x + tok[q] * H)[c];
+    }
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int i = threadIdx.x + q * kThreads;
+        if (i < n) xs[i] = v[q];
+    }
+}
+
+// Copy n (1 <= n <= KPER * 256) contiguous 16-byte chunks into LDS; loads are
+// unconditional (indices clamped into range) so that all are in flight.
+template <int KPER>
+__device__ __forceinline__ void stage_rows(const uint4* __restrict__ src, int n, uint4* dst) {
+    uint4 v[KPER];
+#pragma unroll
+    for (int q = 0; q < KPER; ++q) v[q] = src[min((int)threadIdx.x + q * kThreads, n - 1)];
+#pragma unroll
+    for (int q = 0; q < KPER; ++q) {
+        const int i = (int)threadIdx.x + q * kThreads;
+        if (i < n) dst[i] = v[q];
+    }
+}
+
+// Gate/up rows [r0, r0 + kGURows) of one [2*inter, H] matrix against the
+// tokens tok(0 .. n_rows): out[p][r] = gelu_tanh(gate_r . x_p) * (up_r . x_p).
+// Lanes 0..31 of a wavefront take a gate row, lanes 32..63 the matching up row;
+// each lane owns NJ 8-element chunks of the row.
+template <int NJ, bool INT8>
+__device__ __forceinline__ void gateup_item(const uint16_t* __restrict__ x, int H, const void* W, const float* Ws,
+                            int inter, int r0, const int32_t* toks, int n_rows,
+                            uint16_t* __restrict__ out, uint4* xs) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int half = lane >> 5, hl = lane & 31;
+    const int ra = r0 + wave * 2, rb = ra + 1;
+    const int64_t rowa = half ? (int64_t)inter + ra : ra;
+    const int64_t rowb = half ? (int64_t)inter + rb : rb;
+    // every weight load of this wavefront is in flight before anything waits
+    uint4 wa[NJ], wb[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int64_t col = (int64_t)(hl + 32 * j) * 8;
+        wa[j] = load_w8<INT8>(W, rowa * H + col);
+        wb[j] = load_w8<INT8>(W, rowb * H + col);
+    }
+    float sa = 1.f, sb = 1.f;
+    if (INT8) {
+        sa = Ws[rowa];
+        sb = Ws[rowb];
+    }
+    const int hc8 = H >> 3;
+    for (int pass = 0; pass < n_rows; pass += kPass) {
+        const int nt = min(kPass, n_rows - pass);
+        __syncthreads();  // previous pass done with xs
+        stage_x<NJ>(x, H, toks, pass, nt, xs);
+        __syncthreads();
+#pragma unroll 1
+        for (int n = 0; n < nt; ++n) {
+            const uint4* xr = xs + n * hc8 + hl;
+            float acc_a = 0.f, acc_b = 0.f;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const uint4 xv = xr[32 * j];
+                acc_a = dot8_bf16(as_bf16<INT8>(wa[j]), xv, acc_a);
+                acc_b = dot8_bf16(as_bf16<INT8>(wb[j]), xv, acc_b);
+            }
+            const float va = wave_sum<32>(acc_a) * sa;  // half 0: gate row, half 1: up row
+            const float vb = wave_sum<32>(acc_b) * sb;
+            const float oa = __shfl_xor(va, 32, kWave);
+            const float ob = __shfl_xor(vb, 32, kWave);
+            if (lane == 0) out[(int64_t)(pass + n) * inter + ra] = f32_to_bf16(gelu_tanh(va) * oa);
+            if (lane == 1) out[(int64_t)(pass + n) * inter + rb] = f32_to_bf16(gelu_tanh(vb) * ob);
+        }
+    }
+}
+
+// Router logits of experts [e0, e0 + 8) for all T tokens: two experts per
+// wavefront (one per half). logit = (sum_h x*s*W) * rms(x)^-1 * H^-0.5 + bias,
+// all fp32; the sum of squares comes from the same staged x.
+template <int NJ>
+__device__ __forceinline__ void router_item(const uint16_t* __restrict__ x, int H, const uint16_t* __restrict__ scale,
+                            const uint16_t* __restrict__ wr, const float* __restrict__ bias, int E,
+                            int t0, int t1, float eps, float inv_sqrt_h, int e0,
+                            float* __restrict__ logits, uint4* xs) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int half = lane >> 5, hl = lane & 31;
+    const int e = e0 + wave * 2 + half;
+    const bool live = e < E;
+    uint4 wv[NJ], sv[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int c = hl + 32 * j;
+        wv[j] = live ? reinterpret_cast<const uint4*>(wr + (int64_t)e * H)[c] : make_uint4(0, 0, 0, 0);
+        sv[j] = reinterpret_cast<const uint4*>(scale)[c];
+    }
+    const int hc8 = H >> 3;
+    const float b = (live && bias) ? bias[e] : 0.f;
+    for (int pass = t0; pass < t1; pass += kPass) {
+        const int nt = min(kPass, t1 - pass);
+        __syncthreads();
+        stage_x<NJ>(x, H, nullptr, pass, nt, xs);
+        __syncthreads();
+#pragma unroll 1
+        for (int n = 0; n < nt; ++n) {
+            const uint4* xr = xs + n * hc8 + hl;
+            float acc = 0.f, ss = 0.f;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                float xf[8], fw[8], fs[8];
+                unpack8(xr[32 * j], xf);
+                unpack8(wv[j], fw);
+                unpack8(sv[j], fs);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    acc += (fw[i] * fs[i]) * xf[i];
+                    ss += xf[i] * xf[i];
+                }
+            }
+            const float d = wave_sum<32>(acc);
+            const float q = wave_sum<32>(ss);
+            if (live && hl == 0) {
+                const float rn = 1.0f / sqrtf(q / (float)H + eps);
+                logits[(int64_t)(pass + n) * E + e] = d * (rn * inv_sqrt_h) + b;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- K1
+template <int NJ>
+__global__ __launch_bounds__(kThreads) void decode_front_kernel(StreamArgs a, const uint16_t* scale,
+                                                               const uint16_t* wr, const float* bias,
+                                                               float eps, float inv_sqrt_h,
+                                                               float* logits) {
+    extern __shared__ uint4 xs[];
+    // router items: (group of 8 experts) x (pass of kPass tokens)
+    const int n_groups = (a.E + kRouterExperts - 1) / kRouterExperts;
+    const int n_pass = (a.T + kPass - 1) / kPass;
+    const int n_router = n_groups * n_pass;
+    const int b = blockIdx.x;
+    if (b < n_router) {
+        const int g = b % n_groups, tp = b / n_groups;
+        router_item<NJ>(a.x, a.H, scale, wr, bias, a.E, tp * kPass, min(a.T, (tp + 1) * kPass), eps,
+                        inv_sqrt_h, g * kRouterExperts, logits, xs);
+    } else {
+        gateup_item<NJ, false>(a.x, a.H, a.dgu, nullptr, a.Id, (b - n_router) * kGURows, nullptr,
+                               a.T, a.hd, xs);
+    }
+}
+
+// ---------------------------------------------------------------- K3
+template <int NJ, bool INT8>
+__global__ __launch_bounds__(kThreads) void decode_experts_gateup_kernel(StreamArgs a) {
+    extern __shared__ uint4 xs[];
+    const int ipe = a.I / kGURows;  // items per expert
+    const int slot = blockIdx.x / ipe, g = blockIdx.x - slot * ipe;
+    if (slot >= *a.n_active) return;
+    const int e = a.active[slot];
+    const int p0 = a.offsets[e], n = a.offsets[e + 1] - p0;
+    const int64_t wstride = (int64_t)2 * a.I * a.H;
+    const void* W = INT8 ? (const void*)((const int8_t*)a.gu + e * wstride)
+                         : (const void*)((const uint16_t*)a.gu + e * wstride);
+    const float* Ws = INT8 ? a.gu_scale + (int64_t)e * 2 * a.I : nullptr;
+    gateup_item<NJ, INT8>(a.x, a.H, W, Ws, a.I, g * kGURows, a.perm_token + p0, n,
+                          a.h + (int64_t)p0 * a.I, xs);
+}
+
+// ---------------------------------------------------------------- K2
+// One workgroup: top-k of every token (one wavefront per token), then the
+// stable grouping by expert. With T <= 64 every token is one bit of a 64-bit
+// mask per expert: the rank of pair (t, k) within its expert is the number of
+// lower tokens in that expert's mask, the expert's row count its popcount.
+__global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(StreamArgs a, const float* logits,
+                                                                    const float* pes,
+                                                                    int32_t* topk_idx, float* topk_w) {
+    __shared__ int s_idx[kMaxPairs];
+    __shared__ float s_w[kMaxPairs];
+    __shared__ unsigned long long s_mask[kMaxExperts];
+    __shared__ int s_off[kMaxExperts + 1];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int T = a.T, K = a.K, E = a.E, TK = T * K;
+    for (int e = tid; e < E; e += kRouteThreads) s_mask[e] = 0ull;
+    for (int t = wave; t < T; t += kRouteThreads / kWave) {
+        int ik[kMaxTopK];
+        float wk[kMaxTopK];
+        wave_topk(logits + (int64_t)t * E, pes, E, K, lane, ik, wk);
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k)
+            if (k < K && lane == k) {
+                s_idx[t * K + k] = ik[k];
+                s_w[t * K + k] = wk[k];
+                topk_idx[(int64_t)t * K + k] = ik[k];
+                topk_w[(int64_t)t * K + k] = wk[k];
+            }
+    }
+    __syncthreads();
+    if (tid < TK) atomicOr(&s_mask[s_idx[tid]], 1ull << (tid / K));
+    __syncthreads();
+    if (wave == 0) {
+        int c[4], act[4], csum = 0, asum = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane * 4 + i;
+            c[i] = e < E ? __popcll(s_mask[e]) : 0;
+            act[i] = c[i] > 0;
+            csum += c[i];
+            asum += act[i];
+        }
+        int ci = csum, ai = asum;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int u = __shfl_up(ci, off, kWave), v = __shfl_up(ai, off, kWave);
+            if (lane >= off) {
+                ci += u;
+                ai += v;
+            }
+        }
+        int crun = ci - csum, arun = ai - asum;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane * 4 + i;
+            if (e < E) {
+                s_off[e] = crun;
+                a.offsets[e] = crun;
+                a.counts[e] = c[i];
+                if (act[i]) a.active[arun] = e;
+            }
+            crun += c[i];
+            arun += act[i];
+        }
+        if (lane == kWave - 1) {
+            a.offsets[E] = ci;
+            *a.n_active = ai;
+        }
+    }
+    __syncthreads();
+    if (tid < TK) {
+        const int e = s_idx[tid], t = tid / K;
+        const int pos = s_off[e] + __popcll(s_mask[e] & ((1ull << t) - 1ull));
+        a.perm_token[pos] = t;
+        a.perm_w[pos] = s_w[tid];
+        a.inv_row[tid] = pos;
+    }
+}
+
+// ---------------------------------------------------------------- K4
+// Down projections as independent work items of one touched expert's down
+// matrix (or of the dense down matrix). LPR lanes share a row (8 for the
+// 704-wide expert rows, 32 for the 2112-wide dense rows), each lane owning
+// chunks sub + LPR*j. Each weight row is read once; the item's token rows of h
+// (or hd) are staged in LDS. Outputs are fp32 partial rows: part[p][row] for
+// grouped row p, dpart[t][row] for the dense MLP.
+template <int LPR, int MAXC, bool INT8>
+__device__ __forceinline__ void down_item(const void* W, const float* Ws, int inter, int H, int r0,
+                                          const uint16_t* __restrict__ hrows, int n_rows,
+                                          float* __restrict__ out, uint4* hs) {
+    constexpr int kRPW = kWave / LPR;  // rows per wavefront
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int sub = lane % LPR;
+    const int64_t row = r0 + wave * kRPW + lane / LPR;
+    const int hc8 = inter >> 3;
+    uint4 w[MAXC];
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+        const int c = sub + LPR * j;
+        if (c < hc8) w[j] = load_w8<INT8>(W, row * inter + (int64_t)c * 8);
+    }
+    const float sc = INT8 ? Ws[row] : 1.f;
+    for (int pass = 0; pass < n_rows; pass += kPass) {
+        const int nt = min(kPass, n_rows - pass);
+        __syncthreads();
+        constexpr int kPer = (kPass * LPR * MAXC + kThreads - 1) / kThreads;
+        stage_rows<kPer>(reinterpret_cast<const uint4*>(hrows + (int64_t)pass * inter), nt * hc8, hs);
+        __syncthreads();
+#pragma unroll 1
+        for (int n = 0; n < nt; ++n) {
+            float acc = 0.f;
+#pragma unroll
+            for (int j = 0; j < MAXC; ++j) {
+                const int c = sub + LPR * j;
+                if (c < hc8) acc = dot8_bf16(as_bf16<INT8>(w[j]), hs[n * hc8 + c], acc);
+            }
+#pragma unroll
+            for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off, kWave);
+            if (sub == 0) out[(int64_t)(pass + n) * H + row] = acc * sc;
+        }
+    }
+}
+
+constexpr int kExpertDownRows = 32;  // rows per expert down item (8 lanes per row)
+constexpr int kDenseDownRows = 8;    // rows per dense down item (32 lanes per row)
+
+template <int MAXIC, int MAXDC, bool INT8>
+__global__ __launch_bounds__(kThreads) void decode_down_kernel(StreamArgs a) {
+    extern __shared__ uint4 hs[];  // [kPass][max(I, Id)/8]
+    const int ipe = a.H / kExpertDownRows;
+    const int expert_items = a.max_active * ipe;
+    const int b = blockIdx.x;
+    if (b < expert_items) {
+        const int slot = b / ipe, g = b - slot * ipe;
+        if (slot >= *a.n_active) return;
+        const int e = a.active[slot];
+        const int p0 = a.offsets[e], n = a.offsets[e + 1] - p0;
+        const int64_t wstride = (int64_t)a.H * a.I;
+        const void* W = INT8 ? (const void*)((const int8_t*)a.dw + e * wstride)
+                             : (const void*)((const uint16_t*)a.dw + e * wstride);
+        const float* Ws = INT8 ? a.dw_scale + (int64_t)e * a.H : nullptr;
+        down_item<8, MAXIC, INT8>(W, Ws, a.I, a.H, g * kExpertDownRows, a.h + (int64_t)p0 * a.I, n,
+                                  a.part + (int64_t)p0 * a.H, hs);
+    } else {
+        const int g = b - expert_items;
+        down_item<32, MAXDC, false>(a.ddw, nullptr, a.Id, a.H, g * kDenseDownRows, a.hd, a.T,
+                                    a.dpart, hs);
+    }
+}
+
+// ---------------------------------------------------------------- K5
+// y[t] = dense[t] + sum_k w[t,k] * expert rows, in k order (row "MoE topology").
+__global__ __launch_bounds__(kThreads) void decode_combine_kernel(StreamArgs a) {
+    const int i = blockIdx.x * kThreads + threadIdx.x;  // one thread per 4 features
+    const int per_row = a.H / 4;
+    if (i >= a.T * per_row) return;
+    const int t = i / per_row, c = (i - t * per_row) * 4;
+    float4 v = *reinterpret_cast<const float4*>(a.dpart + (int64_t)t * a.H + c);
+    if (a.max_active > 0) {
+        int p[kMaxTopK];
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k) p[k] = a.inv_row[(int64_t)t * a.K + min(k, a.K - 1)];
+        float wk[kMaxTopK];
+        float4 r[kMaxTopK];
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k) {
+            wk[k] = a.perm_w[p[k]];
+            r[k] = *reinterpret_cast<const float4*>(a.part + (int64_t)p[k] * a.H + c);
+        }
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k) {
+            if (k < a.K) {
+                v.x += wk[k] * r[k].x;
+                v.y += wk[k] * r[k].y;
+                v.z += wk[k] * r[k].z;
+                v.w += wk[k] * r[k].w;
+            }
+        }
+    }
+    *reinterpret_cast<uint2*>(a.y + (int64_t)t * a.H + c) =
+        make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+}
+
+template <int NJ>
+hipError_t launch_front_nj(const StreamArgs& a, const uint16_t* scale, const uint16_t* wr,
+                           const float* bias, float eps, float* logits, bool router,
+                           hipStream_t stream) {
+    const int n_router =
+        router ? ((a.E + kRouterExperts - 1) / kRouterExperts) * ((a.T + kPass - 1) / kPass) : 0;
+    const int blocks = n_router + a.Id / kGURows;
+    const size_t lds = (size_t)kPass * a.H * sizeof(uint16_t);
+    const float inv_sqrt_h = (float)(1.0 / __builtin_sqrt((double)a.H));
+    StreamArgs b = a;
+    if (!router) b.E = 0;  // no router items
+    hipLaunchKernelGGL(decode_front_kernel<NJ>, dim3(blocks), dim3(kThreads), lds, stream, b, scale,
+                       wr, bias, eps, inv_sqrt_h, logits);
+    return hipGetLastError();
+}
+
+template <int NJ>
+hipError_t launch_experts_nj(const StreamArgs& a, bool int8, hipStream_t stream) {
+    const int blocks = a.max_active * (a.I / kGURows);
+    const size_t lds = (size_t)kPass * a.H * sizeof(uint16_t);
+    if (int8)
+        hipLaunchKernelGGL((decode_experts_gateup_kernel<NJ, true>), dim3(blocks), dim3(kThreads), lds, stream, a);
+    else
+        hipLaunchKernelGGL((decode_experts_gateup_kernel<NJ, false>), dim3(blocks), dim3(kThreads), lds, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// NJ = H / 256 chunks per lane; instantiated for hidden sizes up to 4096.
+#define MOE_NJ_SWITCH(nj, CALL)                                   \
+    switch (nj) {                                                 \
+        case 1: return CALL(1);   case 2: return CALL(2);         \
+        case 3: return CALL(3);   case 4: return CALL(4);         \
+        case 5: return CALL(5);   case 6: return CALL(6);         \
+        case 7: return CALL(7);   case 8: return CALL(8);         \
+        case 9: return CALL(9);   case 10: return CALL(10);       \
+        case 11: return CALL(11); case 12: return CALL(12);       \
+        case 13: return CALL(13); case 14: return CALL(14);       \
+        case 15: return CALL(15); case 16: return CALL(16);       \
+        default: return hipErrorInvalidValue;                     \
+    }
+
+hipError_t launch_decode_front(const StreamArgs& a, const uint16_t* scale, const uint16_t* wr,
+                               const float* bias, float eps, float* logits, hipStream_t stream) {
+#define CALL(n) launch_front_nj<n>(a, scale, wr, bias, eps, logits, logits != nullptr, stream)
+    MOE_NJ_SWITCH(a.H / 256, CALL)
+#undef CALL
+}
+
+hipError_t launch_decode_route(const StreamArgs& a, const float* logits, const float* pes,
+                               int32_t* topk_idx, float* topk_w, hipStream_t stream) {
+    hipLaunchKernelGGL(decode_route_kernel, dim3(1), dim3(kRouteThreads), 0, stream, a, logits, pes,
+                       topk_idx, topk_w);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_experts_gateup(const StreamArgs& a, bool int8, hipStream_t stream) {
+#define CALL(n) launch_experts_nj<n>(a, int8, stream)
+    MOE_NJ_SWITCH(a.H / 256, CALL)
+#undef CALL
+}
+
+hipError_t launch_decode_down(const StreamArgs& a, bool int8, hipStream_t stream) {
+    const int ic = a.I / 64;             // expert chunks per lane (8 lanes per row)
+    const int dc = (a.Id / 8 + 31) / 32;  // dense chunks per lane (32 lanes per row)
+    const int blocks = a.max_active * (a.H / kExpertDownRows) + a.H / kDenseDownRows;
+    const size_t lds = (size_t)kPass * (a.I > a.Id ? a.I : a.Id) * sizeof(uint16_t);
+    const dim3 grid(blocks), block(kThreads);
+#define LAUNCH(M, D)                                                                                   \
+    do {                                                                                               \
+        if (int8) hipLaunchKernelGGL((decode_down_kernel<M, D, true>), grid, block, lds, stream, a);   \
+        else hipLaunchKernelGGL((decode_down_kernel<M, D, false>), grid, block, lds, stream, a);       \
+        return hipGetLastError();                                                                      \
+    } while (0)
+#define DENSE(M)                     \
+    do {                             \
+        if (dc <= 2) LAUNCH(M, 2);   \
+        if (dc <= 9) LAUNCH(M, 9);   \
+        if (dc <= 16) LAUNCH(M, 16); \
+    } while (0)
+    if (ic <= 4) DENSE(4);
+    if (ic <= 12) DENSE(12);
+    if (ic <= 16) DENSE(16);
+#undef DENSE
+#undef LAUNCH
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_combine(const StreamArgs& a, hipStream_t stream) {
+    const int n = a.T * (a.H / 4);
+    hipLaunchKernelGGL(decode_combine_kernel, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

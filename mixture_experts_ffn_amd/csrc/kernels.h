@@ -56,15 +56,15 @@ hipError_t launch_gemm_gateup(const GemmArgs& a, bool int8, hipStream_t stream);
 hipError_t launch_gemm_down(const GemmArgs& a, bool int8, hipStream_t stream);
 hipError_t launch_gemm_combine(const GemmArgs& a, hipStream_t stream);
 
-// ---- weight-streaming kernels for small T (stream.hip) --------------------
+// ---- small-batch path (decode.hip) ----------------------------------------
 struct StreamArgs {
     int T, H, I, Id, K, E;
     const uint16_t* x;
     // experts
     const void* gu; const float* gu_scale;   // [E][2I][H]
     const void* dw; const float* dw_scale;   // [E][H][I]
-    const int32_t* active; const int32_t* n_active; const int32_t* offsets;
-    const int32_t* perm_token; const float* perm_w; const int32_t* inv_row;
+    int32_t* counts; int32_t* offsets; int32_t* active; int32_t* n_active;
+    int32_t* perm_token; float* perm_w; int32_t* inv_row;
     int max_active;                           // 0 = dense only
     // dense
     const uint16_t* dgu; const uint16_t* ddw;
@@ -72,9 +72,21 @@ struct StreamArgs {
     uint16_t* h;    // [T*K][I]
     uint16_t* hd;   // [T][Id]
     uint16_t* y;    // [T][H]
+    // fp32 partial outputs of K4: expert rows [T*K][H] (grouped order), dense [T][H]
+    float* part; float* dpart;
 };
-hipError_t launch_stream_gateup(const StreamArgs& a, bool int8, hipStream_t stream);
-hipError_t launch_stream_down(const StreamArgs& a, bool int8, hipStream_t stream);
+// K1: router logits (if logits != null) beside the dense gate/up rows -> hd
+hipError_t launch_decode_front(const StreamArgs& a, const uint16_t* scale, const uint16_t* wr,
+                               const float* bias, float eps, float* logits, hipStream_t stream);
+// K2: top-k and grouping (one workgroup, T <= MOE_STREAM_MAX_TOKENS)
+hipError_t launch_decode_route(const StreamArgs& a, const float* logits, const float* pes,
+                               int32_t* topk_idx, float* topk_w, hipStream_t stream);
+// K3: gate/up of the touched experts -> h
+hipError_t launch_decode_experts_gateup(const StreamArgs& a, bool int8, hipStream_t stream);
+// K4: down of the touched experts and of the dense MLP -> fp32 partial rows
+hipError_t launch_decode_down(const StreamArgs& a, bool int8, hipStream_t stream);
+// K5: y = dense + sum_k w_k * expert rows (k order) -> bf16
+hipError_t launch_decode_combine(const StreamArgs& a, hipStream_t stream);
 
 // ---- int8 quantiser (quant.hip) -------------------------------------------
 hipError_t launch_quantize_int8(const uint16_t* w, int64_t rows, int cols, int8_t* q, float* scale,

@@ -33,7 +33,8 @@ size_t up256(size_t b) { return (b + 255) & ~size_t(255); }
 // Workspace layout at a given T (byte offsets into ws).
 struct Layout {
     size_t logits, topk_idx, topk_w, tile_counts, counts, offsets, active, n_active;
-    size_t perm_token, perm_w, inv_row, mtile_group, mtile_row0, n_mtiles, h, hd, rows, total;
+    size_t perm_token, perm_w, inv_row, mtile_group, mtile_row0, n_mtiles, h, hd, rows;
+    size_t part, dpart, total;
     int max_mtiles;
 };
 
@@ -66,6 +67,10 @@ Layout make_layout(const moe_dims& d, int64_t T) {
     L.h = take(TK * d.expert_inter * 2);
     L.hd = take(T * d.dense_inter * 2);
     L.rows = take(TK * d.hidden * 2);
+    // streaming-path scratch (only T <= MOE_STREAM_MAX_TOKENS uses it)
+    const int64_t Ts = T <= MOE_STREAM_MAX_TOKENS ? T : 0;
+    L.part = take(Ts * K * d.hidden * 4);
+    L.dpart = take(Ts * d.hidden * 4);
     L.total = off;
     return L;
 }
@@ -138,7 +143,9 @@ int stream_limit() {
     return lim < MOE_STREAM_MAX_TOKENS ? lim : MOE_STREAM_MAX_TOKENS;
 }
 
-bool stream_fits(const moe_dims& d) { return d.expert_inter <= 1024 && d.dense_inter <= 4096; }
+bool stream_fits(const moe_dims& d) {
+    return d.hidden <= 4096 && d.expert_inter <= 1024 && d.dense_inter <= 4096;
+}
 
 // Records the stage events of a debug struct around each launch.
 struct Stages {
@@ -213,7 +220,7 @@ int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
         path = (T <= stream_limit() && stream_fits(*d)) ? MOE_PATH_STREAM : MOE_PATH_GROUPED;
     if (path == MOE_PATH_STREAM && (T > MOE_STREAM_MAX_TOKENS || !stream_fits(*d)))
         return fail(MOE_ERR_UNSUPPORTED,
-                    "streaming path needs T <= %d, expert_inter <= 1024, dense_inter <= 4096",
+                    "streaming path needs T <= %d, hidden <= 4096, expert_inter <= 1024, dense_inter <= 4096",
                     MOE_STREAM_MAX_TOKENS);
     g_err[0] = 0;
     if (dbg) {
@@ -246,31 +253,37 @@ int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
     const uint16_t* xb = (const uint16_t*)x;
 
     Stages st{dbg, stream};
-    HIP_TRY(st.begin("router_logits"), "event record");
-    HIP_TRY(moe::launch_router_logits(xb, (const uint16_t*)w->router_scale,
-                                      (const uint16_t*)w->router_w, w->logit_bias, T, H, E,
-                                      d->rms_eps, logits, stream),
-            "router_logits launch");
     if (path == MOE_PATH_STREAM) {
-        HIP_TRY(st.begin("topk_permute"), "event record");
-        HIP_TRY(moe::launch_permute(logits, w->per_expert_scale, topk_idx, topk_w, T, K, E,
-                                    moe::kGemmBM, po, stream),
-                "permute launch");
         moe::StreamArgs sa{};
         sa.T = T; sa.H = H; sa.I = I; sa.Id = Id; sa.K = K; sa.E = E;
         sa.x = xb;
         sa.gu = w->expert_gate_up; sa.gu_scale = w->gate_up_scale;
         sa.dw = w->expert_down; sa.dw_scale = w->down_scale;
-        sa.active = po.active; sa.n_active = po.n_active; sa.offsets = po.offsets;
+        sa.counts = po.counts; sa.offsets = po.offsets; sa.active = po.active; sa.n_active = po.n_active;
         sa.perm_token = po.perm_token; sa.perm_w = po.perm_w; sa.inv_row = po.inv_row;
         sa.max_active = T * K < E ? T * K : E;
         sa.dgu = (const uint16_t*)w->dense_gate_up; sa.ddw = (const uint16_t*)w->dense_down;
         sa.h = h; sa.hd = hd; sa.y = (uint16_t*)y;
-        HIP_TRY(st.begin("stream_gateup"), "event record");
-        HIP_TRY(moe::launch_stream_gateup(sa, int8, stream), "stream_gateup launch");
-        HIP_TRY(st.begin("stream_down_combine"), "event record");
-        HIP_TRY(moe::launch_stream_down(sa, int8, stream), "stream_down launch");
+        sa.part = at<float>(ws, L.part); sa.dpart = at<float>(ws, L.dpart);
+        HIP_TRY(st.begin("decode_front"), "event record");
+        HIP_TRY(moe::launch_decode_front(sa, (const uint16_t*)w->router_scale, (const uint16_t*)w->router_w,
+                                         w->logit_bias, d->rms_eps, logits, stream),
+                "decode_front launch");
+        HIP_TRY(st.begin("decode_route"), "event record");
+        HIP_TRY(moe::launch_decode_route(sa, logits, w->per_expert_scale, topk_idx, topk_w, stream),
+                "decode_route launch");
+        HIP_TRY(st.begin("decode_experts_gateup"), "event record");
+        HIP_TRY(moe::launch_decode_experts_gateup(sa, int8, stream), "decode_experts_gateup launch");
+        HIP_TRY(st.begin("decode_down"), "event record");
+        HIP_TRY(moe::launch_decode_down(sa, int8, stream), "decode_down launch");
+        HIP_TRY(st.begin("decode_combine"), "event record");
+        HIP_TRY(moe::launch_decode_combine(sa, stream), "decode_combine launch");
     } else {
+        HIP_TRY(st.begin("router_logits"), "event record");
+        HIP_TRY(moe::launch_router_logits(xb, (const uint16_t*)w->router_scale,
+                                          (const uint16_t*)w->router_w, w->logit_bias, T, H, E,
+                                          d->rms_eps, logits, stream),
+                "router_logits launch");
         HIP_TRY(st.begin("router_topk"), "event record");
         HIP_TRY(moe::launch_router_topk(logits, w->per_expert_scale, T, E, K, topk_idx, topk_w, stream),
                 "router_topk launch");
@@ -351,8 +364,11 @@ int dense_mlp(const moe_dims* d, const void* dense_gate_up, const void* dense_do
         sa.x = (const uint16_t*)x; sa.max_active = 0;
         sa.dgu = (const uint16_t*)dense_gate_up; sa.ddw = (const uint16_t*)dense_down;
         sa.hd = hd; sa.y = (uint16_t*)y;
-        HIP_TRY(moe::launch_stream_gateup(sa, false, stream), "stream_gateup launch");
-        HIP_TRY(moe::launch_stream_down(sa, false, stream), "stream_down launch");
+        sa.part = at<float>(ws, L.part); sa.dpart = at<float>(ws, L.dpart);
+        HIP_TRY(moe::launch_decode_front(sa, nullptr, nullptr, nullptr, 0.f, nullptr, stream),
+                "decode_front launch");
+        HIP_TRY(moe::launch_decode_down(sa, false, stream), "decode_down launch");
+        HIP_TRY(moe::launch_decode_combine(sa, stream), "decode_combine launch");
     } else {
         moe::GemmArgs gd{};
         gd.A = (const uint16_t*)x; gd.lda = H; gd.B = dense_gate_up; gd.ldb = H; gd.K = H;

@@ -1,5 +1,12 @@
 // Wavefront top-k of one token's router logits (device code, header-only so
-// that the router and the fused small-batch grouping kernel share it).
+// that every router kernel shares it).
+//
+// ONNX export card, "Truthful graph contracts", row "Router": softmax in fp32,
+// top-k, renormalise, per-expert scale. The selection is a radix select over
+// order-preserving 32-bit keys of the fp32 logits using wavefront ballots (no
+// LDS round trips): the k-th largest key is found bit by bit from the top,
+// equal keys at the boundary go to the lower expert index, and the selected
+// experts are then ranked (descending logit, ties -> lower index).
 #pragma once
 #include "common.h"
 
@@ -8,33 +15,89 @@ namespace moe {
 constexpr int kMaxTopK = 8;
 constexpr int kMaxExperts = 256;
 
+// fp32 -> unsigned key with the same order (equal floats, including -0 and
+// +0, get equal keys; NaN sorts below everything)
+__device__ __forceinline__ uint32_t order_key(float f) {
+    if (f != f) return 0u;
+    const uint32_t u = f == 0.f ? 0u : __float_as_uint(f);  // -0 ties with +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 // Run by a full wavefront. lrow: the token's E fp32 logits (E <= 256).
-// softmax over all E in fp32 (max-subtracted), then K rounds of a wavefront
-// argmax: larger logit wins, equal logits go to the lower expert index.
-// The K selected probabilities are renormalised to sum 1 (summed in k order)
-// and multiplied by the per-expert scale. Every lane ends with the same
-// ik[0..K) and wk[0..K).
+// softmax over all E in fp32 (max-subtracted), then the top K by logit; the K
+// probabilities are renormalised to sum 1 (summed in k order) and multiplied
+// by the per-expert scale. Every lane ends with the same ik[0..K), wk[0..K).
 __device__ __forceinline__ void wave_topk(const float* __restrict__ lrow,
                                           const float* __restrict__ pes, int E, int K, int lane,
                                           int* ik, float* wk) {
     float l[4], ex[4];
+    uint32_t key[4];
+    bool valid[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int e = lane + kWave * j;
-        l[j] = (e < E) ? lrow[e] : -INFINITY;
+        valid[j] = e < E;
+        l[j] = valid[j] ? lrow[e] : -INFINITY;
+        key[j] = valid[j] ? order_key(l[j]) : 0u;
     }
+    const int nj = (E + kWave - 1) / kWave;  // uniform
     float m = fmaxf(fmaxf(l[0], l[1]), fmaxf(l[2], l[3]));
     m = wave_max<kWave>(m);
     float s = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int e = lane + kWave * j;
-        ex[j] = (e < E) ? expf(l[j] - m) : 0.f;
+        ex[j] = valid[j] ? expf(l[j] - m) : 0.f;
         s += ex[j];
     }
     s = wave_sum<kWave>(s);
 
-    unsigned sel = 0u;
+    // k-th largest key: the largest v with #{key >= v} >= K
+    uint32_t prefix = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = prefix | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (j < nj) cnt += __popcll(__ballot(valid[j] && key[j] >= cand));
+        if (cnt >= K) prefix = cand;
+    }
+    int ngt = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (j < nj) ngt += __popcll(__ballot(valid[j] && key[j] > prefix));
+    // take the K - ngt lowest-index experts whose key equals the boundary key
+    const int need = K - ngt;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    bool sel[4];
+    int taken = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        sel[j] = false;
+        if (j < nj) {
+            const unsigned long long meq = __ballot(valid[j] && key[j] == prefix);
+            const int r = taken + __popcll(meq & below);
+            sel[j] = valid[j] && (key[j] > prefix || (key[j] == prefix && r < need));
+            taken += __popcll(meq);
+        }
+    }
+    // rank of each selected expert among the selected: larger key first, then lower index
+    int rank[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int j2 = 0; j2 < 4; ++j2) {
+        if (j2 >= nj) break;
+        unsigned long long ms = __ballot(sel[j2]);
+        while (ms) {
+            const int ln = __ffsll((long long)ms) - 1;
+            ms &= ms - 1ull;
+            const uint32_t kk = __builtin_amdgcn_readlane(key[j2], ln);
+            const int ee = ln + kWave * j2;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int e = lane + kWave * j;
+                if (sel[j] && (kk > key[j] || (kk == key[j] && ee < e))) ++rank[j];
+            }
+        }
+    }
     float pk[kMaxTopK];
     float psum = 0.f;
 #pragma unroll
@@ -42,34 +105,17 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ lrow,
         ik[k] = 0;
         pk[k] = 0.f;
         if (k < K) {
-            float bv = -INFINITY, bp = 0.f;
-            int bi = 0x7fffffff;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int e = lane + kWave * j;
-                // ascending j is ascending e: a strict '>' keeps the lower index on ties.
-                // The first unselected expert is always taken, so a NaN or -inf
-                // logit can never leave the winner unset (bi stays a valid index).
-                if (e < E && !((sel >> j) & 1u) && (bi == 0x7fffffff || l[j] > bv)) {
-                    bv = l[j];
-                    bi = e;
-                    bp = ex[j];
+                if (j < nj) {
+                    const unsigned long long mk = __ballot(sel[j] && rank[j] == k);
+                    if (mk) {
+                        const int ln = __ffsll((long long)mk) - 1;
+                        ik[k] = ln + kWave * j;
+                        pk[k] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(ex[j]), ln)) / s;
+                    }
                 }
             }
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) {
-                const float ov = __shfl_xor(bv, off, kWave);
-                const int oi = __shfl_xor(bi, off, kWave);
-                const float op = __shfl_xor(bp, off, kWave);
-                if (ov > bv || (ov == bv && oi < bi)) {
-                    bv = ov;
-                    bi = oi;
-                    bp = op;
-                }
-            }
-            if ((bi & (kWave - 1)) == lane) sel |= 1u << (bi >> 6);
-            ik[k] = bi;
-            pk[k] = bp / s;
             psum += pk[k];
         }
     }

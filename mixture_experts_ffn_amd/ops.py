@@ -165,6 +165,30 @@ def moe_quantize_int8(w: torch.Tensor, q=None, scale=None, stream=None):
     return q, scale
 
 
+class BlockCall:
+    """moe_block with its arguments marshalled once, for repeated calls on the
+    same tensors (the ctypes structures are built here, not per call)."""
+
+    def __init__(self, dims: BlockDims, weights: LayerWeights, x: torch.Tensor, y=None,
+                 workspace=None):
+        self.x = _dev(x, "x")
+        self.T = x.shape[0]
+        self.y = y if y is not None else torch.empty((self.T, dims.hidden), dtype=torch.bfloat16,
+                                                     device=x.device)
+        self.ws, _ = _workspace(dims, self.T, x.device, workspace)
+        self.weights = weights          # keeps the tensors alive
+        self._dims = dims.c()
+        self._w = weights.c()
+
+    def __call__(self, debug: Optional[MoeDebug] = None, stream=None) -> torch.Tensor:
+        rc = _lib().moe_block(ctypes.byref(self._dims), ctypes.byref(self._w), self.x.data_ptr(),
+                              self.T, self.y.data_ptr(),
+                              ctypes.byref(debug) if debug is not None else None,
+                              self.ws.data_ptr(), self.ws.numel(), _stream(stream))
+        _check(rc, "moe_block")
+        return self.y
+
+
 def new_debug(path: int = _abi.MOE_PATH_AUTO, **outputs) -> MoeDebug:
     """A moe_debug struct; keyword arguments name device tensors for its outputs."""
     d = MoeDebug()
