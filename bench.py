@@ -120,10 +120,9 @@ def stage_work(stage: str, shape, T, n_active, int8):
         "router_logits": (router_w + x + T * E * 4, 2 * T * E * H, "router weights + x + logits"),
         "router_topk": (T * E * 4 + E * 4 + TK * 8, 0, "logits + top-k"),
         "permute": (TK * 8 + TK * 12 + E * 8, 0, "top-k + grouping tables"),
-        "gemm_gateup_experts": (n_active * gu_w + x + TK * I * 2, 2 * TK * H * 2 * I,
-                                f"{n_active} experts' gate_up ({gu_w} B each) + x + h"),
-        "gemm_gateup_dense": (2 * Id * H * 2 + x + T * Id * 2, 2 * T * H * 2 * Id,
-                              "dense gate_up + x + hd"),
+        "gemm_gateup": (n_active * gu_w + 2 * Id * H * 2 + x + TK * I * 2 + T * Id * 2,
+                        2 * TK * H * 2 * I + 2 * T * H * 2 * Id,
+                        f"{n_active} experts' gate_up ({gu_w} B each) + dense gate_up + x + h + hd"),
         "gemm_down_experts": (n_active * dn_w + TK * I * 2 + TK * H * 2, 2 * TK * I * H,
                               f"{n_active} experts' down ({dn_w} B each) + h + rows"),
         "gemm_dense_down_combine": (H * Id * 2 + T * Id * 2 + TK * H * 2 + y, 2 * T * Id * H,

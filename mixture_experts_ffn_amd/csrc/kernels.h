@@ -35,7 +35,8 @@ hipError_t launch_permute(const float* logits, const float* pes, int32_t* topk_i
                           int T, int K, int E, int BM, const PermuteOut& o, hipStream_t stream);
 
 // ---- grouped MFMA GEMMs (gemm.hip) -----------------------------------------
-constexpr int kGemmBM = 128;
+constexpr int kGemmBM = 256;  // rows per grouped M-tile
+constexpr int kMaxTopKGemm = 8;
 struct GemmArgs {
     const uint16_t* A; int64_t lda;          // bf16 activations
     const int32_t* a_rows;                    // gather: A row of grouped row p is a_rows[p]; null = p
@@ -52,7 +53,8 @@ struct GemmArgs {
     const float* row_w;                       // down: per-row weight
     const uint16_t* comb; const int32_t* inv_row; int topk;  // combine: rows added to y
 };
-hipError_t launch_gemm_gateup(const GemmArgs& a, bool int8, hipStream_t stream);
+// gate/up of `a`, and of `dense` (bf16, may be null) in the same launch
+hipError_t launch_gemm_gateup(const GemmArgs& a, const GemmArgs* dense, bool int8, hipStream_t stream);
 hipError_t launch_gemm_down(const GemmArgs& a, bool int8, hipStream_t stream);
 hipError_t launch_gemm_combine(const GemmArgs& a, hipStream_t stream);
 

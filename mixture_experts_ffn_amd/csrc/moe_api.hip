@@ -299,14 +299,12 @@ int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
         g.mtile_group = po.mtile_group; g.mtile_row0 = po.mtile_row0; g.n_mtiles = po.n_mtiles;
         g.group_end = po.offsets; g.max_mtiles = L.max_mtiles;
         g.C = h; g.ldc = I;
-        HIP_TRY(st.begin("gemm_gateup_experts"), "event record");
-        HIP_TRY(moe::launch_gemm_gateup(g, int8, stream), "gemm_gateup launch");
-        // dense gate/up + GELU
+        // dense gate/up + GELU, in the same launch
         moe::GemmArgs gd{};
         gd.A = xb; gd.lda = H; gd.B = w->dense_gate_up; gd.ldb = H; gd.K = H;
         gd.n_out = Id; gd.up_off = Id; gd.M_dense = T; gd.C = hd; gd.ldc = Id;
-        HIP_TRY(st.begin("gemm_gateup_dense"), "event record");
-        HIP_TRY(moe::launch_gemm_gateup(gd, false, stream), "gemm_gateup dense launch");
+        HIP_TRY(st.begin("gemm_gateup"), "event record");
+        HIP_TRY(moe::launch_gemm_gateup(g, &gd, int8, stream), "gemm_gateup launch");
         // experts down, weighted rows
         moe::GemmArgs gw{};
         gw.A = h; gw.lda = I; gw.B = w->expert_down; gw.b_group_stride = (int64_t)H * I; gw.ldb = I;
@@ -373,7 +371,7 @@ int dense_mlp(const moe_dims* d, const void* dense_gate_up, const void* dense_do
         moe::GemmArgs gd{};
         gd.A = (const uint16_t*)x; gd.lda = H; gd.B = dense_gate_up; gd.ldb = H; gd.K = H;
         gd.n_out = Id; gd.up_off = Id; gd.M_dense = T; gd.C = hd; gd.ldc = Id;
-        HIP_TRY(moe::launch_gemm_gateup(gd, false, stream), "gemm_gateup dense launch");
+        HIP_TRY(moe::launch_gemm_gateup(gd, nullptr, false, stream), "gemm_gateup dense launch");
         moe::GemmArgs gc{};
         gc.A = hd; gc.lda = Id; gc.B = dense_down; gc.ldb = Id; gc.K = Id; gc.n_out = H;
         gc.M_dense = T; gc.C = (uint16_t*)y; gc.ldc = H;
