@@ -117,8 +117,7 @@ def stage_work(stage: str, shape, T, n_active, int8):
                         2 * TK * I * H + 2 * T * Id * H,
                         f"{n_active} experts' down ({dn_w} B each) + dense down + h + hd"),
         "decode_combine": ((TK + T) * H * 4 + y, 2 * TK * H, "fp32 partial rows + y"),
-        "router_logits": (router_w + x + T * E * 4, 2 * T * E * H, "router weights + x + logits"),
-        "router_topk": (T * E * 4 + E * 4 + TK * 8, 0, "logits + top-k"),
+        "router": (router_w + x + E * 4 + TK * 8, 2 * T * E * H, "router weights + x + top-k"),
         "permute": (TK * 8 + TK * 12 + E * 8, 0, "top-k + grouping tables"),
         "gemm_gateup": (n_active * gu_w + 2 * Id * H * 2 + x + TK * I * 2 + T * Id * 2,
                         2 * TK * H * 2 * I + 2 * T * H * 2 * Id,

@@ -11,13 +11,30 @@ namespace moe {
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* scale, const uint16_t* w,
                                 const float* bias, int T, int H, int E, float eps,
                                 float* logits, hipStream_t stream);
+// MFMA router for larger batches (fp32-exact logits via a hi/lo bf16 split of
+// scale * W): per-slice partial dot products over the hidden dimension, then a
+// finishing kernel (slice sum in fixed order, RMSNorm factor, bias, top-k).
+struct RouterSplit {
+    int slices;       // partial sums per logit
+    int slice_steps;  // 64-wide K-steps per slice
+};
+RouterSplit router_split(int T, int H, int E);
+// partial: router_split(T, H, E).slices * T * E fp32
+hipError_t launch_router_mfma(const uint16_t* x, const uint16_t* scale, const uint16_t* w,
+                              const float* bias, const float* pes, int T, int H, int E, int K,
+                              float eps, int32_t* topk_idx, float* topk_w, float* partial,
+                              hipStream_t stream);
 // softmax over E, top-k (ties -> lower index), renormalise, * per-expert scale
 hipError_t launch_router_topk(const float* logits, const float* pes, int T, int E, int K,
                               int32_t* topk_idx, float* topk_w, hipStream_t stream);
 
 // ---- grouping (permute.hip) ------------------------------------------------
+// Tokens per grouping tile: the unit in which pairs are counted per expert.
+constexpr int kRouteTile = 32;  // 32-bit token masks
+constexpr int kMaxExpertsGroup = 256;
 struct PermuteOut {
-    int32_t* tile_counts;   // [ceil(T/64), E] scratch
+    int32_t* tile_counts;   // [ceil(T/kRouteTile), E]: pairs per (tile, expert) from the
+                            // router; rewritten to the first grouped row of each
     int32_t* counts;        // [E]
     int32_t* offsets;       // [E+1]
     int32_t* perm_token;    // [T*K]
@@ -29,9 +46,9 @@ struct PermuteOut {
     int32_t* mtile_row0;    // [max m-tiles] first grouped row of each tile
     int32_t* n_mtiles;      // [1]
 };
-// If `logits` is non-null the kernel first runs the top-k for all T tokens
-// (small T) and writes topk_idx / topk_w itself.
-hipError_t launch_permute(const float* logits, const float* pes, int32_t* topk_idx, float* topk_w,
+// pair_rank: [T*K] scratch (rank of each pair among its tile's pairs of the
+// same expert)
+hipError_t launch_permute(const int32_t* topk_idx, const float* topk_w, int32_t* pair_rank,
                           int T, int K, int E, int BM, const PermuteOut& o, hipStream_t stream);
 
 // ---- grouped MFMA GEMMs (gemm.hip) -----------------------------------------

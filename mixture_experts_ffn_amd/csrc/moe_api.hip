@@ -30,9 +30,15 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 size_t up256(size_t b) { return (b + 255) & ~size_t(255); }
 
+// moe_route: above this many tokens the MFMA router (fused with the top-k)
+// runs; below it, the per-expert dot-product router and a separate top-k,
+// which spread a small batch over more workgroups.
+constexpr int kRouterMfmaMinT = 64;
+static_assert(kRouterMfmaMinT >= MOE_STREAM_MAX_TOKENS, "the streaming path stages logits");
+
 // Workspace layout at a given T (byte offsets into ws).
 struct Layout {
-    size_t logits, topk_idx, topk_w, tile_counts, counts, offsets, active, n_active;
+    size_t logits, partial, topk_idx, topk_w, pair_rank, tile_counts, counts, offsets, active, n_active;
     size_t perm_token, perm_w, inv_row, mtile_group, mtile_row0, n_mtiles, h, hd, rows;
     size_t part, dpart, total;
     int max_mtiles;
@@ -47,12 +53,16 @@ Layout make_layout(const moe_dims& d, int64_t T) {
         return o;
     };
     const int64_t E = d.num_experts, K = d.top_k, TK = T * K;
-    const int64_t n_tiles = (T + 63) / 64;
+    const int64_t n_tiles = (T + moe::kRouteTile - 1) / moe::kRouteTile;
     const int64_t BM = moe::kGemmBM;
     L.max_mtiles = (int)((TK + BM - 1) / BM + (E < TK ? E : TK));
-    L.logits = take(T * E * 4);
+    // fp32 logits: only the small-batch routers stage them (T <= 64)
+    L.logits = take((T <= kRouterMfmaMinT ? T : 0) * E * 4);
+    // MFMA router's partial sums (every T: the grouped path uses it at any size)
+    L.partial = take(T > 0 ? (size_t)moe::router_split((int)T, d.hidden, (int)E).slices * T * E * 4 : 0);
     L.topk_idx = take(TK * 4);
     L.topk_w = take(TK * 4);
+    L.pair_rank = take(TK * 4);
     L.tile_counts = take(n_tiles * E * 4);
     L.counts = take(E * 4);
     L.offsets = take((E + 1) * 4);
@@ -193,6 +203,14 @@ int moe_route(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
     CHECK_PTR(topk_w, "topk_w", 4);
     if ((rc = check_ws(d, T, ws, ws_bytes))) return rc;
     const Layout L = make_layout(*d, T);
+    if (T > kRouterMfmaMinT) {
+        HIP_TRY(moe::launch_router_mfma((const uint16_t*)x, (const uint16_t*)w->router_scale,
+                                        (const uint16_t*)w->router_w, w->logit_bias,
+                                        w->per_expert_scale, T, d->hidden, d->num_experts, d->top_k,
+                                        d->rms_eps, topk_idx, topk_w, at<float>(ws, L.partial), stream),
+                "router launch");
+        return MOE_OK;
+    }
     float* logits = at<float>(ws, L.logits);
     HIP_TRY(moe::launch_router_logits((const uint16_t*)x, (const uint16_t*)w->router_scale,
                                       (const uint16_t*)w->router_w, w->logit_bias, T, d->hidden,
@@ -235,6 +253,7 @@ int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
     float* logits = at<float>(ws, L.logits);
     int32_t* topk_idx = at<int32_t>(ws, L.topk_idx);
     float* topk_w = at<float>(ws, L.topk_w);
+    int32_t* pair_rank = at<int32_t>(ws, L.pair_rank);
     moe::PermuteOut po;
     po.tile_counts = at<int32_t>(ws, L.tile_counts);
     po.counts = at<int32_t>(ws, L.counts);
@@ -279,16 +298,14 @@ int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
         HIP_TRY(st.begin("decode_combine"), "event record");
         HIP_TRY(moe::launch_decode_combine(sa, stream), "decode_combine launch");
     } else {
-        HIP_TRY(st.begin("router_logits"), "event record");
-        HIP_TRY(moe::launch_router_logits(xb, (const uint16_t*)w->router_scale,
-                                          (const uint16_t*)w->router_w, w->logit_bias, T, H, E,
-                                          d->rms_eps, logits, stream),
-                "router_logits launch");
-        HIP_TRY(st.begin("router_topk"), "event record");
-        HIP_TRY(moe::launch_router_topk(logits, w->per_expert_scale, T, E, K, topk_idx, topk_w, stream),
-                "router_topk launch");
+        HIP_TRY(st.begin("router"), "event record");
+        HIP_TRY(moe::launch_router_mfma(xb, (const uint16_t*)w->router_scale,
+                                        (const uint16_t*)w->router_w, w->logit_bias,
+                                        w->per_expert_scale, T, H, E, K, d->rms_eps, topk_idx,
+                                        topk_w, at<float>(ws, L.partial), stream),
+                "router launch");
         HIP_TRY(st.begin("permute"), "event record");
-        HIP_TRY(moe::launch_permute(nullptr, nullptr, topk_idx, topk_w, T, K, E, moe::kGemmBM, po, stream),
+        HIP_TRY(moe::launch_permute(topk_idx, topk_w, pair_rank, T, K, E, moe::kGemmBM, po, stream),
                 "permute launch");
         moe::GemmArgs g{};
         // experts gate/up + GELU: gathered rows of x

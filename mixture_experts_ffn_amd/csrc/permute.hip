@@ -2,85 +2,69 @@
 //
 // Gathered expert compute (Tenstorrent bundle card, "Configurable knobs",
 // GEMMA4_PREFILL_GATHERED) runs each expert only on the tokens routed to it.
-// This kernel builds that grouping: a stable counting sort of the T*K pairs by
-// expert (ascending expert, then ascending token), with
+// The grouping is a stable counting sort of the T*K pairs by expert (ascending
+// expert, then ascending token), producing
 //   counts[e], offsets[e] (exclusive prefix sum), perm_token / perm_w (token and
 //   router weight of each grouped row), inv_row[t*K+k] (grouped row of a pair),
 //   the list of experts with rows, and the list of BM-row tiles for the
 //   grouped GEMMs.
-// It is exact integer work, and deterministic: ranks within an expert come from
-// bit masks of the lanes of a 64-token tile that picked the expert (popcount of
-// the lower lanes), never from the order of atomic operations.
+// It is exact integer work, and deterministic: ranks come from popcounts of
+// token bit masks, never from the order of atomic operations.
 //
-// One workgroup of 1024 threads handles the whole batch; tokens are taken in
-// tiles of 64 (one lane per token, one wavefront per tile).
+//   group_count_kernel    per tile of kRouteTile tokens: the pairs of every
+//                         expert, and each pair's rank among its tile's pairs
+//                         of the same expert
+//   group_offsets_kernel  one workgroup: per-expert totals, offsets, active
+//                         experts, GEMM M-tiles, and (in place) the first
+//                         grouped row of every (tile, expert)
+//   group_scatter_kernel  one thread per pair: its grouped row, and the
+//                         scatter of token and weight to that row
 #include "common.h"
 #include "kernels.h"
-#include "topk.h"
 
 namespace moe {
 
-constexpr int kPermThreads = 1024;
-constexpr int kPermWaves = kPermThreads / kWave;
+constexpr int kOffThreads = 1024;
+constexpr int kCountThreads = kRouteTile * 8;  // one thread per (token, slot), K <= 8
 
-__global__ __launch_bounds__(kPermThreads) void permute_kernel(
-    const float* __restrict__ logits, const float* __restrict__ pes, int32_t* topk_idx,
-    float* topk_w, int T, int K, int E, int BM, PermuteOut o) {
-    __shared__ unsigned long long mask[kPermWaves][kMaxExperts];  // 32 KB
-    __shared__ int part[kPermThreads];
-    __shared__ int s_cnt[kMaxExperts];
-    __shared__ int s_off[kMaxExperts + 1];
-    __shared__ int s_tile[kMaxExperts + 1];
+__global__ __launch_bounds__(kCountThreads) void group_count_kernel(
+    const int32_t* __restrict__ topk_idx, int T, int K, int E, int32_t* __restrict__ tile_counts,
+    int32_t* __restrict__ pair_rank) {
+    __shared__ uint32_t mask[kMaxExpertsGroup];  // tokens of the tile that picked expert e
+    const int tid = threadIdx.x;
+    const int t0 = blockIdx.x * kRouteTile;
+    const int n_pairs = min(kRouteTile, T - t0) * K;
+    for (int e = tid; e < E; e += kCountThreads) mask[e] = 0u;
+    __syncthreads();
+    const bool live = tid < n_pairs;
+    const int r = tid / K;
+    const int e = live ? topk_idx[(int64_t)t0 * K + tid] : 0;
+    if (live) atomicOr(&mask[e], 1u << r);
+    __syncthreads();
+    for (int ee = tid; ee < E; ee += kCountThreads)
+        tile_counts[(int64_t)blockIdx.x * E + ee] = __popc(mask[ee]);
+    if (live) pair_rank[(int64_t)t0 * K + tid] = __popc(mask[e] & ((1u << r) - 1u));
+}
+
+__global__ __launch_bounds__(kOffThreads) void group_offsets_kernel(int n_tiles, int E, int BM,
+                                                                    PermuteOut o) {
+    __shared__ int part[kOffThreads];
+    __shared__ int s_cnt[kMaxExpertsGroup];
+    __shared__ int s_off[kMaxExpertsGroup + 1];
+    __shared__ int s_tile[kMaxExpertsGroup + 1];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 
-    // fused top-k for small batches
-    if (logits) {
-        for (int t = wave; t < T; t += kPermWaves) {
-            int ik[kMaxTopK];
-            float wk[kMaxTopK];
-            wave_topk(logits + (size_t)t * E, pes, E, K, lane, ik, wk);
-            if (lane == 0) {
-#pragma unroll
-                for (int k = 0; k < kMaxTopK; ++k)
-                    if (k < K) {
-                        topk_idx[(size_t)t * K + k] = ik[k];
-                        topk_w[(size_t)t * K + k] = wk[k];
-                    }
-            }
-        }
-        block_sync_global();
-    }
-
-    const int n_tiles = (T + 63) / 64;
-    // phase 1: experts picked by each 64-token tile, as lane masks -> counts
-    for (int base = 0; base < n_tiles; base += kPermWaves) {
-        const int tile = base + wave;
-        for (int e = lane; e < E; e += kWave) mask[wave][e] = 0ull;
-        __syncthreads();
-        const int t = tile * 64 + lane;
-        if (tile < n_tiles && t < T) {
-            for (int k = 0; k < K; ++k)
-                atomicOr(&mask[wave][topk_idx[(size_t)t * K + k]], 1ull << lane);
-        }
-        __syncthreads();
-        if (tile < n_tiles)
-            for (int e = lane; e < E; e += kWave)
-                o.tile_counts[(size_t)tile * E + e] = __popcll(mask[wave][e]);
-        __syncthreads();
-    }
-    block_sync_global();
-
-    // phase 2: totals, offsets and the base row of every (tile, expert)
+    // thread (e, p): expert e, the p-th chunk of tiles
     int ep = 1;
     while (ep < E) ep <<= 1;
-    const int nparts = kPermThreads / ep;
+    const int nparts = kOffThreads / ep;
     const int e = tid & (ep - 1), p = tid / ep;
     const int chunk = (n_tiles + nparts - 1) / nparts;
     const int tb = min(n_tiles, p * chunk), te = min(n_tiles, tb + chunk);
     {
         int sum = 0;
         if (e < E) {
-#pragma unroll 8
+#pragma unroll 16
             for (int tl = tb; tl < te; ++tl) sum += o.tile_counts[(size_t)tl * E + e];
         }
         part[tid] = sum;
@@ -139,10 +123,11 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
         }
     }
     __syncthreads();
+    // first grouped row of every (tile, expert): offset + earlier tiles' counts
     if (e < E) {
         int run = s_off[e];
         for (int q = 0; q < p; ++q) run += part[q * ep + e];
-#pragma unroll 8
+#pragma unroll 16
         for (int tl = tb; tl < te; ++tl) {
             const size_t ix = (size_t)tl * E + e;
             const int cnt = o.tile_counts[ix];
@@ -151,46 +136,38 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
         }
     }
     // tiles of BM grouped rows for the grouped GEMMs
-    for (int ee = tid; ee < E; ee += kPermThreads) {
+    for (int ee = tid; ee < E; ee += kOffThreads) {
         const int nt = (s_cnt[ee] + BM - 1) / BM;
         for (int j = 0; j < nt; ++j) {
             o.mtile_group[s_tile[ee] + j] = ee;
             o.mtile_row0[s_tile[ee] + j] = s_off[ee] + j * BM;
         }
     }
-    block_sync_global();
-
-    // phase 3: scatter every pair to its grouped row
-    for (int base = 0; base < n_tiles; base += kPermWaves) {
-        const int tile = base + wave;
-        for (int ee = lane; ee < E; ee += kWave) mask[wave][ee] = 0ull;
-        __syncthreads();
-        const int t = tile * 64 + lane;
-        const bool live = tile < n_tiles && t < T;
-        if (live) {
-            for (int k = 0; k < K; ++k)
-                atomicOr(&mask[wave][topk_idx[(size_t)t * K + k]], 1ull << lane);
-        }
-        __syncthreads();
-        if (live) {
-            const unsigned long long below = (1ull << lane) - 1ull;
-            for (int k = 0; k < K; ++k) {
-                const size_t pk = (size_t)t * K + k;
-                const int ee = topk_idx[pk];
-                const int pos = o.tile_counts[(size_t)tile * E + ee] + __popcll(mask[wave][ee] & below);
-                o.perm_token[pos] = t;
-                o.perm_w[pos] = topk_w[pk];
-                o.inv_row[pk] = pos;
-            }
-        }
-        __syncthreads();
-    }
 }
 
-hipError_t launch_permute(const float* logits, const float* pes, int32_t* topk_idx, float* topk_w,
+__global__ __launch_bounds__(256) void group_scatter_kernel(const int32_t* __restrict__ topk_idx,
+                                                            const float* __restrict__ topk_w,
+                                                            const int32_t* __restrict__ pair_rank,
+                                                            int T, int K, int E, PermuteOut o) {
+    const int64_t pk = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (pk >= (int64_t)T * K) return;
+    const int t = (int)(pk / K);
+    const int e = topk_idx[pk];
+    const int pos = o.tile_counts[(int64_t)(t / kRouteTile) * E + e] + pair_rank[pk];
+    o.perm_token[pos] = t;
+    o.perm_w[pos] = topk_w[pk];
+    o.inv_row[pk] = pos;
+}
+
+hipError_t launch_permute(const int32_t* topk_idx, const float* topk_w, int32_t* pair_rank,
                           int T, int K, int E, int BM, const PermuteOut& o, hipStream_t stream) {
-    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, stream, logits, pes,
-                       topk_idx, topk_w, T, K, E, BM, o);
+    const int n_tiles = (T + kRouteTile - 1) / kRouteTile;
+    hipLaunchKernelGGL(group_count_kernel, dim3(n_tiles), dim3(kCountThreads), 0, stream, topk_idx,
+                       T, K, E, o.tile_counts, pair_rank);
+    hipLaunchKernelGGL(group_offsets_kernel, dim3(1), dim3(kOffThreads), 0, stream, n_tiles, E, BM, o);
+    const int64_t pairs = (int64_t)T * K;
+    hipLaunchKernelGGL(group_scatter_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0,
+                       stream, topk_idx, topk_w, pair_rank, T, K, E, o);
     return hipGetLastError();
 }
 

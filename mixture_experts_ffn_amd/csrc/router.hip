@@ -102,6 +102,244 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     }
 }
 
+// ---------------------------------------------------------------------------
+// Router for larger batches on MFMA.
+//
+// logit[t, e] = rms(x_t)^-1 * H^-0.5 * sum_h x[t,h] * (s[h] * W[e,h]) + bias[e].
+// s[h] * W[e,h] is a product of two bf16 values, so it has at most 16
+// significant bits: it equals hi + lo exactly, with hi its truncation to bf16
+// and lo the (bf16-representable) remainder. x is bf16, so the dot product is
+// two bf16 MFMAs (x.hi + x.lo) whose products are exact and whose sums
+// accumulate in fp32: the logits keep fp32 accuracy, as the router requires.
+//
+// router_partial_kernel: a workgroup takes 32 tokens, all experts (waves split
+//   them in 16-wide column tiles) and one slice of the hidden dimension; it
+//   issues the loads of up to NS K-steps at once (no load waits on another),
+//   then splits, stages through LDS and multiplies step by step. The sums of
+//   each slice go to partial[slice][t][e].
+// router_finish_kernel: one wavefront per token adds the slices in order (the
+//   same order for every run), applies the RMSNorm factor, the H^-0.5 and the
+//   bias, and runs the softmax / top-k.
+namespace {
+
+constexpr int kRT = 32;  // tokens per workgroup: two 16-row MFMA tiles
+constexpr int kRK = 64;  // K-step
+constexpr int kRThreads = 256;
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int rswz(int r, int c) { return r * kRK + ((c ^ (r & 7)) << 3); }
+
+// NQ: router rows staged per thread per K-step (32 NQ experts per workgroup)
+template <int NQ>
+struct RStage {
+    v4u x;       // one 16-byte chunk of the x tile
+    v4u w[NQ];   // NQ 16-byte chunks of router rows
+    v4u sc;      // the matching 8 router-scale values
+};
+
+template <int NQ>
+__device__ __forceinline__ void r_load(RStage<NQ>& st, const uint16_t* xr, const uint16_t* const* wr,
+                                       const uint16_t* sr, int k0) {
+    st.x = *reinterpret_cast<const v4u*>(xr + k0);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) st.w[q] = *reinterpret_cast<const v4u*>(wr[q] + k0);
+    st.sc = *reinterpret_cast<const v4u*>(sr + k0);
+}
+
+// split 8 products s*w into bf16 hi (truncation) and lo (exact remainder)
+__device__ __forceinline__ void split8(const v4u& w, const v4u& sc, v4u& hi, v4u& lo) {
+    unsigned h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const unsigned wu = w[i], su = sc[i];
+        const float p0 = bf16_lo(wu) * bf16_lo(su);  // exact in fp32
+        const float p1 = bf16_hi(wu) * bf16_hi(su);
+        const unsigned h0 = __float_as_uint(p0) & 0xFFFF0000u, h1 = __float_as_uint(p1) & 0xFFFF0000u;
+        const float r0 = p0 - __uint_as_float(h0), r1 = p1 - __uint_as_float(h1);  // exact, fits bf16
+        h[i] = (h0 >> 16) | h1;
+        l[i] = (__float_as_uint(r0) >> 16) | (__float_as_uint(r1) & 0xFFFF0000u);
+    }
+    hi = v4u{h[0], h[1], h[2], h[3]};
+    lo = v4u{l[0], l[1], l[2], l[3]};
+}
+
+template <int NQ, int NS>
+__global__ __launch_bounds__(kRThreads) void router_partial_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ scale,
+    const uint16_t* __restrict__ w, int T, int H, int E, int slice_steps,
+    float* __restrict__ partial) {
+    constexpr int kMaxE = 32 * NQ, kMaxCT = kMaxE / 64;  // column tiles per wave
+    // per stage: x tile [32][64], hi and lo tiles [32 NQ][64] (bf16)
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][kRT * kRK];
+    __shared__ __attribute__((aligned(16))) uint16_t ws_hi[2][kMaxE * kRK];
+    __shared__ __attribute__((aligned(16))) uint16_t ws_lo[2][kMaxE * kRK];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int t0 = blockIdx.x * kRT;
+    const int nt = min(kRT, T - t0);
+    const int n_ct = (E + 15) / 16;
+    const int e_pad = n_ct * 16;
+    const int nk = H / kRK, last = nk - 1;
+    const int kb = blockIdx.y * slice_steps, ke = min(nk, kb + slice_steps);
+
+    // staging sources: x chunk (row tid>>3, chunk tid&7); router rows tid>>3 + 32 q
+    const int xr_row = tid >> 3, cc = tid & 7;
+    const uint16_t* xr = x + (int64_t)(t0 + min(xr_row, nt - 1)) * H + cc * 8;
+    const uint16_t* wr[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) wr[q] = w + (int64_t)min(xr_row + 32 * q, E - 1) * H + cc * 8;
+    const uint16_t* sr = scale + cc * 8;
+
+    f32x4_t acc[2][kMaxCT];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < kMaxCT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    int step = 0;  // steps multiplied so far (selects the LDS buffer)
+    for (int c0 = kb; c0 < ke; c0 += NS) {
+        RStage<NQ> st[NS];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) r_load(st[i], xr, wr, sr, min(c0 + i, last) * kRK);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            if (c0 + i < ke) {  // uniform
+                const int buf = (step + i) & 1;
+                *reinterpret_cast<v4u*>(&xs[buf][rswz(xr_row, cc)]) = st[i].x;
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    const int r = xr_row + 32 * q;
+                    if (r < e_pad) {
+                        v4u hi, lo;
+                        split8(st[i].w[q], st[i].sc, hi, lo);
+                        if (r >= E) hi = lo = v4u{0u, 0u, 0u, 0u};
+                        *reinterpret_cast<v4u*>(&ws_hi[buf][rswz(r, cc)]) = hi;
+                        *reinterpret_cast<v4u*>(&ws_lo[buf][rswz(r, cc)]) = lo;
+                    }
+                }
+                __syncthreads();
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const int c = s * 4 + (lane >> 4);
+                    bf16x8_t af[2];
+#pragma unroll
+                    for (int ii = 0; ii < 2; ++ii)
+                        af[ii] = *reinterpret_cast<const bf16x8_t*>(&xs[buf][rswz(ii * 16 + (lane & 15), c)]);
+#pragma unroll
+                    for (int j = 0; j < kMaxCT; ++j) {
+                        const int ct = wave + 4 * j;
+                        if (ct < n_ct) {
+                            const int r = ct * 16 + (lane & 15);
+                            const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(&ws_hi[buf][rswz(r, c)]);
+                            const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(&ws_lo[buf][rswz(r, c)]);
+#pragma unroll
+                            for (int ii = 0; ii < 2; ++ii) {
+                                acc[ii][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ii], bh, acc[ii][j], 0, 0, 0);
+                                acc[ii][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ii], bl, acc[ii][j], 0, 0, 0);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        step += NS;
+    }
+
+    float* out = partial + (int64_t)blockIdx.y * T * E;
+#pragma unroll
+    for (int j = 0; j < kMaxCT; ++j) {
+        const int ct = wave + 4 * j;
+        const int e = ct * 16 + (lane & 15);
+        if (ct < n_ct && e < E) {
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int r = ii * 16 + (lane >> 4) * 4 + v;
+                    if (r < nt) out[(int64_t)(t0 + r) * E + e] = acc[ii][j][v];
+                }
+        }
+    }
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void router_finish_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ partial, int S,
+    const float* __restrict__ bias, const float* __restrict__ pes, int T, int H, int E, int K,
+    float eps, float inv_sqrt_h, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= T) return;  // uniform per wavefront
+    float lv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = lane + kWave * j;
+        float a = 0.f;
+        if (e < E)
+            for (int sl = 0; sl < S; ++sl) a += partial[((int64_t)sl * T + t) * E + e];
+        lv[j] = a;
+    }
+    float q = 0.f;  // sum of squares of x_t
+    const uint16_t* row = x + (int64_t)t * H;
+    for (int k = lane * 8; k < H; k += kWave * 8) {
+        float f[8];
+        unpack8(*reinterpret_cast<const uint4*>(row + k), f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q += f[i] * f[i];
+    }
+    q = wave_sum<kWave>(q);
+    const float f = (1.0f / sqrtf(q / (float)H + eps)) * inv_sqrt_h;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = lane + kWave * j;
+        lv[j] = lv[j] * f + ((bias && e < E) ? bias[e] : 0.f);
+    }
+    int ik[kMaxTopK];
+    float wk[kMaxTopK];
+    wave_topk_vals(lv, pes, E, K, lane, ik, wk);
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k)
+        if (k < K && lane == k) {
+            topk_idx[(int64_t)t * K + k] = ik[k];
+            topk_w[(int64_t)t * K + k] = wk[k];
+        }
+}
+
+RouterSplit router_split(int T, int H, int E) {
+    const int n_tiles = (T + kRT - 1) / kRT;
+    const int nk = H / kRK;
+    const int ns = E <= 128 ? 6 : 3;
+    // about two workgroups per CU; slices of at least ns K-steps
+    int S = (512 + n_tiles - 1) / n_tiles;
+    S = S < 1 ? 1 : S;
+    const int max_s = (nk + ns - 1) / ns;
+    S = S > max_s ? max_s : S;
+    const int steps = (nk + S - 1) / S;
+    RouterSplit r;
+    r.slice_steps = steps;
+    r.slices = (nk + steps - 1) / steps;
+    return r;
+}
+
+hipError_t launch_router_mfma(const uint16_t* x, const uint16_t* scale, const uint16_t* w,
+                              const float* bias, const float* pes, int T, int H, int E, int K,
+                              float eps, int32_t* topk_idx, float* topk_w, float* partial,
+                              hipStream_t stream) {
+    const float inv_sqrt_h = (float)(1.0 / __builtin_sqrt((double)H));
+    const RouterSplit rs = router_split(T, H, E);
+    const dim3 grid((T + kRT - 1) / kRT, rs.slices);
+    if (E <= 128)
+        hipLaunchKernelGGL((router_partial_kernel<4, 6>), grid, dim3(kRThreads), 0, stream, x, scale,
+                           w, T, H, E, rs.slice_steps, partial);
+    else
+        hipLaunchKernelGGL((router_partial_kernel<8, 3>), grid, dim3(kRThreads), 0, stream, x, scale,
+                           w, T, H, E, rs.slice_steps, partial);
+    hipLaunchKernelGGL(router_finish_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, x, partial,
+                       rs.slices, bias, pes, T, H, E, K, eps, inv_sqrt_h, topk_idx, topk_w);
+    return hipGetLastError();
+}
+
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* scale, const uint16_t* w,
                                 const float* bias, int T, int H, int E, float eps, float* logits,
                                 hipStream_t stream) {

@@ -23,13 +23,13 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Run by a full wavefront. lrow: the token's E fp32 logits (E <= 256).
+// Run by a full wavefront. lv[j]: the token's logit of expert lane + 64 j
+// (E <= 256; entries with that index >= E are ignored).
 // softmax over all E in fp32 (max-subtracted), then the top K by logit; the K
 // probabilities are renormalised to sum 1 (summed in k order) and multiplied
 // by the per-expert scale. Every lane ends with the same ik[0..K), wk[0..K).
-__device__ __forceinline__ void wave_topk(const float* __restrict__ lrow,
-                                          const float* __restrict__ pes, int E, int K, int lane,
-                                          int* ik, float* wk) {
+__device__ __forceinline__ void wave_topk_vals(const float (&lv)[4], const float* __restrict__ pes,
+                                               int E, int K, int lane, int* ik, float* wk) {
     float l[4], ex[4];
     uint32_t key[4];
     bool valid[4];
@@ -37,7 +37,7 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ lrow,
     for (int j = 0; j < 4; ++j) {
         const int e = lane + kWave * j;
         valid[j] = e < E;
-        l[j] = valid[j] ? lrow[e] : -INFINITY;
+        l[j] = valid[j] ? lv[j] : -INFINITY;
         key[j] = valid[j] ? order_key(l[j]) : 0u;
     }
     const int nj = (E + kWave - 1) / kWave;  // uniform
@@ -121,6 +121,19 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ lrow,
     }
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k) wk[k] = (k < K) ? pk[k] / psum * pes[ik[k]] : 0.f;
+}
+
+// Same, with the logits read from lrow[0..E).
+__device__ __forceinline__ void wave_topk(const float* __restrict__ lrow,
+                                          const float* __restrict__ pes, int E, int K, int lane,
+                                          int* ik, float* wk) {
+    float lv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = lane + kWave * j;
+        lv[j] = e < E ? lrow[e] : 0.f;
+    }
+    wave_topk_vals(lv, pes, E, K, lane, ik, wk);
 }
 
 }  // namespace moe
