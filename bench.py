@@ -122,10 +122,10 @@ def stage_work(stage: str, shape, T, n_active, int8):
         "gemm_gateup": (n_active * gu_w + 2 * Id * H * 2 + x + TK * I * 2 + T * Id * 2,
                         2 * TK * H * 2 * I + 2 * T * H * 2 * Id,
                         f"{n_active} experts' gate_up ({gu_w} B each) + dense gate_up + x + h + hd"),
-        "gemm_down_experts": (n_active * dn_w + TK * I * 2 + TK * H * 2, 2 * TK * I * H,
-                              f"{n_active} experts' down ({dn_w} B each) + h + rows"),
-        "gemm_dense_down_combine": (H * Id * 2 + T * Id * 2 + TK * H * 2 + y, 2 * T * Id * H,
-                                    "dense down + hd + expert rows + y"),
+        "gemm_down": (n_active * dn_w + TK * I * 2 + TK * H * 2 + H * Id * 2 + T * Id * 2 + T * H * 4,
+                      2 * TK * I * H + 2 * T * Id * H,
+                      f"{n_active} experts' down ({dn_w} B each) + h + rows + dense down + hd + fp32 dense out"),
+        "combine": (T * H * 4 + TK * H * 2 + TK * 4 + y, TK * H, "fp32 dense out + expert rows + y"),
     }
     return table[stage]
 
@@ -133,7 +133,7 @@ def stage_work(stage: str, shape, T, n_active, int8):
 # ---------------------------------------------------------------- workloads
 def run_workload(name, steps, warmup, layers, dev, ev: HipEvents, log):
     import torch
-    from mixture_experts_ffn_amd import BlockCall, moe_quantize_int8, new_debug, _abi
+    from mixture_experts_ffn_amd import BlockCall, moe_quantize_int8, new_debug, tile_layer, _abi
     from mixture_experts_ffn_amd.ops import BlockDims, LayerWeights
 
     wl = moe_synth.WORKLOADS[name]
@@ -159,9 +159,10 @@ def run_workload(name, steps, warmup, layers, dev, ev: HipEvents, log):
     if wl.int8:
         base.expert_gate_up, base.gate_up_scale = moe_quantize_int8(base.expert_gate_up)
         base.expert_down, base.down_scale = moe_quantize_int8(base.expert_down)
+    base = tile_layer(base)  # the block reads its matrices in the tiled layout
     copies = [base]
     for _ in range(layers - 1):
-        copies.append(LayerWeights(**{k: (None if v is None else v.clone())
+        copies.append(LayerWeights(**{k: (v.clone() if isinstance(v, torch.Tensor) else v)
                                       for k, v in vars(base).items()}))
     dims = BlockDims(s.hidden, s.num_experts, s.top_k, s.expert_inter, s.dense_inter, s.rms_eps)
     xd = bf(x)

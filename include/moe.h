@@ -71,6 +71,22 @@ extern "C" {
 /* Largest T the streaming path accepts (its per-block staging is sized for it). */
 #define MOE_STREAM_MAX_TOKENS 64
 
+/* Storage of the expert and dense weight matrices (moe_weights.layout).
+ * MOE_LAYOUT_TILED is the one the block kernels read: a row-major matrix
+ * W [rows, cols] (rows % 16 == 0, cols % 64 == 0) is cut into 16-row x
+ * 64-column tiles, stored tile-row-major (tile (i, j) at tile index
+ * i * cols/64 + j); inside a tile, element (r, c) sits at lane
+ * 16 * (c / 16) + r, position c % 16 of that lane's 16 values, and
+ *   bf16: tile = 2048 bytes, byte (c % 16 / 8) * 1024 + lane * 16 + (c % 8) * 2
+ *   int8: tile = 1024 bytes, byte lane * 16 + c % 16.
+ * So each 16-byte piece a lane of a 64-lane wavefront needs for one 16x16x32
+ * MFMA operand (or one 16-row GEMV step) is one piece of a contiguous 1 KB
+ * run, and a 16-row block of W is one contiguous stream. A tiled matrix has
+ * the size of the row-major one, and an expert's matrix starts where it would
+ * in the row-major [E, rows, cols] array. moe_tile_weights produces it. */
+#define MOE_LAYOUT_ROWS  0  /* row-major: not accepted by moe_block / dense_mlp */
+#define MOE_LAYOUT_TILED 1
+
 /* Block dimensions. [INF2] "The architecture (a dual-path FFN)": hidden 2816,
  * 128 experts, top 8, expert intermediate 704, dense intermediate 2112.
  * rms_eps: the router's RMSNorm epsilon (added to mean(x^2) inside the root). */
@@ -83,7 +99,8 @@ typedef struct moe_dims {
     float   rms_eps;
 } moe_dims;
 
-/* One layer's weights (all device pointers).
+/* One layer's weights (all device pointers). Router tensors are row-major;
+ * the four expert / dense matrices are in the layout named by `layout`.
  * Router, [ONNX] row "Router": logits = (x / rms(x)) * router_scale * H^-0.5 @ router_w^T
  *   (+ logit_bias), softmax in fp32, top-k, renormalise, * per_expert_scale.
  * Experts, [INF2] "How it works (the recipe)" and [ONNX] row "Mixture of Experts":
@@ -102,6 +119,7 @@ typedef struct moe_weights {
     const float* down_scale;        /* [E, H]  fp32 per-row scales (INT8 only; else ignored) */
     const void*  dense_gate_up;     /* [2Id, H] bf16 */
     const void*  dense_down;        /* [H, Id]  bf16 */
+    int32_t      layout;            /* MOE_LAYOUT_TILED (MOE_LAYOUT_ROWS is rejected) */
 } moe_weights;
 
 #define MOE_MAX_STAGES 8
@@ -120,7 +138,7 @@ typedef struct moe_debug {
     hipEvent_t stage_event[MOE_MAX_STAGES + 1]; /* in: if non-NULL, event i is recorded on `stream`
                                    before stage i and event n_stages after the last one */
     int32_t  path_taken;       /* out (host): the path used */
-    int32_t  n_stages;         /* out (host): stages launched; each stage is one kernel launch */
+    int32_t  n_stages;         /* out (host): stages launched; a stage is one to three kernel launches */
     const char* stage_name[MOE_MAX_STAGES]; /* out (host): kernel of each stage (static strings) */
 } moe_debug;
 
@@ -151,7 +169,7 @@ int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
 
 /* The shared dense MLP alone ([ONNX] row "MoE topology"): y [T, H] bf16 =
  * dense_down @ (gelu_tanh(gate @ x) * (up @ x)), with dense_gate_up [2Id, H]
- * (gate rows first) and dense_down [H, Id], all bf16. Uses d->hidden and
+ * (gate rows first) and dense_down [H, Id], all bf16 and in MOE_LAYOUT_TILED. Uses d->hidden and
  * d->dense_inter; the expert fields of d must still be valid. */
 int dense_mlp(const moe_dims* d, const void* dense_gate_up, const void* dense_down,
               const void* x, int32_t T, void* y, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -164,6 +182,14 @@ int dense_mlp(const moe_dims* d, const void* dense_gate_up, const void* dense_do
  * and scale [rows] fp32. */
 int moe_quantize_int8(const void* w_bf16, int64_t rows, int32_t cols, int8_t* q, float* scale,
                       hipStream_t stream);
+
+/* Re-lays a row-major matrix into MOE_LAYOUT_TILED (see above): src [rows, cols]
+ * of dtype MOE_DTYPE_BF16 or MOE_DTYPE_INT8 -> dst, same size, a different
+ * buffer. An [E, rows, cols] stack of expert matrices is one matrix of E * rows
+ * rows. rows % 16 == 0, cols % 64 == 0, rows >= 0. Pure data movement: the
+ * values are the same bits. */
+int moe_tile_weights(const void* src, int64_t rows, int32_t cols, int32_t dtype, void* dst,
+                     hipStream_t stream);
 
 /* Message for the last non-zero status returned on this thread ("" if none). */
 const char* moe_last_error(void);

@@ -35,6 +35,8 @@ MOE_PATH_STREAM = 1
 MOE_PATH_GROUPED = 2
 MOE_STREAM_MAX_TOKENS = 64
 MOE_MAX_STAGES = 8
+MOE_LAYOUT_ROWS = 0
+MOE_LAYOUT_TILED = 1
 
 
 class MoeDims(ctypes.Structure):
@@ -49,7 +51,7 @@ class MoeWeights(ctypes.Structure):
                 ("expert_gate_up", ctypes.c_void_p), ("expert_down", ctypes.c_void_p),
                 ("expert_dtype", ctypes.c_int32), ("gate_up_scale", ctypes.c_void_p),
                 ("down_scale", ctypes.c_void_p), ("dense_gate_up", ctypes.c_void_p),
-                ("dense_down", ctypes.c_void_p)]
+                ("dense_down", ctypes.c_void_p), ("layout", ctypes.c_int32)]
 
 
 class MoeDebug(ctypes.Structure):
@@ -63,7 +65,7 @@ class MoeDebug(ctypes.Structure):
 
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_block", "dense_mlp",
-           "moe_quantize_int8", "moe_last_error")
+           "moe_quantize_int8", "moe_tile_weights", "moe_last_error")
 
 _lib = None
 
@@ -90,6 +92,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.dense_mlp.restype = ctypes.c_int
     lib.moe_quantize_int8.argtypes = [vp, i64, i32, vp, vp, vp]
     lib.moe_quantize_int8.restype = ctypes.c_int
+    lib.moe_tile_weights.argtypes = [vp, i64, i32, i32, vp, vp]
+    lib.moe_tile_weights.restype = ctypes.c_int
     lib.moe_last_error.argtypes = []
     lib.moe_last_error.restype = ctypes.c_char_p
     if path is None:

@@ -1,23 +1,29 @@
 // Small-batch (decode) path of the MoE FFN block on gfx950.
 //
 // With a handful of tokens per expert the block is bound by reading the
-// touched experts' weights from HBM once. Four launches, each filling the chip:
+// touched experts' weights from HBM once. The weights are in the tiled layout
+// (16 rows x 64 k per tile, lane l of a wavefront owning row l % 16, k
+// 16 (l / 16) .. + 16 of each tile), so a wavefront streams a 16-row block of
+// a matrix as contiguous 1 KB loads; each lane dots its 16-value pieces with
+// the matching x values (from LDS) and four lanes' partial sums make a row.
+// Five launches, each filling the chip:
 //
 //   K1 decode_front: router logits (two experts per wavefront) side by side
-//      with the dense MLP's gate/up rows; both only need x.
+//      with the dense MLP's gate/up tiles; both only need x.
 //   K2 decode_route: one workgroup: softmax/top-k of every token (ONNX export
 //      card, "Truthful graph contracts", row "Router") and the grouping of the
 //      routed pairs by expert (counts, offsets, grouped rows, inverse rows,
 //      list of touched experts).
-//   K3 decode_experts_gateup: 8 gate rows (+ the 8 matching up rows) of one
-//      touched expert per workgroup; every weight row is read exactly once
-//      with wide non-temporal loads issued before anything waits, then dotted
-//      with the expert's tokens staged in LDS.
-//   K4 decode_down: output-stationary. A workgroup owns 8 output features and
-//      reads those rows of every touched expert's down matrix (double-buffered
-//      in registers) and of the dense down matrix, then forms
-//      y = dense + sum_k w_k * expert_k in k order (row "MoE topology") without
-//      a rows buffer and without atomics.
+//   K3 decode_experts_gateup: 16 gate columns (+ the 16 matching up columns)
+//      of one touched expert per workgroup, K split over its 4 wavefronts;
+//      every weight byte is read exactly once with wide non-temporal loads
+//      issued before anything waits, then dotted with the expert's tokens
+//      staged in LDS.
+//   K4 decode_down: one 16-row tile of a touched expert's down matrix per
+//      wavefront (fp32 partial rows per routed pair), and the dense down
+//      matrix with K split over a workgroup's wavefronts.
+//   K5 decode_combine: y = dense + sum_k w_k * expert_k in k order (row "MoE
+//      topology"), without atomics.
 // int8 experts (int8 experts card, "How it works") are read as int8, widened
 // exactly in registers, and their per-row scale multiplies the dot product.
 #include "common.h"
@@ -30,7 +36,7 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kGURows = 8;         // gate rows per gate/up work item: 2 per wavefront
+constexpr int kWaves = kThreads / kWave;
 constexpr int kPass = 4;           // tokens staged per pass
 constexpr int kRouterExperts = 8;  // experts per router work item: 2 per wavefront
 constexpr int kRouteThreads = 1024;
@@ -147,54 +153,104 @@ __device__ __forceinline__ void stage_rows(const uint4* __restrict__ src, int n,
     }
 }
 
-// Gate/up rows [r0, r0 + kGURows) of one [2*inter, H] matrix against the
-// tokens tok(0 .. n_rows): out[p][r] = gelu_tanh(gate_r . x_p) * (up_r . x_p).
-// Lanes 0..31 of a wavefront take a gate row, lanes 32..63 the matching up row;
-// each lane owns NJ 8-element chunks of the row.
-template <int NJ, bool INT8>
-__device__ __forceinline__ void gateup_item(const uint16_t* __restrict__ x, int H, const void* W, const float* Ws,
-                            int inter, int r0, const int32_t* toks, int n_rows,
-                            uint16_t* __restrict__ out, uint4* xs) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int half = lane >> 5, hl = lane & 31;
-    const int ra = r0 + wave * 2, rb = ra + 1;
-    const int64_t rowa = half ? (int64_t)inter + ra : ra;
-    const int64_t rowb = half ? (int64_t)inter + rb : rb;
-    // every weight load of this wavefront is in flight before anything waits
-    uint4 wa[NJ], wb[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int64_t col = (int64_t)(hl + 32 * j) * 8;
-        wa[j] = load_w8<INT8>(W, rowa * H + col);
-        wb[j] = load_w8<INT8>(W, rowb * H + col);
-    }
-    float sa = 1.f, sb = 1.f;
+// 16 int8 (one tiled-layout piece) -> two groups of 8 bf16 (exact)
+__device__ __forceinline__ void i8x16_to_bf16(const uint4& v, uint4& lo, uint4& hi) {
+    lo = i8x8_to_bf16(make_uint4(v.x, v.y, 0u, 0u));
+    hi = i8x8_to_bf16(make_uint4(v.z, v.w, 0u, 0u));
+}
+
+// One K-step of a lane's piece of a tile (bf16: two 16-byte halves, 8 k each;
+// int8: one 16-byte piece, 16 k) dotted with the 16 matching x values.
+template <bool INT8>
+__device__ __forceinline__ float piece_dot(const uint4 (&w)[INT8 ? 1 : 2], const uint16_t* xp,
+                                           float acc) {
+    const uint4 x0 = *reinterpret_cast<const uint4*>(xp);
+    const uint4 x1 = *reinterpret_cast<const uint4*>(xp + 8);
     if (INT8) {
-        sa = Ws[rowa];
-        sb = Ws[rowb];
+        uint4 lo, hi;
+        i8x16_to_bf16(w[0], lo, hi);
+        acc = dot8_bf16(lo, x0, acc);
+        return dot8_bf16(hi, x1, acc);
     }
+    acc = dot8_bf16(w[0], x0, acc);
+    return dot8_bf16(w[INT8 ? 0 : 1], x1, acc);
+}
+
+// sum of the four lanes holding one row of a tile (lanes r, r+16, r+32, r+48)
+__device__ __forceinline__ float tile_row_sum(float v) {
+    v += __shfl_xor(v, 16, kWave);
+    return v + __shfl_xor(v, 32, kWave);
+}
+
+template <bool INT8>
+constexpr int kTileBytes = INT8 ? 1024 : 2048;
+
+// Load steps kt0 .. kt0 + NS - 1 (clamped to the last step nk - 1) of this
+// lane's pieces of a tile whose step 0 starts at `tile`; all loads issued at once.
+template <int NS, bool INT8>
+__device__ __forceinline__ void tile_load(const char* tile, int kt0, int nk, int lane,
+                                          uint4 (&w)[NS][INT8 ? 1 : 2]) {
+    const char* p = tile + lane * 16;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int64_t off = (int64_t)min(kt0 + s, nk - 1) * kTileBytes<INT8>;
+        w[s][0] = ld_nt16(p + off);
+        if (!INT8) w[s][INT8 ? 0 : 1] = ld_nt16(p + off + 1024);
+    }
+}
+
+// Gate/up of 16 h columns (gate tile hc of a tiled [2*inter, H] matrix and the
+// matching up tile inter/16 + hc) against tokens tok(0 .. n_rows):
+// out[p][16 hc + r] = gelu_tanh(gate_r . x_p) * (up_r . x_p). Wavefront w takes
+// K-steps [w NS, (w + 1) NS) of both tiles (NS = H / 256); the four partial
+// sums of a column are added in wavefront order through LDS.
+template <int NS, bool INT8>
+__device__ __forceinline__ void gateup_item(const uint16_t* __restrict__ x, int H, const void* W,
+                                            const float* Ws, int inter, int hc, const int32_t* toks,
+                                            int n_rows, uint16_t* __restrict__ out, uint4* xs,
+                                            float* red) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int nk = H >> 6, kt0 = wave * NS;
+    const char* Wb = reinterpret_cast<const char*>(W);
+    uint4 wg[NS][INT8 ? 1 : 2], wu[NS][INT8 ? 1 : 2];
+    tile_load<NS, INT8>(Wb + (int64_t)hc * nk * kTileBytes<INT8>, kt0, nk, lane, wg);
+    tile_load<NS, INT8>(Wb + (int64_t)(inter / 16 + hc) * nk * kTileBytes<INT8>, kt0, nk, lane, wu);
     const int hc8 = H >> 3;
     for (int pass = 0; pass < n_rows; pass += kPass) {
         const int nt = min(kPass, n_rows - pass);
-        __syncthreads();  // previous pass done with xs
-        stage_x<NJ>(x, H, toks, pass, nt, xs);
+        __syncthreads();  // previous pass done with xs and red
+        stage_x<NS>(x, H, toks, pass, nt, xs);
         __syncthreads();
 #pragma unroll 1
         for (int n = 0; n < nt; ++n) {
-            const uint4* xr = xs + n * hc8 + hl;
-            float acc_a = 0.f, acc_b = 0.f;
+            const uint16_t* xr = reinterpret_cast<const uint16_t*>(xs + n * hc8) + kt0 * 64 + (lane >> 4) * 16;
+            float ag = 0.f, au = 0.f;
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const uint4 xv = xr[32 * j];
-                acc_a = dot8_bf16(as_bf16<INT8>(wa[j]), xv, acc_a);
-                acc_b = dot8_bf16(as_bf16<INT8>(wb[j]), xv, acc_b);
+            for (int s = 0; s < NS; ++s) {
+                ag = piece_dot<INT8>(wg[s], xr + s * 64, ag);
+                au = piece_dot<INT8>(wu[s], xr + s * 64, au);
             }
-            const float va = wave_sum<32>(acc_a) * sa;  // half 0: gate row, half 1: up row
-            const float vb = wave_sum<32>(acc_b) * sb;
-            const float oa = __shfl_xor(va, 32, kWave);
-            const float ob = __shfl_xor(vb, 32, kWave);
-            if (lane == 0) out[(int64_t)(pass + n) * inter + ra] = f32_to_bf16(gelu_tanh(va) * oa);
-            if (lane == 1) out[(int64_t)(pass + n) * inter + rb] = f32_to_bf16(gelu_tanh(vb) * ob);
+            ag = tile_row_sum(ag);
+            au = tile_row_sum(au);
+            if (lane < 16) {
+                red[((wave * kPass + n) * 2) * 16 + lane] = ag;
+                red[((wave * kPass + n) * 2 + 1) * 16 + lane] = au;
+            }
+        }
+        __syncthreads();
+        if (tid < nt * 16) {
+            const int n = tid >> 4, r = tid & 15, col = hc * 16 + r;
+            float g = 0.f, u = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                g += red[((w * kPass + n) * 2) * 16 + r];
+                u += red[((w * kPass + n) * 2 + 1) * 16 + r];
+            }
+            if (INT8) {
+                g *= Ws[col];
+                u *= Ws[inter + col];
+            }
+            out[(int64_t)(pass + n) * inter + col] = f32_to_bf16(gelu_tanh(g) * u);
         }
     }
 }
@@ -268,8 +324,9 @@ __global__ __launch_bounds__(kThreads) void decode_front_kernel(StreamArgs a, co
         router_item<NJ>(a.x, a.H, scale, wr, bias, a.E, tp * kPass, min(a.T, (tp + 1) * kPass), eps,
                         inv_sqrt_h, g * kRouterExperts, logits, xs);
     } else {
-        gateup_item<NJ, false>(a.x, a.H, a.dgu, nullptr, a.Id, (b - n_router) * kGURows, nullptr,
-                               a.T, a.hd, xs);
+        __shared__ float red[kWaves * kPass * 2 * 16];
+        gateup_item<NJ, false>(a.x, a.H, a.dgu, nullptr, a.Id, b - n_router, nullptr, a.T, a.hd, xs,
+                               red);
     }
 }
 
@@ -277,8 +334,9 @@ __global__ __launch_bounds__(kThreads) void decode_front_kernel(StreamArgs a, co
 template <int NJ, bool INT8>
 __global__ __launch_bounds__(kThreads) void decode_experts_gateup_kernel(StreamArgs a) {
     extern __shared__ uint4 xs[];
-    const int ipe = a.I / kGURows;  // items per expert
-    const int slot = blockIdx.x / ipe, g = blockIdx.x - slot * ipe;
+    __shared__ float red[kWaves * kPass * 2 * 16];
+    const int ipe = a.I / 16;  // items (16 h columns) per expert
+    const int slot = blockIdx.x / ipe, hc = blockIdx.x - slot * ipe;
     if (slot >= *a.n_active) return;
     const int e = a.active[slot];
     const int p0 = a.offsets[e], n = a.offsets[e + 1] - p0;
@@ -286,8 +344,8 @@ __global__ __launch_bounds__(kThreads) void decode_experts_gateup_kernel(StreamA
     const void* W = INT8 ? (const void*)((const int8_t*)a.gu + e * wstride)
                          : (const void*)((const uint16_t*)a.gu + e * wstride);
     const float* Ws = INT8 ? a.gu_scale + (int64_t)e * 2 * a.I : nullptr;
-    gateup_item<NJ, INT8>(a.x, a.H, W, Ws, a.I, g * kGURows, a.perm_token + p0, n,
-                          a.h + (int64_t)p0 * a.I, xs);
+    gateup_item<NJ, INT8>(a.x, a.H, W, Ws, a.I, hc, a.perm_token + p0, n, a.h + (int64_t)p0 * a.I,
+                          xs, red);
 }
 
 // ---------------------------------------------------------------- K2
@@ -369,73 +427,85 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(StreamArgs 
 }
 
 // ---------------------------------------------------------------- K4
-// Down projections as independent work items of one touched expert's down
-// matrix (or of the dense down matrix). LPR lanes share a row (8 for the
-// 704-wide expert rows, 32 for the 2112-wide dense rows), each lane owning
-// chunks sub + LPR*j. Each weight row is read once; the item's token rows of h
-// (or hd) are staged in LDS. Outputs are fp32 partial rows: part[p][row] for
-// grouped row p, dpart[t][row] for the dense MLP.
-template <int LPR, int MAXC, bool INT8>
-__device__ __forceinline__ void down_item(const void* W, const float* Ws, int inter, int H, int r0,
-                                          const uint16_t* __restrict__ hrows, int n_rows,
-                                          float* __restrict__ out, uint4* hs) {
-    constexpr int kRPW = kWave / LPR;  // rows per wavefront
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int sub = lane % LPR;
-    const int64_t row = r0 + wave * kRPW + lane / LPR;
-    const int hc8 = inter >> 3;
-    uint4 w[MAXC];
+// Down projections. A wavefront reads K-steps [kt0, kt0 + n_steps) (n_steps <=
+// NS) of one 16-row tile of a tiled [H, inter] matrix and dots them with the
+// token rows of h (or hd) staged in LDS; returns, in lanes 0..15, the partial
+// sum of row lane of the tile for token n of the pass.
+template <int NS, bool INT8>
+__device__ __forceinline__ float down_dot(const uint4 (&w)[NS][INT8 ? 1 : 2], const uint16_t* hrow,
+                                          int kt0, int n_steps, int lane) {
+    const uint16_t* hp = hrow + kt0 * 64 + (lane >> 4) * 16;
+    float acc = 0.f;
 #pragma unroll
-    for (int j = 0; j < MAXC; ++j) {
-        const int c = sub + LPR * j;
-        if (c < hc8) w[j] = load_w8<INT8>(W, row * inter + (int64_t)c * 8);
-    }
-    const float sc = INT8 ? Ws[row] : 1.f;
-    for (int pass = 0; pass < n_rows; pass += kPass) {
-        const int nt = min(kPass, n_rows - pass);
-        __syncthreads();
-        constexpr int kPer = (kPass * LPR * MAXC + kThreads - 1) / kThreads;
-        stage_rows<kPer>(reinterpret_cast<const uint4*>(hrows + (int64_t)pass * inter), nt * hc8, hs);
-        __syncthreads();
-#pragma unroll 1
-        for (int n = 0; n < nt; ++n) {
-            float acc = 0.f;
-#pragma unroll
-            for (int j = 0; j < MAXC; ++j) {
-                const int c = sub + LPR * j;
-                if (c < hc8) acc = dot8_bf16(as_bf16<INT8>(w[j]), hs[n * hc8 + c], acc);
-            }
-#pragma unroll
-            for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off, kWave);
-            if (sub == 0) out[(int64_t)(pass + n) * H + row] = acc * sc;
-        }
-    }
+    for (int s = 0; s < NS; ++s)
+        if (s < n_steps) acc = piece_dot<INT8>(w[s], hp + s * 64, acc);
+    return tile_row_sum(acc);
 }
 
-constexpr int kExpertDownRows = 32;  // rows per expert down item (8 lanes per row)
-constexpr int kDenseDownRows = 8;    // rows per dense down item (32 lanes per row)
-
-template <int MAXIC, int MAXDC, bool INT8>
+template <int NS, bool INT8>
 __global__ __launch_bounds__(kThreads) void decode_down_kernel(StreamArgs a) {
-    extern __shared__ uint4 hs[];  // [kPass][max(I, Id)/8]
-    const int ipe = a.H / kExpertDownRows;
+    extern __shared__ uint4 hs[];  // [kPass][max(I, Id)] bf16
+    __shared__ float red[kWaves * kPass * 16];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int ipe = a.H / 64;  // expert items: 4 tiles (one per wavefront) of 16 rows
     const int expert_items = a.max_active * ipe;
     const int b = blockIdx.x;
     if (b < expert_items) {
         const int slot = b / ipe, g = b - slot * ipe;
         if (slot >= *a.n_active) return;
         const int e = a.active[slot];
-        const int p0 = a.offsets[e], n = a.offsets[e + 1] - p0;
+        const int p0 = a.offsets[e], n_rows = a.offsets[e + 1] - p0;
         const int64_t wstride = (int64_t)a.H * a.I;
-        const void* W = INT8 ? (const void*)((const int8_t*)a.dw + e * wstride)
-                             : (const void*)((const uint16_t*)a.dw + e * wstride);
-        const float* Ws = INT8 ? a.dw_scale + (int64_t)e * a.H : nullptr;
-        down_item<8, MAXIC, INT8>(W, Ws, a.I, a.H, g * kExpertDownRows, a.h + (int64_t)p0 * a.I, n,
-                                  a.part + (int64_t)p0 * a.H, hs);
+        const char* W = INT8 ? (const char*)((const int8_t*)a.dw + e * wstride)
+                             : (const char*)((const uint16_t*)a.dw + e * wstride);
+        const int nk = a.I >> 6, tile = g * kWaves + wave;
+        uint4 w[NS][INT8 ? 1 : 2];
+        tile_load<NS, INT8>(W + (int64_t)tile * nk * kTileBytes<INT8>, 0, nk, lane, w);
+        const float sc = INT8 ? a.dw_scale[(int64_t)e * a.H + tile * 16 + (lane & 15)] : 1.f;
+        const int hc8 = a.I >> 3;
+        for (int pass = 0; pass < n_rows; pass += kPass) {
+            const int nt = min(kPass, n_rows - pass);
+            __syncthreads();
+            stage_rows<(kPass * 128 + kThreads - 1) / kThreads>(
+                reinterpret_cast<const uint4*>(a.h + (int64_t)(p0 + pass) * a.I), nt * hc8, hs);
+            __syncthreads();
+#pragma unroll 1
+            for (int n = 0; n < nt; ++n) {
+                const float v = down_dot<NS, INT8>(w, reinterpret_cast<const uint16_t*>(hs + n * hc8), 0,
+                                                   nk, lane);
+                if (lane < 16) a.part[(int64_t)(p0 + pass + n) * a.H + tile * 16 + lane] = v * sc;
+            }
+        }
     } else {
-        const int g = b - expert_items;
-        down_item<32, MAXDC, false>(a.ddw, nullptr, a.Id, a.H, g * kDenseDownRows, a.hd, a.T,
-                                    a.dpart, hs);
+        // dense down: one 16-row tile per workgroup, K split over the wavefronts
+        const int tile = b - expert_items;
+        const int nk = a.Id >> 6, kd = (nk + kWaves - 1) / kWaves;
+        const int kt0 = wave * kd, n_steps = max(0, min(kd, nk - kt0));
+        uint4 w[NS][2];
+        tile_load<NS, false>(reinterpret_cast<const char*>(a.ddw) + (int64_t)tile * nk * kTileBytes<false>,
+                             kt0, nk, lane, w);
+        const int hc8 = a.Id >> 3;
+        for (int pass = 0; pass < a.T; pass += kPass) {
+            const int nt = min(kPass, a.T - pass);
+            __syncthreads();
+            stage_rows<(kPass * 512 + kThreads - 1) / kThreads>(
+                reinterpret_cast<const uint4*>(a.hd + (int64_t)pass * a.Id), nt * hc8, hs);
+            __syncthreads();
+#pragma unroll 1
+            for (int n = 0; n < nt; ++n) {
+                const float v = down_dot<NS, false>(w, reinterpret_cast<const uint16_t*>(hs + n * hc8),
+                                                    kt0, n_steps, lane);
+                if (lane < 16) red[(wave * kPass + n) * 16 + lane] = v;
+            }
+            __syncthreads();
+            if (tid < nt * 16) {
+                const int n = tid >> 4, r = tid & 15;
+                float v = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < kWaves; ++ww) v += red[(ww * kPass + n) * 16 + r];
+                a.dpart[(int64_t)(pass + n) * a.H + tile * 16 + r] = v;
+            }
+        }
     }
 }
 
@@ -478,7 +548,7 @@ hipError_t launch_front_nj(const StreamArgs& a, const uint16_t* scale, const uin
                            hipStream_t stream) {
     const int n_router =
         router ? ((a.E + kRouterExperts - 1) / kRouterExperts) * ((a.T + kPass - 1) / kPass) : 0;
-    const int blocks = n_router + a.Id / kGURows;
+    const int blocks = n_router + a.Id / 16;
     const size_t lds = (size_t)kPass * a.H * sizeof(uint16_t);
     const float inv_sqrt_h = (float)(1.0 / __builtin_sqrt((double)a.H));
     StreamArgs b = a;
@@ -490,7 +560,7 @@ hipError_t launch_front_nj(const StreamArgs& a, const uint16_t* scale, const uin
 
 template <int NJ>
 hipError_t launch_experts_nj(const StreamArgs& a, bool int8, hipStream_t stream) {
-    const int blocks = a.max_active * (a.I / kGURows);
+    const int blocks = a.max_active * (a.I / 16);
     const size_t lds = (size_t)kPass * a.H * sizeof(uint16_t);
     if (int8)
         hipLaunchKernelGGL((decode_experts_gateup_kernel<NJ, true>), dim3(blocks), dim3(kThreads), lds, stream, a);
@@ -501,7 +571,7 @@ hipError_t launch_experts_nj(const StreamArgs& a, bool int8, hipStream_t stream)
 
 }  // namespace
 
-// NJ = H / 256 chunks per lane; instantiated for hidden sizes up to 4096.
+// NJ = H / 256 K-steps per wavefront; instantiated for hidden sizes up to 3072.
 #define MOE_NJ_SWITCH(nj, CALL)                                   \
     switch (nj) {                                                 \
         case 1: return CALL(1);   case 2: return CALL(2);         \
@@ -510,8 +580,6 @@ hipError_t launch_experts_nj(const StreamArgs& a, bool int8, hipStream_t stream)
         case 7: return CALL(7);   case 8: return CALL(8);         \
         case 9: return CALL(9);   case 10: return CALL(10);       \
         case 11: return CALL(11); case 12: return CALL(12);       \
-        case 13: return CALL(13); case 14: return CALL(14);       \
-        case 15: return CALL(15); case 16: return CALL(16);       \
         default: return hipErrorInvalidValue;                     \
     }
 
@@ -536,27 +604,24 @@ hipError_t launch_decode_experts_gateup(const StreamArgs& a, bool int8, hipStrea
 }
 
 hipError_t launch_decode_down(const StreamArgs& a, bool int8, hipStream_t stream) {
-    const int ic = a.I / 64;             // expert chunks per lane (8 lanes per row)
-    const int dc = (a.Id / 8 + 31) / 32;  // dense chunks per lane (32 lanes per row)
-    const int blocks = a.max_active * (a.H / kExpertDownRows) + a.H / kDenseDownRows;
+    // K-steps a wavefront holds: a whole expert tile (I / 64) or a quarter of
+    // a dense tile (Id / 256, rounded up)
+    const int need = max(a.I / 64, (a.Id / 64 + kWaves - 1) / kWaves);
+    const int blocks = a.max_active * (a.H / 64) + a.H / 16;
     const size_t lds = (size_t)kPass * (a.I > a.Id ? a.I : a.Id) * sizeof(uint16_t);
     const dim3 grid(blocks), block(kThreads);
-#define LAUNCH(M, D)                                                                                   \
-    do {                                                                                               \
-        if (int8) hipLaunchKernelGGL((decode_down_kernel<M, D, true>), grid, block, lds, stream, a);   \
-        else hipLaunchKernelGGL((decode_down_kernel<M, D, false>), grid, block, lds, stream, a);       \
-        return hipGetLastError();                                                                      \
+#define LAUNCH(N)                                                                                   \
+    do {                                                                                            \
+        if (int8) hipLaunchKernelGGL((decode_down_kernel<N, true>), grid, block, lds, stream, a);   \
+        else hipLaunchKernelGGL((decode_down_kernel<N, false>), grid, block, lds, stream, a);       \
+        return hipGetLastError();                                                                   \
     } while (0)
-#define DENSE(M)                     \
-    do {                             \
-        if (dc <= 2) LAUNCH(M, 2);   \
-        if (dc <= 9) LAUNCH(M, 9);   \
-        if (dc <= 16) LAUNCH(M, 16); \
-    } while (0)
-    if (ic <= 4) DENSE(4);
-    if (ic <= 12) DENSE(12);
-    if (ic <= 16) DENSE(16);
-#undef DENSE
+    if (need <= 2) LAUNCH(2);
+    if (need <= 4) LAUNCH(4);
+    if (need <= 8) LAUNCH(8);
+    if (need <= 11) LAUNCH(11);
+    if (need <= 12) LAUNCH(12);
+    if (need <= 16) LAUNCH(16);
 #undef LAUNCH
     return hipErrorInvalidValue;
 }

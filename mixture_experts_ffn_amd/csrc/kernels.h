@@ -52,7 +52,7 @@ hipError_t launch_permute(const int32_t* topk_idx, const float* topk_w, int32_t*
                           int T, int K, int E, int BM, const PermuteOut& o, hipStream_t stream);
 
 // ---- grouped MFMA GEMMs (gemm.hip) -----------------------------------------
-constexpr int kGemmBM = 256;  // rows per grouped M-tile
+constexpr int kGemmBM = 128;  // rows per grouped M-tile
 constexpr int kMaxTopKGemm = 8;
 struct GemmArgs {
     const uint16_t* A; int64_t lda;          // bf16 activations
@@ -67,13 +67,18 @@ struct GemmArgs {
     int M_dense;                              // rows when not grouped
     int max_mtiles;                           // grid height
     uint16_t* C; int64_t ldc;                 // bf16 output
-    const float* row_w;                       // down: per-row weight
-    const uint16_t* comb; const int32_t* inv_row; int topk;  // combine: rows added to y
+    float* Cf;                                // down: fp32 output instead (dense MLP)
+    const float* row_w;                       // down: per-row weight of the bf16 output (null = 1)
 };
-// gate/up of `a`, and of `dense` (bf16, may be null) in the same launch
-hipError_t launch_gemm_gateup(const GemmArgs& a, const GemmArgs* dense, bool int8, hipStream_t stream);
-hipError_t launch_gemm_down(const GemmArgs& a, bool int8, hipStream_t stream);
-hipError_t launch_gemm_combine(const GemmArgs& a, hipStream_t stream);
+// gate/up + GELU of the experts, and of `dense` (bf16, may be null), in one launch
+hipError_t launch_gemm_gateup(const GemmArgs& experts, const GemmArgs* dense, bool int8,
+                              hipStream_t stream);
+// down of the experts (weighted bf16 rows) and of `dense` (fp32, may be null), in one launch
+hipError_t launch_gemm_down(const GemmArgs& experts, const GemmArgs* dense, bool int8,
+                            hipStream_t stream);
+// y[t] = dense_out[t] + sum_k rows[inv_row[t*K + k]], in k order, rounded once to bf16
+hipError_t launch_combine(const float* dense_out, const uint16_t* rows, const int32_t* inv_row,
+                          int T, int H, int K, uint16_t* y, hipStream_t stream);
 
 // ---- small-batch path (decode.hip) ----------------------------------------
 struct StreamArgs {
@@ -108,6 +113,9 @@ hipError_t launch_decode_down(const StreamArgs& a, bool int8, hipStream_t stream
 hipError_t launch_decode_combine(const StreamArgs& a, hipStream_t stream);
 
 // ---- int8 quantiser (quant.hip) -------------------------------------------
+// row-major [rows, cols] -> tiled layout (16 x 64 tiles); rows % 16 == 0, cols % 64 == 0
+hipError_t launch_tile_weights(const void* src, int64_t rows, int cols, bool int8, void* dst,
+                               hipStream_t stream);
 hipError_t launch_quantize_int8(const uint16_t* w, int64_t rows, int cols, int8_t* q, float* scale,
                                 hipStream_t stream);
 

@@ -40,7 +40,7 @@ static_assert(kRouterMfmaMinT >= MOE_STREAM_MAX_TOKENS, "the streaming path stag
 struct Layout {
     size_t logits, partial, topk_idx, topk_w, pair_rank, tile_counts, counts, offsets, active, n_active;
     size_t perm_token, perm_w, inv_row, mtile_group, mtile_row0, n_mtiles, h, hd, rows;
-    size_t part, dpart, total;
+    size_t dout, part, dpart, total;
     int max_mtiles;
 };
 
@@ -77,6 +77,7 @@ Layout make_layout(const moe_dims& d, int64_t T) {
     L.h = take(TK * d.expert_inter * 2);
     L.hd = take(T * d.dense_inter * 2);
     L.rows = take(TK * d.hidden * 2);
+    L.dout = take(T * d.hidden * 4);  // dense MLP output (fp32) before the combine
     // streaming-path scratch (only T <= MOE_STREAM_MAX_TOKENS uses it)
     const int64_t Ts = T <= MOE_STREAM_MAX_TOKENS ? T : 0;
     L.part = take(Ts * K * d.hidden * 4);
@@ -154,7 +155,7 @@ int stream_limit() {
 }
 
 bool stream_fits(const moe_dims& d) {
-    return d.hidden <= 4096 && d.expert_inter <= 1024 && d.dense_inter <= 4096;
+    return d.hidden <= 3072 && d.expert_inter <= 1024 && d.dense_inter <= 4096;
 }
 
 // Records the stage events of a debug struct around each launch.
@@ -226,6 +227,9 @@ int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
               moe_debug* dbg, void* ws, size_t ws_bytes, hipStream_t stream) {
     int rc;
     if ((rc = check_dims(d)) || (rc = check_T(T)) || (rc = check_weights(w))) return rc;
+    if (w->layout != MOE_LAYOUT_TILED)
+        return fail(MOE_ERR_UNSUPPORTED, "layout=%d: expert and dense weights must be MOE_LAYOUT_TILED "
+                    "(see moe_tile_weights)", w->layout);
     if (T > 0) {  // empty batch: x, y and ws may be NULL
         CHECK_PTR(x, "x", 16);
         CHECK_PTR(y, "y", 16);
@@ -238,7 +242,7 @@ int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
         path = (T <= stream_limit() && stream_fits(*d)) ? MOE_PATH_STREAM : MOE_PATH_GROUPED;
     if (path == MOE_PATH_STREAM && (T > MOE_STREAM_MAX_TOKENS || !stream_fits(*d)))
         return fail(MOE_ERR_UNSUPPORTED,
-                    "streaming path needs T <= %d, hidden <= 4096, expert_inter <= 1024, dense_inter <= 4096",
+                    "streaming path needs T <= %d, hidden <= 3072, expert_inter <= 1024, dense_inter <= 4096",
                     MOE_STREAM_MAX_TOKENS);
     g_err[0] = 0;
     if (dbg) {
@@ -330,15 +334,16 @@ int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
         gw.mtile_group = po.mtile_group; gw.mtile_row0 = po.mtile_row0; gw.n_mtiles = po.n_mtiles;
         gw.group_end = po.offsets; gw.max_mtiles = L.max_mtiles;
         gw.C = rows; gw.ldc = H; gw.row_w = po.perm_w;
-        HIP_TRY(st.begin("gemm_down_experts"), "event record");
-        HIP_TRY(moe::launch_gemm_down(gw, int8, stream), "gemm_down launch");
-        // dense down + combine
+        // dense down (fp32), in the same launch
+        float* dout = at<float>(ws, L.dout);
         moe::GemmArgs gc{};
         gc.A = hd; gc.lda = Id; gc.B = w->dense_down; gc.ldb = Id; gc.K = Id; gc.n_out = H;
-        gc.M_dense = T; gc.C = (uint16_t*)y; gc.ldc = H;
-        gc.comb = rows; gc.inv_row = po.inv_row; gc.topk = K;
-        HIP_TRY(st.begin("gemm_dense_down_combine"), "event record");
-        HIP_TRY(moe::launch_gemm_combine(gc, stream), "gemm_combine launch");
+        gc.M_dense = T; gc.Cf = dout; gc.ldc = H;
+        HIP_TRY(st.begin("gemm_down"), "event record");
+        HIP_TRY(moe::launch_gemm_down(gw, &gc, int8, stream), "gemm_down launch");
+        HIP_TRY(st.begin("combine"), "event record");
+        HIP_TRY(moe::launch_combine(dout, rows, po.inv_row, T, H, K, (uint16_t*)y, stream),
+                "combine launch");
     }
     HIP_TRY(st.end(), "event record");
 
@@ -392,7 +397,7 @@ int dense_mlp(const moe_dims* d, const void* dense_gate_up, const void* dense_do
         moe::GemmArgs gc{};
         gc.A = hd; gc.lda = Id; gc.B = dense_down; gc.ldb = Id; gc.K = Id; gc.n_out = H;
         gc.M_dense = T; gc.C = (uint16_t*)y; gc.ldc = H;
-        HIP_TRY(moe::launch_gemm_combine(gc, stream), "gemm_combine launch");
+        HIP_TRY(moe::launch_gemm_down(gc, nullptr, false, stream), "gemm_down dense launch");
     }
     return MOE_OK;
 }
@@ -409,6 +414,23 @@ int moe_quantize_int8(const void* w_bf16, int64_t rows, int32_t cols, int8_t* q,
     if (rows == 0) return MOE_OK;
     HIP_TRY(moe::launch_quantize_int8((const uint16_t*)w_bf16, rows, cols, q, scale, stream),
             "quantize launch");
+    return MOE_OK;
+}
+
+int moe_tile_weights(const void* src, int64_t rows, int32_t cols, int32_t dtype, void* dst,
+                     hipStream_t stream) {
+    if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_INT8)
+        return fail(MOE_ERR_UNSUPPORTED, "dtype %d", dtype);
+    if (rows < 0 || rows % 16 || cols <= 0 || cols % 64)
+        return fail(MOE_ERR_SHAPE, "rows=%lld cols=%d (need rows %% 16 == 0, cols %% 64 == 0)",
+                    (long long)rows, cols);
+    CHECK_PTR(src, "src", 16);
+    CHECK_PTR(dst, "dst", 16);
+    if (src == dst) return fail(MOE_ERR_SHAPE, "src and dst must be different buffers");
+    g_err[0] = 0;
+    if (rows == 0) return MOE_OK;
+    HIP_TRY(moe::launch_tile_weights(src, rows, cols, dtype == MOE_DTYPE_INT8, dst, stream),
+            "tile launch");
     return MOE_OK;
 }
 

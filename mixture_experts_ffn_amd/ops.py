@@ -39,7 +39,9 @@ class BlockDims:
 
 @dataclasses.dataclass
 class LayerWeights:
-    """Device tensors of one layer (layouts as in include/moe.h)."""
+    """Device tensors of one layer (layouts as in include/moe.h). The expert and
+    dense matrices must be in the tiled layout for moe_block: tile_layer()
+    returns such a copy of a layer held row-major."""
     router_scale: torch.Tensor            # [H] bf16
     router_w: torch.Tensor                # [E, H] bf16
     per_expert_scale: torch.Tensor        # [E] fp32
@@ -50,6 +52,7 @@ class LayerWeights:
     logit_bias: Optional[torch.Tensor] = None   # [E] fp32
     gate_up_scale: Optional[torch.Tensor] = None  # [E, 2I] fp32 (int8)
     down_scale: Optional[torch.Tensor] = None     # [E, H] fp32 (int8)
+    layout: int = _abi.MOE_LAYOUT_ROWS            # of the four expert / dense matrices
 
     @property
     def expert_dtype(self) -> int:
@@ -61,7 +64,7 @@ class LayerWeights:
         return MoeWeights(ptr(self.router_scale), ptr(self.router_w), ptr(self.per_expert_scale),
                           ptr(self.logit_bias), ptr(self.expert_gate_up), ptr(self.expert_down),
                           self.expert_dtype, ptr(self.gate_up_scale), ptr(self.down_scale),
-                          ptr(self.dense_gate_up), ptr(self.dense_down))
+                          ptr(self.dense_gate_up), ptr(self.dense_down), int(self.layout))
 
 
 def _lib():
@@ -163,6 +166,38 @@ def moe_quantize_int8(w: torch.Tensor, q=None, scale=None, stream=None):
                                   _dev(scale, "scale").data_ptr(), _stream(stream))
     _check(rc, "moe_quantize_int8")
     return q, scale
+
+
+def moe_tile_weights(w: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+    """Tiled-layout copy of a row-major bf16 or int8 matrix [..., rows, cols]
+    (all leading dimensions stacked as rows). Same shape and dtype; the data is
+    re-laid into 16 x 64 tiles (include/moe.h, MOE_LAYOUT_TILED)."""
+    w = _dev(w, "w")
+    if w.dtype == torch.bfloat16:
+        dtype = _abi.MOE_DTYPE_BF16
+    elif w.dtype == torch.int8:
+        dtype = _abi.MOE_DTYPE_INT8
+    else:
+        raise TypeError(f"w must be bf16 or int8, got {w.dtype}")
+    cols = w.shape[-1]
+    rows = w.numel() // cols
+    if out is None:
+        out = torch.empty_like(w)
+    rc = _lib().moe_tile_weights(w.data_ptr(), rows, cols, dtype, _dev(out, "out").data_ptr(),
+                                 _stream(stream))
+    _check(rc, "moe_tile_weights")
+    return out
+
+
+def tile_layer(w: LayerWeights, stream=None) -> LayerWeights:
+    """A copy of a row-major layer with its expert and dense matrices tiled."""
+    if w.layout == _abi.MOE_LAYOUT_TILED:
+        return w
+    return dataclasses.replace(
+        w, expert_gate_up=moe_tile_weights(w.expert_gate_up, stream=stream),
+        expert_down=moe_tile_weights(w.expert_down, stream=stream),
+        dense_gate_up=moe_tile_weights(w.dense_gate_up, stream=stream),
+        dense_down=moe_tile_weights(w.dense_down, stream=stream), layout=_abi.MOE_LAYOUT_TILED)
 
 
 class BlockCall:

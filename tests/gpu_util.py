@@ -6,7 +6,7 @@ import torch
 
 import moe_synth
 import oracle
-from mixture_experts_ffn_amd import BlockDims, LayerWeights, moe_quantize_int8
+from mixture_experts_ffn_amd import BlockDims, LayerWeights, moe_quantize_int8, tile_layer
 
 COS_MIN = 0.9999
 REL_BF16 = 1e-2
@@ -28,8 +28,9 @@ def f32_dev(a, dev):
 
 
 def upload(w: dict, dev, int8: bool = False) -> LayerWeights:
-    """Device copy of a generated layer. int8 experts are quantised on the GPU
-    by the library's own quantiser."""
+    """Device copy of a generated layer, its expert and dense matrices in the
+    tiled layout the block reads. int8 experts are quantised on the GPU by the
+    library's own quantiser (row-major), then tiled."""
     gu = bf16_dev(w["expert_gate_up"], dev)
     dn = bf16_dev(w["expert_down"], dev)
     lw = LayerWeights(
@@ -41,7 +42,7 @@ def upload(w: dict, dev, int8: bool = False) -> LayerWeights:
         lw.expert_gate_up, lw.gate_up_scale = moe_quantize_int8(gu)
         lw.expert_down, lw.down_scale = moe_quantize_int8(dn)
         del gu, dn
-    return lw
+    return tile_layer(lw)
 
 
 def oracle_int8_weights(w: dict) -> dict:

@@ -57,7 +57,8 @@ FAKE = 0x7F0000000000  # 256-aligned host-side value; never dereferenced
 
 
 def _weights(**over):
-    w = _abi.MoeWeights(FAKE, FAKE, FAKE, None, FAKE, FAKE, _abi.MOE_DTYPE_BF16, None, None, FAKE, FAKE)
+    w = _abi.MoeWeights(FAKE, FAKE, FAKE, None, FAKE, FAKE, _abi.MOE_DTYPE_BF16, None, None, FAKE, FAKE,
+                        _abi.MOE_LAYOUT_TILED)
     for k, v in over.items():
         setattr(w, k, v)
     return w
@@ -107,6 +108,9 @@ def test_block_argument_errors(L):
     # int8 experts need their scales
     assert call(w=_weights(expert_dtype=_abi.MOE_DTYPE_INT8)) == _abi.MOE_ERR_NULL
     assert b"gate_up_scale" in L.moe_last_error()
+    # the block reads tiled weights only
+    assert call(w=_weights(layout=_abi.MOE_LAYOUT_ROWS)) == _abi.MOE_ERR_UNSUPPORTED
+    assert b"moe_tile_weights" in L.moe_last_error()
     # an empty batch is a valid no-op (nothing is launched)
     assert call(T=0, ws_bytes=L.moe_workspace_bytes(ctypes.byref(d), 0)) == _abi.MOE_OK
     assert call(T=0, x=None, y=None, ws=None, ws_bytes=0) == _abi.MOE_OK
@@ -138,3 +142,15 @@ def test_route_dense_quant_argument_errors(L):
     assert L.moe_quantize_int8(FAKE, -1, 16, FAKE, FAKE, None) == _abi.MOE_ERR_SHAPE
     assert L.moe_quantize_int8(FAKE, 0, 16, FAKE, FAKE, None) == _abi.MOE_OK
     assert L.moe_quantize_int8(FAKE + 4, 4, 16, FAKE, FAKE, None) == _abi.MOE_ERR_ALIGN
+
+
+def test_tile_weights_argument_errors(L):
+    OTHER = FAKE + 4096
+    assert L.moe_tile_weights(FAKE, 24, 128, _abi.MOE_DTYPE_BF16, OTHER, None) == _abi.MOE_ERR_SHAPE
+    assert L.moe_tile_weights(FAKE, 32, 96, _abi.MOE_DTYPE_BF16, OTHER, None) == _abi.MOE_ERR_SHAPE
+    assert L.moe_tile_weights(FAKE, -16, 128, _abi.MOE_DTYPE_INT8, OTHER, None) == _abi.MOE_ERR_SHAPE
+    assert L.moe_tile_weights(FAKE, 32, 128, 5, OTHER, None) == _abi.MOE_ERR_UNSUPPORTED
+    assert L.moe_tile_weights(None, 32, 128, _abi.MOE_DTYPE_BF16, OTHER, None) == _abi.MOE_ERR_NULL
+    assert L.moe_tile_weights(FAKE + 8, 32, 128, _abi.MOE_DTYPE_BF16, OTHER, None) == _abi.MOE_ERR_ALIGN
+    assert L.moe_tile_weights(FAKE, 32, 128, _abi.MOE_DTYPE_BF16, FAKE, None) == _abi.MOE_ERR_SHAPE
+    assert L.moe_tile_weights(FAKE, 0, 128, _abi.MOE_DTYPE_INT8, OTHER, None) == _abi.MOE_OK

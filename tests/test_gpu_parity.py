@@ -16,7 +16,8 @@ import torch
 import moe_synth
 import oracle
 from mixture_experts_ffn_amd import (MOE_PATH_GROUPED, MOE_PATH_STREAM, MoEError, dense_mlp,
-                                     moe_block, moe_quantize_int8, moe_route, new_debug)
+                                     moe_block, moe_quantize_int8, moe_route, moe_tile_weights,
+                                     new_debug)
 from gpu_util import (REL_BF16, REL_INT8, bf16_dev, check_routing, compare_y, dims_of,
                       oracle_int8_weights, routing_for, to_np, upload, y_f64)
 
@@ -77,6 +78,55 @@ def run_block(wl, lw, xd, path):
 
 
 # ----------------------------------------------------------------------------
+def _tiled_reference(w: np.ndarray) -> np.ndarray:
+    """The tiled layout as the header defines it, from index arithmetic:
+    element (r, c) of tile (r // 16, c // 64) sits at lane 16 ((c % 64) // 16)
+    + r % 16, position c % 16 of that lane; bf16 tiles store positions 0..7 of
+    all lanes, then 8..15; int8 tiles store each lane's 16 positions together."""
+    rows, cols = w.shape
+    out = np.empty(w.size, dtype=w.dtype)
+    tb = 1024 if w.dtype == np.int8 else 2048
+    esz = w.dtype.itemsize
+    for r in range(rows):
+        for c in range(cols):
+            tile = (r // 16) * (cols // 64) + c // 64
+            lane = 16 * ((c % 64) // 16) + r % 16
+            pos = c % 16
+            if esz == 1:
+                byte = lane * 16 + pos
+            else:
+                byte = (pos // 8) * 1024 + lane * 16 + (pos % 8) * 2
+            out[(tile * tb + byte) // esz] = w[r, c]
+    return out
+
+
+def _tiled(w: np.ndarray) -> np.ndarray:
+    """Vectorised form of _tiled_reference (checked against it below)."""
+    rows, cols = w.shape
+    if w.dtype == np.int8:  # (ti, r, tj, g, pos) -> (ti, tj, g, r, pos)
+        return w.reshape(rows // 16, 16, cols // 64, 4, 16).transpose(0, 2, 3, 1, 4).ravel()
+    # (ti, r, tj, g, h, e) -> (ti, tj, h, g, r, e)
+    return w.reshape(rows // 16, 16, cols // 64, 4, 2, 8).transpose(0, 2, 4, 3, 1, 5).ravel()
+
+
+@pytest.mark.parametrize("dtype,shape", [("bf16", (48, 192)), ("int8", (32, 128)), ("bf16", (2, 16, 64))])
+def test_tile_weights_layout(dev, dtype, shape):
+    say(f"case: moe_tile_weights {dtype} {shape}")
+    rng = np.random.default_rng(7)
+    if dtype == "bf16":
+        w = rng.integers(-32768, 32767, size=shape, dtype=np.int16)
+        t = moe_tile_weights(torch.from_numpy(w).view(torch.bfloat16).to(dev))
+        got = to_np(t.view(torch.int16)).ravel()
+    else:
+        w = rng.integers(-127, 128, size=shape, dtype=np.int8)
+        t = moe_tile_weights(torch.from_numpy(w).to(dev))
+        got = to_np(t).ravel()
+    torch.cuda.synchronize()
+    ref = _tiled_reference(w.reshape(-1, shape[-1]))
+    np.testing.assert_array_equal(got, ref)
+    np.testing.assert_array_equal(_tiled(w.reshape(-1, shape[-1])), ref)
+
+
 def test_quantize_int8_bit_exact(dev):
     say("case: int8 quantiser, real-shape expert weights (seed 4)")
     wl, w, x, lw, xd = inputs("int8_decode", dev)
@@ -85,9 +135,9 @@ def test_quantize_int8_bit_exact(dev):
     q, s = moe_quantize_int8(gu)
     np.testing.assert_array_equal(to_np(q), q_ref)
     np.testing.assert_array_equal(to_np(s).view(np.uint32), s_ref.view(np.uint32))
-    # the full layer as uploaded for the block
+    # the full layer as uploaded for the block (quantised, then tiled)
     qd_ref, sd_ref = oracle.quantize_int8(w["expert_down"])
-    np.testing.assert_array_equal(to_np(lw.expert_down), qd_ref)
+    np.testing.assert_array_equal(to_np(lw.expert_down).ravel(), _tiled(qd_ref.reshape(-1, qd_ref.shape[-1])))
     np.testing.assert_array_equal(to_np(lw.down_scale).view(np.uint32), sd_ref.view(np.uint32))
     # zero rows and halfway cases
     row = np.array([[127.0, 2.5, 3.5, -2.5, -0.5, 0.49, 126.5, -127.0]], dtype=np.float32)
