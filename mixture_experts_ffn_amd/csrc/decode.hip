@@ -363,10 +363,19 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(StreamArgs 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int T = a.T, K = a.K, E = a.E, TK = T * K;
     for (int e = tid; e < E; e += kRouteThreads) s_mask[e] = 0ull;
+    // every wavefront holds the per-expert scales, loaded with its logits
+    float pv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pv[j] = (lane + kWave * j < E) ? pes[lane + kWave * j] : 0.f;
     for (int t = wave; t < T; t += kRouteThreads / kWave) {
         int ik[kMaxTopK];
-        float wk[kMaxTopK];
-        wave_topk(logits + (int64_t)t * E, pes, E, K, lane, ik, wk);
+        float wk[kMaxTopK], lv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = lane + kWave * j;
+            lv[j] = e < E ? logits[(int64_t)t * E + e] : 0.f;
+        }
+        wave_topk_vals<true>(lv, pes, E, K, lane, ik, wk, pv);
 #pragma unroll
         for (int k = 0; k < kMaxTopK; ++k)
             if (k < K && lane == k) {
@@ -551,8 +560,9 @@ hipError_t launch_front_nj(const StreamArgs& a, const uint16_t* scale, const uin
     const int blocks = n_router + a.Id / 16;
     const size_t lds = (size_t)kPass * a.H * sizeof(uint16_t);
     const float inv_sqrt_h = (float)(1.0 / __builtin_sqrt((double)a.H));
+    if (blocks <= 0) return hipSuccess;
     StreamArgs b = a;
-    if (!router) b.E = 0;  // no router items
+    if (!router) b.E = 0;  // no router items: the kernel derives their count from E
     hipLaunchKernelGGL(decode_front_kernel<NJ>, dim3(blocks), dim3(kThreads), lds, stream, b, scale,
                        wr, bias, eps, inv_sqrt_h, logits);
     return hipGetLastError();

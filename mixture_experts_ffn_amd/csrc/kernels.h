@@ -99,7 +99,7 @@ struct StreamArgs {
     // fp32 partial outputs of K4: expert rows [T*K][H] (grouped order), dense [T][H]
     float* part; float* dpart;
 };
-// K1: router logits (if logits != null) beside the dense gate/up rows -> hd
+// K1: router logits (if logits != null) beside the dense gate/up tiles -> hd
 hipError_t launch_decode_front(const StreamArgs& a, const uint16_t* scale, const uint16_t* wr,
                                const float* bias, float eps, float* logits, hipStream_t stream);
 // K2: top-k and grouping (one workgroup, T <= MOE_STREAM_MAX_TOKENS)

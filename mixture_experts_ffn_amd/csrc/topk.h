@@ -28,8 +28,12 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 // softmax over all E in fp32 (max-subtracted), then the top K by logit; the K
 // probabilities are renormalised to sum 1 (summed in k order) and multiplied
 // by the per-expert scale. Every lane ends with the same ik[0..K), wk[0..K).
+// pv (used when PV): pv[j] = pes[lane + 64 j] already in registers, so that no
+// load waits on the selection.
+template <bool PV = false>
 __device__ __forceinline__ void wave_topk_vals(const float (&lv)[4], const float* __restrict__ pes,
-                                               int E, int K, int lane, int* ik, float* wk) {
+                                               int E, int K, int lane, int* ik, float* wk,
+                                               const float (&pv)[4] = {0.f, 0.f, 0.f, 0.f}) {
     float l[4], ex[4];
     uint32_t key[4];
     bool valid[4];
@@ -98,12 +102,13 @@ __device__ __forceinline__ void wave_topk_vals(const float (&lv)[4], const float
             }
         }
     }
-    float pk[kMaxTopK];
+    float pk[kMaxTopK], sk[kMaxTopK];
     float psum = 0.f;
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k) {
         ik[k] = 0;
         pk[k] = 0.f;
+        sk[k] = 0.f;
         if (k < K) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -113,6 +118,7 @@ __device__ __forceinline__ void wave_topk_vals(const float (&lv)[4], const float
                         const int ln = __ffsll((long long)mk) - 1;
                         ik[k] = ln + kWave * j;
                         pk[k] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(ex[j]), ln)) / s;
+                        if (PV) sk[k] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(pv[j]), ln));
                     }
                 }
             }
@@ -120,7 +126,7 @@ __device__ __forceinline__ void wave_topk_vals(const float (&lv)[4], const float
         }
     }
 #pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k) wk[k] = (k < K) ? pk[k] / psum * pes[ik[k]] : 0.f;
+    for (int k = 0; k < kMaxTopK; ++k) wk[k] = (k < K) ? pk[k] / psum * (PV ? sk[k] : pes[ik[k]]) : 0.f;
 }
 
 // Same, with the logits read from lrow[0..E).
