@@ -317,6 +317,9 @@ def main():
     ap.add_argument("--layers", type=int, default=4, help="distinct weight copies cycled per step")
     ap.add_argument("--no-prefill", action="store_true", help="skip the T=2048 secondary line")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0 = skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain device copies of MIB MiB (the known-size kernel that "
+                         "scales rocprofv3's FETCH_SIZE / WRITE_SIZE to bytes), then exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -331,13 +334,24 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_copy": n, "copies": 5}), flush=True)
+        return
     from mixture_experts_ffn_amd import load_library
     load_library()
     dev = torch.device("cuda:0")
     ev = HipEvents()
 
     primary = run_workload(args.workload, args.steps, args.warmup, args.layers, dev, ev, log)
-    bound = "hbm" if primary["path"] == "stream" or primary["workload"] in ("prefill",) else "mfma"
+    # the metric names HBM GB/s for the weight-streaming (decode) path and MFMA % for the
+    # grouped (prefill) path
+    bound = "hbm" if primary["path"] == "stream" else "mfma"
     roof = roofline_for(primary, bound)
     out = {
         "metric": METRIC,
@@ -350,7 +364,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if primary["path"] == "stream" else "bf16",
+        "dtype": "bf16",  # bf16 operands, fp32 accumulation (MFMA or v_dot2 with fp32 sums)
         "data": "synthetic: seeded random tokens and random-init weights of the real block shape",
         "config": {"workload": f"{args.workload}: {moe_synth.WORKLOADS[args.workload].note}",
                    "T": primary["T"], "hidden": 2816 if args.workload != "tiny" else 512,
@@ -371,7 +385,7 @@ def main():
         out["prefill"] = {k: pre[k] for k in ("T", "path", "ms_per_step", "tokens_per_s", "block_gbs",
                                               "block_hbm_frac", "block_tflops", "block_mfma_frac",
                                               "experts_touched", "stages_us", "stages_gbs", "dominant")}
-        out["prefill"]["roofline"] = roofline_for(pre, "hbm")
+        out["prefill"]["roofline"] = roofline_for(pre, "mfma")
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds, log)
     else:

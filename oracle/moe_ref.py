@@ -38,7 +38,7 @@ then evaluated exactly, in float64, on those fp32 values). The int8 quantiser
 runs in fp32, the precision the GPU quantiser uses, so both take the same
 integer decisions.
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
 RMSNorm is ``x / sqrt(mean(x^2) + eps)`` with eps inside the root; the learned
 scale is a per-channel vector; top-k selects by logit, descending, ties going
 to the lower expert index, and emits the experts in that order; gate rows come
