@@ -255,9 +255,25 @@ __device__ __forceinline__ void gateup_item(const uint16_t* __restrict__ x, int 
     }
 }
 
+// Sum over each 32-lane half of a wavefront through DPP (no LDS): the half's
+// total lands in lane 31 (lanes 0..31) and lane 63 (lanes 32..63).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, false));
+}
+__device__ __forceinline__ float half_wave_sum_dpp(float v) {
+    v = dpp_add<0x111, 0xf>(v);  // row_shr:1
+    v = dpp_add<0x112, 0xf>(v);  // row_shr:2
+    v = dpp_add<0x114, 0xf>(v);  // row_shr:4
+    v = dpp_add<0x118, 0xf>(v);  // row_shr:8
+    return dpp_add<0x142, 0xa>(v);  // row_bcast:15: row 0 into row 1, row 2 into row 3
+}
+
 // Router logits of experts [e0, e0 + 8) for all T tokens: two experts per
 // wavefront (one per half). logit = (sum_h x*s*W) * rms(x)^-1 * H^-0.5 + bias,
-// all fp32; the sum of squares comes from the same staged x.
+// all fp32; s*W is formed once per lane (exact products of two bf16 values),
+// the tokens of a pass are dotted together, and the sum of squares comes from
+// the same staged x.
 template <int NJ>
 __device__ __forceinline__ void router_item(const uint16_t* __restrict__ x, int H, const uint16_t* __restrict__ scale,
                             const uint16_t* __restrict__ wr, const float* __restrict__ bias, int E,
@@ -267,12 +283,23 @@ __device__ __forceinline__ void router_item(const uint16_t* __restrict__ x, int 
     const int half = lane >> 5, hl = lane & 31;
     const int e = e0 + wave * 2 + half;
     const bool live = e < E;
-    uint4 wv[NJ], sv[NJ];
+    float sw[NJ][8];
+    {
+        uint4 wv[NJ], sv[NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int c = hl + 32 * j;
-        wv[j] = live ? reinterpret_cast<const uint4*>(wr + (int64_t)e * H)[c] : make_uint4(0, 0, 0, 0);
-        sv[j] = reinterpret_cast<const uint4*>(scale)[c];
+        for (int j = 0; j < NJ; ++j) {
+            const int c = hl + 32 * j;
+            wv[j] = reinterpret_cast<const uint4*>(wr + (int64_t)(live ? e : 0) * H)[c];
+            sv[j] = reinterpret_cast<const uint4*>(scale)[c];
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            float fw[8], fs[8];
+            unpack8(wv[j], fw);
+            unpack8(sv[j], fs);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sw[j][i] = fw[i] * fs[i];
+        }
     }
     const int hc8 = H >> 3;
     const float b = (live && bias) ? bias[e] : 0.f;
@@ -281,27 +308,34 @@ __device__ __forceinline__ void router_item(const uint16_t* __restrict__ x, int 
         __syncthreads();
         stage_x<NJ>(x, H, nullptr, pass, nt, xs);
         __syncthreads();
-#pragma unroll 1
-        for (int n = 0; n < nt; ++n) {
-            const uint4* xr = xs + n * hc8 + hl;
-            float acc = 0.f, ss = 0.f;
+        float acc[kPass], ss[kPass];
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                float xf[8], fw[8], fs[8];
-                unpack8(xr[32 * j], xf);
-                unpack8(wv[j], fw);
-                unpack8(sv[j], fs);
+        for (int n = 0; n < kPass; ++n) acc[n] = ss[n] = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+            for (int n = 0; n < kPass; ++n) {
+                float xf[8];
+                unpack8(xs[n * hc8 + hl + 32 * j], xf);  // rows n >= nt hold stale data, never stored
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    acc += (fw[i] * fs[i]) * xf[i];
-                    ss += xf[i] * xf[i];
+                    acc[n] += sw[j][i] * xf[i];
+                    ss[n] += xf[i] * xf[i];
                 }
             }
-            const float d = wave_sum<32>(acc);
-            const float q = wave_sum<32>(ss);
-            if (live && hl == 0) {
-                const float rn = 1.0f / sqrtf(q / (float)H + eps);
-                logits[(int64_t)(pass + n) * E + e] = d * (rn * inv_sqrt_h) + b;
+        }
+#pragma unroll
+        for (int n = 0; n < kPass; ++n) {
+            acc[n] = half_wave_sum_dpp(acc[n]);
+            ss[n] = half_wave_sum_dpp(ss[n]);
+        }
+        if (live && hl == 31) {
+#pragma unroll
+            for (int n = 0; n < kPass; ++n) {
+                if (n < nt) {
+                    const float rn = 1.0f / sqrtf(ss[n] / (float)H + eps);
+                    logits[(int64_t)(pass + n) * E + e] = acc[n] * (rn * inv_sqrt_h) + b;
+                }
             }
         }
     }
