@@ -6,14 +6,17 @@
 // 16 (l / 16) .. + 16 of each tile), so a wavefront streams a 16-row block of
 // a matrix as contiguous 1 KB loads; each lane dots its 16-value pieces with
 // the matching x values (from LDS) and four lanes' partial sums make a row.
-// Five launches, each filling the chip:
+// Five launches, each filling the chip (the dense MLP's items ride along in
+// K1, K2 and K4 when with_dense is set):
 //
 //   K1 decode_front: router logits (two experts per wavefront) side by side
-//      with the dense MLP's gate/up tiles; both only need x.
+//      with the dense MLP's gate/up tiles, whose K range is split over
+//      kDenseSplit workgroups (fp32 partial sums); both only need x.
 //   K2 decode_route: one workgroup: softmax/top-k of every token (ONNX export
 //      card, "Truthful graph contracts", row "Router") and the grouping of the
 //      routed pairs by expert (counts, offsets, grouped rows, inverse rows,
-//      list of touched experts).
+//      list of touched experts); the other workgroups add the dense partial
+//      sums and form the dense intermediate gelu_tanh(gate) * up.
 //   K3 decode_experts_gateup: 16 gate columns (+ the 16 matching up columns)
 //      of one touched expert per workgroup, K split over its 4 wavefronts;
 //      every weight byte is read exactly once with wide non-temporal loads
@@ -38,6 +41,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kPass = 4;           // tokens staged per pass
+constexpr int kDensePass = 8;      // tokens per pass of the dense gate/up partial sums
 constexpr int kRouterExperts = 8;  // experts per router work item: 2 per wavefront
 constexpr int kRouteThreads = 1024;
 constexpr int kMaxPairs = MOE_STREAM_MAX_TOKENS * MOE_MAX_TOPK;
@@ -153,6 +157,32 @@ __device__ __forceinline__ void stage_rows(const uint4* __restrict__ src, int n,
     }
 }
 
+// Rows of a pass staged through LDS in two halves, so that other loads can be
+// issued between them. rows_load: chunk i = tid + 256 q (i < n = nt * len8,
+// n >= 1) is 16-byte piece i % len8, from element k0, of row r = i / len8 of
+// the pass, which is src row toks[pass + r] (or pass + r without toks);
+// indices are clamped into range, so every load is unconditional and all are
+// in flight together. rows_store writes them to LDS as [nt][len8] chunks.
+template <int KPER>
+__device__ __forceinline__ void rows_load(const uint16_t* __restrict__ src, int64_t stride, int k0, int len8,
+                                          const int32_t* toks, int pass, int n, uint4 (&v)[KPER]) {
+#pragma unroll
+    for (int q = 0; q < KPER; ++q) {
+        const int i = min((int)threadIdx.x + q * kThreads, n - 1);
+        const int r = i / len8;
+        const int64_t row = toks ? (int64_t)toks[pass + r] : (int64_t)(pass + r);
+        v[q] = reinterpret_cast<const uint4*>(src + row * stride + k0)[i - r * len8];
+    }
+}
+template <int KPER>
+__device__ __forceinline__ void rows_store(const uint4 (&v)[KPER], int n, uint4* xs) {
+#pragma unroll
+    for (int q = 0; q < KPER; ++q) {
+        const int i = (int)threadIdx.x + q * kThreads;
+        if (i < n) xs[i] = v[q];
+    }
+}
+
 // 16 int8 (one tiled-layout piece) -> two groups of 8 bf16 (exact)
 __device__ __forceinline__ void i8x16_to_bf16(const uint4& v, uint4& lo, uint4& hi) {
     lo = i8x8_to_bf16(make_uint4(v.x, v.y, 0u, 0u));
@@ -196,6 +226,23 @@ __device__ __forceinline__ void tile_load(const char* tile, int kt0, int nk, int
         const int64_t off = (int64_t)min(kt0 + s, nk - 1) * kTileBytes<INT8>;
         w[s][0] = ld_nt16(p + off);
         if (!INT8) w[s][INT8 ? 0 : 1] = ld_nt16(p + off + 1024);
+    }
+}
+
+// tile_load of two tiles at once, their loads interleaved step by step (so
+// that step s of both has landed once 2 (s + 1) of them have).
+template <int NS, bool INT8>
+__device__ __forceinline__ void tile_load2(const char* ta, const char* tb, int kt0, int nk, int lane,
+                                           uint4 (&wa)[NS][INT8 ? 1 : 2], uint4 (&wb)[NS][INT8 ? 1 : 2]) {
+    const char* pa = ta + lane * 16;
+    const char* pb = tb + lane * 16;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int64_t off = (int64_t)min(kt0 + s, nk - 1) * kTileBytes<INT8>;
+        wa[s][0] = ld_nt16(pa + off);
+        if (!INT8) wa[s][INT8 ? 0 : 1] = ld_nt16(pa + off + 1024);
+        wb[s][0] = ld_nt16(pb + off);
+        if (!INT8) wb[s][INT8 ? 0 : 1] = ld_nt16(pb + off + 1024);
     }
 }
 
@@ -269,20 +316,26 @@ __device__ __forceinline__ float half_wave_sum_dpp(float v) {
     return dpp_add<0x142, 0xa>(v);  // row_bcast:15: row 0 into row 1, row 2 into row 3
 }
 
-// Router logits of experts [e0, e0 + 8) for all T tokens: two experts per
-// wavefront (one per half). logit = (sum_h x*s*W) * rms(x)^-1 * H^-0.5 + bias,
-// all fp32; s*W is formed once per lane (exact products of two bf16 values),
-// the tokens of a pass are dotted together, and the sum of squares comes from
-// the same staged x.
+// Router logits of experts [e0, e0 + 8) for tokens t0 .. t0 + nt (nt <=
+// kPass): two experts per wavefront (one per half).
+// logit = (sum_h x*s*W) * rms(x)^-1 * H^-0.5 + bias, all fp32; s*W is formed
+// once per lane (exact products of two bf16 values), the tokens are dotted
+// together, and wavefront n forms the sum of squares of token n from the
+// staged x. x is requested first, so that it lands in LDS while the weights
+// are in flight.
 template <int NJ>
 __device__ __forceinline__ void router_item(const uint16_t* __restrict__ x, int H, const uint16_t* __restrict__ scale,
                             const uint16_t* __restrict__ wr, const float* __restrict__ bias, int E,
-                            int t0, int t1, float eps, float inv_sqrt_h, int e0,
-                            float* __restrict__ logits, uint4* xs) {
+                            int t0, int nt, float eps, float inv_sqrt_h, int e0,
+                            float* __restrict__ logits, uint4* xs, float* s_rn) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int half = lane >> 5, hl = lane & 31;
     const int e = e0 + wave * 2 + half;
     const bool live = e < E;
+    const int hc8 = H >> 3;
+    constexpr int kPer = (kPass * 32 * NJ + kThreads - 1) / kThreads;
+    uint4 xv[kPer];
+    rows_load<kPer>(x, H, 0, hc8, nullptr, t0, nt * hc8, xv);
     float sw[NJ][8];
     {
         uint4 wv[NJ], sv[NJ];
@@ -292,6 +345,7 @@ __device__ __forceinline__ void router_item(const uint16_t* __restrict__ x, int 
             wv[j] = reinterpret_cast<const uint4*>(wr + (int64_t)(live ? e : 0) * H)[c];
             sv[j] = reinterpret_cast<const uint4*>(scale)[c];
         }
+        rows_store<kPer>(xv, nt * hc8, xs);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             float fw[8], fs[8];
@@ -301,42 +355,109 @@ __device__ __forceinline__ void router_item(const uint16_t* __restrict__ x, int 
             for (int i = 0; i < 8; ++i) sw[j][i] = fw[i] * fs[i];
         }
     }
-    const int hc8 = H >> 3;
     const float b = (live && bias) ? bias[e] : 0.f;
-    for (int pass = t0; pass < t1; pass += kPass) {
-        const int nt = min(kPass, t1 - pass);
-        __syncthreads();
-        stage_x<NJ>(x, H, nullptr, pass, nt, xs);
-        __syncthreads();
-        float acc[kPass], ss[kPass];
+    __syncthreads();
+    if (wave < nt) {  // rms of token t0 + wave
+        float ss = 0.f;
+        for (int c = lane; c < hc8; c += kWave) {
+            float xf[8];
+            unpack8(xs[wave * hc8 + c], xf);
 #pragma unroll
-        for (int n = 0; n < kPass; ++n) acc[n] = ss[n] = 0.f;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-#pragma unroll
-            for (int n = 0; n < kPass; ++n) {
-                float xf[8];
-                unpack8(xs[n * hc8 + hl + 32 * j], xf);  // rows n >= nt hold stale data, never stored
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    acc[n] += sw[j][i] * xf[i];
-                    ss[n] += xf[i] * xf[i];
-                }
-            }
+            for (int i = 0; i < 8; ++i) ss += xf[i] * xf[i];
         }
+        ss = wave_sum_f32(ss);
+        if (lane == 0) s_rn[wave] = 1.0f / sqrtf(ss / (float)H + eps);
+    }
+    float acc[kPass];
+#pragma unroll
+    for (int n = 0; n < kPass; ++n) acc[n] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
 #pragma unroll
         for (int n = 0; n < kPass; ++n) {
-            acc[n] = half_wave_sum_dpp(acc[n]);
-            ss[n] = half_wave_sum_dpp(ss[n]);
-        }
-        if (live && hl == 31) {
+            float xf[8];
+            unpack8(xs[n * hc8 + hl + 32 * j], xf);  // rows n >= nt hold stale data, never stored
 #pragma unroll
-            for (int n = 0; n < kPass; ++n) {
-                if (n < nt) {
-                    const float rn = 1.0f / sqrtf(ss[n] / (float)H + eps);
-                    logits[(int64_t)(pass + n) * E + e] = acc[n] * (rn * inv_sqrt_h) + b;
+            for (int i = 0; i < 8; ++i) acc[n] += sw[j][i] * xf[i];
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < kPass; ++n) acc[n] = half_wave_sum_dpp(acc[n]);
+    __syncthreads();  // s_rn
+    if (live && hl == 31) {
+#pragma unroll
+        for (int n = 0; n < kPass; ++n)
+            if (n < nt) logits[(int64_t)(t0 + n) * E + e] = acc[n] * (s_rn[n] * inv_sqrt_h) + b;
+    }
+}
+
+// Dense gate/up partial sums, K split over kDenseSplit workgroups. Workgroup
+// (hc, ks) takes K-steps [kb, kb + 4 NS), kb = 4 NS ks, of gate tile hc and
+// up tile Id / 16 + hc of the tiled [2 Id, H] matrix; wavefront w takes NS of
+// them from kb + w NS (steps past the matrix contribute 0). The four
+// wavefronts' fp32 sums, added in wavefront order, go to
+// part[ks][t][16 hc + r] (gate) and part[ks][t][Id + 16 hc + r] (up).
+// The first pass's x slice is requested before the weights: loads complete in
+// issue order, so it lands in LDS while the weights are still in flight.
+template <int NS>
+__device__ __forceinline__ void dense_gateup_part(const uint16_t* __restrict__ x, int H, const void* W,
+                                                  int Id, int hc, int ks, int T,
+                                                  float* __restrict__ part, uint4* xs, float* red) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int nk = H >> 6;
+    const int kb = ks * kWaves * NS, kt0 = kb + wave * NS;
+    const int n_steps = max(0, min(NS, nk - kt0));
+    const int blk_steps = max(0, min(kWaves * NS, nk - kb));
+    const char* Wb = reinterpret_cast<const char*>(W);
+    const int len8 = blk_steps * 8;  // 16-byte chunks of x per token
+    constexpr int kPer = (kDensePass * kWaves * NS * 8 + kThreads - 1) / kThreads;
+    uint4 wg[NS][2], wu[NS][2];
+    for (int pass = 0; pass < T; pass += kDensePass) {
+        const int nt = min(kDensePass, T - pass);
+        if (blk_steps > 0) {
+            uint4 xv[kPer];
+            rows_load<kPer>(x, H, kb * 64, len8, nullptr, pass, nt * len8, xv);
+            if (pass == 0)
+                tile_load2<NS, false>(Wb + (int64_t)hc * nk * kTileBytes<false>,
+                                      Wb + (int64_t)(Id / 16 + hc) * nk * kTileBytes<false>, kt0, nk, lane, wg, wu);
+            else
+                __syncthreads();  // previous pass done with xs and red
+            rows_store<kPer>(xv, nt * len8, xs);
+            __syncthreads();
+            const uint16_t* xr = reinterpret_cast<const uint16_t*>(xs) + (kt0 - kb) * 64 + (lane >> 4) * 16;
+            float ag[kDensePass], au[kDensePass];
+#pragma unroll
+            for (int n = 0; n < kDensePass; ++n) ag[n] = au[n] = 0.f;
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                if (s < n_steps) {
+#pragma unroll
+                    for (int n = 0; n < kDensePass; ++n)
+                        if (n < nt) {
+                            ag[n] = piece_dot<false>(wg[s], xr + n * len8 * 8 + s * 64, ag[n]);
+                            au[n] = piece_dot<false>(wu[s], xr + n * len8 * 8 + s * 64, au[n]);
+                        }
                 }
+#pragma unroll
+            for (int n = 0; n < kDensePass; ++n)
+                if (n < nt) {
+                    ag[n] = tile_row_sum(ag[n]);
+                    au[n] = tile_row_sum(au[n]);
+                    if (lane < 16) {
+                        red[((wave * kDensePass + n) * 2) * 16 + lane] = ag[n];
+                        red[((wave * kDensePass + n) * 2 + 1) * 16 + lane] = au[n];
+                    }
+                }
+            __syncthreads();
+        }
+        if (tid < nt * 32) {
+            const int n = tid >> 5, m = (tid >> 4) & 1, r = tid & 15;
+            float v = 0.f;
+            if (blk_steps > 0) {
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) v += red[((w * kDensePass + n) * 2 + m) * 16 + r];
             }
+            part[((int64_t)ks * T + pass + n) * 2 * Id + m * Id + hc * 16 + r] = v;
         }
     }
 }
@@ -354,13 +475,16 @@ __global__ __launch_bounds__(kThreads) void decode_front_kernel(StreamArgs a, co
     const int n_router = n_groups * n_pass;
     const int b = blockIdx.x;
     if (b < n_router) {
+        __shared__ float s_rn[kPass];
         const int g = b % n_groups, tp = b / n_groups;
-        router_item<NJ>(a.x, a.H, scale, wr, bias, a.E, tp * kPass, min(a.T, (tp + 1) * kPass), eps,
-                        inv_sqrt_h, g * kRouterExperts, logits, xs);
+        router_item<NJ>(a.x, a.H, scale, wr, bias, a.E, tp * kPass, min(kPass, a.T - tp * kPass), eps,
+                        inv_sqrt_h, g * kRouterExperts, logits, xs, s_rn);
     } else {
-        __shared__ float red[kWaves * kPass * 2 * 16];
-        gateup_item<NJ, false>(a.x, a.H, a.dgu, nullptr, a.Id, b - n_router, nullptr, a.T, a.hd, xs,
-                               red);
+        // dense items: kDenseSplit K ranges of each gate/up tile pair
+        __shared__ float red[kWaves * kDensePass * 2 * 16];
+        const int i = b - n_router, hc = i / kDenseSplit, ks = i - hc * kDenseSplit;
+        dense_gateup_part<(NJ + kDenseSplit - 1) / kDenseSplit>(a.x, a.H, a.dgu, a.Id, hc, ks, a.T,
+                                                                a.dgu_part, xs, red);
     }
 }
 
@@ -387,9 +511,36 @@ __global__ __launch_bounds__(kThreads) void decode_experts_gateup_kernel(StreamA
 // stable grouping by expert. With T <= 64 every token is one bit of a 64-bit
 // mask per expert: the rank of pair (t, k) within its expert is the number of
 // lower tokens in that expert's mask, the expert's row count its popcount.
+// Dense gate/up finish: hd[t][c] = gelu_tanh(gate) * up, each the sum of its
+// kDenseSplit partial sums in split order; one thread per (t, c).
+__device__ __forceinline__ void dense_finish(const StreamArgs& a, int blk) {
+    const int i = blk * kRouteThreads + threadIdx.x;
+    if (i >= a.T * a.Id) return;
+    const int t = i / a.Id, c = i - t * a.Id;
+    float gp[kDenseSplit], up[kDenseSplit];
+#pragma unroll
+    for (int ks = 0; ks < kDenseSplit; ++ks) {
+        const float* row = a.dgu_part + ((int64_t)ks * a.T + t) * 2 * a.Id;
+        gp[ks] = row[c];
+        up[ks] = row[a.Id + c];
+    }
+    float g = gp[0], u = up[0];
+#pragma unroll
+    for (int ks = 1; ks < kDenseSplit; ++ks) {
+        g += gp[ks];
+        u += up[ks];
+    }
+    a.hd[(int64_t)t * a.Id + c] = f32_to_bf16(gelu_tanh(g) * u);
+}
+
 __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(StreamArgs a, const float* logits,
                                                                     const float* pes,
                                                                     int32_t* topk_idx, float* topk_w) {
+    // workgroup 0 routes (if there are logits); the others finish the dense gate/up
+    if (!logits || blockIdx.x > 0) {
+        dense_finish(a, (int)blockIdx.x - (logits ? 1 : 0));
+        return;
+    }
     __shared__ int s_idx[kMaxPairs];
     __shared__ float s_w[kMaxPairs];
     __shared__ unsigned long long s_mask[kMaxExperts];
@@ -491,9 +642,11 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(StreamArgs a) {
     __shared__ float red[kWaves * kPass * 16];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int ipe = a.H / 64;  // expert items: 4 tiles (one per wavefront) of 16 rows
-    const int expert_items = a.max_active * ipe;
-    const int b = blockIdx.x;
-    if (b < expert_items) {
+    // the dense items (a longer reduction each) come first in the grid, so
+    // that they run beside the expert items instead of after them
+    const int dense_items = a.with_dense ? a.H / 16 : 0;
+    const int b = (int)blockIdx.x - dense_items;
+    if (b >= 0) {
         const int slot = b / ipe, g = b - slot * ipe;
         if (slot >= *a.n_active) return;
         const int e = a.active[slot];
@@ -521,7 +674,7 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(StreamArgs a) {
         }
     } else {
         // dense down: one 16-row tile per workgroup, K split over the wavefronts
-        const int tile = b - expert_items;
+        const int tile = (int)blockIdx.x;
         const int nk = a.Id >> 6, kd = (nk + kWaves - 1) / kWaves;
         const int kt0 = wave * kd, n_steps = max(0, min(kd, nk - kt0));
         uint4 w[NS][2];
@@ -591,8 +744,10 @@ hipError_t launch_front_nj(const StreamArgs& a, const uint16_t* scale, const uin
                            hipStream_t stream) {
     const int n_router =
         router ? ((a.E + kRouterExperts - 1) / kRouterExperts) * ((a.T + kPass - 1) / kPass) : 0;
-    const int blocks = n_router + a.Id / 16;
-    const size_t lds = (size_t)kPass * a.H * sizeof(uint16_t);
+    const int blocks = n_router + (a.with_dense ? (a.Id / 16) * kDenseSplit : 0);
+    // x rows of a router pass, or the x slices of a dense pass
+    const int ns = (a.H / 256 + kDenseSplit - 1) / kDenseSplit;
+    const size_t lds = (size_t)max(kPass * a.H, kDensePass * kWaves * ns * 64) * sizeof(uint16_t);
     const float inv_sqrt_h = (float)(1.0 / __builtin_sqrt((double)a.H));
     if (blocks <= 0) return hipSuccess;
     StreamArgs b = a;
@@ -636,7 +791,10 @@ hipError_t launch_decode_front(const StreamArgs& a, const uint16_t* scale, const
 
 hipError_t launch_decode_route(const StreamArgs& a, const float* logits, const float* pes,
                                int32_t* topk_idx, float* topk_w, hipStream_t stream) {
-    hipLaunchKernelGGL(decode_route_kernel, dim3(1), dim3(kRouteThreads), 0, stream, a, logits, pes,
+    const int blocks =
+        (logits ? 1 : 0) + (a.with_dense ? (a.T * a.Id + kRouteThreads - 1) / kRouteThreads : 0);
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(decode_route_kernel, dim3(blocks), dim3(kRouteThreads), 0, stream, a, logits, pes,
                        topk_idx, topk_w);
     return hipGetLastError();
 }
@@ -651,7 +809,8 @@ hipError_t launch_decode_down(const StreamArgs& a, bool int8, hipStream_t stream
     // K-steps a wavefront holds: a whole expert tile (I / 64) or a quarter of
     // a dense tile (Id / 256, rounded up)
     const int need = max(a.I / 64, (a.Id / 64 + kWaves - 1) / kWaves);
-    const int blocks = a.max_active * (a.H / 64) + a.H / 16;
+    const int blocks = a.max_active * (a.H / 64) + (a.with_dense ? a.H / 16 : 0);
+    if (blocks <= 0) return hipSuccess;
     const size_t lds = (size_t)kPass * (a.I > a.Id ? a.I : a.Id) * sizeof(uint16_t);
     const dim3 grid(blocks), block(kThreads);
 #define LAUNCH(N)                                                                                   \

@@ -89,8 +89,9 @@ struct StreamArgs {
     const void* dw; const float* dw_scale;   // [E][H][I]
     int32_t* counts; int32_t* offsets; int32_t* active; int32_t* n_active;
     int32_t* perm_token; float* perm_w; int32_t* inv_row;
-    int max_active;                           // 0 = dense only
+    int max_active;                           // 0 = no expert items
     // dense
+    int with_dense;                           // the launch carries the dense MLP's items
     const uint16_t* dgu; const uint16_t* ddw;
     // intermediates and output
     uint16_t* h;    // [T*K][I]
@@ -98,11 +99,16 @@ struct StreamArgs {
     uint16_t* y;    // [T][H]
     // fp32 partial outputs of K4: expert rows [T*K][H] (grouped order), dense [T][H]
     float* part; float* dpart;
+    // fp32 partial sums of the dense gate/up, K split: [kDenseSplit][T][2 Id] (gate, then up)
+    float* dgu_part;
 };
-// K1: router logits (if logits != null) beside the dense gate/up tiles -> hd
+// workgroups sharing the K range of one dense gate/up tile pair in K1
+constexpr int kDenseSplit = 4;
+// K1: router logits (if logits != null) beside the dense gate/up partial sums -> dgu_part
 hipError_t launch_decode_front(const StreamArgs& a, const uint16_t* scale, const uint16_t* wr,
                                const float* bias, float eps, float* logits, hipStream_t stream);
-// K2: top-k and grouping (one workgroup, T <= MOE_STREAM_MAX_TOKENS)
+// K2: top-k and grouping (one workgroup, T <= MOE_STREAM_MAX_TOKENS; none if
+// logits == null) beside the dense gate/up finish (dgu_part -> hd)
 hipError_t launch_decode_route(const StreamArgs& a, const float* logits, const float* pes,
                                int32_t* topk_idx, float* topk_w, hipStream_t stream);
 // K3: gate/up of the touched experts -> h

@@ -40,7 +40,7 @@ static_assert(kRouterMfmaMinT >= MOE_STREAM_MAX_TOKENS, "the streaming path stag
 struct Layout {
     size_t logits, partial, topk_idx, topk_w, pair_rank, tile_counts, counts, offsets, active, n_active;
     size_t perm_token, perm_w, inv_row, mtile_group, mtile_row0, n_mtiles, h, hd, rows;
-    size_t dout, part, dpart, total;
+    size_t dout, part, dpart, dgu_part, total;
     int max_mtiles;
 };
 
@@ -82,6 +82,7 @@ Layout make_layout(const moe_dims& d, int64_t T) {
     const int64_t Ts = T <= MOE_STREAM_MAX_TOKENS ? T : 0;
     L.part = take(Ts * K * d.hidden * 4);
     L.dpart = take(Ts * d.hidden * 4);
+    L.dgu_part = take(Ts * moe::kDenseSplit * 2 * d.dense_inter * 4);
     L.total = off;
     return L;
 }
@@ -288,6 +289,8 @@ int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
         sa.dgu = (const uint16_t*)w->dense_gate_up; sa.ddw = (const uint16_t*)w->dense_down;
         sa.h = h; sa.hd = hd; sa.y = (uint16_t*)y;
         sa.part = at<float>(ws, L.part); sa.dpart = at<float>(ws, L.dpart);
+        sa.dgu_part = at<float>(ws, L.dgu_part);
+        sa.with_dense = 1;  // the dense MLP's items ride along in K1, K2 and K4
         HIP_TRY(st.begin("decode_front"), "event record");
         HIP_TRY(moe::launch_decode_front(sa, (const uint16_t*)w->router_scale, (const uint16_t*)w->router_w,
                                          w->logit_bias, d->rms_eps, logits, stream),
@@ -381,12 +384,15 @@ int dense_mlp(const moe_dims* d, const void* dense_gate_up, const void* dense_do
     if (T <= stream_limit() && stream_fits(*d)) {
         moe::StreamArgs sa{};
         sa.T = T; sa.H = H; sa.I = d->expert_inter; sa.Id = Id; sa.K = d->top_k; sa.E = d->num_experts;
-        sa.x = (const uint16_t*)x; sa.max_active = 0;
+        sa.x = (const uint16_t*)x; sa.max_active = 0; sa.with_dense = 1;
         sa.dgu = (const uint16_t*)dense_gate_up; sa.ddw = (const uint16_t*)dense_down;
         sa.hd = hd; sa.y = (uint16_t*)y;
         sa.part = at<float>(ws, L.part); sa.dpart = at<float>(ws, L.dpart);
+        sa.dgu_part = at<float>(ws, L.dgu_part);
         HIP_TRY(moe::launch_decode_front(sa, nullptr, nullptr, nullptr, 0.f, nullptr, stream),
                 "decode_front launch");
+        HIP_TRY(moe::launch_decode_route(sa, nullptr, nullptr, nullptr, nullptr, stream),
+                "decode_route (dense finish) launch");
         HIP_TRY(moe::launch_decode_down(sa, false, stream), "decode_down launch");
         HIP_TRY(moe::launch_decode_combine(sa, stream), "decode_combine launch");
     } else {
