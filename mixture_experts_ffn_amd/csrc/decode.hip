@@ -507,10 +507,6 @@ __global__ __launch_bounds__(kThreads) void decode_experts_gateup_kernel(StreamA
 }
 
 // ---------------------------------------------------------------- K2
-// One workgroup: top-k of every token (one wavefront per token), then the
-// stable grouping by expert. With T <= 64 every token is one bit of a 64-bit
-// mask per expert: the rank of pair (t, k) within its expert is the number of
-// lower tokens in that expert's mask, the expert's row count its popcount.
 // Dense gate/up finish: hd[t][c] = gelu_tanh(gate) * up, each the sum of its
 // kDenseSplit partial sums in split order; one thread per (t, c).
 __device__ __forceinline__ void dense_finish(const StreamArgs& a, int blk) {
@@ -533,42 +529,83 @@ __device__ __forceinline__ void dense_finish(const StreamArgs& a, int blk) {
     a.hd[(int64_t)t * a.Id + c] = f32_to_bf16(gelu_tanh(g) * u);
 }
 
+// Workgroup 0 routes every token (ONNX export card, "Truthful graph
+// contracts", row "Router"), the other workgroups finish the dense gate/up.
+//
+// Selection by rank, one thread per (token, expert) pair: each logit becomes
+// the 64-bit composite (order-preserving key, ~expert), so that a larger
+// composite means a larger logit or, for equal logits, the lower expert; the
+// rank of a pair is the number of its token's composites above its own, and
+// ranks 0 .. K-1 are the top K in order (descending logit, ties to the lower
+// index). The renormalised weight of the k-th selected expert is
+// exp(l_k - l_0) / sum_j exp(l_j - l_0) over the K selected (the softmax
+// denominator over all experts cancels in the renormalisation), summed in k
+// order, times its per-expert scale.
+//
+// Then the stable grouping by expert. With T <= 64 every token is one bit of a
+// 64-bit mask per expert: the rank of pair (t, k) within its expert is the
+// number of lower tokens in that expert's mask, the expert's row count its
+// popcount.
 __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(StreamArgs a, const float* logits,
                                                                     const float* pes,
                                                                     int32_t* topk_idx, float* topk_w) {
-    // workgroup 0 routes (if there are logits); the others finish the dense gate/up
     if (!logits || blockIdx.x > 0) {
         dense_finish(a, (int)blockIdx.x - (logits ? 1 : 0));
         return;
     }
     __shared__ int s_idx[kMaxPairs];
     __shared__ float s_w[kMaxPairs];
+    __shared__ float s_l[kMaxPairs];   // logit of each selected pair
+    __shared__ float s_e[kMaxPairs];   // its exp relative to the token's largest
     __shared__ unsigned long long s_mask[kMaxExperts];
     __shared__ int s_off[kMaxExperts + 1];
+    __shared__ float s_pes[kMaxExperts];
+    __shared__ unsigned long long s_comp[kRouteThreads];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int T = a.T, K = a.K, E = a.E, TK = T * K;
-    for (int e = tid; e < E; e += kRouteThreads) s_mask[e] = 0ull;
-    // every wavefront holds the per-expert scales, loaded with its logits
-    float pv[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) pv[j] = (lane + kWave * j < E) ? pes[lane + kWave * j] : 0.f;
-    for (int t = wave; t < T; t += kRouteThreads / kWave) {
-        int ik[kMaxTopK];
-        float wk[kMaxTopK], lv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = lane + kWave * j;
-            lv[j] = e < E ? logits[(int64_t)t * E + e] : 0.f;
-        }
-        wave_topk_vals<true>(lv, pes, E, K, lane, ik, wk, pv);
-#pragma unroll
-        for (int k = 0; k < kMaxTopK; ++k)
-            if (k < K && lane == k) {
-                s_idx[t * K + k] = ik[k];
-                s_w[t * K + k] = wk[k];
-                topk_idx[(int64_t)t * K + k] = ik[k];
-                topk_w[(int64_t)t * K + k] = wk[k];
+    // experts padded to a power of two: a chunk holds kRouteThreads / Ep tokens
+    const int Ep = E <= 64 ? 64 : E <= 128 ? 128 : 256;
+    const int tc = kRouteThreads / Ep;
+    const int tl = tid / Ep, e = tid - tl * Ep;
+    if (tid < E) {
+        s_mask[tid] = 0ull;
+        s_pes[tid] = pes[tid];
+    }
+    for (int t0 = 0; t0 < T; t0 += tc) {
+        const int t = t0 + tl;
+        const bool live = t < T && e < E;
+        const float l = live ? logits[(int64_t)t * E + e] : 0.f;
+        const unsigned long long comp =
+            live ? ((unsigned long long)order_key(l) << 32) | (unsigned)(~e) : 0ull;
+        if (t0 > 0) __syncthreads();  // previous chunk done with s_comp
+        s_comp[tid] = comp;
+        __syncthreads();
+        if (live) {
+            const unsigned long long* row = s_comp + tl * Ep;
+            int rank = 0;
+            for (int j = 0; j < E; j += 2) {  // an odd E reads the padding slot E, which holds 0
+                const unsigned long long c0 = row[j], c1 = row[j + 1];
+                rank += (c0 > comp) + (c1 > comp);
             }
+            if (rank < K) {
+                s_idx[t * K + rank] = e;
+                s_l[t * K + rank] = l;
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < TK)  // exp of each selected logit relative to the token's largest
+        s_e[tid] = expf(s_l[tid] - s_l[(tid / K) * K]);
+    __syncthreads();
+    if (tid < TK) {
+        const int t = tid / K;
+        float sum = 0.f;
+        for (int k = 0; k < K; ++k) sum += s_e[t * K + k];
+        const int ei = s_idx[tid];
+        const float wt = s_e[tid] / sum * s_pes[ei];
+        s_w[tid] = wt;
+        topk_idx[tid] = ei;
+        topk_w[tid] = wt;
     }
     __syncthreads();
     if (tid < TK) atomicOr(&s_mask[s_idx[tid]], 1ull << (tid / K));
