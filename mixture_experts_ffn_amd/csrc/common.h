@@ -39,6 +39,23 @@ __device__ __forceinline__ void unpack8_i8(const uint2& v, float* f) {
     for (int i = 0; i < 4; ++i) f[4 + i] = (float)(int8_t)((v.y >> (8 * i)) & 0xFF);
 }
 
+// Products s*w of 8 bf16 pairs (packed two per word) are exact in fp32 (16
+// significant bits); each is split into a bf16 hi (its truncation) and a bf16
+// lo (the remainder, exactly representable), so hi + lo = s*w and two bf16 MFMAs
+// against hi and lo accumulate the exact products in fp32.
+__device__ __forceinline__ void split_products8(const uint32_t (&w)[4], const uint32_t (&s)[4],
+                                                uint32_t (&hi)[4], uint32_t (&lo)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float p0 = bf16_lo(w[i]) * bf16_lo(s[i]);
+        const float p1 = bf16_hi(w[i]) * bf16_hi(s[i]);
+        const uint32_t h0 = __float_as_uint(p0) & 0xFFFF0000u, h1 = __float_as_uint(p1) & 0xFFFF0000u;
+        const float r0 = p0 - __uint_as_float(h0), r1 = p1 - __uint_as_float(h1);
+        hi[i] = (h0 >> 16) | h1;
+        lo[i] = (__float_as_uint(r0) >> 16) | (__float_as_uint(r1) & 0xFFFF0000u);
+    }
+}
+
 // GELU, tanh approximation ("gelu_pytorch_tanh"):
 // 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))), evaluated in fp32.
 __device__ __forceinline__ float gelu_tanh(float z) {

@@ -9,14 +9,16 @@
 // Five launches, each filling the chip (the dense MLP's items ride along in
 // K1, K2 and K4 when with_dense is set):
 //
-//   K1 decode_front: router logits (two experts per wavefront) side by side
-//      with the dense MLP's gate/up tiles, whose K range is split over
-//      kDenseSplit workgroups (fp32 partial sums); both only need x.
-//   K2 decode_route: one workgroup: softmax/top-k of every token (ONNX export
-//      card, "Truthful graph contracts", row "Router") and the grouping of the
-//      routed pairs by expert (counts, offsets, grouped rows, inverse rows,
-//      list of touched experts); the other workgroups add the dense partial
-//      sums and form the dense intermediate gelu_tanh(gate) * up.
+//   K1 decode_front: router partial logits (16 experts per workgroup) side by
+//      side with the dense MLP's gate/up tiles, both as bf16 MFMAs of the
+//      batch against 16-row weight tiles, the K range of each split over
+//      kFrontSplit workgroups (fp32 partial sums); both only need x.
+//   K2 decode_route: one workgroup: the logits from the partial sums, the
+//      softmax/top-k of every token (ONNX export card, "Truthful graph
+//      contracts", row "Router") and the grouping of the routed pairs by
+//      expert (counts, offsets, grouped rows, inverse rows, list of touched
+//      experts); the other workgroups add the dense partial sums and form the
+//      dense intermediate gelu_tanh(gate) * up.
 //   K3 decode_experts_gateup: 16 gate columns (+ the 16 matching up columns)
 //      of one touched expert per workgroup, K split over its 4 wavefronts;
 //      every weight byte is read exactly once with wide non-temporal loads
@@ -41,8 +43,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kPass = 4;           // tokens staged per pass
-constexpr int kDensePass = 8;      // tokens per pass of the dense gate/up partial sums
-constexpr int kRouterExperts = 8;  // experts per router work item: 2 per wavefront
 constexpr int kRouteThreads = 1024;
 constexpr int kMaxPairs = MOE_STREAM_MAX_TOKENS * MOE_MAX_TOPK;
 
@@ -154,32 +154,6 @@ __device__ __forceinline__ void stage_rows(const uint4* __restrict__ src, int n,
     for (int q = 0; q < KPER; ++q) {
         const int i = (int)threadIdx.x + q * kThreads;
         if (i < n) dst[i] = v[q];
-    }
-}
-
-// Rows of a pass staged through LDS in two halves, so that other loads can be
-// issued between them. rows_load: chunk i = tid + 256 q (i < n = nt * len8,
-// n >= 1) is 16-byte piece i % len8, from element k0, of row r = i / len8 of
-// the pass, which is src row toks[pass + r] (or pass + r without toks);
-// indices are clamped into range, so every load is unconditional and all are
-// in flight together. rows_store writes them to LDS as [nt][len8] chunks.
-template <int KPER>
-__device__ __forceinline__ void rows_load(const uint16_t* __restrict__ src, int64_t stride, int k0, int len8,
-                                          const int32_t* toks, int pass, int n, uint4 (&v)[KPER]) {
-#pragma unroll
-    for (int q = 0; q < KPER; ++q) {
-        const int i = min((int)threadIdx.x + q * kThreads, n - 1);
-        const int r = i / len8;
-        const int64_t row = toks ? (int64_t)toks[pass + r] : (int64_t)(pass + r);
-        v[q] = reinterpret_cast<const uint4*>(src + row * stride + k0)[i - r * len8];
-    }
-}
-template <int KPER>
-__device__ __forceinline__ void rows_store(const uint4 (&v)[KPER], int n, uint4* xs) {
-#pragma unroll
-    for (int q = 0; q < KPER; ++q) {
-        const int i = (int)threadIdx.x + q * kThreads;
-        if (i < n) xs[i] = v[q];
     }
 }
 
@@ -302,189 +276,183 @@ __device__ __forceinline__ void gateup_item(const uint16_t* __restrict__ x, int 
     }
 }
 
-// Sum over each 32-lane half of a wavefront through DPP (no LDS): the half's
-// total lands in lane 31 (lanes 0..31) and lane 63 (lanes 32..63).
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_add(float x) {
-    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, false));
-}
-__device__ __forceinline__ float half_wave_sum_dpp(float v) {
-    v = dpp_add<0x111, 0xf>(v);  // row_shr:1
-    v = dpp_add<0x112, 0xf>(v);  // row_shr:2
-    v = dpp_add<0x114, 0xf>(v);  // row_shr:4
-    v = dpp_add<0x118, 0xf>(v);  // row_shr:8
-    return dpp_add<0x142, 0xa>(v);  // row_bcast:15: row 0 into row 1, row 2 into row 3
+// ---------------------------------------------------------------- K1
+// The front items are small matrix products of the batch (T <= 64 tokens,
+// taken 16 at a time as the M rows of a bf16 MFMA 16x16x32) with 16-row weight
+// tiles. The tiled layout gives lane l the 16 k values 16 (l / 16) .. + 16 of
+// row l % 16 of a 64-wide K-step, which is the MFMA B operand of two MFMAs
+// (its first and second 8 values) once the A operand enumerates the same k:
+// lane l loads x[token l % 16][64 kt + 16 (l / 16) .. + 16] straight from
+// global memory. Token rows past the batch repeat its last token and are never
+// stored. The K range of an item is split over kFrontSplit workgroups of four
+// wavefronts (NS K-steps each); a workgroup adds its wavefronts' sums in
+// wavefront order through LDS and writes fp32 partial sums of its slice.
+
+__device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Router logits of experts [e0, e0 + 8) for tokens t0 .. t0 + nt (nt <=
-// kPass): two experts per wavefront (one per half).
-// logit = (sum_h x*s*W) * rms(x)^-1 * H^-0.5 + bias, all fp32; s*W is formed
-// once per lane (exact products of two bf16 values), the tokens are dotted
-// together, and wavefront n forms the sum of squares of token n from the
-// staged x. x is requested first, so that it lands in LDS while the weights
-// are in flight.
-template <int NJ>
-__device__ __forceinline__ void router_item(const uint16_t* __restrict__ x, int H, const uint16_t* __restrict__ scale,
-                            const uint16_t* __restrict__ wr, const float* __restrict__ bias, int E,
-                            int t0, int nt, float eps, float inv_sqrt_h, int e0,
-                            float* __restrict__ logits, uint4* xs, float* s_rn) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int half = lane >> 5, hl = lane & 31;
-    const int e = e0 + wave * 2 + half;
-    const bool live = e < E;
-    const int hc8 = H >> 3;
-    constexpr int kPer = (kPass * 32 * NJ + kThreads - 1) / kThreads;
-    uint4 xv[kPer];
-    rows_load<kPer>(x, H, 0, hc8, nullptr, t0, nt * hc8, xv);
-    float sw[NJ][8];
-    {
-        uint4 wv[NJ], sv[NJ];
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int c = hl + 32 * j;
-            wv[j] = reinterpret_cast<const uint4*>(wr + (int64_t)(live ? e : 0) * H)[c];
-            sv[j] = reinterpret_cast<const uint4*>(scale)[c];
-        }
-        rows_store<kPer>(xv, nt * hc8, xs);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            float fw[8], fs[8];
-            unpack8(wv[j], fw);
-            unpack8(sv[j], fs);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) sw[j][i] = fw[i] * fs[i];
-        }
-    }
-    const float b = (live && bias) ? bias[e] : 0.f;
-    __syncthreads();
-    if (wave < nt) {  // rms of token t0 + wave
-        float ss = 0.f;
-        for (int c = lane; c < hc8; c += kWave) {
-            float xf[8];
-            unpack8(xs[wave * hc8 + c], xf);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ss += xf[i] * xf[i];
-        }
-        ss = wave_sum_f32(ss);
-        if (lane == 0) s_rn[wave] = 1.0f / sqrtf(ss / (float)H + eps);
-    }
-    float acc[kPass];
-#pragma unroll
-    for (int n = 0; n < kPass; ++n) acc[n] = 0.f;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-#pragma unroll
-        for (int n = 0; n < kPass; ++n) {
-            float xf[8];
-            unpack8(xs[n * hc8 + hl + 32 * j], xf);  // rows n >= nt hold stale data, never stored
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[n] += sw[j][i] * xf[i];
-        }
-    }
-#pragma unroll
-    for (int n = 0; n < kPass; ++n) acc[n] = half_wave_sum_dpp(acc[n]);
-    __syncthreads();  // s_rn
-    if (live && hl == 31) {
-#pragma unroll
-        for (int n = 0; n < kPass; ++n)
-            if (n < nt) logits[(int64_t)(t0 + n) * E + e] = acc[n] * (s_rn[n] * inv_sqrt_h) + b;
-    }
-}
-
-// Dense gate/up partial sums, K split over kDenseSplit workgroups. Workgroup
-// (hc, ks) takes K-steps [kb, kb + 4 NS), kb = 4 NS ks, of gate tile hc and
-// up tile Id / 16 + hc of the tiled [2 Id, H] matrix; wavefront w takes NS of
-// them from kb + w NS (steps past the matrix contribute 0). The four
-// wavefronts' fp32 sums, added in wavefront order, go to
-// part[ks][t][16 hc + r] (gate) and part[ks][t][Id + 16 hc + r] (up).
-// The first pass's x slice is requested before the weights: loads complete in
-// issue order, so it lands in LDS while the weights are still in flight.
+// A fragments of K-steps kt0 .. kt0 + NS - 1 (clamped to the last step) for
+// token row tok.
 template <int NS>
-__device__ __forceinline__ void dense_gateup_part(const uint16_t* __restrict__ x, int H, const void* W,
-                                                  int Id, int hc, int ks, int T,
-                                                  float* __restrict__ part, uint4* xs, float* red) {
+__device__ __forceinline__ void a_frags(const uint16_t* __restrict__ x, int H, int tok, int kt0, int nk,
+                                        int lane, uint4 (&a)[NS][2]) {
+    const uint16_t* row = x + (int64_t)tok * H + (lane >> 4) * 16;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const uint4* p = reinterpret_cast<const uint4*>(row + min(kt0 + s, nk - 1) * 64);
+        a[s][0] = p[0];
+        a[s][1] = p[1];
+    }
+}
+
+// The 16 x 16 accumulators of the four wavefronts (red[w][m][row][col], m <
+// n_m matrices) summed in wavefront order; output o = tid + 256 q is
+// (m, row, col) = (o / 256, o / 16 % 16, o % 16).
+__device__ __forceinline__ void red_store(float* red, int wave, int m, int lane, const f32x4_t& c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[(wave * 2 + m) * 256 + ((lane >> 4) * 4 + i) * 16 + (lane & 15)] = c[i];
+}
+__device__ __forceinline__ float red_sum(const float* red, int m, int rc) {
+    float v = red[m * 256 + rc];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) v += red[(w * 2 + m) * 256 + rc];
+    return v;
+}
+
+// Dense gate/up, item (hc, ks): gate tile hc and up tile Id / 16 + hc of the
+// tiled [2 Id, H] matrix over K-steps [4 NS ks, 4 NS (ks + 1)) (steps past the
+// matrix contribute 0) -> part[ks][t][16 hc + c] (gate), part[ks][t][Id + 16 hc + c] (up).
+template <int NS>
+__device__ __forceinline__ void dense_gateup_part(const uint16_t* __restrict__ x, int H, const void* W, int Id,
+                                                  int hc, int ks, int T, float* __restrict__ part, float* red) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nk = H >> 6;
-    const int kb = ks * kWaves * NS, kt0 = kb + wave * NS;
+    const int kt0 = (ks * kWaves + wave) * NS;
     const int n_steps = max(0, min(NS, nk - kt0));
-    const int blk_steps = max(0, min(kWaves * NS, nk - kb));
     const char* Wb = reinterpret_cast<const char*>(W);
-    const int len8 = blk_steps * 8;  // 16-byte chunks of x per token
-    constexpr int kPer = (kDensePass * kWaves * NS * 8 + kThreads - 1) / kThreads;
     uint4 wg[NS][2], wu[NS][2];
-    for (int pass = 0; pass < T; pass += kDensePass) {
-        const int nt = min(kDensePass, T - pass);
-        if (blk_steps > 0) {
-            uint4 xv[kPer];
-            rows_load<kPer>(x, H, kb * 64, len8, nullptr, pass, nt * len8, xv);
-            if (pass == 0)
-                tile_load2<NS, false>(Wb + (int64_t)hc * nk * kTileBytes<false>,
-                                      Wb + (int64_t)(Id / 16 + hc) * nk * kTileBytes<false>, kt0, nk, lane, wg, wu);
-            else
-                __syncthreads();  // previous pass done with xs and red
-            rows_store<kPer>(xv, nt * len8, xs);
-            __syncthreads();
-            const uint16_t* xr = reinterpret_cast<const uint16_t*>(xs) + (kt0 - kb) * 64 + (lane >> 4) * 16;
-            float ag[kDensePass], au[kDensePass];
+    for (int pass = 0; pass < T; pass += 16) {
+        uint4 xa[NS][2];
+        a_frags<NS>(x, H, min(pass + (lane & 15), T - 1), kt0, nk, lane, xa);
+        if (pass == 0)
+            tile_load2<NS, false>(Wb + (int64_t)hc * nk * kTileBytes<false>,
+                                  Wb + (int64_t)(Id / 16 + hc) * nk * kTileBytes<false>, kt0, nk, lane, wg, wu);
+        f32x4_t cg = {0.f, 0.f, 0.f, 0.f}, cu = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int n = 0; n < kDensePass; ++n) ag[n] = au[n] = 0.f;
+        for (int s = 0; s < NS; ++s)
+            if (s < n_steps) {
 #pragma unroll
-            for (int s = 0; s < NS; ++s)
-                if (s < n_steps) {
-#pragma unroll
-                    for (int n = 0; n < kDensePass; ++n)
-                        if (n < nt) {
-                            ag[n] = piece_dot<false>(wg[s], xr + n * len8 * 8 + s * 64, ag[n]);
-                            au[n] = piece_dot<false>(wu[s], xr + n * len8 * 8 + s * 64, au[n]);
-                        }
+                for (int h = 0; h < 2; ++h) {
+                    cg = mfma16(xa[s][h], wg[s][h], cg);
+                    cu = mfma16(xa[s][h], wu[s][h], cu);
                 }
-#pragma unroll
-            for (int n = 0; n < kDensePass; ++n)
-                if (n < nt) {
-                    ag[n] = tile_row_sum(ag[n]);
-                    au[n] = tile_row_sum(au[n]);
-                    if (lane < 16) {
-                        red[((wave * kDensePass + n) * 2) * 16 + lane] = ag[n];
-                        red[((wave * kDensePass + n) * 2 + 1) * 16 + lane] = au[n];
-                    }
-                }
-            __syncthreads();
-        }
-        if (tid < nt * 32) {
-            const int n = tid >> 5, m = (tid >> 4) & 1, r = tid & 15;
-            float v = 0.f;
-            if (blk_steps > 0) {
-#pragma unroll
-                for (int w = 0; w < kWaves; ++w) v += red[((w * kDensePass + n) * 2 + m) * 16 + r];
             }
-            part[((int64_t)ks * T + pass + n) * 2 * Id + m * Id + hc * 16 + r] = v;
+        if (pass > 0) __syncthreads();  // the previous pass is done with red
+        red_store(red, wave, 0, lane, cg);
+        red_store(red, wave, 1, lane, cu);
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int o = tid + kThreads * q, m = o >> 8, rc = o & 255, r = rc >> 4, c = rc & 15;
+            if (pass + r < T)
+                part[((int64_t)ks * T + pass + r) * 2 * Id + m * Id + hc * 16 + c] = red_sum(red, m, rc);
         }
     }
 }
 
-// ---------------------------------------------------------------- K1
-template <int NJ>
+// Router, item (nt, ks): partial logits of experts [16 nt, 16 nt + 16) over
+// the same K range. The B operand is s*W of the row-major router matrix,
+// split into bf16 hi and lo (exact products, fp32 accumulation); the lanes
+// also add the squares of their x values, and the four lanes of a token row
+// (l, l + 16, l + 32, l + 48) then the wavefronts add them up.
+// -> lpart[ks][t][e] = sum over the range of x[t] * s * W[e]; ss[ks][t] = sum of x[t]^2
+// (written by the items of nt = 0).
+template <int NS>
+__device__ __forceinline__ void router_part(const uint16_t* __restrict__ x, int H,
+                                            const uint16_t* __restrict__ scale, const uint16_t* __restrict__ wr,
+                                            int E, int nt, int ks, int T, float* __restrict__ lpart,
+                                            float* __restrict__ ss_part, float* red) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int nk = H >> 6;
+    const int kt0 = (ks * kWaves + wave) * NS;
+    const int n_steps = max(0, min(NS, nk - kt0));
+    const int e = min(nt * 16 + (lane & 15), E - 1);
+    uint4 bh[NS][2], bl[NS][2];
+    {
+        uint4 wv[NS][2], sv[NS][2];
+        const uint16_t* wrow = wr + (int64_t)e * H + (lane >> 4) * 16;
+        const uint16_t* srow = scale + (lane >> 4) * 16;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int k = min(kt0 + s, nk - 1) * 64;
+            wv[s][0] = reinterpret_cast<const uint4*>(wrow + k)[0];
+            wv[s][1] = reinterpret_cast<const uint4*>(wrow + k)[1];
+            sv[s][0] = reinterpret_cast<const uint4*>(srow + k)[0];
+            sv[s][1] = reinterpret_cast<const uint4*>(srow + k)[1];
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t w4[4] = {wv[s][h].x, wv[s][h].y, wv[s][h].z, wv[s][h].w};
+                const uint32_t s4[4] = {sv[s][h].x, sv[s][h].y, sv[s][h].z, sv[s][h].w};
+                uint32_t h4[4], l4[4];
+                split_products8(w4, s4, h4, l4);
+                bh[s][h] = make_uint4(h4[0], h4[1], h4[2], h4[3]);
+                bl[s][h] = make_uint4(l4[0], l4[1], l4[2], l4[3]);
+            }
+    }
+    for (int pass = 0; pass < T; pass += 16) {
+        uint4 xa[NS][2];
+        a_frags<NS>(x, H, min(pass + (lane & 15), T - 1), kt0, nk, lane, xa);
+        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+        float sq = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            if (s < n_steps) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    c = mfma16(xa[s][h], bh[s][h], c);
+                    c = mfma16(xa[s][h], bl[s][h], c);
+                    float f[8];
+                    unpack8(xa[s][h], f);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) sq += f[i] * f[i];
+                }
+            }
+        sq = tile_row_sum(sq);
+        if (pass > 0) __syncthreads();  // the previous pass is done with red
+        red_store(red, wave, 0, lane, c);
+        if (lane < 16) red[kWaves * 512 + wave * 16 + lane] = sq;
+        __syncthreads();
+        const int r = tid >> 4, cc = tid & 15, t = pass + r, ee = nt * 16 + cc;
+        if (t < T && ee < E) lpart[((int64_t)ks * T + t) * E + ee] = red_sum(red, 0, tid);
+        if (nt == 0 && tid < 16 && pass + tid < T) {
+            float v = red[kWaves * 512 + tid];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) v += red[kWaves * 512 + w * 16 + tid];
+            ss_part[ks * T + pass + tid] = v;
+        }
+    }
+}
+
+// Router items first (ceil(E / 16) x kFrontSplit), then the dense gate/up
+// items (Id / 16 x kFrontSplit) if with_dense.
+template <int NS>
 __global__ __launch_bounds__(kThreads) void decode_front_kernel(StreamArgs a, const uint16_t* scale,
-                                                               const uint16_t* wr, const float* bias,
-                                                               float eps, float inv_sqrt_h,
-                                                               float* logits) {
-    extern __shared__ uint4 xs[];
-    // router items: (group of 8 experts) x (pass of kPass tokens)
-    const int n_groups = (a.E + kRouterExperts - 1) / kRouterExperts;
-    const int n_pass = (a.T + kPass - 1) / kPass;
-    const int n_router = n_groups * n_pass;
+                                                               const uint16_t* wr, float* lpart,
+                                                               float* ss_part) {
+    __shared__ float red[kWaves * 512 + kWaves * 16];
+    const int n_router = wr ? ((a.E + 15) / 16) * kFrontSplit : 0;
     const int b = blockIdx.x;
     if (b < n_router) {
-        __shared__ float s_rn[kPass];
-        const int g = b % n_groups, tp = b / n_groups;
-        router_item<NJ>(a.x, a.H, scale, wr, bias, a.E, tp * kPass, min(kPass, a.T - tp * kPass), eps,
-                        inv_sqrt_h, g * kRouterExperts, logits, xs, s_rn);
+        const int nt = b / kFrontSplit, ks = b - nt * kFrontSplit;
+        router_part<NS>(a.x, a.H, scale, wr, a.E, nt, ks, a.T, lpart, ss_part, red);
     } else {
-        // dense items: kDenseSplit K ranges of each gate/up tile pair
-        __shared__ float red[kWaves * kDensePass * 2 * 16];
-        const int i = b - n_router, hc = i / kDenseSplit, ks = i - hc * kDenseSplit;
-        dense_gateup_part<(NJ + kDenseSplit - 1) / kDenseSplit>(a.x, a.H, a.dgu, a.Id, hc, ks, a.T,
-                                                                a.dgu_part, xs, red);
+        const int i = b - n_router, hc = i / kFrontSplit, ks = i - hc * kFrontSplit;
+        dense_gateup_part<NS>(a.x, a.H, a.dgu, a.Id, hc, ks, a.T, a.dgu_part, red);
     }
 }
 
@@ -508,21 +476,21 @@ __global__ __launch_bounds__(kThreads) void decode_experts_gateup_kernel(StreamA
 
 // ---------------------------------------------------------------- K2
 // Dense gate/up finish: hd[t][c] = gelu_tanh(gate) * up, each the sum of its
-// kDenseSplit partial sums in split order; one thread per (t, c).
+// kFrontSplit partial sums in split order; one thread per (t, c).
 __device__ __forceinline__ void dense_finish(const StreamArgs& a, int blk) {
     const int i = blk * kRouteThreads + threadIdx.x;
     if (i >= a.T * a.Id) return;
     const int t = i / a.Id, c = i - t * a.Id;
-    float gp[kDenseSplit], up[kDenseSplit];
+    float gp[kFrontSplit], up[kFrontSplit];
 #pragma unroll
-    for (int ks = 0; ks < kDenseSplit; ++ks) {
+    for (int ks = 0; ks < kFrontSplit; ++ks) {
         const float* row = a.dgu_part + ((int64_t)ks * a.T + t) * 2 * a.Id;
         gp[ks] = row[c];
         up[ks] = row[a.Id + c];
     }
     float g = gp[0], u = up[0];
 #pragma unroll
-    for (int ks = 1; ks < kDenseSplit; ++ks) {
+    for (int ks = 1; ks < kFrontSplit; ++ks) {
         g += gp[ks];
         u += up[ks];
     }
@@ -546,11 +514,13 @@ __device__ __forceinline__ void dense_finish(const StreamArgs& a, int blk) {
 // 64-bit mask per expert: the rank of pair (t, k) within its expert is the
 // number of lower tokens in that expert's mask, the expert's row count its
 // popcount.
-__global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(StreamArgs a, const float* logits,
-                                                                    const float* pes,
-                                                                    int32_t* topk_idx, float* topk_w) {
-    if (!logits || blockIdx.x > 0) {
-        dense_finish(a, (int)blockIdx.x - (logits ? 1 : 0));
+__global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(StreamArgs a, const float* lpart,
+                                                                    const float* ss_part, const float* bias,
+                                                                    const float* pes, float eps,
+                                                                    float inv_sqrt_h, int32_t* topk_idx,
+                                                                    float* topk_w) {
+    if (!lpart || blockIdx.x > 0) {
+        dense_finish(a, (int)blockIdx.x - (lpart ? 1 : 0));
         return;
     }
     __shared__ int s_idx[kMaxPairs];
@@ -574,7 +544,18 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(StreamArgs 
     for (int t0 = 0; t0 < T; t0 += tc) {
         const int t = t0 + tl;
         const bool live = t < T && e < E;
-        const float l = live ? logits[(int64_t)t * E + e] : 0.f;
+        // logit = (sum_h x s W) * rms(x)^-1 * H^-0.5 + bias, the slices added in order
+        float l = 0.f;
+        if (live) {
+            float acc = lpart[(int64_t)t * E + e], sq = ss_part[t];
+#pragma unroll
+            for (int ks = 1; ks < kFrontSplit; ++ks) {
+                acc += lpart[((int64_t)ks * T + t) * E + e];
+                sq += ss_part[ks * T + t];
+            }
+            const float rn = 1.0f / sqrtf(sq / (float)a.H + eps);
+            l = acc * (rn * inv_sqrt_h) + (bias ? bias[e] : 0.f);
+        }
         const unsigned long long comp =
             live ? ((unsigned long long)order_key(l) << 32) | (unsigned)(~e) : 0ull;
         if (t0 > 0) __syncthreads();  // previous chunk done with s_comp
@@ -775,22 +756,14 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(StreamArgs a) 
         make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
 }
 
-template <int NJ>
-hipError_t launch_front_nj(const StreamArgs& a, const uint16_t* scale, const uint16_t* wr,
-                           const float* bias, float eps, float* logits, bool router,
-                           hipStream_t stream) {
-    const int n_router =
-        router ? ((a.E + kRouterExperts - 1) / kRouterExperts) * ((a.T + kPass - 1) / kPass) : 0;
-    const int blocks = n_router + (a.with_dense ? (a.Id / 16) * kDenseSplit : 0);
-    // x rows of a router pass, or the x slices of a dense pass
-    const int ns = (a.H / 256 + kDenseSplit - 1) / kDenseSplit;
-    const size_t lds = (size_t)max(kPass * a.H, kDensePass * kWaves * ns * 64) * sizeof(uint16_t);
-    const float inv_sqrt_h = (float)(1.0 / __builtin_sqrt((double)a.H));
+template <int NS>
+hipError_t launch_front_ns(const StreamArgs& a, const uint16_t* scale, const uint16_t* wr, float* lpart,
+                           float* ss_part, hipStream_t stream) {
+    const int n_router = wr ? ((a.E + 15) / 16) * kFrontSplit : 0;
+    const int blocks = n_router + (a.with_dense ? (a.Id / 16) * kFrontSplit : 0);
     if (blocks <= 0) return hipSuccess;
-    StreamArgs b = a;
-    if (!router) b.E = 0;  // no router items: the kernel derives their count from E
-    hipLaunchKernelGGL(decode_front_kernel<NJ>, dim3(blocks), dim3(kThreads), lds, stream, b, scale,
-                       wr, bias, eps, inv_sqrt_h, logits);
+    hipLaunchKernelGGL(decode_front_kernel<NS>, dim3(blocks), dim3(kThreads), 0, stream, a, scale, wr, lpart,
+                       ss_part);
     return hipGetLastError();
 }
 
@@ -819,20 +792,26 @@ hipError_t launch_experts_nj(const StreamArgs& a, bool int8, hipStream_t stream)
         default: return hipErrorInvalidValue;                     \
     }
 
-hipError_t launch_decode_front(const StreamArgs& a, const uint16_t* scale, const uint16_t* wr,
-                               const float* bias, float eps, float* logits, hipStream_t stream) {
-#define CALL(n) launch_front_nj<n>(a, scale, wr, bias, eps, logits, logits != nullptr, stream)
-    MOE_NJ_SWITCH(a.H / 256, CALL)
-#undef CALL
+hipError_t launch_decode_front(const StreamArgs& a, const uint16_t* scale, const uint16_t* wr, float* lpart,
+                               float* ss_part, hipStream_t stream) {
+    // K-steps per wavefront: the H / 64 steps over kFrontSplit workgroups of four
+    switch ((a.H / 64 + kFrontSplit * kWaves - 1) / (kFrontSplit * kWaves)) {
+        case 1: return launch_front_ns<1>(a, scale, wr, lpart, ss_part, stream);
+        case 2: return launch_front_ns<2>(a, scale, wr, lpart, ss_part, stream);
+        case 3: return launch_front_ns<3>(a, scale, wr, lpart, ss_part, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
-hipError_t launch_decode_route(const StreamArgs& a, const float* logits, const float* pes,
-                               int32_t* topk_idx, float* topk_w, hipStream_t stream) {
+hipError_t launch_decode_route(const StreamArgs& a, const float* lpart, const float* ss_part, const float* bias,
+                               const float* pes, float eps, int32_t* topk_idx, float* topk_w,
+                               hipStream_t stream) {
     const int blocks =
-        (logits ? 1 : 0) + (a.with_dense ? (a.T * a.Id + kRouteThreads - 1) / kRouteThreads : 0);
+        (lpart ? 1 : 0) + (a.with_dense ? (a.T * a.Id + kRouteThreads - 1) / kRouteThreads : 0);
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(decode_route_kernel, dim3(blocks), dim3(kRouteThreads), 0, stream, a, logits, pes,
-                       topk_idx, topk_w);
+    const float inv_sqrt_h = (float)(1.0 / __builtin_sqrt((double)a.H));
+    hipLaunchKernelGGL(decode_route_kernel, dim3(blocks), dim3(kRouteThreads), 0, stream, a, lpart, ss_part,
+                       bias, pes, eps, inv_sqrt_h, topk_idx, topk_w);
     return hipGetLastError();
 }
 

@@ -99,18 +99,22 @@ struct StreamArgs {
     uint16_t* y;    // [T][H]
     // fp32 partial outputs of K4: expert rows [T*K][H] (grouped order), dense [T][H]
     float* part; float* dpart;
-    // fp32 partial sums of the dense gate/up, K split: [kDenseSplit][T][2 Id] (gate, then up)
+    // fp32 partial sums of the dense gate/up, K split: [kFrontSplit][T][2 Id] (gate, then up)
     float* dgu_part;
 };
-// workgroups sharing the K range of one dense gate/up tile pair in K1
-constexpr int kDenseSplit = 4;
-// K1: router logits (if logits != null) beside the dense gate/up partial sums -> dgu_part
-hipError_t launch_decode_front(const StreamArgs& a, const uint16_t* scale, const uint16_t* wr,
-                               const float* bias, float eps, float* logits, hipStream_t stream);
-// K2: top-k and grouping (one workgroup, T <= MOE_STREAM_MAX_TOKENS; none if
-// logits == null) beside the dense gate/up finish (dgu_part -> hd)
-hipError_t launch_decode_route(const StreamArgs& a, const float* logits, const float* pes,
-                               int32_t* topk_idx, float* topk_w, hipStream_t stream);
+// workgroups sharing the K range of one router or dense gate/up item in K1
+constexpr int kFrontSplit = 4;
+// K1: router partial logits lpart [kFrontSplit][T][E] and sums of squares of x
+// ss_part [kFrontSplit][T] (if wr != null), beside the dense gate/up partial
+// sums -> dgu_part (if a.with_dense)
+hipError_t launch_decode_front(const StreamArgs& a, const uint16_t* scale, const uint16_t* wr, float* lpart,
+                               float* ss_part, hipStream_t stream);
+// K2: logits from the partial sums, top-k and grouping (one workgroup, T <=
+// MOE_STREAM_MAX_TOKENS; none if lpart == null) beside the dense gate/up
+// finish (dgu_part -> hd, if a.with_dense)
+hipError_t launch_decode_route(const StreamArgs& a, const float* lpart, const float* ss_part, const float* bias,
+                               const float* pes, float eps, int32_t* topk_idx, float* topk_w,
+                               hipStream_t stream);
 // K3: gate/up of the touched experts -> h
 hipError_t launch_decode_experts_gateup(const StreamArgs& a, bool int8, hipStream_t stream);
 // K4: down of the touched experts and of the dense MLP -> fp32 partial rows

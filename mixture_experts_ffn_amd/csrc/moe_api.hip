@@ -34,13 +34,12 @@ size_t up256(size_t b) { return (b + 255) & ~size_t(255); }
 // runs; below it, the per-expert dot-product router and a separate top-k,
 // which spread a small batch over more workgroups.
 constexpr int kRouterMfmaMinT = 64;
-static_assert(kRouterMfmaMinT >= MOE_STREAM_MAX_TOKENS, "the streaming path stages logits");
 
 // Workspace layout at a given T (byte offsets into ws).
 struct Layout {
     size_t logits, partial, topk_idx, topk_w, pair_rank, tile_counts, counts, offsets, active, n_active;
     size_t perm_token, perm_w, inv_row, mtile_group, mtile_row0, n_mtiles, h, hd, rows;
-    size_t dout, part, dpart, dgu_part, total;
+    size_t dout, part, dpart, dgu_part, lpart, ss_part, total;
     int max_mtiles;
 };
 
@@ -56,7 +55,7 @@ Layout make_layout(const moe_dims& d, int64_t T) {
     const int64_t n_tiles = (T + moe::kRouteTile - 1) / moe::kRouteTile;
     const int64_t BM = moe::kGemmBM;
     L.max_mtiles = (int)((TK + BM - 1) / BM + (E < TK ? E : TK));
-    // fp32 logits: only the small-batch routers stage them (T <= 64)
+    // fp32 logits: only moe_route's small-batch router stages them
     L.logits = take((T <= kRouterMfmaMinT ? T : 0) * E * 4);
     // MFMA router's partial sums (every T: the grouped path uses it at any size)
     L.partial = take(T > 0 ? (size_t)moe::router_split((int)T, d.hidden, (int)E).slices * T * E * 4 : 0);
@@ -82,7 +81,9 @@ Layout make_layout(const moe_dims& d, int64_t T) {
     const int64_t Ts = T <= MOE_STREAM_MAX_TOKENS ? T : 0;
     L.part = take(Ts * K * d.hidden * 4);
     L.dpart = take(Ts * d.hidden * 4);
-    L.dgu_part = take(Ts * moe::kDenseSplit * 2 * d.dense_inter * 4);
+    L.dgu_part = take(Ts * moe::kFrontSplit * 2 * d.dense_inter * 4);
+    L.lpart = take(Ts * moe::kFrontSplit * E * 4);
+    L.ss_part = take(Ts * moe::kFrontSplit * 4);
     L.total = off;
     return L;
 }
@@ -255,7 +256,6 @@ int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
     const Layout L = make_layout(*d, T);
     const bool int8 = w->expert_dtype == MOE_DTYPE_INT8;
     const int H = d->hidden, E = d->num_experts, K = d->top_k, I = d->expert_inter, Id = d->dense_inter;
-    float* logits = at<float>(ws, L.logits);
     int32_t* topk_idx = at<int32_t>(ws, L.topk_idx);
     float* topk_w = at<float>(ws, L.topk_w);
     int32_t* pair_rank = at<int32_t>(ws, L.pair_rank);
@@ -292,11 +292,14 @@ int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
         sa.dgu_part = at<float>(ws, L.dgu_part);
         sa.with_dense = 1;  // the dense MLP's items ride along in K1, K2 and K4
         HIP_TRY(st.begin("decode_front"), "event record");
+        float* lpart = at<float>(ws, L.lpart);
+        float* ss_part = at<float>(ws, L.ss_part);
         HIP_TRY(moe::launch_decode_front(sa, (const uint16_t*)w->router_scale, (const uint16_t*)w->router_w,
-                                         w->logit_bias, d->rms_eps, logits, stream),
+                                         lpart, ss_part, stream),
                 "decode_front launch");
         HIP_TRY(st.begin("decode_route"), "event record");
-        HIP_TRY(moe::launch_decode_route(sa, logits, w->per_expert_scale, topk_idx, topk_w, stream),
+        HIP_TRY(moe::launch_decode_route(sa, lpart, ss_part, w->logit_bias, w->per_expert_scale, d->rms_eps,
+                                         topk_idx, topk_w, stream),
                 "decode_route launch");
         HIP_TRY(st.begin("decode_experts_gateup"), "event record");
         HIP_TRY(moe::launch_decode_experts_gateup(sa, int8, stream), "decode_experts_gateup launch");
@@ -389,9 +392,9 @@ int dense_mlp(const moe_dims* d, const void* dense_gate_up, const void* dense_do
         sa.hd = hd; sa.y = (uint16_t*)y;
         sa.part = at<float>(ws, L.part); sa.dpart = at<float>(ws, L.dpart);
         sa.dgu_part = at<float>(ws, L.dgu_part);
-        HIP_TRY(moe::launch_decode_front(sa, nullptr, nullptr, nullptr, 0.f, nullptr, stream),
+        HIP_TRY(moe::launch_decode_front(sa, nullptr, nullptr, nullptr, nullptr, stream),
                 "decode_front launch");
-        HIP_TRY(moe::launch_decode_route(sa, nullptr, nullptr, nullptr, nullptr, stream),
+        HIP_TRY(moe::launch_decode_route(sa, nullptr, nullptr, nullptr, nullptr, 0.f, nullptr, nullptr, stream),
                 "decode_route (dense finish) launch");
         HIP_TRY(moe::launch_decode_down(sa, false, stream), "decode_down launch");
         HIP_TRY(moe::launch_decode_combine(sa, stream), "decode_combine launch");

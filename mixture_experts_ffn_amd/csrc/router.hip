@@ -149,17 +149,9 @@ __device__ __forceinline__ void r_load(RStage<NQ>& st, const uint16_t* xr, const
 
 // split 8 products s*w into bf16 hi (truncation) and lo (exact remainder)
 __device__ __forceinline__ void split8(const v4u& w, const v4u& sc, v4u& hi, v4u& lo) {
-    unsigned h[4], l[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const unsigned wu = w[i], su = sc[i];
-        const float p0 = bf16_lo(wu) * bf16_lo(su);  // exact in fp32
-        const float p1 = bf16_hi(wu) * bf16_hi(su);
-        const unsigned h0 = __float_as_uint(p0) & 0xFFFF0000u, h1 = __float_as_uint(p1) & 0xFFFF0000u;
-        const float r0 = p0 - __uint_as_float(h0), r1 = p1 - __uint_as_float(h1);  // exact, fits bf16
-        h[i] = (h0 >> 16) | h1;
-        l[i] = (__float_as_uint(r0) >> 16) | (__float_as_uint(r1) & 0xFFFF0000u);
-    }
+    const uint32_t wa[4] = {w[0], w[1], w[2], w[3]}, sa[4] = {sc[0], sc[1], sc[2], sc[3]};
+    uint32_t h[4], l[4];
+    split_products8(wa, sa, h, l);
     hi = v4u{h[0], h[1], h[2], h[3]};
     lo = v4u{l[0], l[1], l[2], l[3]};
 }
