@@ -57,11 +57,15 @@ __device__ __forceinline__ void split_products8(const uint32_t (&w)[4], const ui
 }
 
 // GELU, tanh approximation ("gelu_pytorch_tanh"):
-// 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))), evaluated in fp32.
+// 0.5 z (1 + tanh(u)), u = sqrt(2/pi) (z + 0.044715 z^3). Since
+// 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)), this is z / (1 + 2^(-2 u log2 e)),
+// evaluated in fp32 with the hardware exp2 and reciprocal (a few ulp; the
+// limits are exact: 2^t overflows to inf for very negative z, giving -0, and
+// underflows to 0 for very positive z, giving z).
 __device__ __forceinline__ float gelu_tanh(float z) {
-    const float c = 0.7978845608028654f;  // sqrt(2/pi)
-    float inner = c * (z + 0.044715f * z * z * z);
-    return 0.5f * z * (1.0f + tanhf(inner));
+    const float k = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+    const float t = k * (z + 0.044715f * z * z * z);
+    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
 }
 
 // Butterfly reductions over the lanes [base, base + width) of a wavefront.

@@ -94,6 +94,12 @@ __device__ __forceinline__ void raw_barrier() {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
+// barrier after this wavefront's LDS accesses have completed; its global
+// stores may still be in flight
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited on
+    raw_barrier();
+}
 constexpr int kAStageElems = BM * BK;  // bf16 elements per LDS stage of A
 
 // One K-step of the wavefront's B fragments: bf16 q[2 j + s] = column tile j,
@@ -186,6 +192,7 @@ __device__ __forceinline__ void mma_step(const uint16_t* As, const BStep<INT8>& 
 struct Lds {
     uint16_t* a[kDepth];
     uint16_t* ep;
+    float* rw;  // down: router weight of each row of the tile
 };
 
 // s_waitcnt vmcnt(n) lgkmcnt(0) (vmcnt split over bits 3:0 and 15:14)
@@ -256,37 +263,27 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
     const int wn = wave;
     const int n_nt = n_tiles_of<MODE>(p);
 
-    // XCD-aware mapping: XCD x owns M-tiles [c0, c1) = [x * chunk, (x + 1) * chunk)
-    // with all their N-tiles. Its blocks run in order over runs of M-tiles
-    // that share their weights (one expert's M-tiles, or the whole chunk for
-    // the dense MLP): per run, for each N-tile, its M-tiles back to back. Those
-    // blocks start together on one XCD, so an N-tile's weights come from HBM
-    // once per run and the other M-tiles find them in L2. The run holding
-    // local block l contains M-tile c0 + l / n_nt.
-    const int m_total = p.mtile_group ? *p.n_mtiles : (p.M_dense + BM - 1) / BM;
-    const int chunk = (m_total + kXcds - 1) / kXcds;
-    const int xcd = b % kXcds, local = b / kXcds;
-    const int c0 = xcd * chunk, c1 = min(c0 + chunk, m_total);
-    const int u = local / n_nt;
-    if (c0 + u >= c1) return;
-    int r0 = c0, r1 = c1;
-    if (p.mtile_group) {
-        const int mu = c0 + u, g = p.mtile_group[mu];
-        const int beg = p.group_end[g], cnt = p.group_end[g + 1] - beg;
-        const int first = mu - (p.mtile_row0[mu] - beg) / BM;  // the expert's first M-tile
-        r0 = max(first, c0);
-        r1 = min(first + (cnt + BM - 1) / BM, c1);
-    }
-    const int rl = r1 - r0, o = local - (r0 - c0) * n_nt;
-    const int nt = o / rl;
-    const int mt = r0 + (o - nt * rl);
-
-    int group = 0, row0, rows_valid;
-    if (p.mtile_group) {
-        group = p.mtile_group[mt];
-        row0 = p.mtile_row0[mt];
-        rows_valid = min(BM, p.group_end[group + 1] - row0);
+    // XCD-aware mapping (gemm_expert_blocks): the routed experts' tile of this
+    // block comes precomputed from the grouping; the dense problem's XCD x
+    // owns M-tiles [x * chunk, (x + 1) * chunk) and runs them, per N-tile, back
+    // to back, so an N-tile's weights come from HBM once per XCD.
+    int group = 0, row0, rows_valid, nt;
+    if (p.tiles) {
+        const int2 te = p.tiles[b];
+        if (te.y < 0) return;
+        row0 = te.x;
+        group = te.y & 511;
+        rows_valid = (te.y >> 9) & 255;
+        nt = te.y >> 17;
     } else {
+        const int m_total = (p.M_dense + BM - 1) / BM;
+        const int chunk = (m_total + kXcds - 1) / kXcds;
+        const int xcd = b % kXcds, local = b / kXcds;
+        const int c0 = xcd * chunk, c1 = min(c0 + chunk, m_total);
+        if (c0 + local / n_nt >= c1) return;
+        const int rl = c1 - c0;
+        nt = local / rl;
+        const int mt = c0 + (local - nt * rl);
         row0 = mt * BM;
         rows_valid = min(BM, p.M_dense - row0);
     }
@@ -322,6 +319,23 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
         const int64_t arow = p.a_rows ? p.a_rows[row0 + rr] : (int64_t)(row0 + rr);
         ap[q] = reinterpret_cast<const char*>(p.A + arow * p.lda + c * 8);
     }
+    // epilogue operands, loaded now so that their latency hides behind the K
+    // loop: int8 column scales of this lane's columns, router weight of row tid
+    const int col_l = lane & 15;
+    float sc0 = 1.f, sc1 = 1.f, row_wt = 1.f;
+    if (INT8) {
+        const float* bs = p.b_scale + (int64_t)group * p.scale_group_stride;
+        if (MODE == MODE_GATEUP) {
+            const int hc = min(nt * kHalfN + wn * 16 + col_l, p.n_out - 1);
+            sc0 = bs[hc];
+            sc1 = bs[p.up_off + hc];
+        } else {
+            sc0 = bs[nt * BN + wn * 32 + col_l];
+            sc1 = bs[nt * BN + wn * 32 + 16 + col_l];
+        }
+    }
+    if (MODE == MODE_DOWN && !p.Cf && tid < BM)
+        row_wt = tid >= rows_valid ? 0.f : p.row_w ? p.row_w[row0 + tid] : 1.f;
     switch (nsl) {  // uniform per wavefront
         case 0: k_loop<INT8, 0>(ap, bp, nk, L, wave, lane, acc); break;
         case 1: k_loop<INT8, 1>(ap, bp, nk, L, wave, lane, acc); break;
@@ -331,25 +345,18 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
     }
 
     // epilogue: acc[i][jj][v] is C[row = 16 i + 4 (lane>>4) + v][column tile jj, lane&15]
-    const int col_l = lane & 15;
     if (MODE == MODE_GATEUP) {
         uint16_t* Ht = L.ep;  // [BM][128] bf16 (32 KB)
         const int hl = wn * 16 + col_l;  // column within the 128-wide h tile
-        const int hc = min(nt * kHalfN + hl, p.n_out - 1);
-        float gs = 1.f, us = 1.f;
-        if (INT8) {
-            gs = p.b_scale[group * p.scale_group_stride + hc];
-            us = p.b_scale[group * p.scale_group_stride + p.up_off + hc];
-        }
 #pragma unroll
         for (int i = 0; i < kSlabs; ++i)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int r = i * 16 + (lane >> 4) * 4 + v;
-                const float g = acc[i][0][v] * gs, u = acc[i][1][v] * us;
+                const float g = acc[i][0][v] * sc0, u = acc[i][1][v] * sc1;
                 Ht[r * kHalfN + hl] = f32_to_bf16(gelu_tanh(g) * u);
             }
-        __syncthreads();
+        lds_barrier();
         const int h_valid = min(kHalfN, p.n_out - nt * kHalfN);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -374,22 +381,23 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
     } else {
         // bf16 rows times the router weight, staged through LDS in two halves of 64 rows (32 KB each)
         uint16_t* Ot = L.ep;
+        if (tid < BM) L.rw[tid] = row_wt;
+        lds_barrier();
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
                 const int cl = wn * 32 + jj * 16 + col_l;
-                const float sc = INT8 ? p.b_scale[group * p.scale_group_stride + nt * BN + cl] : 1.f;
+                const float sc = jj ? sc1 : sc0;
 #pragma unroll
                 for (int i = half * 4; i < half * 4 + 4; ++i)
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         const int r = i * 16 + (lane >> 4) * 4 + v;
-                        const float wgt = r >= rows_valid ? 0.f : p.row_w ? p.row_w[row0 + r] : 1.f;
-                        Ot[(r - half * 64) * BN + cl] = f32_to_bf16(acc[i][jj][v] * sc * wgt);
+                        Ot[(r - half * 64) * BN + cl] = f32_to_bf16(acc[i][jj][v] * sc * L.rw[r]);
                     }
             }
-            __syncthreads();
+            lds_barrier();
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int c = tid + kThreads * q, rl = c >> 5, cc = c & 31;
@@ -398,7 +406,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
                     *reinterpret_cast<uint4*>(p.C + (int64_t)(row0 + r) * p.ldc + nt * BN + cc * 8) =
                         *reinterpret_cast<const uint4*>(Ot + rl * BN + cc * 8);
             }
-            __syncthreads();
+            lds_barrier();  // every wavefront has read its half before the next overwrites it
         }
     }
 }
@@ -413,7 +421,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p0, GemmArgs p1
     __shared__ __attribute__((aligned(16))) uint16_t st4[kAStageElems];
     __shared__ __attribute__((aligned(16))) uint16_t st5[kAStageElems];
     __shared__ __attribute__((aligned(16))) uint16_t ep[BM * kHalfN];
-    const Lds L{{st0, st1, st2, st3, st4, st5}, ep};
+    __shared__ float rw[BM];
+    const Lds L{{st0, st1, st2, st3, st4, st5}, ep, rw};
     const int b = blockIdx.x;
     if (b < split) gemm_block<MODE, INT8_0>(p0, b, L);
     else gemm_block<MODE, INT8_1>(p1, b - split, L);

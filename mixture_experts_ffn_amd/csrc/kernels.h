@@ -45,6 +45,12 @@ struct PermuteOut {
     int32_t* mtile_group;   // [max m-tiles] expert of each BM-row tile
     int32_t* mtile_row0;    // [max m-tiles] first grouped row of each tile
     int32_t* n_mtiles;      // [1]
+    // the tile of every block of the two expert GEMMs (0: gate/up, 1: down),
+    // gemm_expert_blocks(max_mtiles, n_nt[i]) entries each: {first grouped row,
+    // expert | rows << 9 | N-tile << 17}, or y = -1 for a block with no tile
+    int2* tiles[2];
+    int n_nt[2];
+    int max_mtiles;
 };
 // pair_rank: [T*K] scratch (rank of each pair among its tile's pairs of the
 // same expert)
@@ -53,6 +59,19 @@ hipError_t launch_permute(const int32_t* topk_idx, const float* topk_w, int32_t*
 
 // ---- grouped MFMA GEMMs (gemm.hip) -----------------------------------------
 constexpr int kGemmBM = 128;  // rows per grouped M-tile
+constexpr int kGemmBN = 256;  // output columns per N-tile (gate/up: 128 h columns)
+constexpr int kGemmXcds = 8;  // block b of a GEMM runs on XCD b % 8
+// N-tiles of the gate/up (h columns) and down GEMMs
+inline int gemm_n_tiles_gateup(int inter) { return (inter + kGemmBN / 2 - 1) / (kGemmBN / 2); }
+inline int gemm_n_tiles_down(int hidden) { return hidden / kGemmBN; }
+// blocks of an expert GEMM: kGemmXcds x ceil(max_mtiles / kGemmXcds) M-tile
+// slots x n_nt N-tiles. XCD x owns a contiguous chunk of the M-tiles with all
+// their N-tiles, and runs them expert by expert: for each N-tile, the expert's
+// M-tiles back to back, so that an N-tile's weights come from HBM once per
+// expert and its other M-tiles find them in the XCD's L2.
+inline int gemm_expert_blocks(int max_mtiles, int n_nt) {
+    return kGemmXcds * ((max_mtiles + kGemmXcds - 1) / kGemmXcds) * n_nt;
+}
 constexpr int kMaxTopKGemm = 8;
 struct GemmArgs {
     const uint16_t* A; int64_t lda;          // bf16 activations
@@ -69,6 +88,7 @@ struct GemmArgs {
     uint16_t* C; int64_t ldc;                 // bf16 output
     float* Cf;                                // down: fp32 output instead (dense MLP)
     const float* row_w;                       // down: per-row weight of the bf16 output (null = 1)
+    const int2* tiles;                        // grouped: the tile of every block (PermuteOut::tiles)
 };
 // gate/up + GELU of the experts, and of `dense` (bf16, may be null), in one launch
 hipError_t launch_gemm_gateup(const GemmArgs& experts, const GemmArgs* dense, bool int8,

@@ -38,7 +38,7 @@ constexpr int kRouterMfmaMinT = 64;
 // Workspace layout at a given T (byte offsets into ws).
 struct Layout {
     size_t logits, partial, topk_idx, topk_w, pair_rank, tile_counts, counts, offsets, active, n_active;
-    size_t perm_token, perm_w, inv_row, mtile_group, mtile_row0, n_mtiles, h, hd, rows;
+    size_t perm_token, perm_w, inv_row, mtile_group, mtile_row0, n_mtiles, gemm_tiles[2], h, hd, rows;
     size_t dout, part, dpart, dgu_part, lpart, ss_part, total;
     int max_mtiles;
 };
@@ -73,6 +73,8 @@ Layout make_layout(const moe_dims& d, int64_t T) {
     L.mtile_group = take((size_t)L.max_mtiles * 4);
     L.mtile_row0 = take((size_t)L.max_mtiles * 4);
     L.n_mtiles = take(4);
+    L.gemm_tiles[0] = take((size_t)moe::gemm_expert_blocks(L.max_mtiles, moe::gemm_n_tiles_gateup(d.expert_inter)) * 8);
+    L.gemm_tiles[1] = take((size_t)moe::gemm_expert_blocks(L.max_mtiles, moe::gemm_n_tiles_down(d.hidden)) * 8);
     L.h = take(TK * d.expert_inter * 2);
     L.hd = take(T * d.dense_inter * 2);
     L.rows = take(TK * d.hidden * 2);
@@ -259,7 +261,7 @@ int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
     int32_t* topk_idx = at<int32_t>(ws, L.topk_idx);
     float* topk_w = at<float>(ws, L.topk_w);
     int32_t* pair_rank = at<int32_t>(ws, L.pair_rank);
-    moe::PermuteOut po;
+    moe::PermuteOut po{};
     po.tile_counts = at<int32_t>(ws, L.tile_counts);
     po.counts = at<int32_t>(ws, L.counts);
     po.offsets = at<int32_t>(ws, L.offsets);
@@ -271,6 +273,11 @@ int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
     po.mtile_group = at<int32_t>(ws, L.mtile_group);
     po.mtile_row0 = at<int32_t>(ws, L.mtile_row0);
     po.n_mtiles = at<int32_t>(ws, L.n_mtiles);
+    po.tiles[0] = at<int2>(ws, L.gemm_tiles[0]);
+    po.tiles[1] = at<int2>(ws, L.gemm_tiles[1]);
+    po.n_nt[0] = moe::gemm_n_tiles_gateup(I);
+    po.n_nt[1] = moe::gemm_n_tiles_down(H);
+    po.max_mtiles = L.max_mtiles;
     uint16_t* h = at<uint16_t>(ws, L.h);
     uint16_t* hd = at<uint16_t>(ws, L.hd);
     uint16_t* rows = at<uint16_t>(ws, L.rows);
@@ -324,7 +331,7 @@ int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
         g.b_scale = int8 ? w->gate_up_scale : nullptr; g.scale_group_stride = 2 * I;
         g.K = H; g.n_out = I; g.up_off = I;
         g.mtile_group = po.mtile_group; g.mtile_row0 = po.mtile_row0; g.n_mtiles = po.n_mtiles;
-        g.group_end = po.offsets; g.max_mtiles = L.max_mtiles;
+        g.group_end = po.offsets; g.max_mtiles = L.max_mtiles; g.tiles = po.tiles[0];
         g.C = h; g.ldc = I;
         // dense gate/up + GELU, in the same launch
         moe::GemmArgs gd{};
@@ -338,7 +345,7 @@ int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
         gw.b_scale = int8 ? w->down_scale : nullptr; gw.scale_group_stride = H;
         gw.K = I; gw.n_out = H;
         gw.mtile_group = po.mtile_group; gw.mtile_row0 = po.mtile_row0; gw.n_mtiles = po.n_mtiles;
-        gw.group_end = po.offsets; gw.max_mtiles = L.max_mtiles;
+        gw.group_end = po.offsets; gw.max_mtiles = L.max_mtiles; gw.tiles = po.tiles[1];
         gw.C = rows; gw.ldc = H; gw.row_w = po.perm_w;
         // dense down (fp32), in the same launch
         float* dout = at<float>(ws, L.dout);

@@ -143,6 +143,39 @@ __global__ __launch_bounds__(kOffThreads) void group_offsets_kernel(int n_tiles,
             o.mtile_row0[s_tile[ee] + j] = s_off[ee] + j * BM;
         }
     }
+    // the tile of every GEMM block (mapping of gemm_expert_blocks): block b
+    // is slot local = b / kGemmXcds of XCD x = b % kGemmXcds; XCD x owns
+    // M-tiles [c0, c1); its slots run over expert runs (the expert's M-tiles
+    // inside the chunk), per run each N-tile with the run's M-tiles in a row
+    const int m_total = s_tile[E];
+    const int mchunk = (m_total + kGemmXcds - 1) / kGemmXcds;
+    const int slots = (o.max_mtiles + kGemmXcds - 1) / kGemmXcds;
+    for (int gi = 0; gi < 2; ++gi) {
+        const int n_nt = o.n_nt[gi];
+        const int n_blocks = kGemmXcds * slots * n_nt;
+        for (int b = tid; b < n_blocks; b += kOffThreads) {
+            const int xcd = b % kGemmXcds, local = b / kGemmXcds;
+            const int c0 = xcd * mchunk, c1 = min(c0 + mchunk, m_total);
+            const int mu = c0 + local / n_nt;
+            int2 te = make_int2(0, -1);
+            if (mu < c1) {
+                int lo = 0, hi = E - 1;  // the expert g with s_tile[g] <= mu < s_tile[g + 1]
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (s_tile[mid] <= mu) lo = mid;
+                    else hi = mid - 1;
+                }
+                const int g = lo, first = s_tile[g];
+                const int r0 = max(first, c0), r1 = min(s_tile[g + 1], c1), rl = r1 - r0;
+                const int ol = local - (r0 - c0) * n_nt;
+                const int nt = ol / rl, mt = r0 + (ol - nt * rl);
+                const int row0 = s_off[g] + (mt - first) * BM;
+                const int rows = min(BM, s_off[g] + s_cnt[g] - row0);
+                te = make_int2(row0, g | (rows << 9) | (nt << 17));
+            }
+            o.tiles[gi][b] = te;
+        }
+    }
 }
 
 __global__ __launch_bounds__(256) void group_scatter_kernel(const int32_t* __restrict__ topk_idx,
