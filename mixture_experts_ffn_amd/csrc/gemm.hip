@@ -15,9 +15,11 @@
 // the dense output and its K weighted expert rows (ONNX export card, "Truthful
 // graph contracts", row "MoE topology": dense + moe).
 //
-// Tile 128 x 256 x 64, 512 threads = 8 wavefronts side by side in N, each
-// owning all 128 rows and 32 columns (8 x 2 MFMA 16x16x32 tiles); 16-row slabs
-// past the tile's last valid row skip their MFMAs.
+// Tile 256 x 256 x 64, 512 threads = 8 wavefronts side by side in N, each
+// owning all 256 rows and 32 columns (16 x 2 MFMA 16x16x32 tiles); 16-row slabs
+// past the tile's last valid row (in groups of four) skip their MFMAs. With
+// about 128 routed rows per expert a 256-row tile holds an expert's rows in one
+// M-tile, so each weight tile streams through a CU once per expert.
 //
 // The weights (B) are the stream that HBM bounds. They are stored tiled (16
 // rows x 64 k per tile, in the order of the MFMA operand: lane l holds column
@@ -27,10 +29,11 @@
 // shared by all wavefronts) move from global memory straight into LDS
 // (global_load_lds_dwordx4: each lane's 16 bytes land at the wavefront's LDS
 // base + 16 * lane, so the lanes fetch the XOR-swizzled chunk order directly)
-// through kDepth LDS stages. Both run kDepth - 1 K-steps ahead: about 240 KB
-// per CU in flight. Blocks are mapped XCD-aware: block b runs on XCD b % 8, and
+// through kDepth LDS stages, which the epilogue reuses to stage its output.
+// Both run kDepth - 1 K-steps ahead: about 192 KB per CU in flight. Blocks
+// are mapped XCD-aware (gemm_expert_blocks): block b runs on XCD b % 8, and
 // each XCD owns a contiguous run of M-tiles with all their N-tiles, so an
-// M-tile's A rows and the M-tiles of one expert meet in the same L2. A launch
+// M-tile's A rows and an expert's weight tiles meet in the same L2. A launch
 // carries two problems (the routed experts and the dense MLP) back to back.
 #include "common.h"
 #include "kernels.h"
@@ -39,14 +42,16 @@ namespace moe {
 
 namespace {
 
-constexpr int BM = kGemmBM, BN = 256, BK = 64;
+constexpr int BM = kGemmBM, BN = kGemmBN, BK = 64;
 constexpr int kHalfN = BN / 2;  // gate/up: h columns per tile
 constexpr int kThreads = 512;
-constexpr int kXcds = 8;
-constexpr int kDepth = 6;       // K-steps of B in flight per wavefront
+constexpr int kWaves = kThreads / 64;
+constexpr int kXcds = kGemmXcds;
+constexpr int kDepth = 4;       // K-steps in flight per wavefront: A stages and B slots
 constexpr int kSlabs = BM / 16;
+constexpr int kADma = BM / kWaves / 8;  // A loads (8 rows, 1 KB each) per wavefront per K-step
 enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
-static_assert(BM == 128 && kThreads / 64 * 32 == BN, "8 wavefronts x 32 columns");
+static_assert(BM == 256 && kWaves * 32 == BN, "8 wavefronts x 32 columns, 256 rows");
 
 __device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ (r & 7)) << 3); }
 
@@ -144,55 +149,56 @@ __device__ __forceinline__ bf16x8_t b_frag(const BStep<INT8>& r, int j, int s) {
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// A: wavefront w moves rows [16w, 16w+16) of the K-step (2 x 1 KB); within
+// A: wavefront w moves rows [32w, 32w+32) of the K-step (4 x 1 KB); within
 // each 1 KB (8 rows of 128 B) lane l lands in row l/8, physical chunk l%8, and
 // so fetches logical chunk (l%8) ^ (row & 7).
 // The waits below count loads in issue order, so the compiler may not move
-// any other load across these two: compiler-only memory barriers on both sides.
-__device__ __forceinline__ void a_dma(const char* const (&ap)[2], int kt, uint16_t* stage, int wave) {
+// any other load across these: compiler-only memory barriers on both sides.
+__device__ __forceinline__ void a_dma(const char* const (&ap)[kADma], int kt, uint16_t* stage, int wave) {
     const int64_t off = (int64_t)kt * BK * 2;
     asm volatile("" ::: "memory");
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int q = 0; q < kADma; ++q)
         __builtin_amdgcn_global_load_lds((glb_void_t*)(ap[q] + off),
-                                         (lds_void_t*)(stage + (wave * 16 + q * 8) * BK), 16, 0, 0);
+                                         (lds_void_t*)(stage + (wave * kADma * 8 + q * 8) * BK), 16, 0, 0);
     asm volatile("" ::: "memory");
 }
 
 // MFMAs of one K-step over the first NSL 16-row slabs: A fragments from LDS
 // (row 16 i + l % 16, k chunk 2 (l / 16) + s: the same k as the B fragment of
-// the lane), B from registers.
+// the lane), B from registers. Slabs go in groups of four: the group's A
+// fragments are read before its MFMAs, so that the LDS latency is paid once
+// per group rather than once per fragment.
 template <bool INT8, int NSL>
 __device__ __forceinline__ void mma_step(const uint16_t* As, const BStep<INT8>& rb, int lane,
                                          f32x4_t (&acc)[kSlabs][2]) {
-    // all A fragments of a sub-step are read before its MFMAs, so that the LDS
-    // latency is paid once per sub-step rather than once per fragment
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
         const bf16x8_t b0 = b_frag<INT8>(rb, 0, s), b1 = b_frag<INT8>(rb, 1, s);
         const int c = (lane >> 4) * 2 + s;
-        bf16x8_t af[NSL > 0 ? NSL : 1];
 #pragma unroll
-        for (int i = 0; i < NSL; ++i)
-            af[i] = *reinterpret_cast<const bf16x8_t*>(As + swz(i * 16 + (lane & 15), c));
+        for (int g = 0; g < NSL; g += 4) {
+            bf16x8_t af[4];
 #pragma unroll
-        for (int i = 0; i < NSL; ++i) {
-            acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], b0, acc[i][0], 0, 0, 0);
-            acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], b1, acc[i][1], 0, 0, 0);
+            for (int i = 0; i < 4; ++i)
+                af[i] = *reinterpret_cast<const bf16x8_t*>(As + swz((g + i) * 16 + (lane & 15), c));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[g + i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], b0, acc[g + i][0], 0, 0, 0);
+                acc[g + i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], b1, acc[g + i][1], 0, 0, 0);
+            }
+            // DS reads first, then the MFMAs, in one scheduling group each
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         }
-        // DS reads first, then the MFMAs, in one scheduling group each
-        __builtin_amdgcn_sched_group_barrier(0x100, NSL, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NSL, 0);
     }
 }
 
 // LDS of a workgroup: kDepth distinct stages of A (distinct objects, so that
-// the compiler can tell which stage a pending direct load writes) and the
-// epilogue tile.
+// the compiler can tell which stage a pending direct load writes).
 struct Lds {
-    uint16_t* a[kDepth];
-    uint16_t* ep;
-    float* rw;  // down: router weight of each row of the tile
+    uint16_t* a[kDepth];  // after the K loop, also the epilogue's staging
+    float* rw;            // down: router weight of each row of the tile
 };
 
 // s_waitcnt vmcnt(n) lgkmcnt(0) (vmcnt split over bits 3:0 and 15:14)
@@ -201,10 +207,10 @@ constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 
 // The K loop over NSL slabs (NSL = 0: a wavefront with no valid column still
 // moves its share of A and keeps the barriers, but loads no B).
 //
-// Pipeline, distance kDepth - 1 for both operands: step k issues A(k+5) into
-// the LDS stage read at step k-1 and B(k+5) into the register slot read at
+// Pipeline, distance kDepth - 1 for both operands: step k issues A(k+3) into
+// the LDS stage read at step k-1 and B(k+3) into the register slot read at
 // step k-1, then runs the MFMAs of step k. Loads complete in issue order, so
-// before step k the wavefront waits until at most the loads of the four later
+// before step k the wavefront waits until at most the loads of the two later
 // steps are pending: then its A(k) and B(k) have landed. A barrier then
 // publishes every wavefront's A share and frees the stage read at step k-1.
 // (A shallower A distance would drain the B ring too: waiting for an A load
@@ -212,30 +218,24 @@ constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 
 // loads against compiler scheduling; loads past the last K-step repeat the
 // last one, so every step issues the same loads.
 template <bool INT8, int NSL>
-__device__ __forceinline__ void k_loop(const char* const (&ap)[2], const char* const (&bp)[2], int nk,
+__device__ __forceinline__ void k_loop(const char* const (&ap)[kADma], const char* const (&bp)[2], int nk,
                                        const Lds& L, int wave, int lane, f32x4_t (&acc)[kSlabs][2]) {
     constexpr int kB = NSL > 0 ? kBLoads<INT8> : 0;
-    constexpr int kWait = wait_vm_lgkm0((kDepth - 2) * (2 + kB));
-    static_assert((kDepth - 2) * (2 + kB) < 64, "vmcnt range");
-    static_assert(kDepth == 6, "six stages and slots below");
+    constexpr int kWait = wait_vm_lgkm0((kDepth - 2) * (kADma + kB));
+    static_assert((kDepth - 2) * (kADma + kB) < 64, "vmcnt range");
+    static_assert(kDepth == 4, "four stages and slots below");
     const int last = nk - 1;
-    BStep<INT8> rb0, rb1, rb2, rb3, rb4, rb5;
+    BStep<INT8> rb0, rb1, rb2, rb3;
     uint16_t* const S0 = L.a[0];
     uint16_t* const S1 = L.a[1];
     uint16_t* const S2 = L.a[2];
     uint16_t* const S3 = L.a[3];
-    uint16_t* const S4 = L.a[4];
-    uint16_t* const S5 = L.a[5];
     a_dma(ap, 0, S0, wave);
     if (NSL > 0) b_load<INT8>(bp, 0, rb0);
     a_dma(ap, min(1, last), S1, wave);
     if (NSL > 0) b_load<INT8>(bp, min(1, last), rb1);
     a_dma(ap, min(2, last), S2, wave);
     if (NSL > 0) b_load<INT8>(bp, min(2, last), rb2);
-    a_dma(ap, min(3, last), S3, wave);
-    if (NSL > 0) b_load<INT8>(bp, min(3, last), rb3);
-    a_dma(ap, min(4, last), S4, wave);
-    if (NSL > 0) b_load<INT8>(bp, min(4, last), rb4);
 #define MOE_GEMM_STEP(U, SA, RB, SN, RN)                                    \
     __builtin_amdgcn_s_waitcnt(kWait);                                      \
     raw_barrier();                                                          \
@@ -245,12 +245,10 @@ __device__ __forceinline__ void k_loop(const char* const (&ap)[2], const char* c
         if (kt + (U) < nk) mma_step<INT8, NSL>(SA, RB, lane, acc);          \
     }
     for (int kt = 0; kt < nk; kt += kDepth) {
-        MOE_GEMM_STEP(0, S0, rb0, S5, rb5)
+        MOE_GEMM_STEP(0, S0, rb0, S3, rb3)
         MOE_GEMM_STEP(1, S1, rb1, S0, rb0)
         MOE_GEMM_STEP(2, S2, rb2, S1, rb1)
         MOE_GEMM_STEP(3, S3, rb3, S2, rb2)
-        MOE_GEMM_STEP(4, S4, rb4, S3, rb3)
-        MOE_GEMM_STEP(5, S5, rb5, S4, rb4)
     }
 #undef MOE_GEMM_STEP
     __builtin_amdgcn_s_waitcnt(7 << 4);  // vmcnt(0) lgkmcnt(0): no load still in flight
@@ -273,8 +271,8 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
         if (te.y < 0) return;
         row0 = te.x;
         group = te.y & 511;
-        rows_valid = (te.y >> 9) & 255;
-        nt = te.y >> 17;
+        rows_valid = (te.y >> 9) & 511;
+        nt = te.y >> 18;
     } else {
         const int m_total = (p.M_dense + BM - 1) / BM;
         const int chunk = (m_total + kXcds - 1) / kXcds;
@@ -292,11 +290,11 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
 #pragma unroll
     for (int i = 0; i < kSlabs; ++i) acc[i][0] = acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // valid 16-row slabs, rounded up to 1, 2, 4 or 8 (the extra slabs hold
+    // valid 16-row slabs, rounded up to a multiple of 4 (the extra slabs hold
     // repeated rows and are never stored); 0 for a gate/up wavefront past the
     // last h column
     const int n_slabs = min(kSlabs, (rows_valid + 15) / 16);
-    int nsl = n_slabs <= 1 ? 1 : n_slabs <= 2 ? 2 : n_slabs <= 4 ? 4 : 8;
+    int nsl = (n_slabs + 3) / 4 * 4;
     if (MODE == MODE_GATEUP && nt * kHalfN + wn * 16 >= p.n_out) nsl = 0;
     const int nk = p.K / BK;
 
@@ -310,10 +308,10 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
         for (int jj = 0; jj < 2; ++jj)
             bp[jj] = B + (int64_t)b_tile<MODE>(p, nt, wn, jj) * nk * (esz * 1024) + lane * 16;
     }
-    const char* ap[2];
+    const char* ap[kADma];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int r = wave * 16 + q * 8 + (lane >> 3);
+    for (int q = 0; q < kADma; ++q) {
+        const int r = wave * kADma * 8 + q * 8 + (lane >> 3);
         const int c = (lane & 7) ^ (r & 7);
         const int rr = min(r, rows_valid - 1);  // rows past the tile end repeat a valid row
         const int64_t arow = p.a_rows ? p.a_rows[row0 + rr] : (int64_t)(row0 + rr);
@@ -338,15 +336,15 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
         row_wt = tid >= rows_valid ? 0.f : p.row_w ? p.row_w[row0 + tid] : 1.f;
     switch (nsl) {  // uniform per wavefront
         case 0: k_loop<INT8, 0>(ap, bp, nk, L, wave, lane, acc); break;
-        case 1: k_loop<INT8, 1>(ap, bp, nk, L, wave, lane, acc); break;
-        case 2: k_loop<INT8, 2>(ap, bp, nk, L, wave, lane, acc); break;
         case 4: k_loop<INT8, 4>(ap, bp, nk, L, wave, lane, acc); break;
-        default: k_loop<INT8, 8>(ap, bp, nk, L, wave, lane, acc); break;
+        case 8: k_loop<INT8, 8>(ap, bp, nk, L, wave, lane, acc); break;
+        case 12: k_loop<INT8, 12>(ap, bp, nk, L, wave, lane, acc); break;
+        default: k_loop<INT8, 16>(ap, bp, nk, L, wave, lane, acc); break;
     }
 
     // epilogue: acc[i][jj][v] is C[row = 16 i + 4 (lane>>4) + v][column tile jj, lane&15]
     if (MODE == MODE_GATEUP) {
-        uint16_t* Ht = L.ep;  // [BM][128] bf16 (32 KB)
+        // the h tile [BM][128] bf16, rows 128 h .. + 128 staged in A stage h (32 KB each)
         const int hl = wn * 16 + col_l;  // column within the 128-wide h tile
 #pragma unroll
         for (int i = 0; i < kSlabs; ++i)
@@ -354,16 +352,16 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
             for (int v = 0; v < 4; ++v) {
                 const int r = i * 16 + (lane >> 4) * 4 + v;
                 const float g = acc[i][0][v] * sc0, u = acc[i][1][v] * sc1;
-                Ht[r * kHalfN + hl] = f32_to_bf16(gelu_tanh(g) * u);
+                L.a[i >> 3][(r & 127) * kHalfN + hl] = f32_to_bf16(gelu_tanh(g) * u);
             }
         lds_barrier();
         const int h_valid = min(kHalfN, p.n_out - nt * kHalfN);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < BM * kHalfN / 8 / kThreads; ++q) {
             const int c = tid + kThreads * q, r = c >> 4, cc = c & 15;
             if (r < rows_valid && cc * 8 < h_valid)
                 *reinterpret_cast<uint4*>(p.C + (int64_t)(row0 + r) * p.ldc + nt * kHalfN + cc * 8) =
-                    *reinterpret_cast<const uint4*>(Ht + r * kHalfN + cc * 8);
+                    *reinterpret_cast<const uint4*>(L.a[r >> 7] + (r & 127) * kHalfN + cc * 8);
         }
     } else if (p.Cf) {
         // fp32 output straight from the accumulators (16 lanes write 64 contiguous bytes)
@@ -379,50 +377,42 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
                 }
             }
     } else {
-        // bf16 rows times the router weight, staged through LDS in two halves of 64 rows (32 KB each)
-        uint16_t* Ot = L.ep;
+        // bf16 rows times the router weight: rows 64 h .. + 64 staged in A stage h (32 KB each)
         if (tid < BM) L.rw[tid] = row_wt;
         lds_barrier();
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
+        for (int jj = 0; jj < 2; ++jj) {
+            const int cl = wn * 32 + jj * 16 + col_l;
+            const float sc = jj ? sc1 : sc0;
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int cl = wn * 32 + jj * 16 + col_l;
-                const float sc = jj ? sc1 : sc0;
+            for (int i = 0; i < kSlabs; ++i)
 #pragma unroll
-                for (int i = half * 4; i < half * 4 + 4; ++i)
+                for (int v = 0; v < 4; ++v) {
+                    const int r = i * 16 + (lane >> 4) * 4 + v;
+                    L.a[i >> 2][(r & 63) * BN + cl] = f32_to_bf16(acc[i][jj][v] * sc * L.rw[r]);
+                }
+        }
+        lds_barrier();
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int r = i * 16 + (lane >> 4) * 4 + v;
-                        Ot[(r - half * 64) * BN + cl] = f32_to_bf16(acc[i][jj][v] * sc * L.rw[r]);
-                    }
-            }
-            lds_barrier();
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int c = tid + kThreads * q, rl = c >> 5, cc = c & 31;
-                const int r = half * 64 + rl;
-                if (r < rows_valid)
-                    *reinterpret_cast<uint4*>(p.C + (int64_t)(row0 + r) * p.ldc + nt * BN + cc * 8) =
-                        *reinterpret_cast<const uint4*>(Ot + rl * BN + cc * 8);
-            }
-            lds_barrier();  // every wavefront has read its half before the next overwrites it
+        for (int q = 0; q < BM * BN / 8 / kThreads; ++q) {
+            const int c = tid + kThreads * q, r = c >> 5, cc = c & 31;
+            if (r < rows_valid)
+                *reinterpret_cast<uint4*>(p.C + (int64_t)(row0 + r) * p.ldc + nt * BN + cc * 8) =
+                    *reinterpret_cast<const uint4*>(L.a[r >> 6] + (r & 63) * BN + cc * 8);
         }
     }
 }
 
 template <int MODE, bool INT8_0, bool INT8_1>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p0, GemmArgs p1, int split) {
-    // six LDS stages of A (128 x 64 bf16, 16 KB each) and a 32 KB epilogue tile
+    // four LDS stages of A (256 x 64 bf16, 32 KB each; after the K loop, the
+    // epilogue's staging) and the tile's router weights
     __shared__ __attribute__((aligned(16))) uint16_t st0[kAStageElems];
     __shared__ __attribute__((aligned(16))) uint16_t st1[kAStageElems];
     __shared__ __attribute__((aligned(16))) uint16_t st2[kAStageElems];
     __shared__ __attribute__((aligned(16))) uint16_t st3[kAStageElems];
-    __shared__ __attribute__((aligned(16))) uint16_t st4[kAStageElems];
-    __shared__ __attribute__((aligned(16))) uint16_t st5[kAStageElems];
-    __shared__ __attribute__((aligned(16))) uint16_t ep[BM * kHalfN];
     __shared__ float rw[BM];
-    const Lds L{{st0, st1, st2, st3, st4, st5}, ep, rw};
+    const Lds L{{st0, st1, st2, st3}, rw};
     const int b = blockIdx.x;
     if (b < split) gemm_block<MODE, INT8_0>(p0, b, L);
     else gemm_block<MODE, INT8_1>(p1, b - split, L);

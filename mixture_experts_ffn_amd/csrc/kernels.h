@@ -47,7 +47,7 @@ struct PermuteOut {
     int32_t* n_mtiles;      // [1]
     // the tile of every block of the two expert GEMMs (0: gate/up, 1: down),
     // gemm_expert_blocks(max_mtiles, n_nt[i]) entries each: {first grouped row,
-    // expert | rows << 9 | N-tile << 17}, or y = -1 for a block with no tile
+    // expert | rows << 9 | N-tile << 18}, or y = -1 for a block with no tile
     int2* tiles[2];
     int n_nt[2];
     int max_mtiles;
@@ -58,7 +58,7 @@ hipError_t launch_permute(const int32_t* topk_idx, const float* topk_w, int32_t*
                           int T, int K, int E, int BM, const PermuteOut& o, hipStream_t stream);
 
 // ---- grouped MFMA GEMMs (gemm.hip) -----------------------------------------
-constexpr int kGemmBM = 128;  // rows per grouped M-tile
+constexpr int kGemmBM = 256;  // rows per grouped M-tile
 constexpr int kGemmBN = 256;  // output columns per N-tile (gate/up: 128 h columns)
 constexpr int kGemmXcds = 8;  // block b of a GEMM runs on XCD b % 8
 // N-tiles of the gate/up (h columns) and down GEMMs

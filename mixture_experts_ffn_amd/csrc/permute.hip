@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kOffThreads) void group_offsets_kernel(int n_tiles,
                 const int nt = ol / rl, mt = r0 + (ol - nt * rl);
                 const int row0 = s_off[g] + (mt - first) * BM;
                 const int rows = min(BM, s_off[g] + s_cnt[g] - row0);
-                te = make_int2(row0, g | (rows << 9) | (nt << 17));
+                te = make_int2(row0, g | (rows << 9) | (nt << 18));
             }
             o.tiles[gi][b] = te;
         }
