@@ -466,8 +466,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 hipError_t launch_gemm_gateup(const GemmArgs& experts, const GemmArgs* dense, bool int8,
                               hipStream_t stream) {
-    return int8 ? launch<MODE_GATEUP, true, false>(experts, dense, stream)
-                : launch<MODE_GATEUP, false, false>(experts, dense, stream);
+    // the dense problem first: its tiles hold full 256-row M-tiles and run
+    // longest, so the shorter expert tiles fill the end of the launch
+    if (!dense) return int8 ? launch<MODE_GATEUP, true, true>(experts, nullptr, stream)
+                            : launch<MODE_GATEUP, false, false>(experts, nullptr, stream);
+    return int8 ? launch<MODE_GATEUP, false, true>(*dense, &experts, stream)
+                : launch<MODE_GATEUP, false, false>(*dense, &experts, stream);
 }
 hipError_t launch_gemm_down(const GemmArgs& experts, const GemmArgs* dense, bool int8,
                             hipStream_t stream) {
