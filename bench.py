@@ -107,10 +107,11 @@ def stage_work(stage: str, shape, T, n_active, int8):
     router_w = E * H * 2 + H * 2
     x, y = T * H * 2, T * H * 2
     table = {
-        "decode_front": (router_w + 2 * Id * H * 2 + x + T * E * 4 + T * Id * 2,
+        "decode_front": (router_w + 2 * Id * H * 2 + x + 4 * T * (E + 1) * 4 + 4 * T * 2 * Id * 4,
                          2 * T * E * H + 2 * T * H * 2 * Id,
-                         "router weights + dense gate_up + x + logits + hd"),
-        "decode_route": (T * E * 4 + E * 4 + TK * 20, 0, "logits + routing tables"),
+                         "router weights + dense gate_up + x + 4 K-slices of partial logits and dense sums"),
+        "decode_route": (4 * T * (E + 1) * 4 + E * 4 + TK * 20 + 4 * T * 2 * Id * 4 + T * Id * 2, 0,
+                         "partial logits + routing tables + dense partial sums + hd"),
         "decode_experts_gateup": (n_active * gu_w + x + TK * I * 2, 2 * TK * H * 2 * I,
                                   f"{n_active} experts' gate_up ({gu_w} B each) + x + h"),
         "decode_down": (n_active * dn_w + H * Id * 2 + TK * I * 2 + T * Id * 2,

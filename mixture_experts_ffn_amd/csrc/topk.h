@@ -2,9 +2,10 @@
 // that every router kernel shares it).
 //
 // ONNX export card, "Truthful graph contracts", row "Router": softmax in fp32,
-// top-k, renormalise, per-expert scale. The selection is a radix select over
-// order-preserving 32-bit keys of the fp32 logits using wavefront ballots (no
-// LDS round trips, wavefront reductions through DPP).
+// top-k, renormalise, per-expert scale. The selection takes K rounds of a
+// wavefront maximum over order-preserving 32-bit keys of the fp32 logits (no
+// LDS round trips: reductions through DPP, the lowest index among equal keys
+// through ballots).
 #pragma once
 #include "common.h"
 
