@@ -19,11 +19,12 @@
 //      expert (counts, offsets, grouped rows, inverse rows, list of touched
 //      experts); the other workgroups add the dense partial sums and form the
 //      dense intermediate gelu_tanh(gate) * up.
-//   K3 decode_experts_gateup: 16 gate columns (+ the 16 matching up columns)
-//      of one touched expert per workgroup, K split over its 4 wavefronts;
-//      every weight byte is read exactly once with wide non-temporal loads
-//      issued before anything waits, then dotted with the expert's tokens
-//      staged in LDS.
+//   K3 decode_experts_gateup: half the K range of 16 gate columns (+ the 16
+//      matching up columns) of one touched expert per workgroup, split over
+//      its 4 wavefronts; every weight byte is read exactly once with wide
+//      non-temporal loads issued before anything waits, then dotted with the
+//      expert's tokens staged in LDS. fp32 partial sums per half; K4 adds the
+//      halves and forms h = gelu_tanh(gate) * up when it stages h.
 //   K4 decode_down: one 16-row tile of a touched expert's down matrix per
 //      wavefront (fp32 partial rows per routed pair), and the dense down
 //      matrix with K split over a workgroup's wavefronts.
@@ -113,36 +114,6 @@ __device__ __forceinline__ float dot8(const float* a, const float* b) {
     return s;
 }
 
-// Stage x rows tok(pass .. pass+nt) into LDS as [kPass][H/8] 16-byte chunks.
-// Every load is unconditional (indices clamped into range) so that all of them
-// are in flight together; only the LDS stores are predicated.
-template <int NJ>
-__device__ __forceinline__ void stage_x(const uint16_t* __restrict__ x, int H, const int32_t* toks,
-                                        int pass, int nt, uint4* xs) {
-    const int hc8 = H >> 3;
-    const int n = nt * hc8;
-    constexpr int kPer = (kPass * 32 * NJ + kThreads - 1) / kThreads;  // chunks per thread
-    int64_t tok[kPer];
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-        const int i = min((int)threadIdx.x + q * kThreads, n - 1);
-        const int r = i / hc8;
-        tok[q] = toks ? (int64_t)toks[pass + r] : (int64_t)(pass + r);
-    }
-    uint4 v[kPer];
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-        const int i = min((int)threadIdx.x + q * kThreads, n - 1);
-        const int c = i - (i / hc8) * hc8;
-        v[q] = reinterpret_cast<const uint4*>(x + tok[q] * H)[c];
-    }
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-        const int i = threadIdx.x + q * kThreads;
-        if (i < n) xs[i] = v[q];
-    }
-}
-
 // Copy n (1 <= n <= KPER * 256) contiguous 16-byte chunks into LDS; loads are
 // unconditional (indices clamped into range) so that all are in flight.
 template <int KPER>
@@ -220,58 +191,71 @@ __device__ __forceinline__ void tile_load2(const char* ta, const char* tb, int k
     }
 }
 
-// Gate/up of 16 h columns (gate tile hc of a tiled [2*inter, H] matrix and the
-// matching up tile inter/16 + hc) against tokens tok(0 .. n_rows):
-// out[p][16 hc + r] = gelu_tanh(gate_r . x_p) * (up_r . x_p). Wavefront w takes
-// K-steps [w NS, (w + 1) NS) of both tiles (NS = H / 256); the four partial
-// sums of a column are added in wavefront order through LDS.
+// Half `half` of the K range of the gate/up of 16 h columns (gate tile hc and
+// up tile inter/16 + hc) against tokens tok(0 .. n_rows): fp32 partial sums
+// part[half][p][16 hc + r] (gate) and part[half][p][inter + 16 hc + r] (up),
+// p the grouped row. Wavefront w takes NS of the half's K-steps from
+// kb + w NS (steps past the half contribute 0); only the half's columns of x
+// are staged.
 template <int NS, bool INT8>
-__device__ __forceinline__ void gateup_item(const uint16_t* __restrict__ x, int H, const void* W,
-                                            const float* Ws, int inter, int hc, const int32_t* toks,
-                                            int n_rows, uint16_t* __restrict__ out, uint4* xs,
-                                            float* red) {
+__device__ __forceinline__ void gateup_half_item(const uint16_t* __restrict__ x, int H, const void* W, int inter,
+                                                 int hc, int half, const int32_t* toks, int n_rows,
+                                                 int64_t half_stride, float* __restrict__ part, uint4* xs,
+                                                 float* red) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int nk = H >> 6, kt0 = wave * NS;
+    const int nk = H >> 6, hk = nk >> 1;  // K-steps of a half
+    const int kb = half * hk, kt0 = kb + wave * NS, ke = kb + hk;
+    const int n_steps = max(0, min(NS, ke - kt0));
     const char* Wb = reinterpret_cast<const char*>(W);
     uint4 wg[NS][INT8 ? 1 : 2], wu[NS][INT8 ? 1 : 2];
-    tile_load<NS, INT8>(Wb + (int64_t)hc * nk * kTileBytes<INT8>, kt0, nk, lane, wg);
-    tile_load<NS, INT8>(Wb + (int64_t)(inter / 16 + hc) * nk * kTileBytes<INT8>, kt0, nk, lane, wu);
-    const int hc8 = H >> 3;
+    // loads clamped to the half's last step
+    tile_load<NS, INT8>(Wb + (int64_t)hc * nk * kTileBytes<INT8>, kt0, ke, lane, wg);
+    tile_load<NS, INT8>(Wb + (int64_t)(inter / 16 + hc) * nk * kTileBytes<INT8>, kt0, ke, lane, wu);
+    const int len8 = hk * 8;  // 16-byte chunks of x per token in the half
+    constexpr int kPer = (kPass * 4 * NS * 8 + kThreads - 1) / kThreads;
     for (int pass = 0; pass < n_rows; pass += kPass) {
-        const int nt = min(kPass, n_rows - pass);
+        const int nt = min(kPass, n_rows - pass), n = nt * len8;
         __syncthreads();  // previous pass done with xs and red
-        stage_x<NS>(x, H, toks, pass, nt, xs);
-        __syncthreads();
-#pragma unroll 1
-        for (int n = 0; n < nt; ++n) {
-            const uint16_t* xr = reinterpret_cast<const uint16_t*>(xs + n * hc8) + kt0 * 64 + (lane >> 4) * 16;
-            float ag = 0.f, au = 0.f;
+        {
+            uint4 v[kPer];
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                ag = piece_dot<INT8>(wg[s], xr + s * 64, ag);
-                au = piece_dot<INT8>(wu[s], xr + s * 64, au);
+            for (int q = 0; q < kPer; ++q) {
+                const int i = min((int)threadIdx.x + q * kThreads, n - 1);
+                const int r = i / len8;
+                v[q] = reinterpret_cast<const uint4*>(x + (int64_t)toks[pass + r] * H + kb * 64)[i - r * len8];
             }
-            ag = tile_row_sum(ag);
-            au = tile_row_sum(au);
-            if (lane < 16) {
-                red[((wave * kPass + n) * 2) * 16 + lane] = ag;
-                red[((wave * kPass + n) * 2 + 1) * 16 + lane] = au;
+#pragma unroll
+            for (int q = 0; q < kPer; ++q) {
+                const int i = (int)threadIdx.x + q * kThreads;
+                if (i < n) xs[i] = v[q];
             }
         }
         __syncthreads();
-        if (tid < nt * 16) {
-            const int n = tid >> 4, r = tid & 15, col = hc * 16 + r;
-            float g = 0.f, u = 0.f;
+#pragma unroll 1
+        for (int t = 0; t < nt; ++t) {
+            const uint16_t* xr =
+                reinterpret_cast<const uint16_t*>(xs + t * len8) + (kt0 - kb) * 64 + (lane >> 4) * 16;
+            float ag = 0.f, au = 0.f;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                g += red[((w * kPass + n) * 2) * 16 + r];
-                u += red[((w * kPass + n) * 2 + 1) * 16 + r];
+            for (int st = 0; st < NS; ++st)
+                if (st < n_steps) {
+                    ag = piece_dot<INT8>(wg[st], xr + st * 64, ag);
+                    au = piece_dot<INT8>(wu[st], xr + st * 64, au);
+                }
+            ag = tile_row_sum(ag);
+            au = tile_row_sum(au);
+            if (lane < 16) {
+                red[((wave * kPass + t) * 2) * 16 + lane] = ag;
+                red[((wave * kPass + t) * 2 + 1) * 16 + lane] = au;
             }
-            if (INT8) {
-                g *= Ws[col];
-                u *= Ws[inter + col];
-            }
-            out[(int64_t)(pass + n) * inter + col] = f32_to_bf16(gelu_tanh(g) * u);
+        }
+        __syncthreads();
+        if (tid < nt * 32) {
+            const int t = tid >> 5, m = (tid >> 4) & 1, r = tid & 15;
+            float v = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) v += red[((w * kPass + t) * 2 + m) * 16 + r];
+            part[half * half_stride + (int64_t)(pass + t) * 2 * inter + m * inter + hc * 16 + r] = v;
         }
     }
 }
@@ -457,21 +441,24 @@ __global__ __launch_bounds__(kThreads) void decode_front_kernel(StreamArgs a, co
 }
 
 // ---------------------------------------------------------------- K3
-template <int NJ, bool INT8>
+// Items of (touched expert, 16 h columns, half of the K range): twice as many
+// workgroups of half the bytes, so that the last ones in flight finish sooner.
+// Writes fp32 partial sums (hpart); the down kernel forms h from them.
+template <int NS, bool INT8>
 __global__ __launch_bounds__(kThreads) void decode_experts_gateup_kernel(StreamArgs a) {
     extern __shared__ uint4 xs[];
     __shared__ float red[kWaves * kPass * 2 * 16];
-    const int ipe = a.I / 16;  // items (16 h columns) per expert
-    const int slot = blockIdx.x / ipe, hc = blockIdx.x - slot * ipe;
+    const int ipe = a.I / 16;  // 16-column items per expert
+    const int slot = blockIdx.x / (2 * ipe), rem = blockIdx.x - slot * 2 * ipe;
+    const int hc = rem >> 1, half = rem & 1;
     if (slot >= *a.n_active) return;
     const int e = a.active[slot];
     const int p0 = a.offsets[e], n = a.offsets[e + 1] - p0;
     const int64_t wstride = (int64_t)2 * a.I * a.H;
     const void* W = INT8 ? (const void*)((const int8_t*)a.gu + e * wstride)
                          : (const void*)((const uint16_t*)a.gu + e * wstride);
-    const float* Ws = INT8 ? a.gu_scale + (int64_t)e * 2 * a.I : nullptr;
-    gateup_item<NJ, INT8>(a.x, a.H, W, Ws, a.I, hc, a.perm_token + p0, n, a.h + (int64_t)p0 * a.I,
-                          xs, red);
+    gateup_half_item<NS, INT8>(a.x, a.H, W, a.I, hc, half, a.perm_token + p0, n,
+                               (int64_t)a.T * a.K * 2 * a.I, a.hpart + (int64_t)p0 * 2 * a.I, xs, red);
 }
 
 // ---------------------------------------------------------------- K2
@@ -638,6 +625,47 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(StreamArgs 
     }
 }
 
+// Rows p0 .. p0 + n / (I / 8) of h into LDS as [n_rows][I / 8] 16-byte chunks:
+// h = gelu_tanh(gate) * up, gate and up each the sum of the two halves' fp32
+// partial sums (times the int8 column scales), rounded to bf16. Loads are
+// unconditional (indices clamped into range); only the LDS stores are predicated.
+template <int KPER, bool INT8>
+__device__ __forceinline__ void stage_h(const StreamArgs& a, int p0, int n, const float* gs, uint4* hs) {
+    const int I = a.I, hc8 = I >> 3;
+    const int64_t half = (int64_t)a.T * a.K * 2 * I;
+#pragma unroll
+    for (int q = 0; q < KPER; ++q) {
+        const int i = min((int)threadIdx.x + q * kThreads, n - 1);
+        const int r = i / hc8, c = (i - r * hc8) * 8;
+        const float* g0 = a.hpart + (int64_t)(p0 + r) * 2 * I + c;
+        float gv[8], uv[8];
+        {
+            const float4 a0 = reinterpret_cast<const float4*>(g0)[0], a1 = reinterpret_cast<const float4*>(g0)[1];
+            const float4 b0 = reinterpret_cast<const float4*>(g0 + half)[0], b1 = reinterpret_cast<const float4*>(g0 + half)[1];
+            const float4 c0 = reinterpret_cast<const float4*>(g0 + I)[0], c1 = reinterpret_cast<const float4*>(g0 + I)[1];
+            const float4 d0 = reinterpret_cast<const float4*>(g0 + half + I)[0], d1 = reinterpret_cast<const float4*>(g0 + half + I)[1];
+            gv[0] = a0.x + b0.x; gv[1] = a0.y + b0.y; gv[2] = a0.z + b0.z; gv[3] = a0.w + b0.w;
+            gv[4] = a1.x + b1.x; gv[5] = a1.y + b1.y; gv[6] = a1.z + b1.z; gv[7] = a1.w + b1.w;
+            uv[0] = c0.x + d0.x; uv[1] = c0.y + d0.y; uv[2] = c0.z + d0.z; uv[3] = c0.w + d0.w;
+            uv[4] = c1.x + d1.x; uv[5] = c1.y + d1.y; uv[6] = c1.z + d1.z; uv[7] = c1.w + d1.w;
+        }
+        uint32_t hw[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float g_lo = gv[2 * j], g_hi = gv[2 * j + 1], u_lo = uv[2 * j], u_hi = uv[2 * j + 1];
+            if (INT8) {
+                g_lo *= gs[c + 2 * j];
+                g_hi *= gs[c + 2 * j + 1];
+                u_lo *= gs[I + c + 2 * j];
+                u_hi *= gs[I + c + 2 * j + 1];
+            }
+            hw[j] = pack_bf16x2(gelu_tanh(g_lo) * u_lo, gelu_tanh(g_hi) * u_hi);
+        }
+        const int ii = (int)threadIdx.x + q * kThreads;
+        if (ii < n) hs[ii] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    }
+}
+
 // ---------------------------------------------------------------- K4
 // Down projections. A wavefront reads K-steps [kt0, kt0 + n_steps) (n_steps <=
 // NS) of one 16-row tile of a tiled [H, inter] matrix and dots them with the
@@ -677,11 +705,11 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(StreamArgs a) {
         tile_load<NS, INT8>(W + (int64_t)tile * nk * kTileBytes<INT8>, 0, nk, lane, w);
         const float sc = INT8 ? a.dw_scale[(int64_t)e * a.H + tile * 16 + (lane & 15)] : 1.f;
         const int hc8 = a.I >> 3;
+        const float* gs = INT8 ? a.gu_scale + (int64_t)e * 2 * a.I : nullptr;
         for (int pass = 0; pass < n_rows; pass += kPass) {
             const int nt = min(kPass, n_rows - pass);
             __syncthreads();
-            stage_rows<(kPass * 128 + kThreads - 1) / kThreads>(
-                reinterpret_cast<const uint4*>(a.h + (int64_t)(p0 + pass) * a.I), nt * hc8, hs);
+            stage_h<(kPass * 128 + kThreads - 1) / kThreads, INT8>(a, p0 + pass, nt * hc8, gs, hs);
             __syncthreads();
 #pragma unroll 1
             for (int n = 0; n < nt; ++n) {
@@ -769,8 +797,8 @@ hipError_t launch_front_ns(const StreamArgs& a, const uint16_t* scale, const uin
 
 template <int NJ>
 hipError_t launch_experts_nj(const StreamArgs& a, bool int8, hipStream_t stream) {
-    const int blocks = a.max_active * (a.I / 16);
-    const size_t lds = (size_t)kPass * a.H * sizeof(uint16_t);
+    const int blocks = a.max_active * (a.I / 16) * 2;
+    const size_t lds = (size_t)kPass * (a.H / 2) * sizeof(uint16_t);
     if (int8)
         hipLaunchKernelGGL((decode_experts_gateup_kernel<NJ, true>), dim3(blocks), dim3(kThreads), lds, stream, a);
     else
@@ -816,8 +844,9 @@ hipError_t launch_decode_route(const StreamArgs& a, const float* lpart, const fl
 }
 
 hipError_t launch_decode_experts_gateup(const StreamArgs& a, bool int8, hipStream_t stream) {
+    // K-steps per wavefront: half of the H / 64 steps over four wavefronts
 #define CALL(n) launch_experts_nj<n>(a, int8, stream)
-    MOE_NJ_SWITCH(a.H / 256, CALL)
+    MOE_NJ_SWITCH((a.H / 128 + kWaves - 1) / kWaves, CALL)
 #undef CALL
 }
 

@@ -121,6 +121,8 @@ struct StreamArgs {
     float* part; float* dpart;
     // fp32 partial sums of the dense gate/up, K split: [kFrontSplit][T][2 Id] (gate, then up)
     float* dgu_part;
+    // fp32 partial sums of the experts' gate/up, the two halves of K: [2][T*K][2 I]
+    float* hpart;
 };
 // workgroups sharing the K range of one router or dense gate/up item in K1
 constexpr int kFrontSplit = 4;
@@ -135,9 +137,9 @@ hipError_t launch_decode_front(const StreamArgs& a, const uint16_t* scale, const
 hipError_t launch_decode_route(const StreamArgs& a, const float* lpart, const float* ss_part, const float* bias,
                                const float* pes, float eps, int32_t* topk_idx, float* topk_w,
                                hipStream_t stream);
-// K3: gate/up of the touched experts -> h
+// K3: gate/up of the touched experts -> fp32 partial sums of the two halves of K (hpart)
 hipError_t launch_decode_experts_gateup(const StreamArgs& a, bool int8, hipStream_t stream);
-// K4: down of the touched experts and of the dense MLP -> fp32 partial rows
+// K4: h from hpart, down of the touched experts and of the dense MLP -> fp32 partial rows
 hipError_t launch_decode_down(const StreamArgs& a, bool int8, hipStream_t stream);
 // K5: y = dense + sum_k w_k * expert rows (k order) -> bf16
 hipError_t launch_decode_combine(const StreamArgs& a, hipStream_t stream);

@@ -39,7 +39,7 @@ constexpr int kRouterMfmaMinT = 64;
 struct Layout {
     size_t logits, partial, topk_idx, topk_w, pair_rank, tile_counts, counts, offsets, active, n_active;
     size_t perm_token, perm_w, inv_row, mtile_group, mtile_row0, n_mtiles, gemm_tiles[2], h, hd, rows;
-    size_t dout, part, dpart, dgu_part, lpart, ss_part, total;
+    size_t dout, part, dpart, dgu_part, lpart, ss_part, hpart, total;
     int max_mtiles;
 };
 
@@ -86,6 +86,7 @@ Layout make_layout(const moe_dims& d, int64_t T) {
     L.dgu_part = take(Ts * moe::kFrontSplit * 2 * d.dense_inter * 4);
     L.lpart = take(Ts * moe::kFrontSplit * E * 4);
     L.ss_part = take(Ts * moe::kFrontSplit * 4);
+    L.hpart = take(2 * Ts * K * 2 * d.expert_inter * 4);
     L.total = off;
     return L;
 }
@@ -297,6 +298,7 @@ int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
         sa.h = h; sa.hd = hd; sa.y = (uint16_t*)y;
         sa.part = at<float>(ws, L.part); sa.dpart = at<float>(ws, L.dpart);
         sa.dgu_part = at<float>(ws, L.dgu_part);
+        sa.hpart = at<float>(ws, L.hpart);
         sa.with_dense = 1;  // the dense MLP's items ride along in K1, K2 and K4
         HIP_TRY(st.begin("decode_front"), "event record");
         float* lpart = at<float>(ws, L.lpart);
