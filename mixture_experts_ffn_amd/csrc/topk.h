@@ -26,18 +26,27 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 // LDS): within each 16-lane row the running value moves up by 1, 2, 4, 8 lanes,
 // so lane 15 of a row holds the row's result; row_bcast:15 and row_bcast:31
 // then fold the rows so that lane 63 holds the wavefront's. Lanes a shift
-// reads from outside the row contribute the identity.
-template <int CTRL, int ROW_MASK>
+// reads from outside the row contribute OLD, the identity of the reduction.
+template <int CTRL, int ROW_MASK, uint32_t OLD>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xf, false);
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)OLD, (int)v, CTRL, ROW_MASK, 0xf, false);
 }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    v = max(v, dpp_u32<0x111, 0xf>(v));  // row_shr:1
-    v = max(v, dpp_u32<0x112, 0xf>(v));  // row_shr:2
-    v = max(v, dpp_u32<0x114, 0xf>(v));  // row_shr:4
-    v = max(v, dpp_u32<0x118, 0xf>(v));  // row_shr:8
-    v = max(v, dpp_u32<0x142, 0xa>(v));  // row_bcast:15 into rows 1, 3
-    v = max(v, dpp_u32<0x143, 0xc>(v));  // row_bcast:31 into rows 2, 3
+    v = max(v, dpp_u32<0x111, 0xf, 0u>(v));  // row_shr:1
+    v = max(v, dpp_u32<0x112, 0xf, 0u>(v));  // row_shr:2
+    v = max(v, dpp_u32<0x114, 0xf, 0u>(v));  // row_shr:4
+    v = max(v, dpp_u32<0x118, 0xf, 0u>(v));  // row_shr:8
+    v = max(v, dpp_u32<0x142, 0xa, 0u>(v));  // row_bcast:15 into rows 1, 3
+    v = max(v, dpp_u32<0x143, 0xc, 0u>(v));  // row_bcast:31 into rows 2, 3
+    return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    v = min(v, dpp_u32<0x111, 0xf, 0xFFFFFFFFu>(v));
+    v = min(v, dpp_u32<0x112, 0xf, 0xFFFFFFFFu>(v));
+    v = min(v, dpp_u32<0x114, 0xf, 0xFFFFFFFFu>(v));
+    v = min(v, dpp_u32<0x118, 0xf, 0xFFFFFFFFu>(v));
+    v = min(v, dpp_u32<0x142, 0xa, 0xFFFFFFFFu>(v));
+    v = min(v, dpp_u32<0x143, 0xc, 0xFFFFFFFFu>(v));
     return __builtin_amdgcn_readlane(v, 63);
 }
 template <int CTRL, int ROW_MASK>
@@ -61,12 +70,15 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 
 // Run by a full wavefront. lv[j]: the token's logit of expert lane + 64 j
 // (E <= 256; entries with that index >= E are ignored).
-// softmax over all E in fp32 (max-subtracted), then the top K by logit; the K
-// probabilities are renormalised to sum 1 (summed in k order) and multiplied
-// by the per-expert scale. Every lane ends with the same ik[0..K), wk[0..K).
-// Selection: K rounds; each takes the largest remaining key (a wavefront
-// maximum) and, among equal keys, the lowest expert index (ballots in index
-// order), so the experts come out in descending logit, ties to the lower index.
+// The top K by logit, then their renormalised softmax weights times the
+// per-expert scale. Every lane ends with the same ik[0..K), wk[0..K).
+// Selection: K rounds, without branches; each takes the largest remaining key
+// (a wavefront maximum of order_key + 1; 0 marks a taken or absent expert)
+// and, among equal keys, the lowest expert index (a wavefront minimum of the
+// indices holding it), so the experts come out in descending logit, ties to
+// the lower index. Weights: exp(l_k - l_0) / sum_j exp(l_j - l_0) over the K
+// selected (summed in k order), which is the softmax over all E renormalised
+// over the selection: the full denominator cancels.
 // pv (used when PV): pv[j] = pes[lane + 64 j] already in registers, so that no
 // load waits on the selection.
 template <bool PV = false>
@@ -74,66 +86,41 @@ __device__ __forceinline__ void wave_topk_vals(const float (&lv)[4], const float
                                                int E, int K, int lane, int* ik, float* wk,
                                                const float (&pv)[4] = {0.f, 0.f, 0.f, 0.f}) {
     uint32_t key[4];
-    bool avail[4];
-    const int nj = (E + kWave - 1) / kWave;  // uniform
-    uint32_t kmax = 0u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        avail[j] = j < nj && lane + kWave * j < E;
-        key[j] = avail[j] ? order_key(lv[j]) : 0u;
-        kmax = max(kmax, key[j]);
-    }
-    const float m = key_value(wave_max_u32(kmax));
-    float ex[4], sl = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        ex[j] = avail[j] ? expf(lv[j] - m) : 0.f;
-        sl += ex[j];
-    }
-    const float s = wave_sum_f32(sl);
-
-    float pk[kMaxTopK], sk[kMaxTopK];
-    float psum = 0.f;
+    for (int j = 0; j < 4; ++j) key[j] = (lane + kWave * j < E) ? order_key(lv[j]) + 1u : 0u;
+    float lk[kMaxTopK], sk[kMaxTopK];
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k) {
         ik[k] = 0;
-        pk[k] = 0.f;
+        lk[k] = 0.f;
         sk[k] = 0.f;
         if (k < K) {  // uniform
-            uint32_t local = 0u;
+            const uint32_t M = wave_max_u32(max(max(key[0], key[1]), max(key[2], key[3])));
+            uint32_t ci = 0xFFFFFFFFu;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) local = max(local, avail[j] ? key[j] : 0u);
-            const uint32_t M = wave_max_u32(local);
-            int sj = -1, sl_ = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (j < nj && sj < 0) {
-                    const unsigned long long b = __ballot(avail[j] && key[j] == M);
-                    if (b) {
-                        sj = j;
-                        sl_ = __ffsll((long long)b) - 1;
-                    }
-                }
+            for (int j = 3; j >= 0; --j)
+                if (key[j] == M) ci = (uint32_t)(lane + kWave * j);
+            const uint32_t sel = wave_min_u32(ci);  // M > 0 while K <= E
+            const int jsel = (int)(sel >> 6), lsel = (int)(sel & 63);
+            ik[k] = (int)sel;
+            lk[k] = key_value(M - 1u);
+            if (PV) {
+                const float p = jsel == 0 ? pv[0] : jsel == 1 ? pv[1] : jsel == 2 ? pv[2] : pv[3];
+                sk[k] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(p), lsel));
             }
-            // sj >= 0: at least K <= E experts are available
-            float e_sel = ex[0], p_sel = pv[0];
-#pragma unroll
-            for (int j = 1; j < 4; ++j)
-                if (sj == j) {
-                    e_sel = ex[j];
-                    p_sel = pv[j];
-                }
-            ik[k] = sl_ + kWave * sj;
-            pk[k] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(e_sel), sl_)) / s;
-            if (PV) sk[k] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(p_sel), sl_));
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                if (sj == j && lane == sl_) avail[j] = false;
-            psum += pk[k];
+                if ((uint32_t)(lane + kWave * j) == sel) key[j] = 0u;
         }
     }
+    float ex[kMaxTopK], sum = 0.f;
 #pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k) wk[k] = (k < K) ? pk[k] / psum * (PV ? sk[k] : pes[ik[k]]) : 0.f;
+    for (int k = 0; k < kMaxTopK; ++k) {
+        ex[k] = k < K ? expf(lk[k] - lk[0]) : 0.f;
+        sum += ex[k];
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) wk[k] = (k < K) ? ex[k] / sum * (PV ? sk[k] : pes[ik[k]]) : 0.f;
 }
 
 // Same, with the logits read from lrow[0..E).
