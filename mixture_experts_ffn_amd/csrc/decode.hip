@@ -9,22 +9,24 @@
 // Five launches, each filling the chip (the dense MLP's items ride along in
 // K1, K2 and K4 when with_dense is set):
 //
-//   K1 decode_front: router partial logits (16 experts per workgroup) side by
-//      side with the dense MLP's gate/up tiles, both as bf16 MFMAs of the
-//      batch against 16-row weight tiles, the K range of each split over
-//      kFrontSplit workgroups (fp32 partial sums); both only need x.
+//   K1 decode_front: router partial logits (16 experts per workgroup), as
+//      bf16 MFMAs of the batch against 16-row weight tiles, the K range split
+//      over kFrontSplit workgroups (fp32 partial sums). (The dense MLP alone
+//      runs its gate/up items here too.)
 //   K2 decode_route: one workgroup: the logits from the partial sums, the
 //      softmax/top-k of every token (ONNX export card, "Truthful graph
 //      contracts", row "Router") and the grouping of the routed pairs by
 //      expert (counts, offsets, grouped rows, inverse rows, list of touched
-//      experts); the other workgroups add the dense partial sums and form the
-//      dense intermediate gelu_tanh(gate) * up.
+//      experts); beside it, the dense MLP's gate/up tiles (fp32 partial sums,
+//      as in K1), which only need x: K1 then holds the router alone.
 //   K3 decode_experts_gateup: half the K range of 16 gate columns (+ the 16
 //      matching up columns) of one touched expert per workgroup, split over
 //      its 4 wavefronts; every weight byte is read exactly once with wide
 //      non-temporal loads issued before anything waits, then dotted with the
 //      expert's tokens staged in LDS. fp32 partial sums per half; K4 adds the
-//      halves and forms h = gelu_tanh(gate) * up when it stages h.
+//      halves and forms h = gelu_tanh(gate) * up when it stages h. Its first
+//      workgroups add the dense gate/up partial sums and form the dense
+//      intermediate gelu_tanh(gate) * up.
 //   K4 decode_down: one 16-row tile of a touched expert's down matrix per
 //      wavefront (fp32 partial rows per routed pair), and the dense down
 //      matrix with K split over a workgroup's wavefronts.
@@ -308,10 +310,13 @@ __device__ __forceinline__ float red_sum(const float* red, int m, int rc) {
 // Dense gate/up, item (hc, ks): gate tile hc and up tile Id / 16 + hc of the
 // tiled [2 Id, H] matrix over K-steps [4 NS ks, 4 NS (ks + 1)) (steps past the
 // matrix contribute 0) -> part[ks][t][16 hc + c] (gate), part[ks][t][Id + 16 hc + c] (up).
+// Run by a group of 256 threads (tid: the thread's index in the group); every
+// thread of the workgroup takes part in its barriers.
 template <int NS>
 __device__ __forceinline__ void dense_gateup_part(const uint16_t* __restrict__ x, int H, const void* W, int Id,
-                                                  int hc, int ks, int T, float* __restrict__ part, float* red) {
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+                                                  int hc, int ks, int T, float* __restrict__ part, float* red,
+                                                  int tid) {
+    const int wave = tid >> 6, lane = tid & 63;
     const int nk = H >> 6;
     const int kt0 = (ks * kWaves + wave) * NS;
     const int n_steps = max(0, min(NS, nk - kt0));
@@ -423,7 +428,8 @@ __device__ __forceinline__ void router_part(const uint16_t* __restrict__ x, int 
 }
 
 // Router items first (ceil(E / 16) x kFrontSplit), then the dense gate/up
-// items (Id / 16 x kFrontSplit) if with_dense.
+// items (Id / 16 x kFrontSplit) if with_dense and front_dense (else the
+// routing launch runs them).
 template <int NS>
 __global__ __launch_bounds__(kThreads) void decode_front_kernel(StreamArgs a, const uint16_t* scale,
                                                                const uint16_t* wr, float* lpart,
@@ -436,36 +442,14 @@ __global__ __launch_bounds__(kThreads) void decode_front_kernel(StreamArgs a, co
         router_part<NS>(a.x, a.H, scale, wr, a.E, nt, ks, a.T, lpart, ss_part, red);
     } else {
         const int i = b - n_router, hc = i / kFrontSplit, ks = i - hc * kFrontSplit;
-        dense_gateup_part<NS>(a.x, a.H, a.dgu, a.Id, hc, ks, a.T, a.dgu_part, red);
+        dense_gateup_part<NS>(a.x, a.H, a.dgu, a.Id, hc, ks, a.T, a.dgu_part, red, (int)threadIdx.x);
     }
 }
 
-// ---------------------------------------------------------------- K3
-// Items of (touched expert, 16 h columns, half of the K range): twice as many
-// workgroups of half the bytes, so that the last ones in flight finish sooner.
-// Writes fp32 partial sums (hpart); the down kernel forms h from them.
-template <int NS, bool INT8>
-__global__ __launch_bounds__(kThreads) void decode_experts_gateup_kernel(StreamArgs a) {
-    extern __shared__ uint4 xs[];
-    __shared__ float red[kWaves * kPass * 2 * 16];
-    const int ipe = a.I / 16;  // 16-column items per expert
-    const int slot = blockIdx.x / (2 * ipe), rem = blockIdx.x - slot * 2 * ipe;
-    const int hc = rem >> 1, half = rem & 1;
-    if (slot >= *a.n_active) return;
-    const int e = a.active[slot];
-    const int p0 = a.offsets[e], n = a.offsets[e + 1] - p0;
-    const int64_t wstride = (int64_t)2 * a.I * a.H;
-    const void* W = INT8 ? (const void*)((const int8_t*)a.gu + e * wstride)
-                         : (const void*)((const uint16_t*)a.gu + e * wstride);
-    gateup_half_item<NS, INT8>(a.x, a.H, W, a.I, hc, half, a.perm_token + p0, n,
-                               (int64_t)a.T * a.K * 2 * a.I, a.hpart + (int64_t)p0 * 2 * a.I, xs, red);
-}
-
-// ---------------------------------------------------------------- K2
 // Dense gate/up finish: hd[t][c] = gelu_tanh(gate) * up, each the sum of its
 // kFrontSplit partial sums in split order; one thread per (t, c).
 __device__ __forceinline__ void dense_finish(const StreamArgs& a, int blk) {
-    const int i = blk * kRouteThreads + threadIdx.x;
+    const int i = blk * kThreads + threadIdx.x;
     if (i >= a.T * a.Id) return;
     const int t = i / a.Id, c = i - t * a.Id;
     float gp[kFrontSplit], up[kFrontSplit];
@@ -484,6 +468,35 @@ __device__ __forceinline__ void dense_finish(const StreamArgs& a, int blk) {
     a.hd[(int64_t)t * a.Id + c] = f32_to_bf16(gelu_tanh(g) * u);
 }
 
+// ---------------------------------------------------------------- K3
+// Items of (touched expert, 16 h columns, half of the K range): twice as many
+// workgroups of half the bytes, so that the last ones in flight finish sooner.
+// Writes fp32 partial sums (hpart); the down kernel forms h from them.
+template <int NS, bool INT8>
+__global__ __launch_bounds__(kThreads) void decode_experts_gateup_kernel(StreamArgs a) {
+    extern __shared__ uint4 xs[];
+    __shared__ float red[kWaves * kPass * 2 * 16];
+    const int n_fin = a.with_dense ? (a.T * a.Id + kThreads - 1) / kThreads : 0;
+    if ((int)blockIdx.x < n_fin) {
+        dense_finish(a, (int)blockIdx.x);
+        return;
+    }
+    const int b = (int)blockIdx.x - n_fin;
+    const int ipe = a.I / 16;  // 16-column items per expert
+    const int slot = b / (2 * ipe), rem = b - slot * 2 * ipe;
+    const int hc = rem >> 1, half = rem & 1;
+    if (slot >= *a.n_active) return;
+    const int e = a.active[slot];
+    const int p0 = a.offsets[e], n = a.offsets[e + 1] - p0;
+    const int64_t wstride = (int64_t)2 * a.I * a.H;
+    const void* W = INT8 ? (const void*)((const int8_t*)a.gu + e * wstride)
+                         : (const void*)((const uint16_t*)a.gu + e * wstride);
+    gateup_half_item<NS, INT8>(a.x, a.H, W, a.I, hc, half, a.perm_token + p0, n,
+                               (int64_t)a.T * a.K * 2 * a.I, a.hpart + (int64_t)p0 * 2 * a.I, xs, red);
+}
+
+// ---------------------------------------------------------------- K2
+
 // Workgroup 0 routes every token (ONNX export card, "Truthful graph
 // contracts", row "Router"), the other workgroups finish the dense gate/up.
 //
@@ -501,13 +514,20 @@ __device__ __forceinline__ void dense_finish(const StreamArgs& a, int blk) {
 // 64-bit mask per expert: the rank of pair (t, k) within its expert is the
 // number of lower tokens in that expert's mask, the expert's row count its
 // popcount.
+template <int NS>
 __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(StreamArgs a, const float* lpart,
                                                                     const float* ss_part, const float* bias,
                                                                     const float* pes, float eps,
                                                                     float inv_sqrt_h, int32_t* topk_idx,
                                                                     float* topk_w) {
     if (!lpart || blockIdx.x > 0) {
-        dense_finish(a, (int)blockIdx.x - (lpart ? 1 : 0));
+        // dense gate/up items (they only need x), four 256-thread groups a workgroup
+        __shared__ float red_d[4][kWaves * 512];
+        const int grp = threadIdx.x >> 8;
+        const int i = ((int)blockIdx.x - (lpart ? 1 : 0)) * 4 + grp;
+        const int hc = i / kFrontSplit, ks = i - hc * kFrontSplit;
+        dense_gateup_part<NS>(a.x, a.H, a.dgu, a.Id, hc, ks, a.T, a.dgu_part, red_d[grp],
+                              (int)threadIdx.x & 255);
         return;
     }
     __shared__ int s_idx[kMaxPairs];
@@ -788,7 +808,7 @@ template <int NS>
 hipError_t launch_front_ns(const StreamArgs& a, const uint16_t* scale, const uint16_t* wr, float* lpart,
                            float* ss_part, hipStream_t stream) {
     const int n_router = wr ? ((a.E + 15) / 16) * kFrontSplit : 0;
-    const int blocks = n_router + (a.with_dense ? (a.Id / 16) * kFrontSplit : 0);
+    const int blocks = n_router + (a.with_dense && a.front_dense ? (a.Id / 16) * kFrontSplit : 0);
     if (blocks <= 0) return hipSuccess;
     hipLaunchKernelGGL(decode_front_kernel<NS>, dim3(blocks), dim3(kThreads), 0, stream, a, scale, wr, lpart,
                        ss_part);
@@ -797,7 +817,9 @@ hipError_t launch_front_ns(const StreamArgs& a, const uint16_t* scale, const uin
 
 template <int NJ>
 hipError_t launch_experts_nj(const StreamArgs& a, bool int8, hipStream_t stream) {
-    const int blocks = a.max_active * (a.I / 16) * 2;
+    const int n_fin = a.with_dense ? (a.T * a.Id + kThreads - 1) / kThreads : 0;
+    const int blocks = n_fin + a.max_active * (a.I / 16) * 2;
+    if (blocks <= 0) return hipSuccess;
     const size_t lds = (size_t)kPass * (a.H / 2) * sizeof(uint16_t);
     if (int8)
         hipLaunchKernelGGL((decode_experts_gateup_kernel<NJ, true>), dim3(blocks), dim3(kThreads), lds, stream, a);
@@ -831,16 +853,29 @@ hipError_t launch_decode_front(const StreamArgs& a, const uint16_t* scale, const
     }
 }
 
+template <int NS>
+hipError_t launch_route_ns(const StreamArgs& a, const float* lpart, const float* ss_part, const float* bias,
+                           const float* pes, float eps, int32_t* topk_idx, float* topk_w, hipStream_t stream) {
+    // the dense items, four a workgroup ((Id / 16) * kFrontSplit is a multiple of 4)
+    const int n_dense = (a.with_dense && !a.front_dense) ? (a.Id / 16) * kFrontSplit / 4 : 0;
+    const int blocks = (lpart ? 1 : 0) + n_dense;
+    if (blocks <= 0) return hipSuccess;
+    const float inv_sqrt_h = (float)(1.0 / __builtin_sqrt((double)a.H));
+    hipLaunchKernelGGL(decode_route_kernel<NS>, dim3(blocks), dim3(kRouteThreads), 0, stream, a, lpart, ss_part,
+                       bias, pes, eps, inv_sqrt_h, topk_idx, topk_w);
+    return hipGetLastError();
+}
+
 hipError_t launch_decode_route(const StreamArgs& a, const float* lpart, const float* ss_part, const float* bias,
                                const float* pes, float eps, int32_t* topk_idx, float* topk_w,
                                hipStream_t stream) {
-    const int blocks =
-        (lpart ? 1 : 0) + (a.with_dense ? (a.T * a.Id + kRouteThreads - 1) / kRouteThreads : 0);
-    if (blocks <= 0) return hipSuccess;
-    const float inv_sqrt_h = (float)(1.0 / __builtin_sqrt((double)a.H));
-    hipLaunchKernelGGL(decode_route_kernel, dim3(blocks), dim3(kRouteThreads), 0, stream, a, lpart, ss_part,
-                       bias, pes, eps, inv_sqrt_h, topk_idx, topk_w);
-    return hipGetLastError();
+    static_assert(kFrontSplit % 4 == 0, "dense items come four a workgroup");
+    switch ((a.H / 64 + kFrontSplit * kWaves - 1) / (kFrontSplit * kWaves)) {
+        case 1: return launch_route_ns<1>(a, lpart, ss_part, bias, pes, eps, topk_idx, topk_w, stream);
+        case 2: return launch_route_ns<2>(a, lpart, ss_part, bias, pes, eps, topk_idx, topk_w, stream);
+        case 3: return launch_route_ns<3>(a, lpart, ss_part, bias, pes, eps, topk_idx, topk_w, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_decode_experts_gateup(const StreamArgs& a, bool int8, hipStream_t stream) {

@@ -112,6 +112,7 @@ struct StreamArgs {
     int max_active;                           // 0 = no expert items
     // dense
     int with_dense;                           // the launch carries the dense MLP's items
+    int front_dense;                          // dense gate/up items in K1 (else in K2)
     const uint16_t* dgu; const uint16_t* ddw;
     // intermediates and output
     uint16_t* h;    // [T*K][I]
@@ -128,16 +129,17 @@ struct StreamArgs {
 constexpr int kFrontSplit = 4;
 // K1: router partial logits lpart [kFrontSplit][T][E] and sums of squares of x
 // ss_part [kFrontSplit][T] (if wr != null), beside the dense gate/up partial
-// sums -> dgu_part (if a.with_dense)
+// sums -> dgu_part (if a.with_dense and a.front_dense)
 hipError_t launch_decode_front(const StreamArgs& a, const uint16_t* scale, const uint16_t* wr, float* lpart,
                                float* ss_part, hipStream_t stream);
 // K2: logits from the partial sums, top-k and grouping (one workgroup, T <=
 // MOE_STREAM_MAX_TOKENS; none if lpart == null) beside the dense gate/up
-// finish (dgu_part -> hd, if a.with_dense)
+// partial sums (-> dgu_part, if a.with_dense and not a.front_dense)
 hipError_t launch_decode_route(const StreamArgs& a, const float* lpart, const float* ss_part, const float* bias,
                                const float* pes, float eps, int32_t* topk_idx, float* topk_w,
                                hipStream_t stream);
-// K3: gate/up of the touched experts -> fp32 partial sums of the two halves of K (hpart)
+// K3: the dense gate/up finish (dgu_part -> hd, if a.with_dense), then the gate/up of the
+// touched experts -> fp32 partial sums of the two halves of K (hpart)
 hipError_t launch_decode_experts_gateup(const StreamArgs& a, bool int8, hipStream_t stream);
 // K4: h from hpart, down of the touched experts and of the dense MLP -> fp32 partial rows
 hipError_t launch_decode_down(const StreamArgs& a, bool int8, hipStream_t stream);

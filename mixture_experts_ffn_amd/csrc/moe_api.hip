@@ -299,7 +299,7 @@ int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
         sa.part = at<float>(ws, L.part); sa.dpart = at<float>(ws, L.dpart);
         sa.dgu_part = at<float>(ws, L.dgu_part);
         sa.hpart = at<float>(ws, L.hpart);
-        sa.with_dense = 1;  // the dense MLP's items ride along in K1, K2 and K4
+        sa.with_dense = 1;  // the dense MLP's items ride along in K2, K3 and K4
         HIP_TRY(st.begin("decode_front"), "event record");
         float* lpart = at<float>(ws, L.lpart);
         float* ss_part = at<float>(ws, L.ss_part);
@@ -396,15 +396,14 @@ int dense_mlp(const moe_dims* d, const void* dense_gate_up, const void* dense_do
     if (T <= stream_limit() && stream_fits(*d)) {
         moe::StreamArgs sa{};
         sa.T = T; sa.H = H; sa.I = d->expert_inter; sa.Id = Id; sa.K = d->top_k; sa.E = d->num_experts;
-        sa.x = (const uint16_t*)x; sa.max_active = 0; sa.with_dense = 1;
+        sa.x = (const uint16_t*)x; sa.max_active = 0; sa.with_dense = 1; sa.front_dense = 1;
         sa.dgu = (const uint16_t*)dense_gate_up; sa.ddw = (const uint16_t*)dense_down;
         sa.hd = hd; sa.y = (uint16_t*)y;
         sa.part = at<float>(ws, L.part); sa.dpart = at<float>(ws, L.dpart);
         sa.dgu_part = at<float>(ws, L.dgu_part);
         HIP_TRY(moe::launch_decode_front(sa, nullptr, nullptr, nullptr, nullptr, stream),
                 "decode_front launch");
-        HIP_TRY(moe::launch_decode_route(sa, nullptr, nullptr, nullptr, nullptr, 0.f, nullptr, nullptr, stream),
-                "decode_route (dense finish) launch");
+        HIP_TRY(moe::launch_decode_experts_gateup(sa, false, stream), "dense finish launch");
         HIP_TRY(moe::launch_decode_down(sa, false, stream), "decode_down launch");
         HIP_TRY(moe::launch_decode_combine(sa, stream), "decode_combine launch");
     } else {
