@@ -783,13 +783,14 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(StreamArgs a) 
         int p[kMaxTopK];
 #pragma unroll
         for (int k = 0; k < kMaxTopK; ++k) p[k] = a.inv_row[(int64_t)t * a.K + min(k, a.K - 1)];
+        // the router weight of pair (t, k) (the same value as perm_w of its
+        // grouped row), loaded beside the inverse rows rather than after them
         float wk[kMaxTopK];
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k) wk[k] = a.topk_w[(int64_t)t * a.K + min(k, a.K - 1)];
         float4 r[kMaxTopK];
 #pragma unroll
-        for (int k = 0; k < kMaxTopK; ++k) {
-            wk[k] = a.perm_w[p[k]];
-            r[k] = *reinterpret_cast<const float4*>(a.part + (int64_t)p[k] * a.H + c);
-        }
+        for (int k = 0; k < kMaxTopK; ++k) r[k] = *reinterpret_cast<const float4*>(a.part + (int64_t)p[k] * a.H + c);
 #pragma unroll
         for (int k = 0; k < kMaxTopK; ++k) {
             if (k < a.K) {

@@ -109,6 +109,7 @@ struct StreamArgs {
     const void* dw; const float* dw_scale;   // [E][H][I]
     int32_t* counts; int32_t* offsets; int32_t* active; int32_t* n_active;
     int32_t* perm_token; float* perm_w; int32_t* inv_row;
+    const float* topk_w;                      // [T][K] router weights (K2 writes them)
     int max_active;                           // 0 = no expert items
     // dense
     int with_dense;                           // the launch carries the dense MLP's items

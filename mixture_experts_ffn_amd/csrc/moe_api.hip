@@ -293,6 +293,7 @@ int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
         sa.dw = w->expert_down; sa.dw_scale = w->down_scale;
         sa.counts = po.counts; sa.offsets = po.offsets; sa.active = po.active; sa.n_active = po.n_active;
         sa.perm_token = po.perm_token; sa.perm_w = po.perm_w; sa.inv_row = po.inv_row;
+        sa.topk_w = topk_w;
         sa.max_active = T * K < E ? T * K : E;
         sa.dgu = (const uint16_t*)w->dense_gate_up; sa.ddw = (const uint16_t*)w->dense_down;
         sa.h = h; sa.hd = hd; sa.y = (uint16_t*)y;
