@@ -83,12 +83,19 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-// Make global writes of this workgroup visible to its other waves (the
-// writers release, the barrier orders, the readers acquire).
-__device__ __forceinline__ void block_sync_global() {
-    __threadfence();
-    __syncthreads();
-    __threadfence();
+// Workgroup barrier with no memory fence: the compiler moves no memory access
+// across it, and the hardware waits for nothing (unlike __syncthreads, whose
+// release waits for the wavefront's global loads and stores).
+__device__ __forceinline__ void raw_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+// Barrier after this wavefront's LDS accesses have completed; its global
+// loads and stores may still be in flight.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited on
+    raw_barrier();
 }
 
 }  // namespace moe

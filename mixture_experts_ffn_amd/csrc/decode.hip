@@ -500,20 +500,63 @@ __global__ __launch_bounds__(kThreads) void decode_experts_gateup_kernel(StreamA
 // Workgroup 0 routes every token (ONNX export card, "Truthful graph
 // contracts", row "Router"), the other workgroups finish the dense gate/up.
 //
-// Selection by rank, one thread per (token, expert) pair: each logit becomes
-// the 64-bit composite (order-preserving key, ~expert), so that a larger
-// composite means a larger logit or, for equal logits, the lower expert; the
-// rank of a pair is the number of its token's composites above its own, and
-// ranks 0 .. K-1 are the top K in order (descending logit, ties to the lower
-// index). The renormalised weight of the k-th selected expert is
-// exp(l_k - l_0) / sum_j exp(l_j - l_0) over the K selected (the softmax
-// denominator over all experts cancels in the renormalisation), summed in k
-// order, times its per-expert scale.
+// Selection: one wavefront a token, the top K of its E logits by the
+// wavefront top-k (descending logit, ties to the lower index), with the
+// renormalised weights exp(l_k - l_0) / sum_j exp(l_j - l_0) over the K
+// selected (the softmax denominator over all experts cancels), summed in k
+// order, times the per-expert scale.
 //
 // Then the stable grouping by expert. With T <= 64 every token is one bit of a
 // 64-bit mask per expert: the rank of pair (t, k) within its expert is the
 // number of lower tokens in that expert's mask, the expert's row count its
 // popcount.
+// Top K of token t, run by one wavefront: the logits (the kFrontSplit slices of
+// the router product and of the sum of squares added in slice order), then the
+// wavefront top-k; lane k < K returns pair (t, k). Every load is issued before
+// any is used (indices clamped to E - 1, lanes past E masked afterwards).
+template <int NJ>
+__device__ __forceinline__ void route_token(const float* __restrict__ lpart, const float* __restrict__ ss_part,
+                                            const float* __restrict__ bias, const float* __restrict__ pes,
+                                            int T, int E, int K, int H, float eps, float inv_sqrt_h, int t,
+                                            int lane, int& ei, float& wt) {
+    float sqv[kFrontSplit], lp[NJ][kFrontSplit], bv[NJ], pvl[NJ];
+#pragma unroll
+    for (int ks = 0; ks < kFrontSplit; ++ks) sqv[ks] = ss_part[ks * T + t];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int e = min(lane + kWave * j, E - 1);
+#pragma unroll
+        for (int ks = 0; ks < kFrontSplit; ++ks) lp[j][ks] = lpart[((int64_t)ks * T + t) * E + e];
+        bv[j] = bias ? bias[e] : 0.f;
+        pvl[j] = pes[e];
+    }
+    float sq = sqv[0];
+#pragma unroll
+    for (int ks = 1; ks < kFrontSplit; ++ks) sq += sqv[ks];
+    // logit = (sum_h x s W) * rms(x)^-1 * H^-0.5 + bias
+    const float f = (1.0f / sqrtf(sq / (float)H + eps)) * inv_sqrt_h;
+    float lv[4] = {0.f, 0.f, 0.f, 0.f}, pv[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        float acc = lp[j][0];
+#pragma unroll
+        for (int ks = 1; ks < kFrontSplit; ++ks) acc += lp[j][ks];
+        lv[j] = acc * f + bv[j];
+        pv[j] = pvl[j];
+    }
+    int ik[kMaxTopK];
+    float wk[kMaxTopK];
+    wave_topk_vals<true, NJ>(lv, pes, E, K, lane, ik, wk, pv);
+    ei = ik[0];
+    wt = wk[0];
+#pragma unroll
+    for (int k = 1; k < kMaxTopK; ++k)
+        if (lane == k) {
+            ei = ik[k];
+            wt = wk[k];
+        }
+}
+
 template <int NS>
 __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(StreamArgs a, const float* lpart,
                                                                     const float* ss_part, const float* bias,
@@ -532,72 +575,28 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(StreamArgs 
     }
     __shared__ int s_idx[kMaxPairs];
     __shared__ float s_w[kMaxPairs];
-    __shared__ float s_l[kMaxPairs];   // logit of each selected pair
-    __shared__ float s_e[kMaxPairs];   // its exp relative to the token's largest
     __shared__ unsigned long long s_mask[kMaxExperts];
     __shared__ int s_off[kMaxExperts + 1];
-    __shared__ float s_pes[kMaxExperts];
-    __shared__ unsigned long long s_comp[kRouteThreads];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int T = a.T, K = a.K, E = a.E, TK = T * K;
-    // experts padded to a power of two: a chunk holds kRouteThreads / Ep tokens
-    const int Ep = E <= 64 ? 64 : E <= 128 ? 128 : 256;
-    const int tc = kRouteThreads / Ep;
-    const int tl = tid / Ep, e = tid - tl * Ep;
-    if (tid < E) {
-        s_mask[tid] = 0ull;
-        s_pes[tid] = pes[tid];
-    }
-    for (int t0 = 0; t0 < T; t0 += tc) {
-        const int t = t0 + tl;
-        const bool live = t < T && e < E;
-        // logit = (sum_h x s W) * rms(x)^-1 * H^-0.5 + bias, the slices added in order
-        float l = 0.f;
-        if (live) {
-            float acc = lpart[(int64_t)t * E + e], sq = ss_part[t];
-#pragma unroll
-            for (int ks = 1; ks < kFrontSplit; ++ks) {
-                acc += lpart[((int64_t)ks * T + t) * E + e];
-                sq += ss_part[ks * T + t];
-            }
-            const float rn = 1.0f / sqrtf(sq / (float)a.H + eps);
-            l = acc * (rn * inv_sqrt_h) + (bias ? bias[e] : 0.f);
-        }
-        const unsigned long long comp =
-            live ? ((unsigned long long)order_key(l) << 32) | (unsigned)(~e) : 0ull;
-        if (t0 > 0) __syncthreads();  // previous chunk done with s_comp
-        s_comp[tid] = comp;
-        __syncthreads();
-        if (live) {
-            const unsigned long long* row = s_comp + tl * Ep;
-            int rank = 0;
-            for (int j = 0; j < E; j += 2) {  // an odd E reads the padding slot E, which holds 0
-                const unsigned long long c0 = row[j], c1 = row[j + 1];
-                rank += (c0 > comp) + (c1 > comp);
-            }
-            if (rank < K) {
-                s_idx[t * K + rank] = e;
-                s_l[t * K + rank] = l;
-            }
+    if (tid < E) s_mask[tid] = 0ull;
+    // one wavefront a token
+    for (int t = wave; t < T; t += kRouteThreads / kWave) {
+        int ei;
+        float wt;
+        if (E <= 2 * kWave)
+            route_token<2>(lpart, ss_part, bias, pes, T, E, K, a.H, eps, inv_sqrt_h, t, lane, ei, wt);
+        else
+            route_token<4>(lpart, ss_part, bias, pes, T, E, K, a.H, eps, inv_sqrt_h, t, lane, ei, wt);
+        if (lane < K) {
+            s_idx[t * K + lane] = ei;
+            s_w[t * K + lane] = wt;
         }
     }
-    __syncthreads();
-    if (tid < TK)  // exp of each selected logit relative to the token's largest
-        s_e[tid] = expf(s_l[tid] - s_l[(tid / K) * K]);
-    __syncthreads();
-    if (tid < TK) {
-        const int t = tid / K;
-        float sum = 0.f;
-        for (int k = 0; k < K; ++k) sum += s_e[t * K + k];
-        const int ei = s_idx[tid];
-        const float wt = s_e[tid] / sum * s_pes[ei];
-        s_w[tid] = wt;
-        topk_idx[tid] = ei;
-        topk_w[tid] = wt;
-    }
-    __syncthreads();
+    // LDS-only barriers: no global store is waited on before the end
+    lds_barrier();
     if (tid < TK) atomicOr(&s_mask[s_idx[tid]], 1ull << (tid / K));
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) {
         int c[4], act[4], csum = 0, asum = 0;
 #pragma unroll
@@ -608,15 +607,10 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(StreamArgs 
             csum += c[i];
             asum += act[i];
         }
-        int ci = csum, ai = asum;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const int u = __shfl_up(ci, off, kWave), v = __shfl_up(ai, off, kWave);
-            if (lane >= off) {
-                ci += u;
-                ai += v;
-            }
-        }
+        // one scan of both: rows (<= 512) in the low half, active experts
+        // (<= 256) in the high half
+        const uint32_t sc = wave_incl_scan_u32((uint32_t)csum | ((uint32_t)asum << 16));
+        const int ci = (int)(sc & 0xffffu), ai = (int)(sc >> 16);
         int crun = ci - csum, arun = ai - asum;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -635,12 +629,15 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(StreamArgs 
             *a.n_active = ai;
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < TK) {
         const int e = s_idx[tid], t = tid / K;
+        const float wt = s_w[tid];
         const int pos = s_off[e] + __popcll(s_mask[e] & ((1ull << t) - 1ull));
+        topk_idx[tid] = e;
+        topk_w[tid] = wt;
         a.perm_token[pos] = t;
-        a.perm_w[pos] = s_w[tid];
+        a.perm_w[pos] = wt;
         a.inv_row[tid] = pos;
     }
 }

@@ -94,17 +94,6 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 // s_barrier with compiler-only memory barriers on both sides: memory accesses
 // may not be moved across it, and no hardware wait is added (the caller issues
 // the s_waitcnt it needs).
-__device__ __forceinline__ void raw_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-// barrier after this wavefront's LDS accesses have completed; its global
-// stores may still be in flight
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited on
-    raw_barrier();
-}
 constexpr int kAStageElems = BM * BK;  // bf16 elements per LDS stage of A
 
 // One K-step of the wavefront's B fragments: bf16 q[2 j + s] = column tile j,

@@ -40,15 +40,6 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     v = max(v, dpp_u32<0x143, 0xc, 0u>(v));  // row_bcast:31 into rows 2, 3
     return __builtin_amdgcn_readlane(v, 63);
 }
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-    v = min(v, dpp_u32<0x111, 0xf, 0xFFFFFFFFu>(v));
-    v = min(v, dpp_u32<0x112, 0xf, 0xFFFFFFFFu>(v));
-    v = min(v, dpp_u32<0x114, 0xf, 0xFFFFFFFFu>(v));
-    v = min(v, dpp_u32<0x118, 0xf, 0xFFFFFFFFu>(v));
-    v = min(v, dpp_u32<0x142, 0xa, 0xFFFFFFFFu>(v));
-    v = min(v, dpp_u32<0x143, 0xc, 0xFFFFFFFFu>(v));
-    return __builtin_amdgcn_readlane(v, 63);
-}
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ float dpp_add_f32(float x) {
     return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, false));
@@ -63,31 +54,51 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// Inclusive prefix sum over the wavefront's lanes (lane l gets v_0 + .. +
+// v_l): within each 16-lane row by row shifts of 1, 2, 4, 8 (lanes shifted in
+// from outside the row add 0), then row 15's total into rows 1 and 3 and lane
+// 31's running total into rows 2 and 3.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_add_u32(uint32_t x) {
+    return x + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xf, false);
+}
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+    v = dpp_add_u32<0x111, 0xf>(v);
+    v = dpp_add_u32<0x112, 0xf>(v);
+    v = dpp_add_u32<0x114, 0xf>(v);
+    v = dpp_add_u32<0x118, 0xf>(v);
+    v = dpp_add_u32<0x142, 0xa>(v);
+    v = dpp_add_u32<0x143, 0xc>(v);
+    return v;
+}
+
 // inverse of order_key (key 0, a NaN, maps back to a NaN)
 __device__ __forceinline__ float key_value(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
 // Run by a full wavefront. lv[j]: the token's logit of expert lane + 64 j
-// (E <= 256; entries with that index >= E are ignored).
+// (E <= 64 NJ; entries with that index >= E are ignored).
 // The top K by logit, then their renormalised softmax weights times the
 // per-expert scale. Every lane ends with the same ik[0..K), wk[0..K).
 // Selection: K rounds, without branches; each takes the largest remaining key
 // (a wavefront maximum of order_key + 1; 0 marks a taken or absent expert)
-// and, among equal keys, the lowest expert index (a wavefront minimum of the
-// indices holding it), so the experts come out in descending logit, ties to
-// the lower index. Weights: exp(l_k - l_0) / sum_j exp(l_j - l_0) over the K
-// selected (summed in k order), which is the softmax over all E renormalised
-// over the selection: the full denominator cancels.
+// and, among equal keys, the lowest expert index: the lowest j whose ballot of
+// key[j] == max is not empty, then the lowest lane in that ballot (expert
+// lane + 64 j). So the experts come out in descending logit, ties to the lower
+// index. Weights: exp(l_k - l_0) / sum_j exp(l_j - l_0) over the K selected
+// (summed in k order), which is the softmax over all E renormalised over the
+// selection: the full denominator cancels.
 // pv (used when PV): pv[j] = pes[lane + 64 j] already in registers, so that no
 // load waits on the selection.
-template <bool PV = false>
+template <bool PV = false, int NJ = 4>
 __device__ __forceinline__ void wave_topk_vals(const float (&lv)[4], const float* __restrict__ pes,
                                                int E, int K, int lane, int* ik, float* wk,
                                                const float (&pv)[4] = {0.f, 0.f, 0.f, 0.f}) {
-    uint32_t key[4];
+    static_assert(NJ >= 1 && NJ <= 4, "at most 256 experts");
+    uint32_t key[NJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) key[j] = (lane + kWave * j < E) ? order_key(lv[j]) + 1u : 0u;
+    for (int j = 0; j < NJ; ++j) key[j] = (lane + kWave * j < E) ? order_key(lv[j]) + 1u : 0u;
     float lk[kMaxTopK], sk[kMaxTopK];
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k) {
@@ -95,22 +106,34 @@ __device__ __forceinline__ void wave_topk_vals(const float (&lv)[4], const float
         lk[k] = 0.f;
         sk[k] = 0.f;
         if (k < K) {  // uniform
-            const uint32_t M = wave_max_u32(max(max(key[0], key[1]), max(key[2], key[3])));
-            uint32_t ci = 0xFFFFFFFFu;
+            uint32_t m = key[0];
 #pragma unroll
-            for (int j = 3; j >= 0; --j)
-                if (key[j] == M) ci = (uint32_t)(lane + kWave * j);
-            const uint32_t sel = wave_min_u32(ci);  // M > 0 while K <= E
-            const int jsel = (int)(sel >> 6), lsel = (int)(sel & 63);
-            ik[k] = (int)sel;
+            for (int j = 1; j < NJ; ++j) m = max(m, key[j]);
+            const uint32_t M = wave_max_u32(m);  // > 0 while K <= E
+            unsigned long long bj[NJ];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) bj[j] = __ballot(key[j] == M);
+            int jsel = NJ - 1;
+            unsigned long long bs = bj[NJ - 1];
+#pragma unroll
+            for (int j = NJ - 2; j >= 0; --j)
+                if (bj[j] != 0ull) {
+                    jsel = j;
+                    bs = bj[j];
+                }
+            const int lsel = __ffsll((long long)bs) - 1;
+            ik[k] = lsel + kWave * jsel;
             lk[k] = key_value(M - 1u);
             if (PV) {
-                const float p = jsel == 0 ? pv[0] : jsel == 1 ? pv[1] : jsel == 2 ? pv[2] : pv[3];
+                float p = pv[0];
+#pragma unroll
+                for (int j = 1; j < NJ; ++j)
+                    if (jsel == j) p = pv[j];
                 sk[k] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(p), lsel));
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if ((uint32_t)(lane + kWave * j) == sel) key[j] = 0u;
+            for (int j = 0; j < NJ; ++j)
+                if (j == jsel && lane == lsel) key[j] = 0u;
         }
     }
     float ex[kMaxTopK], sum = 0.f;
