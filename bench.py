@@ -210,6 +210,23 @@ def run_workload(name, steps, warmup, layers, dev, ev: HipEvents, log):
     elapsed = time.perf_counter() - t_start
     ms_step = elapsed * 1e3 / steps
 
+    # the same steps replayed from a HIP graph holding one call per weight copy
+    # (reported beside the eager time; `value` stays the eager rate)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // layers)
+    t_g = time.perf_counter()
+    for _ in range(reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms_graph = (time.perf_counter() - t_g) * 1e3 / (reps * layers)
+    del graph
+
     # dominant kernel: HIP events on the library's stream around that kernel in
     # every step of a second timed run (an event marker costs a few us of
     # stream time, so it is kept out of the run above)
@@ -231,6 +248,7 @@ def run_workload(name, steps, warmup, layers, dev, ev: HipEvents, log):
     res = {
         "workload": name, "T": T, "path": {1: "stream", 2: "grouped"}.get(path, path),
         "ms_per_step": ms_step, "tokens_per_s": T / (ms_step * 1e-3),
+        "graph": {"ms_per_step": ms_graph, "tokens_per_s": T / (ms_graph * 1e-3)},
         "experts_touched": n_active, "max_rows_per_expert": int(cnt.max()),
         "block_bytes": work["bytes"], "block_flops": work["flops"],
         "block_gbs": work["bytes"] / (ms_step * 1e-3) / 1e9,
@@ -243,7 +261,8 @@ def run_workload(name, steps, warmup, layers, dev, ev: HipEvents, log):
     }
     res["block_hbm_frac"] = res["block_gbs"] / HBM_PEAK_GBS
     res["block_mfma_frac"] = res["block_tflops"] / MFMA_BF16_PEAK_TFLOPS
-    log(f"[bench] {name}: {ms_step * 1e3:.1f} us/step, {res['tokens_per_s']:.0f} tok/s, "
+    log(f"[bench] {name}: {ms_step * 1e3:.1f} us/step ({ms_graph * 1e3:.1f} replayed from a graph), "
+        f"{res['tokens_per_s']:.0f} tok/s, "
         f"{res['block_gbs']:.0f} GB/s, dominant {dom_name} {dom_ms * 1e3:.1f} us, stages {res['stages_us']} "
         f"GB/s {res['stages_gbs']}")
     del calls, copies, base
@@ -376,6 +395,7 @@ def main():
                    "seed": moe_synth.WORKLOADS[args.workload].seed,
                    "layers_cycled": args.layers, "path": primary["path"]},
         "roofline": roof,
+        "graph": primary["graph"],
         "block": {k: primary[k] for k in ("block_bytes", "block_gbs", "block_hbm_frac", "block_flops",
                                           "block_tflops", "block_mfma_frac", "experts_touched",
                                           "stages_us", "stages_gbs", "dominant")},
@@ -383,7 +403,7 @@ def main():
     if args.workload == "decode" and not args.no_prefill:
         pre = run_workload("prefill", max(10, args.steps // 4), max(3, args.warmup // 4), args.layers,
                            dev, ev, log)
-        out["prefill"] = {k: pre[k] for k in ("T", "path", "ms_per_step", "tokens_per_s", "block_gbs",
+        out["prefill"] = {k: pre[k] for k in ("T", "path", "ms_per_step", "tokens_per_s", "graph", "block_gbs",
                                               "block_hbm_frac", "block_tflops", "block_mfma_frac",
                                               "experts_touched", "stages_us", "stages_gbs", "dominant")}
         out["prefill"]["roofline"] = roofline_for(pre, "mfma")

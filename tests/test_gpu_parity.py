@@ -15,9 +15,9 @@ import torch
 
 import moe_synth
 import oracle
-from mixture_experts_ffn_amd import (MOE_PATH_GROUPED, MOE_PATH_STREAM, MoEError, dense_mlp,
+from mixture_experts_ffn_amd import (MOE_PATH_GROUPED, MOE_PATH_STREAM, BlockCall, MoEError, dense_mlp,
                                      moe_block, moe_quantize_int8, moe_route, moe_tile_weights,
-                                     new_debug)
+                                     moe_workspace_bytes, new_debug)
 from gpu_util import (REL_BF16, REL_INT8, bf16_dev, check_routing, compare_y, dims_of,
                       oracle_int8_weights, routing_for, to_np, upload, y_f64)
 
@@ -296,3 +296,35 @@ def test_empty_batch_and_errors(dev):
     with pytest.raises(MoEError, match="UNSUPPORTED"):
         wl2, w2, x2, lw2, xd2 = inputs("prefill", dev)
         moe_block(dims_of(wl2.shape), lw2, xd2[:100].contiguous(), debug=new_debug(MOE_PATH_STREAM))
+
+
+@pytest.mark.parametrize("name,path", [("tiny", MOE_PATH_STREAM), ("tiny", MOE_PATH_GROUPED),
+                                       ("decode", MOE_PATH_STREAM)])
+def test_graph_replay(dev, name, path):
+    """The block captured into a HIP graph: every replay, with eager calls of
+    the block on other tokens (same workspace) and synchronisations between
+    the replays, gives the eager result bit for bit (no kernel depends on
+    scratch left by an earlier call, and the kernels are deterministic)."""
+    wl, w, x, lw, xd = inputs(name, dev)
+    say(f"case: graph replay {name} path={path}")
+    d = dims_of(wl.shape)
+    T = xd.shape[0]
+    ws = torch.empty(moe_workspace_bytes(d, T), dtype=torch.uint8, device=dev)
+    y_eager = moe_block(d, lw, xd, debug=new_debug(path), workspace=ws).clone()
+    torch.cuda.synchronize()
+    y_g = torch.empty_like(y_eager)
+    call = BlockCall(d, lw, xd, y=y_g, workspace=ws)
+    dbg = new_debug(path)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(dbg)
+    torch.cuda.synchronize()
+    x_other = torch.flip(xd, dims=[0]).contiguous()
+    for rep in range(3):
+        y_g.zero_()
+        moe_block(d, lw, x_other, debug=new_debug(path), workspace=ws)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_g, y_eager), f"replay {rep} differs from the eager result"
+
