@@ -91,9 +91,6 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 // native 4 x u32 vector (a first-class type that stays in registers)
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
-// s_barrier with compiler-only memory barriers on both sides: memory accesses
-// may not be moved across it, and no hardware wait is added (the caller issues
-// the s_waitcnt it needs).
 constexpr int kAStageElems = BM * BK;  // bf16 elements per LDS stage of A
 
 // One K-step of the wavefront's B fragments: bf16 q[2 j + s] = column tile j,
