@@ -53,7 +53,16 @@ constexpr int kADma = BM / kWaves / 8;  // A loads (8 rows, 1 KB each) per wavef
 enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
 static_assert(BM == 256 && kWaves * 32 == BN, "8 wavefronts x 32 columns, 256 rows");
 
-__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ (r & 7)) << 3); }
+// LDS position of A's 16-byte chunk c (of 8) of tile row r: chunk c ^ f(r),
+// f(r) = (r & 7) ^ ((r >> 3) & 1). A 128-bit LDS read serves 16 lanes a cycle
+// across 64 banks (256 B, two 128-byte rows' worth): the MFMA A fragments read
+// chunk c of rows R .. R + 15 (R a multiple of 16), which must land on 16
+// distinct (row parity, chunk) bank groups, and f gives that (r & 7 alone maps
+// rows r and r + 8 onto the same banks: a two-way conflict on every fragment
+// read). f depends on r % 16 only, so a wavefront's fragment addresses differ
+// between slabs by a constant offset.
+__device__ __forceinline__ int a_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ a_swz(r)) << 3); }
 
 template <int MODE>
 __host__ __device__ __forceinline__ int n_tiles_of(const GemmArgs& p) {
@@ -137,7 +146,7 @@ __device__ __forceinline__ bf16x8_t b_frag(const BStep<INT8>& r, int j, int s) {
 
 // A: wavefront w moves rows [32w, 32w+32) of the K-step (4 x 1 KB); within
 // each 1 KB (8 rows of 128 B) lane l lands in row l/8, physical chunk l%8, and
-// so fetches logical chunk (l%8) ^ (row & 7).
+// so fetches logical chunk (l%8) ^ a_swz(row).
 // The waits below count loads in issue order, so the compiler may not move
 // any other load across these: compiler-only memory barriers on both sides.
 __device__ __forceinline__ void a_dma(const char* const (&ap)[kADma], int kt, uint16_t* stage, int wave) {
@@ -298,7 +307,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
 #pragma unroll
     for (int q = 0; q < kADma; ++q) {
         const int r = wave * kADma * 8 + q * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ (r & 7);
+        const int c = (lane & 7) ^ a_swz(r);
         const int rr = min(r, rows_valid - 1);  // rows past the tile end repeat a valid row
         const int64_t arow = p.a_rows ? p.a_rows[row0 + rr] : (int64_t)(row0 + rr);
         ap[q] = reinterpret_cast<const char*>(p.A + arow * p.lda + c * 8);

@@ -128,7 +128,10 @@ constexpr int kRThreads = 256;
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ int rswz(int r, int c) { return r * kRK + ((c ^ (r & 7)) << 3); }
+// 16-byte chunk c of LDS row r at chunk c ^ ((r & 7) ^ ((r >> 3) & 1)): 128-bit
+// reads of chunk c of 16 consecutive rows (one cycle's 16 lanes over 64 banks)
+// then hit 16 distinct (row parity, chunk) bank groups
+__device__ __forceinline__ int rswz(int r, int c) { return r * kRK + ((c ^ ((r & 7) ^ ((r >> 3) & 1))) << 3); }
 
 // NQ: router rows staged per thread per K-step (32 NQ experts per workgroup)
 template <int NQ>
