@@ -134,7 +134,10 @@ template <bool INT8>
 __device__ __forceinline__ bf16x8_t b_frag(const BStep<INT8>& r, int j, int s) {
     v4u v;
     if (INT8) {
-        const v4u w = r.q[j & 1];
+        // the piece made opaque here, so that each fragment is widened where it
+        // is used rather than all of them ahead (registers the loop lacks)
+        v4u w = r.q[j & 1];
+        asm volatile("" : "+v"(w));
         const unsigned w0 = s ? w.z : w.x, w1 = s ? w.w : w.y;
         v = v4u{i8pair_to_bf16(w0, 0), i8pair_to_bf16(w0, 16), i8pair_to_bf16(w1, 0),
                 i8pair_to_bf16(w1, 16)};
