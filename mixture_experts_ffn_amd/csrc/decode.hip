@@ -138,14 +138,19 @@ __device__ __forceinline__ void i8x16_to_bf16(const uint4& v, uint4& lo, uint4& 
 
 // One K-step of a lane's piece of a tile (bf16: two 16-byte halves, 8 k each;
 // int8: one 16-byte piece, 16 k) dotted with the 16 matching x values.
-template <bool INT8>
+// OPAQUE (int8): the piece is made opaque before it is widened, so that the
+// compiler widens it where it is used instead of hoisting every step's widened
+// copy (twice the registers) out of the caller's loop over tokens.
+template <bool INT8, bool OPAQUE = false>
 __device__ __forceinline__ float piece_dot(const uint4 (&w)[INT8 ? 1 : 2], const uint16_t* xp,
                                            float acc) {
     const uint4 x0 = *reinterpret_cast<const uint4*>(xp);
     const uint4 x1 = *reinterpret_cast<const uint4*>(xp + 8);
     if (INT8) {
+        uint4 v = w[0];
+        if (OPAQUE) asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
         uint4 lo, hi;
-        i8x16_to_bf16(w[0], lo, hi);
+        i8x16_to_bf16(v, lo, hi);
         acc = dot8_bf16(lo, x0, acc);
         return dot8_bf16(hi, x1, acc);
     }
@@ -695,7 +700,7 @@ __device__ __forceinline__ float down_dot(const uint4 (&w)[NS][INT8 ? 1 : 2], co
     float acc = 0.f;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-        if (s < n_steps) acc = piece_dot<INT8>(w[s], hp + s * 64, acc);
+        if (s < n_steps) acc = piece_dot<INT8, true>(w[s], hp + s * 64, acc);
     return tile_row_sum(acc);
 }
 
