@@ -24,8 +24,8 @@ What the block computes (one input x feeds router, experts and dense MLP):
   (activation ``gelu_pytorch_tanh``); [INF2] "How it works (the recipe)" maps
   each expert onto a fused gate_up linear and a down linear.
 * Block output -- [ONNX] row "MoE topology": a dense MLP (intermediate 2112)
-  in parallel with the MoE; the block result here is ``dense(x) + moe(x)``
-  (the post-FF norm and residual around it are outside the block).
+  in parallel with the MoE; the block result here is ``dense(x) + moe(x)``.
+  ``ffn_layer`` adds the norms and the residual around it (see there).
 * Sparse top-8 equals all-experts-dense with zero weight on the unselected
   experts -- [INF2] "How it works (the recipe)", first bullet.
 * int8 experts -- [INT8] intro and "How it works": per-channel symmetric int8
@@ -54,8 +54,9 @@ import numpy as np
 
 __all__ = [
     "bf16_to_f64", "gelu_tanh", "rms_normalise", "router_logits", "route",
-    "permute_pairs", "expert_ffn", "dense_mlp", "moe_block", "masked_dense_block",
+    "permute_pairs", "expert_ffn", "dense_mlp", "moe_part", "moe_block", "masked_dense_block",
     "quantize_int8", "dequantize_int8", "brute_force_block", "NEAR_TIE",
+    "round_bf16", "rms_norm_scaled", "FFN_NORMS", "ffn_layer",
 ]
 
 #: logit gap under which a top-k decision is reported as a near-tie
@@ -210,16 +211,10 @@ def _expert_weights(weights, e, dtype):
     return weights["expert_gate_up"][e], weights["expert_down"][e]
 
 
-def moe_block(x, weights, top_k, eps, expert_dtype="bf16", routing=None):
-    """y = dense(x) + sum_k w[t,k] * expert_{e[t,k]}(x_t)  (the sparse top-k form).
-
-    ``weights`` uses the keys of ``moe_synth.make_weights``; for
-    ``expert_dtype="int8"`` it must also hold ``expert_gate_up_q``,
-    ``expert_gate_up_scale``, ``expert_down_q``, ``expert_down_scale``
-    (see ``quantize_int8``). ``routing`` may supply a precomputed ``route``
-    result (or one with a different but equally valid index set).
-    Returns ``(y [T,H] float64, routing)``.
-    """
+def moe_part(x, weights, top_k, eps, expert_dtype="bf16", routing=None):
+    """moe = sum_k w[t,k] * expert_{e[t,k]}(x_t), added in k order (the sparse
+    top-k form of the MoE branch). Returns ``(moe [T,H] float64, routing)``;
+    arguments as for ``moe_block``."""
     x64 = _f64(x)
     if routing is None:
         routing = route(x64, weights["router_scale"], weights["router_w"],
@@ -235,8 +230,68 @@ def moe_block(x, weights, top_k, eps, expert_dtype="bf16", routing=None):
     moe = np.zeros_like(x64)
     for k in range(K):                             # k order
         moe += contrib[:, k]
+    return moe, routing
+
+
+def moe_block(x, weights, top_k, eps, expert_dtype="bf16", routing=None):
+    """y = dense(x) + sum_k w[t,k] * expert_{e[t,k]}(x_t)  (the sparse top-k form).
+
+    ``weights`` uses the keys of ``moe_synth.make_weights``; for
+    ``expert_dtype="int8"`` it must also hold ``expert_gate_up_q``,
+    ``expert_gate_up_scale``, ``expert_down_q``, ``expert_down_scale``
+    (see ``quantize_int8``). ``routing`` may supply a precomputed ``route``
+    result (or one with a different but equally valid index set).
+    Returns ``(y [T,H] float64, routing)``.
+    """
+    x64 = _f64(x)
+    moe, routing = moe_part(x64, weights, top_k, eps, expert_dtype, routing)
     dense = dense_mlp(x64, weights["dense_gate_up"], weights["dense_down"])
     return moe + dense, routing
+
+
+# --------------------------------------------------------------------------
+# the layer's FFN around the block: [INF2] "The architecture (a dual-path
+# FFN)" (the two branches pass through four feed-forward layernorms) and
+# [ONNX] "Truthful graph contracts", row "MoE topology" (post_ff_norm of
+# dense + moe, then the residual)
+# --------------------------------------------------------------------------
+#: the norm positions of ``ffn_layer``: the dense and MoE branches' inputs and
+#: outputs, and their sum
+FFN_NORMS = ("pre_dense", "pre_moe", "post_dense", "post_moe", "post")
+
+
+def round_bf16(v):
+    """The nearest bfloat16 values, through float32 (ties to even at both
+    steps: the kernel forms the value in fp32 and rounds it once to bf16)."""
+    f = np.asarray(v, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    r = ((u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)) << np.uint64(16)
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def rms_norm_scaled(v, scale, eps):
+    """RMSNorm with a learned per-channel gain, ``v / sqrt(mean(v^2) + eps) *
+    scale`` per token; ``scale`` None leaves ``v`` unchanged (no norm there)."""
+    if scale is None:
+        return _f64(v)
+    return rms_normalise(v, eps) * _f64(scale)[None, :]
+
+
+def ffn_layer(h, weights, norms, top_k, eps, expert_dtype="bf16", routing=None):
+    """out = h + N_post(N_post_dense(dense(x_d)) + N_post_moe(moe(x_m))), with
+    x_d = N_pre_dense(h) and x_m = N_pre_moe(h) rounded to bf16 (the block's
+    input precision); N_k is ``rms_norm_scaled`` with ``norms[k]`` (None: no
+    norm at that position) and ``norms["eps"]``. ``eps`` is the router's.
+    Returns ``(out [T,H] float64, routing)``; routing is that of x_m.
+    """
+    h64 = _f64(h)
+    ne = norms["eps"]
+    xd = h64 if norms["pre_dense"] is None else round_bf16(rms_norm_scaled(h64, norms["pre_dense"], ne))
+    xm = h64 if norms["pre_moe"] is None else round_bf16(rms_norm_scaled(h64, norms["pre_moe"], ne))
+    dense = dense_mlp(xd, weights["dense_gate_up"], weights["dense_down"])
+    moe, routing = moe_part(xm, weights, top_k, eps, expert_dtype, routing)
+    s = rms_norm_scaled(dense, norms["post_dense"], ne) + rms_norm_scaled(moe, norms["post_moe"], ne)
+    return h64 + rms_norm_scaled(s, norms["post"], ne), routing
 
 
 def masked_dense_block(x, weights, top_k, eps, expert_dtype="bf16", routing=None):

@@ -340,3 +340,110 @@ def test_fp16_accumulation_loses_accuracy_at_real_hidden():
     e16 = np.linalg.norm(acc16 - exact) / np.linalg.norm(exact)
     e32 = np.linalg.norm(acc32 - exact) / np.linalg.norm(exact)
     assert e16 > 10 * e32
+
+
+# ---------------------------------------------------------------- the layer's FFN (norms, residual)
+NO_NORMS = {**dict.fromkeys(oracle.FFN_NORMS), "eps": 1e-6}
+
+
+def test_rms_norm_scaled_invariants():
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal((6, 256)) * rng.uniform(0.1, 10.0, (6, 1))
+    s = 1.0 + 0.1 * rng.standard_normal(256)
+    ones = np.ones(256)
+    # invariant under scaling the row (eps = 0)
+    np.testing.assert_allclose(oracle.rms_norm_scaled(3.7 * v, s, 0.0), oracle.rms_norm_scaled(v, s, 0.0),
+                               rtol=1e-13)
+    # unit gain: the output's mean square is ms / (ms + eps), in closed form
+    eps = 0.25
+    ms = np.mean(v * v, axis=1)
+    out = oracle.rms_norm_scaled(v, ones, eps)
+    np.testing.assert_allclose(np.mean(out * out, axis=1), ms / (ms + eps), rtol=1e-13)
+    # unit gain, eps = 0: normalising a normalised row changes nothing
+    n1 = oracle.rms_norm_scaled(v, ones, 0.0)
+    np.testing.assert_allclose(oracle.rms_norm_scaled(n1, ones, 0.0), n1, rtol=1e-13)
+    # the gain scales channels (columns), not tokens
+    np.testing.assert_allclose(oracle.rms_norm_scaled(v, s, 0.0), n1 * s[None, :], rtol=1e-13)
+    # no gain: no norm at that position
+    assert np.array_equal(oracle.rms_norm_scaled(v, None, 0.5), v)
+
+
+def test_round_bf16_ties_to_even_and_generator_agreement():
+    v = np.array([1.0, 1 + 2.0**-8, 1 + 3 * 2.0**-8, -(1 + 2.0**-8), 2.5])
+    np.testing.assert_array_equal(oracle.round_bf16(v), [1.0, 1.0, 1 + 2.0**-6, -1.0, 2.5])
+    r = np.random.default_rng(1).standard_normal(20000).astype(np.float32)
+    np.testing.assert_array_equal(oracle.round_bf16(r),
+                                  moe_synth.bf16_bits_to_f32(moe_synth.f32_to_bf16_bits(r)).astype(np.float64))
+
+
+def test_ffn_layer_without_norms_is_residual_plus_block(tiny):
+    wl, w, x = tiny
+    y, r = oracle.moe_block(x, w, wl.shape.top_k, wl.shape.rms_eps)
+    out, _ = oracle.ffn_layer(x, w, NO_NORMS, wl.shape.top_k, wl.shape.rms_eps, routing=r)
+    np.testing.assert_array_equal(out, oracle.bf16_to_f64(x) + y)
+
+
+def test_ffn_layer_equal_pre_norms_feed_router_and_both_branches(tiny):
+    """Equal pre-norm gains on both branches: the layer is the residual plus
+    the block run on the normalised input rounded to bf16, and the router
+    reads that input."""
+    wl, w, x = tiny
+    K, eps = wl.shape.top_k, wl.shape.rms_eps
+    g = oracle.round_bf16(1.0 + 0.1 * np.random.default_rng(2).standard_normal(wl.shape.hidden))
+    norms = {**NO_NORMS, "pre_dense": g, "pre_moe": g, "eps": 1e-5}
+    out, r = oracle.ffn_layer(x, w, norms, K, eps)
+    xn = oracle.round_bf16(oracle.rms_normalise(x, 1e-5) * g[None, :])
+    r_ref = oracle.route(xn, w["router_scale"], w["router_w"], w["per_expert_scale"], K, eps)
+    np.testing.assert_array_equal(r["topk_idx"], r_ref["topk_idx"])
+    y, _ = oracle.moe_block(xn, w, K, eps, routing=r)
+    np.testing.assert_array_equal(out, oracle.bf16_to_f64(x) + y)
+
+
+def test_ffn_layer_moe_branch_alone(tiny):
+    """No dense weights, unit post gains and eps 0: the dense branch adds
+    nothing and the outer norm of an already normalised row changes nothing,
+    so the layer is h + N(moe(h))."""
+    wl, w, x = tiny
+    K, eps = wl.shape.top_k, wl.shape.rms_eps
+    w0 = dict(w)
+    w0["dense_gate_up"] = np.zeros_like(w["dense_gate_up"])
+    w0["dense_down"] = np.zeros_like(w["dense_down"])
+    ones = np.ones(wl.shape.hidden)
+    norms = {**NO_NORMS, "post_moe": ones, "post": ones, "eps": 0.0}
+    out, r = oracle.ffn_layer(x, w0, norms, K, eps)
+    moe, _ = oracle.moe_part(x, w0, K, eps, routing=r)
+    np.testing.assert_allclose(out, oracle.bf16_to_f64(x) + oracle.rms_normalise(moe, 0.0), rtol=1e-12,
+                               atol=1e-12)
+
+
+def test_ffn_layer_post_norms_act_per_branch(tiny):
+    """Scaling the dense branch's down matrix by c > 0 leaves its post-normed
+    output (eps 0) unchanged; without that norm the layer changes."""
+    wl, w, x = tiny
+    K, eps = wl.shape.top_k, wl.shape.rms_eps
+    H = wl.shape.hidden
+    w2 = dict(w)
+    w2["dense_down"] = oracle.bf16_to_f64(w["dense_down"]) * 4.0  # exact: a power of two
+    g = 1.0 + 0.1 * np.random.default_rng(3).standard_normal(H)
+    with_norm = {**NO_NORMS, "post_dense": g, "post_moe": g, "post": g, "eps": 0.0}
+    a, r = oracle.ffn_layer(x, w, with_norm, K, eps)
+    b, _ = oracle.ffn_layer(x, w2, with_norm, K, eps, routing=r)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+    c, _ = oracle.ffn_layer(x, w, NO_NORMS, K, eps, routing=r)
+    d, _ = oracle.ffn_layer(x, w2, NO_NORMS, K, eps, routing=r)
+    assert np.max(np.abs(c - d)) > 1e-3
+
+
+def test_ffn_layer_pre_norms_act_per_branch(tiny):
+    """A pre-norm on the MoE branch only: the router and experts read the
+    normalised input, the dense MLP the raw one."""
+    wl, w, x = tiny
+    K, eps = wl.shape.top_k, wl.shape.rms_eps
+    g = oracle.round_bf16(1.0 + 0.1 * np.random.default_rng(4).standard_normal(wl.shape.hidden))
+    out, r = oracle.ffn_layer(x, w, {**NO_NORMS, "pre_moe": g}, K, eps)
+    xn = oracle.round_bf16(oracle.rms_normalise(x, 1e-6) * g[None, :])
+    moe, _ = oracle.moe_part(xn, w, K, eps, routing=r)
+    dense = oracle.dense_mlp(x, w["dense_gate_up"], w["dense_down"])
+    np.testing.assert_array_equal(out, oracle.bf16_to_f64(x) + (dense + moe))
+    r_ref = oracle.route(xn, w["router_scale"], w["router_w"], w["per_expert_scale"], K, eps)
+    np.testing.assert_array_equal(r["topk_idx"], r_ref["topk_idx"])
