@@ -174,6 +174,35 @@ int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
 int dense_mlp(const moe_dims* d, const void* dense_gate_up, const void* dense_down,
               const void* x, int32_t T, void* y, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Gains of the feed-forward layernorms around the block (moe_ffn_layer). Each
+ * is a device pointer to H bf16 values (16-byte aligned), or NULL: no norm at
+ * that position. N_g(v) = v / sqrt(mean(v^2) + eps) * g, per token, in fp32. */
+typedef struct moe_ffn_norms {
+    const void* pre_dense;   /* dense MLP branch input */
+    const void* pre_moe;     /* MoE branch input (router and experts) */
+    const void* post_dense;  /* dense MLP branch output */
+    const void* post_moe;    /* MoE branch output */
+    const void* post;        /* their sum, before the residual */
+    float eps;
+} moe_ffn_norms;
+
+/* The layer's feed-forward part around the block ([INF2] "The architecture (a
+ * dual-path FFN)": the dense MLP and the MoE run in parallel and pass through
+ * four feed-forward layernorms; [ONNX] "Truthful graph contracts", row "MoE
+ * topology": post_ff_norm(dense + moe) + residual):
+ *   out = h + N_post(N_post_dense(dense(x_d)) + N_post_moe(moe(x_m))),
+ *   x_d = bf16(N_pre_dense(h)), x_m = bf16(N_pre_moe(h)),
+ * dense and moe as in moe_block (router, top-k, experts on x_m; the dense MLP on
+ * x_d); the branch outputs stay fp32 through the post-norms and the residual
+ * add, and out is rounded once to bf16. h, out [T, H] bf16 (out may not alias
+ * h); n as above (NULL: every norm absent, the residual kept); ws as for
+ * moe_block (moe_ffn_workspace_bytes: its size); dbg as for moe_block, its
+ * routing being that of x_m. Errors as for moe_block, plus MOE_ERR_ALIGN for a
+ * misaligned gain. */
+size_t moe_ffn_workspace_bytes(const moe_dims* d, int32_t T);
+int moe_ffn_layer(const moe_dims* d, const moe_weights* w, const moe_ffn_norms* n, const void* h,
+                  int32_t T, void* out, moe_debug* dbg, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Per-row symmetric int8 quantisation of a bf16 matrix [rows, cols], as the
  * int8 build quantises the fused expert weights when it loads them ([INT8]
  * "How it works"): scale[r] = max_c |w[r,c]| / 127 (fp32), q[r,c] =

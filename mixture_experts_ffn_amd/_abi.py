@@ -64,7 +64,14 @@ class MoeDebug(ctypes.Structure):
                 ("stage_name", ctypes.c_char_p * MOE_MAX_STAGES)]
 
 
+class MoeFfnNorms(ctypes.Structure):
+    _fields_ = [("pre_dense", ctypes.c_void_p), ("pre_moe", ctypes.c_void_p),
+                ("post_dense", ctypes.c_void_p), ("post_moe", ctypes.c_void_p),
+                ("post", ctypes.c_void_p), ("eps", ctypes.c_float)]
+
+
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_block", "dense_mlp",
+           "moe_ffn_workspace_bytes", "moe_ffn_layer",
            "moe_quantize_int8", "moe_tile_weights", "moe_last_error")
 
 _lib = None
@@ -90,6 +97,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.moe_block.restype = ctypes.c_int
     lib.dense_mlp.argtypes = [P(MoeDims), vp, vp, vp, i32, vp, vp, sz, vp]
     lib.dense_mlp.restype = ctypes.c_int
+    lib.moe_ffn_workspace_bytes.argtypes = [P(MoeDims), i32]
+    lib.moe_ffn_workspace_bytes.restype = sz
+    lib.moe_ffn_layer.argtypes = [P(MoeDims), P(MoeWeights), P(MoeFfnNorms), vp, i32, vp, P(MoeDebug), vp, sz,
+                                  vp]
+    lib.moe_ffn_layer.restype = ctypes.c_int
     lib.moe_quantize_int8.argtypes = [vp, i64, i32, vp, vp, vp]
     lib.moe_quantize_int8.restype = ctypes.c_int
     lib.moe_tile_weights.argtypes = [vp, i64, i32, i32, vp, vp]

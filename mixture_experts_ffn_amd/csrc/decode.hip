@@ -447,7 +447,7 @@ __global__ __launch_bounds__(kThreads) void decode_front_kernel(StreamArgs a, co
         router_part<NS>(a.x, a.H, scale, wr, a.E, nt, ks, a.T, lpart, ss_part, red);
     } else {
         const int i = b - n_router, hc = i / kFrontSplit, ks = i - hc * kFrontSplit;
-        dense_gateup_part<NS>(a.x, a.H, a.dgu, a.Id, hc, ks, a.T, a.dgu_part, red, (int)threadIdx.x);
+        dense_gateup_part<NS>(a.xd, a.H, a.dgu, a.Id, hc, ks, a.T, a.dgu_part, red, (int)threadIdx.x);
     }
 }
 
@@ -574,7 +574,7 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(StreamArgs 
         const int grp = threadIdx.x >> 8;
         const int i = ((int)blockIdx.x - (lpart ? 1 : 0)) * 4 + grp;
         const int hc = i / kFrontSplit, ks = i - hc * kFrontSplit;
-        dense_gateup_part<NS>(a.x, a.H, a.dgu, a.Id, hc, ks, a.T, a.dgu_part, red_d[grp],
+        dense_gateup_part<NS>(a.xd, a.H, a.dgu, a.Id, hc, ks, a.T, a.dgu_part, red_d[grp],
                               (int)threadIdx.x & 255);
         return;
     }

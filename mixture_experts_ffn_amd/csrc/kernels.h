@@ -103,7 +103,8 @@ hipError_t launch_combine(const float* dense_out, const uint16_t* rows, const in
 // ---- small-batch path (decode.hip) ----------------------------------------
 struct StreamArgs {
     int T, H, I, Id, K, E;
-    const uint16_t* x;
+    const uint16_t* x;                        // router and experts input
+    const uint16_t* xd;                       // dense MLP input
     // experts
     const void* gu; const float* gu_scale;   // [E][2I][H]
     const void* dw; const float* dw_scale;   // [E][H][I]
@@ -153,5 +154,16 @@ hipError_t launch_tile_weights(const void* src, int64_t rows, int cols, bool int
                                hipStream_t stream);
 hipError_t launch_quantize_int8(const uint16_t* w, int64_t rows, int cols, int8_t* q, float* scale,
                                 hipStream_t stream);
+
+// ---- the layer's feed-forward norms around the block (ffn.hip) ----------------
+// x_d = bf16(N_gd(h)), x_m = bf16(N_gm(h)) per token (only those whose gain is given)
+hipError_t launch_ffn_prenorm(const uint16_t* h, int T, int H, const uint16_t* gd, const uint16_t* gm, float eps,
+                              uint16_t* xd, uint16_t* xm, hipStream_t stream);
+// out = h + N_gp(N_gpd(dense) + N_gpm(moe)), moe = sum_k rows[inv_row[t K + k]] in k order
+// (f32_rows: fp32 rows times topk_w; else bf16 rows already weighted); absent gain: no norm
+hipError_t launch_ffn_post(const uint16_t* h, const float* dense, const void* rows, bool f32_rows,
+                           const int32_t* inv_row, const float* topk_w, int T, int H, int K,
+                           const uint16_t* gpd, const uint16_t* gpm, const uint16_t* gp, float eps, uint16_t* out,
+                           hipStream_t stream);
 
 }  // namespace moe

@@ -110,6 +110,13 @@ int check_dims(const moe_dims* d) {
     return MOE_OK;
 }
 
+int check_tiled(const moe_weights* w) {
+    if (w->layout != MOE_LAYOUT_TILED)
+        return fail(MOE_ERR_UNSUPPORTED, "layout=%d: expert and dense weights must be MOE_LAYOUT_TILED "
+                    "(see moe_tile_weights)", w->layout);
+    return MOE_OK;
+}
+
 int check_T(int32_t T) {
     if (T < 0 || T > MOE_MAX_TOKENS) return fail(MOE_ERR_SHAPE, "T=%d outside [0, %d]", T, MOE_MAX_TOKENS);
     return MOE_OK;
@@ -187,6 +194,190 @@ struct Stages {
 template <typename T>
 T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
 
+// moe_ffn_layer's workspace: the block's, then the two branches' bf16 inputs
+struct FfnLayout {
+    size_t total;
+};
+FfnLayout ffn_layout(const moe_dims& d, int64_t T) {
+    return {make_layout(d, T).total + 2 * up256((size_t)T * d.hidden * 2)};
+}
+
+// The block's pipeline. The router and the experts read x, the dense MLP xd;
+// without norms y = dense + moe (moe_block), with them (moe_ffn_layer) the
+// last stage forms y = h + N_post(N_post_dense(dense) + N_post_moe(moe)).
+// Arguments are checked by the callers.
+int block_impl(const moe_dims* d, const moe_weights* w, const void* x, const void* xd_in, int32_t T, void* y,
+               const moe_ffn_norms* norms, const void* hres, moe_debug* dbg, void* ws, hipStream_t stream) {
+    int path = dbg ? dbg->path : MOE_PATH_AUTO;
+    if (path != MOE_PATH_AUTO && path != MOE_PATH_STREAM && path != MOE_PATH_GROUPED)
+        return fail(MOE_ERR_UNSUPPORTED, "unknown path %d", path);
+    if (path == MOE_PATH_AUTO)
+        path = (T <= stream_limit() && stream_fits(*d)) ? MOE_PATH_STREAM : MOE_PATH_GROUPED;
+    if (path == MOE_PATH_STREAM && (T > MOE_STREAM_MAX_TOKENS || !stream_fits(*d)))
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "streaming path needs T <= %d, hidden <= 3072, expert_inter <= 1024, dense_inter <= 4096",
+                    MOE_STREAM_MAX_TOKENS);
+    g_err[0] = 0;
+    if (dbg) {
+        dbg->path_taken = path;
+        dbg->n_stages = 0;
+    }
+    if (T == 0) return MOE_OK;
+
+    const Layout L = make_layout(*d, T);
+    const bool int8 = w->expert_dtype == MOE_DTYPE_INT8;
+    const int H = d->hidden, E = d->num_experts, K = d->top_k, I = d->expert_inter, Id = d->dense_inter;
+    int32_t* topk_idx = at<int32_t>(ws, L.topk_idx);
+    float* topk_w = at<float>(ws, L.topk_w);
+    int32_t* pair_rank = at<int32_t>(ws, L.pair_rank);
+    moe::PermuteOut po{};
+    po.tile_counts = at<int32_t>(ws, L.tile_counts);
+    po.counts = at<int32_t>(ws, L.counts);
+    po.offsets = at<int32_t>(ws, L.offsets);
+    po.perm_token = at<int32_t>(ws, L.perm_token);
+    po.perm_w = at<float>(ws, L.perm_w);
+    po.inv_row = at<int32_t>(ws, L.inv_row);
+    po.active = at<int32_t>(ws, L.active);
+    po.n_active = at<int32_t>(ws, L.n_active);
+    po.mtile_group = at<int32_t>(ws, L.mtile_group);
+    po.mtile_row0 = at<int32_t>(ws, L.mtile_row0);
+    po.n_mtiles = at<int32_t>(ws, L.n_mtiles);
+    po.tiles[0] = at<int2>(ws, L.gemm_tiles[0]);
+    po.tiles[1] = at<int2>(ws, L.gemm_tiles[1]);
+    po.n_nt[0] = moe::gemm_n_tiles_gateup(I);
+    po.n_nt[1] = moe::gemm_n_tiles_down(H);
+    po.max_mtiles = L.max_mtiles;
+    uint16_t* h = at<uint16_t>(ws, L.h);
+    uint16_t* hd = at<uint16_t>(ws, L.hd);
+    uint16_t* rows = at<uint16_t>(ws, L.rows);
+    const uint16_t* xb = (const uint16_t*)x;
+    const uint16_t* xdb = (const uint16_t*)xd_in;
+    const uint16_t* g_pd = norms ? (const uint16_t*)norms->post_dense : nullptr;
+    const uint16_t* g_pm = norms ? (const uint16_t*)norms->post_moe : nullptr;
+    const uint16_t* g_p = norms ? (const uint16_t*)norms->post : nullptr;
+
+    Stages st{dbg, stream};
+    if (norms && (norms->pre_dense || norms->pre_moe)) {
+        // the branches' normalised inputs, after the block's own workspace
+        const size_t xoff = L.total;
+        uint16_t* xn_d = norms->pre_dense ? at<uint16_t>(ws, xoff) : nullptr;
+        uint16_t* xn_m = norms->pre_moe ? at<uint16_t>(ws, xoff + up256((size_t)T * H * 2)) : nullptr;
+        HIP_TRY(st.begin("ffn_prenorm"), "event record");
+        HIP_TRY(moe::launch_ffn_prenorm(xb, T, H, (const uint16_t*)norms->pre_dense, (const uint16_t*)norms->pre_moe,
+                                        norms->eps, xn_d, xn_m, stream),
+                "ffn_prenorm launch");
+        if (xn_d) xdb = xn_d;
+        if (xn_m) xb = xn_m;
+    }
+    if (path == MOE_PATH_STREAM) {
+        moe::StreamArgs sa{};
+        sa.T = T; sa.H = H; sa.I = I; sa.Id = Id; sa.K = K; sa.E = E;
+        sa.x = xb; sa.xd = xdb;
+        sa.gu = w->expert_gate_up; sa.gu_scale = w->gate_up_scale;
+        sa.dw = w->expert_down; sa.dw_scale = w->down_scale;
+        sa.counts = po.counts; sa.offsets = po.offsets; sa.active = po.active; sa.n_active = po.n_active;
+        sa.perm_token = po.perm_token; sa.perm_w = po.perm_w; sa.inv_row = po.inv_row;
+        sa.topk_w = topk_w;
+        sa.max_active = T * K < E ? T * K : E;
+        sa.dgu = (const uint16_t*)w->dense_gate_up; sa.ddw = (const uint16_t*)w->dense_down;
+        sa.h = h; sa.hd = hd; sa.y = (uint16_t*)y;
+        sa.part = at<float>(ws, L.part); sa.dpart = at<float>(ws, L.dpart);
+        sa.dgu_part = at<float>(ws, L.dgu_part);
+        sa.hpart = at<float>(ws, L.hpart);
+        sa.with_dense = 1;  // the dense MLP's items ride along in K2, K3 and K4
+        HIP_TRY(st.begin("decode_front"), "event record");
+        float* lpart = at<float>(ws, L.lpart);
+        float* ss_part = at<float>(ws, L.ss_part);
+        HIP_TRY(moe::launch_decode_front(sa, (const uint16_t*)w->router_scale, (const uint16_t*)w->router_w,
+                                         lpart, ss_part, stream),
+                "decode_front launch");
+        HIP_TRY(st.begin("decode_route"), "event record");
+        HIP_TRY(moe::launch_decode_route(sa, lpart, ss_part, w->logit_bias, w->per_expert_scale, d->rms_eps,
+                                         topk_idx, topk_w, stream),
+                "decode_route launch");
+        HIP_TRY(st.begin("decode_experts_gateup"), "event record");
+        HIP_TRY(moe::launch_decode_experts_gateup(sa, int8, stream), "decode_experts_gateup launch");
+        HIP_TRY(st.begin("decode_down"), "event record");
+        HIP_TRY(moe::launch_decode_down(sa, int8, stream), "decode_down launch");
+        if (norms) {
+            HIP_TRY(st.begin("ffn_post"), "event record");
+            HIP_TRY(moe::launch_ffn_post((const uint16_t*)hres, sa.dpart, sa.part, true, po.inv_row, topk_w, T, H,
+                                         K, g_pd, g_pm, g_p, norms->eps, (uint16_t*)y, stream),
+                    "ffn_post launch");
+        } else {
+            HIP_TRY(st.begin("decode_combine"), "event record");
+            HIP_TRY(moe::launch_decode_combine(sa, stream), "decode_combine launch");
+        }
+    } else {
+        HIP_TRY(st.begin("router"), "event record");
+        HIP_TRY(moe::launch_router_mfma(xb, (const uint16_t*)w->router_scale,
+                                        (const uint16_t*)w->router_w, w->logit_bias,
+                                        w->per_expert_scale, T, H, E, K, d->rms_eps, topk_idx,
+                                        topk_w, at<float>(ws, L.partial), stream),
+                "router launch");
+        HIP_TRY(st.begin("permute"), "event record");
+        HIP_TRY(moe::launch_permute(topk_idx, topk_w, pair_rank, T, K, E, moe::kGemmBM, po, stream),
+                "permute launch");
+        moe::GemmArgs g{};
+        // experts gate/up + GELU: gathered rows of x
+        g.A = xb; g.lda = H; g.a_rows = po.perm_token;
+        g.B = w->expert_gate_up; g.b_group_stride = (int64_t)2 * I * H; g.ldb = H;
+        g.b_scale = int8 ? w->gate_up_scale : nullptr; g.scale_group_stride = 2 * I;
+        g.K = H; g.n_out = I; g.up_off = I;
+        g.mtile_group = po.mtile_group; g.mtile_row0 = po.mtile_row0; g.n_mtiles = po.n_mtiles;
+        g.group_end = po.offsets; g.max_mtiles = L.max_mtiles; g.tiles = po.tiles[0];
+        g.C = h; g.ldc = I;
+        // dense gate/up + GELU, in the same launch
+        moe::GemmArgs gd{};
+        gd.A = xdb; gd.lda = H; gd.B = w->dense_gate_up; gd.ldb = H; gd.K = H;
+        gd.n_out = Id; gd.up_off = Id; gd.M_dense = T; gd.C = hd; gd.ldc = Id;
+        HIP_TRY(st.begin("gemm_gateup"), "event record");
+        HIP_TRY(moe::launch_gemm_gateup(g, &gd, int8, stream), "gemm_gateup launch");
+        // experts down, weighted rows
+        moe::GemmArgs gw{};
+        gw.A = h; gw.lda = I; gw.B = w->expert_down; gw.b_group_stride = (int64_t)H * I; gw.ldb = I;
+        gw.b_scale = int8 ? w->down_scale : nullptr; gw.scale_group_stride = H;
+        gw.K = I; gw.n_out = H;
+        gw.mtile_group = po.mtile_group; gw.mtile_row0 = po.mtile_row0; gw.n_mtiles = po.n_mtiles;
+        gw.group_end = po.offsets; gw.max_mtiles = L.max_mtiles; gw.tiles = po.tiles[1];
+        gw.C = rows; gw.ldc = H; gw.row_w = po.perm_w;
+        // dense down (fp32), in the same launch
+        float* dout = at<float>(ws, L.dout);
+        moe::GemmArgs gc{};
+        gc.A = hd; gc.lda = Id; gc.B = w->dense_down; gc.ldb = Id; gc.K = Id; gc.n_out = H;
+        gc.M_dense = T; gc.Cf = dout; gc.ldc = H;
+        HIP_TRY(st.begin("gemm_down"), "event record");
+        HIP_TRY(moe::launch_gemm_down(gw, &gc, int8, stream), "gemm_down launch");
+        if (norms) {
+            HIP_TRY(st.begin("ffn_post"), "event record");
+            HIP_TRY(moe::launch_ffn_post((const uint16_t*)hres, dout, rows, false, po.inv_row, nullptr, T, H, K,
+                                         g_pd, g_pm, g_p, norms->eps, (uint16_t*)y, stream),
+                    "ffn_post launch");
+        } else {
+            HIP_TRY(st.begin("combine"), "event record");
+            HIP_TRY(moe::launch_combine(dout, rows, po.inv_row, T, H, K, (uint16_t*)y, stream),
+                    "combine launch");
+        }
+    }
+    HIP_TRY(st.end(), "event record");
+
+    if (dbg) {
+        const int64_t TK = (int64_t)T * K;
+        struct { void* dst; const void* src; size_t bytes; } cp[] = {
+            {dbg->topk_idx, topk_idx, (size_t)TK * 4},
+            {dbg->topk_w, topk_w, (size_t)TK * 4},
+            {dbg->counts, po.counts, (size_t)E * 4},
+            {dbg->offsets, po.offsets, (size_t)(E + 1) * 4},
+            {dbg->perm_token, po.perm_token, (size_t)TK * 4},
+            {dbg->inv_row, po.inv_row, (size_t)TK * 4},
+        };
+        for (auto& c : cp)
+            if (c.dst) HIP_TRY(hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyDeviceToDevice, stream),
+                               "debug copy");
+    }
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -231,153 +422,42 @@ int moe_route(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
 int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T, void* y,
               moe_debug* dbg, void* ws, size_t ws_bytes, hipStream_t stream) {
     int rc;
-    if ((rc = check_dims(d)) || (rc = check_T(T)) || (rc = check_weights(w))) return rc;
-    if (w->layout != MOE_LAYOUT_TILED)
-        return fail(MOE_ERR_UNSUPPORTED, "layout=%d: expert and dense weights must be MOE_LAYOUT_TILED "
-                    "(see moe_tile_weights)", w->layout);
+    if ((rc = check_dims(d)) || (rc = check_T(T)) || (rc = check_weights(w)) || (rc = check_tiled(w))) return rc;
     if (T > 0) {  // empty batch: x, y and ws may be NULL
         CHECK_PTR(x, "x", 16);
         CHECK_PTR(y, "y", 16);
         if ((rc = check_ws(d, T, ws, ws_bytes))) return rc;
     }
-    int path = dbg ? dbg->path : MOE_PATH_AUTO;
-    if (path != MOE_PATH_AUTO && path != MOE_PATH_STREAM && path != MOE_PATH_GROUPED)
-        return fail(MOE_ERR_UNSUPPORTED, "unknown path %d", path);
-    if (path == MOE_PATH_AUTO)
-        path = (T <= stream_limit() && stream_fits(*d)) ? MOE_PATH_STREAM : MOE_PATH_GROUPED;
-    if (path == MOE_PATH_STREAM && (T > MOE_STREAM_MAX_TOKENS || !stream_fits(*d)))
-        return fail(MOE_ERR_UNSUPPORTED,
-                    "streaming path needs T <= %d, hidden <= 3072, expert_inter <= 1024, dense_inter <= 4096",
-                    MOE_STREAM_MAX_TOKENS);
-    g_err[0] = 0;
-    if (dbg) {
-        dbg->path_taken = path;
-        dbg->n_stages = 0;
-    }
-    if (T == 0) return MOE_OK;
+    return block_impl(d, w, x, x, T, y, nullptr, nullptr, dbg, ws, stream);
+}
 
-    const Layout L = make_layout(*d, T);
-    const bool int8 = w->expert_dtype == MOE_DTYPE_INT8;
-    const int H = d->hidden, E = d->num_experts, K = d->top_k, I = d->expert_inter, Id = d->dense_inter;
-    int32_t* topk_idx = at<int32_t>(ws, L.topk_idx);
-    float* topk_w = at<float>(ws, L.topk_w);
-    int32_t* pair_rank = at<int32_t>(ws, L.pair_rank);
-    moe::PermuteOut po{};
-    po.tile_counts = at<int32_t>(ws, L.tile_counts);
-    po.counts = at<int32_t>(ws, L.counts);
-    po.offsets = at<int32_t>(ws, L.offsets);
-    po.perm_token = at<int32_t>(ws, L.perm_token);
-    po.perm_w = at<float>(ws, L.perm_w);
-    po.inv_row = at<int32_t>(ws, L.inv_row);
-    po.active = at<int32_t>(ws, L.active);
-    po.n_active = at<int32_t>(ws, L.n_active);
-    po.mtile_group = at<int32_t>(ws, L.mtile_group);
-    po.mtile_row0 = at<int32_t>(ws, L.mtile_row0);
-    po.n_mtiles = at<int32_t>(ws, L.n_mtiles);
-    po.tiles[0] = at<int2>(ws, L.gemm_tiles[0]);
-    po.tiles[1] = at<int2>(ws, L.gemm_tiles[1]);
-    po.n_nt[0] = moe::gemm_n_tiles_gateup(I);
-    po.n_nt[1] = moe::gemm_n_tiles_down(H);
-    po.max_mtiles = L.max_mtiles;
-    uint16_t* h = at<uint16_t>(ws, L.h);
-    uint16_t* hd = at<uint16_t>(ws, L.hd);
-    uint16_t* rows = at<uint16_t>(ws, L.rows);
-    const uint16_t* xb = (const uint16_t*)x;
+size_t moe_ffn_workspace_bytes(const moe_dims* d, int32_t T) {
+    if (check_dims(d) != MOE_OK || check_T(T) != MOE_OK) return 0;
+    return ffn_layout(*d, T).total;
+}
 
-    Stages st{dbg, stream};
-    if (path == MOE_PATH_STREAM) {
-        moe::StreamArgs sa{};
-        sa.T = T; sa.H = H; sa.I = I; sa.Id = Id; sa.K = K; sa.E = E;
-        sa.x = xb;
-        sa.gu = w->expert_gate_up; sa.gu_scale = w->gate_up_scale;
-        sa.dw = w->expert_down; sa.dw_scale = w->down_scale;
-        sa.counts = po.counts; sa.offsets = po.offsets; sa.active = po.active; sa.n_active = po.n_active;
-        sa.perm_token = po.perm_token; sa.perm_w = po.perm_w; sa.inv_row = po.inv_row;
-        sa.topk_w = topk_w;
-        sa.max_active = T * K < E ? T * K : E;
-        sa.dgu = (const uint16_t*)w->dense_gate_up; sa.ddw = (const uint16_t*)w->dense_down;
-        sa.h = h; sa.hd = hd; sa.y = (uint16_t*)y;
-        sa.part = at<float>(ws, L.part); sa.dpart = at<float>(ws, L.dpart);
-        sa.dgu_part = at<float>(ws, L.dgu_part);
-        sa.hpart = at<float>(ws, L.hpart);
-        sa.with_dense = 1;  // the dense MLP's items ride along in K2, K3 and K4
-        HIP_TRY(st.begin("decode_front"), "event record");
-        float* lpart = at<float>(ws, L.lpart);
-        float* ss_part = at<float>(ws, L.ss_part);
-        HIP_TRY(moe::launch_decode_front(sa, (const uint16_t*)w->router_scale, (const uint16_t*)w->router_w,
-                                         lpart, ss_part, stream),
-                "decode_front launch");
-        HIP_TRY(st.begin("decode_route"), "event record");
-        HIP_TRY(moe::launch_decode_route(sa, lpart, ss_part, w->logit_bias, w->per_expert_scale, d->rms_eps,
-                                         topk_idx, topk_w, stream),
-                "decode_route launch");
-        HIP_TRY(st.begin("decode_experts_gateup"), "event record");
-        HIP_TRY(moe::launch_decode_experts_gateup(sa, int8, stream), "decode_experts_gateup launch");
-        HIP_TRY(st.begin("decode_down"), "event record");
-        HIP_TRY(moe::launch_decode_down(sa, int8, stream), "decode_down launch");
-        HIP_TRY(st.begin("decode_combine"), "event record");
-        HIP_TRY(moe::launch_decode_combine(sa, stream), "decode_combine launch");
-    } else {
-        HIP_TRY(st.begin("router"), "event record");
-        HIP_TRY(moe::launch_router_mfma(xb, (const uint16_t*)w->router_scale,
-                                        (const uint16_t*)w->router_w, w->logit_bias,
-                                        w->per_expert_scale, T, H, E, K, d->rms_eps, topk_idx,
-                                        topk_w, at<float>(ws, L.partial), stream),
-                "router launch");
-        HIP_TRY(st.begin("permute"), "event record");
-        HIP_TRY(moe::launch_permute(topk_idx, topk_w, pair_rank, T, K, E, moe::kGemmBM, po, stream),
-                "permute launch");
-        moe::GemmArgs g{};
-        // experts gate/up + GELU: gathered rows of x
-        g.A = xb; g.lda = H; g.a_rows = po.perm_token;
-        g.B = w->expert_gate_up; g.b_group_stride = (int64_t)2 * I * H; g.ldb = H;
-        g.b_scale = int8 ? w->gate_up_scale : nullptr; g.scale_group_stride = 2 * I;
-        g.K = H; g.n_out = I; g.up_off = I;
-        g.mtile_group = po.mtile_group; g.mtile_row0 = po.mtile_row0; g.n_mtiles = po.n_mtiles;
-        g.group_end = po.offsets; g.max_mtiles = L.max_mtiles; g.tiles = po.tiles[0];
-        g.C = h; g.ldc = I;
-        // dense gate/up + GELU, in the same launch
-        moe::GemmArgs gd{};
-        gd.A = xb; gd.lda = H; gd.B = w->dense_gate_up; gd.ldb = H; gd.K = H;
-        gd.n_out = Id; gd.up_off = Id; gd.M_dense = T; gd.C = hd; gd.ldc = Id;
-        HIP_TRY(st.begin("gemm_gateup"), "event record");
-        HIP_TRY(moe::launch_gemm_gateup(g, &gd, int8, stream), "gemm_gateup launch");
-        // experts down, weighted rows
-        moe::GemmArgs gw{};
-        gw.A = h; gw.lda = I; gw.B = w->expert_down; gw.b_group_stride = (int64_t)H * I; gw.ldb = I;
-        gw.b_scale = int8 ? w->down_scale : nullptr; gw.scale_group_stride = H;
-        gw.K = I; gw.n_out = H;
-        gw.mtile_group = po.mtile_group; gw.mtile_row0 = po.mtile_row0; gw.n_mtiles = po.n_mtiles;
-        gw.group_end = po.offsets; gw.max_mtiles = L.max_mtiles; gw.tiles = po.tiles[1];
-        gw.C = rows; gw.ldc = H; gw.row_w = po.perm_w;
-        // dense down (fp32), in the same launch
-        float* dout = at<float>(ws, L.dout);
-        moe::GemmArgs gc{};
-        gc.A = hd; gc.lda = Id; gc.B = w->dense_down; gc.ldb = Id; gc.K = Id; gc.n_out = H;
-        gc.M_dense = T; gc.Cf = dout; gc.ldc = H;
-        HIP_TRY(st.begin("gemm_down"), "event record");
-        HIP_TRY(moe::launch_gemm_down(gw, &gc, int8, stream), "gemm_down launch");
-        HIP_TRY(st.begin("combine"), "event record");
-        HIP_TRY(moe::launch_combine(dout, rows, po.inv_row, T, H, K, (uint16_t*)y, stream),
-                "combine launch");
+int moe_ffn_layer(const moe_dims* d, const moe_weights* w, const moe_ffn_norms* n, const void* h, int32_t T,
+                  void* out, moe_debug* dbg, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int rc;
+    if ((rc = check_dims(d)) || (rc = check_T(T)) || (rc = check_weights(w)) || (rc = check_tiled(w))) return rc;
+    moe_ffn_norms none{};
+    if (!n) n = &none;
+    const void* gains[] = {n->pre_dense, n->pre_moe, n->post_dense, n->post_moe, n->post};
+    const char* names[] = {"pre_dense", "pre_moe", "post_dense", "post_moe", "post"};
+    for (int i = 0; i < 5; ++i)
+        if (gains[i] && !aligned(gains[i], 16)) return fail(MOE_ERR_ALIGN, "norm gain %s is not 16-byte aligned", names[i]);
+    if (!(n->eps >= 0.f) || n->eps > 1.f) return fail(MOE_ERR_SHAPE, "norm eps=%g must be in [0, 1]", (double)n->eps);
+    if (T > 0) {  // empty batch: h, out and ws may be NULL
+        CHECK_PTR(h, "h", 16);
+        CHECK_PTR(out, "out", 16);
+        if (out == h) return fail(MOE_ERR_SHAPE, "out may not alias h");
+        if (!ws) return fail(MOE_ERR_NULL, "workspace is NULL");
+        if (!aligned(ws, 256)) return fail(MOE_ERR_ALIGN, "workspace must be 256-byte aligned");
+        const size_t need = ffn_layout(*d, T).total;
+        if (ws_bytes < need)
+            return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed at T=%d", ws_bytes, need, T);
     }
-    HIP_TRY(st.end(), "event record");
-
-    if (dbg) {
-        const int64_t TK = (int64_t)T * K;
-        struct { void* dst; const void* src; size_t bytes; } cp[] = {
-            {dbg->topk_idx, topk_idx, (size_t)TK * 4},
-            {dbg->topk_w, topk_w, (size_t)TK * 4},
-            {dbg->counts, po.counts, (size_t)E * 4},
-            {dbg->offsets, po.offsets, (size_t)(E + 1) * 4},
-            {dbg->perm_token, po.perm_token, (size_t)TK * 4},
-            {dbg->inv_row, po.inv_row, (size_t)TK * 4},
-        };
-        for (auto& c : cp)
-            if (c.dst) HIP_TRY(hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyDeviceToDevice, stream),
-                               "debug copy");
-    }
-    return MOE_OK;
+    return block_impl(d, w, h, h, T, out, n, h, dbg, ws, stream);
 }
 
 int dense_mlp(const moe_dims* d, const void* dense_gate_up, const void* dense_down, const void* x,
@@ -397,7 +477,7 @@ int dense_mlp(const moe_dims* d, const void* dense_gate_up, const void* dense_do
     if (T <= stream_limit() && stream_fits(*d)) {
         moe::StreamArgs sa{};
         sa.T = T; sa.H = H; sa.I = d->expert_inter; sa.Id = Id; sa.K = d->top_k; sa.E = d->num_experts;
-        sa.x = (const uint16_t*)x; sa.max_active = 0; sa.with_dense = 1; sa.front_dense = 1;
+        sa.x = (const uint16_t*)x; sa.xd = sa.x; sa.max_active = 0; sa.with_dense = 1; sa.front_dense = 1;
         sa.dgu = (const uint16_t*)dense_gate_up; sa.ddw = (const uint16_t*)dense_down;
         sa.hd = hd; sa.y = (uint16_t*)y;
         sa.part = at<float>(ws, L.part); sa.dpart = at<float>(ws, L.dpart);

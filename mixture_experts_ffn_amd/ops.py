@@ -153,6 +153,52 @@ def dense_mlp(dims: BlockDims, dense_gate_up: torch.Tensor, dense_down: torch.Te
     return y
 
 
+@dataclasses.dataclass
+class FfnNorms:
+    """Gains of the layer's feed-forward norms around the block (bf16 [H]
+    device tensors, or None: no norm at that position); see moe_ffn_layer."""
+    pre_dense: Optional[torch.Tensor] = None
+    pre_moe: Optional[torch.Tensor] = None
+    post_dense: Optional[torch.Tensor] = None
+    post_moe: Optional[torch.Tensor] = None
+    post: Optional[torch.Tensor] = None
+    eps: float = 1e-6
+
+    def c(self) -> _abi.MoeFfnNorms:
+        def p(t, name):
+            return None if t is None else _dev(t, name).data_ptr()
+        return _abi.MoeFfnNorms(p(self.pre_dense, "pre_dense"), p(self.pre_moe, "pre_moe"),
+                                p(self.post_dense, "post_dense"), p(self.post_moe, "post_moe"),
+                                p(self.post, "post"), self.eps)
+
+
+def moe_ffn_workspace_bytes(dims: BlockDims, T: int) -> int:
+    n = _lib().moe_ffn_workspace_bytes(ctypes.byref(dims.c()), T)
+    if n == 0:
+        raise MoEError(_abi.MOE_ERR_SHAPE, "moe_ffn_workspace_bytes", _lib().moe_last_error().decode())
+    return n
+
+
+def moe_ffn_layer(dims: BlockDims, weights: LayerWeights, norms: Optional[FfnNorms], h: torch.Tensor,
+                  out=None, debug: Optional[MoeDebug] = None, workspace=None, stream=None) -> torch.Tensor:
+    """The layer's FFN: out = h + N_post(N_post_dense(dense(x_d)) + N_post_moe(moe(x_m)))
+    with x_d, x_m the pre-normed h (bf16 [T, H] in and out)."""
+    h = _dev(h, "h")
+    T = h.shape[0]
+    if out is None:
+        out = torch.empty((T, dims.hidden), dtype=torch.bfloat16, device=h.device)
+    need = moe_ffn_workspace_bytes(dims, T)
+    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=h.device)
+    ws = _dev(ws, "workspace")
+    cn = norms.c() if norms is not None else None
+    rc = _lib().moe_ffn_layer(ctypes.byref(dims.c()), ctypes.byref(weights.c()),
+                              ctypes.byref(cn) if cn is not None else None, h.data_ptr(), T,
+                              _dev(out, "out").data_ptr(), ctypes.byref(debug) if debug is not None else None,
+                              ws.data_ptr(), ws.numel(), _stream(stream))
+    _check(rc, "moe_ffn_layer")
+    return out
+
+
 def moe_quantize_int8(w: torch.Tensor, q=None, scale=None, stream=None):
     """Per-row symmetric int8 of a bf16 tensor [..., cols]: returns (q int8, scale fp32 [...])."""
     w = _dev(w, "w")

@@ -154,3 +154,42 @@ def test_tile_weights_argument_errors(L):
     assert L.moe_tile_weights(FAKE + 8, 32, 128, _abi.MOE_DTYPE_BF16, OTHER, None) == _abi.MOE_ERR_ALIGN
     assert L.moe_tile_weights(FAKE, 32, 128, _abi.MOE_DTYPE_BF16, FAKE, None) == _abi.MOE_ERR_SHAPE
     assert L.moe_tile_weights(FAKE, 0, 128, _abi.MOE_DTYPE_INT8, OTHER, None) == _abi.MOE_OK
+
+
+def test_ffn_layer_argument_errors(L):
+    """moe_ffn_layer: its workspace (the block's plus the two branch inputs)
+    and every error it reports before launching anything."""
+    d = _real()
+    T, H = 8, 2816
+    wsb = L.moe_workspace_bytes(ctypes.byref(d), T)
+    ws = L.moe_ffn_workspace_bytes(ctypes.byref(d), T)
+    assert ws == wsb + 2 * T * H * 2
+    assert L.moe_ffn_workspace_bytes(ctypes.byref(d), -1) == 0
+    norms = _abi.MoeFfnNorms(FAKE, FAKE, FAKE, FAKE, FAKE, 1e-6)
+    ok = dict(h=FAKE, T=T, out=FAKE + (1 << 20), ws=FAKE, ws_bytes=ws)
+
+    def call(n=norms, w=None, dbg=None, **kw):
+        a = dict(ok, **kw)
+        w = w or _weights()
+        return L.moe_ffn_layer(ctypes.byref(d), ctypes.byref(w), ctypes.byref(n) if n is not None else None,
+                               a["h"], a["T"], a["out"], dbg, a["ws"], a["ws_bytes"], None)
+
+    assert call(h=None) == _abi.MOE_ERR_NULL
+    assert call(out=None) == _abi.MOE_ERR_NULL
+    assert call(ws=None) == _abi.MOE_ERR_NULL
+    assert call(out=FAKE) == _abi.MOE_ERR_SHAPE            # out aliases h
+    assert call(h=FAKE + 8) == _abi.MOE_ERR_ALIGN
+    assert call(ws_bytes=ws - 1) == _abi.MOE_ERR_WORKSPACE
+    assert call(ws_bytes=wsb) == _abi.MOE_ERR_WORKSPACE    # the block's alone is too small
+    assert call(n=_abi.MoeFfnNorms(FAKE, FAKE + 2, FAKE, FAKE, FAKE, 1e-6)) == _abi.MOE_ERR_ALIGN
+    assert b"pre_moe" in L.moe_last_error()
+    assert call(n=_abi.MoeFfnNorms(FAKE, FAKE, FAKE, FAKE, FAKE, -1.0)) == _abi.MOE_ERR_SHAPE
+    assert call(w=_weights(layout=_abi.MOE_LAYOUT_ROWS)) == _abi.MOE_ERR_UNSUPPORTED
+    # a forced path that cannot run is refused before the pre-norm launch
+    dbg = _abi.MoeDebug()
+    dbg.path = _abi.MOE_PATH_STREAM
+    wsT = L.moe_ffn_workspace_bytes(ctypes.byref(d), 100)
+    assert call(dbg=ctypes.byref(dbg), T=100, ws_bytes=wsT) == _abi.MOE_ERR_UNSUPPORTED
+    # an empty batch is a valid no-op, with or without gains
+    assert call(T=0, h=None, out=None, ws=None, ws_bytes=0) == _abi.MOE_OK
+    assert call(n=None, T=0, h=None, out=None, ws=None, ws_bytes=0) == _abi.MOE_OK

@@ -15,9 +15,9 @@ import torch
 
 import moe_synth
 import oracle
-from mixture_experts_ffn_amd import (MOE_PATH_GROUPED, MOE_PATH_STREAM, BlockCall, MoEError, dense_mlp,
-                                     moe_block, moe_quantize_int8, moe_route, moe_tile_weights,
-                                     moe_workspace_bytes, new_debug)
+from mixture_experts_ffn_amd import (MOE_PATH_GROUPED, MOE_PATH_STREAM, BlockCall, FfnNorms, MoEError,
+                                     dense_mlp, moe_block, moe_ffn_layer, moe_quantize_int8, moe_route,
+                                     moe_tile_weights, moe_workspace_bytes, new_debug)
 from gpu_util import (REL_BF16, REL_INT8, bf16_dev, check_routing, compare_y, dims_of,
                       oracle_int8_weights, routing_for, to_np, upload, y_f64)
 
@@ -327,4 +327,55 @@ def test_graph_replay(dev, name, path):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y_g, y_eager), f"replay {rep} differs from the eager result"
+
+
+# ---------------------------------------------------------------- the layer's FFN around the block
+FFN_SETS = {"all": oracle.FFN_NORMS, "post_only": ("post",), "pre_moe": ("pre_moe", "post_moe"), "none": ()}
+
+
+@pytest.mark.parametrize("name,path,which", [
+    ("tiny", MOE_PATH_STREAM, "all"), ("tiny", MOE_PATH_GROUPED, "all"), ("tiny", MOE_PATH_GROUPED, "none"),
+    ("decode", MOE_PATH_STREAM, "all"), ("decode", MOE_PATH_STREAM, "post_only"),
+    ("decode", MOE_PATH_GROUPED, "pre_moe"), ("prefill", MOE_PATH_GROUPED, "all")])
+def test_ffn_layer(dev, name, path, which):
+    """moe_ffn_layer against the oracle's ffn_layer. Routing as in the block
+    tests (on the MoE branch's input); the output compared whole and, since
+    the residual dominates it, also minus h, with the rounding of the output
+    to bf16 (half an ulp, 2^-9 relative) added to the bound."""
+    wl, w, x, lw, xd = inputs(name, dev)
+    s = wl.shape
+    K, H = s.top_k, s.hidden
+    say(f"case: ffn layer {name} path={path} norms={which}")
+    rng = np.random.default_rng(7)
+    gains = {k: moe_synth.f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal(H)).astype(np.float32))
+             for k in oracle.FFN_NORMS}
+    sel = FFN_SETS[which]
+    eps = 1e-5
+    norms_np = {**{k: (gains[k] if k in sel else None) for k in oracle.FFN_NORMS}, "eps": eps}
+    norms = FfnNorms(**{k: (torch.from_numpy(gains[k].view(np.int16)).view(torch.bfloat16).to(dev)
+                            if k in sel else None) for k in oracle.FFN_NORMS}, eps=eps)
+    T = xd.shape[0]
+    out_t = dict(topk_idx=torch.empty((T, K), dtype=torch.int32, device=dev),
+                 topk_w=torch.empty((T, K), dtype=torch.float32, device=dev))
+    dbg = new_debug(path, **out_t)
+    out = moe_ffn_layer(dims_of(s), lw, norms, xd, debug=dbg)
+    torch.cuda.synchronize()
+    assert dbg.path_taken == path
+    toks = np.arange(T) if T <= 64 else sample_tokens(T, n=16, seed=5)
+    gi, gw = to_np(out_t["topk_idx"])[toks], to_np(out_t["topk_w"])[toks]
+    _, ref_r = oracle.ffn_layer(x[toks], w, norms_np, K, s.rms_eps)
+    check_routing(gi, gw, ref_r, w["per_expert_scale"])
+    ref, _ = oracle.ffn_layer(x[toks], w, norms_np, K, s.rms_eps,
+                              routing=routing_for(gi, ref_r, w["per_expert_scale"]))
+    got = y_f64(out)[toks]
+    h64 = oracle.bf16_to_f64(x[toks])
+    compare_y(got, ref, REL_BF16)
+    # the branches' part alone: its rel-L2 error may grow by the output's rounding
+    # (2^-9 of |out| per element) and its cosine falls accordingly (1 - rel^2 / 2)
+    branch_ref = ref - h64
+    bound = REL_BF16 + 2.0**-9 * np.linalg.norm(ref) / np.linalg.norm(branch_ref)
+    a, b = (got - h64).ravel(), branch_ref.ravel()
+    rel = float(np.linalg.norm(a - b) / np.linalg.norm(b))
+    cos = float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+    assert rel <= bound and cos >= 1.0 - bound * bound / 2, f"branches: rel-L2 {rel:.3g} (bound {bound:.3g}), cos {cos:.6f}"
 
