@@ -227,6 +227,25 @@ def run_workload(name, steps, warmup, layers, dev, ev: HipEvents, log):
     ms_graph = (time.perf_counter() - t_g) * 1e3 / (reps * layers)
     del graph
 
+    # the layer's FFN around the block (all five feed-forward norms present):
+    # the same steps through moe_ffn_layer, for the cost of the norms and residual
+    from mixture_experts_ffn_amd import FfnCall, FfnNorms
+    rng = np.random.default_rng(wl.seed)
+    gains = {k: bf(moe_synth.f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal(s.hidden)).astype(np.float32)))
+             for k in ("pre_dense", "pre_moe", "post_dense", "post_moe", "post")}
+    norms = FfnNorms(**gains, eps=1e-6)
+    out_ffn = torch.empty_like(y)
+    ffn_calls = [FfnCall(dims, c, norms, xd, out=out_ffn) for c in copies]
+    for i in range(warmup):
+        ffn_calls[i % layers]()
+    torch.cuda.synchronize()
+    t_f = time.perf_counter()
+    for i in range(steps):
+        ffn_calls[i % layers]()
+    torch.cuda.synchronize()
+    ms_ffn = (time.perf_counter() - t_f) * 1e3 / steps
+    del ffn_calls
+
     # dominant kernel: HIP events on the library's stream around that kernel in
     # every step of a second timed run (an event marker costs a few us of
     # stream time, so it is kept out of the run above)
@@ -249,6 +268,8 @@ def run_workload(name, steps, warmup, layers, dev, ev: HipEvents, log):
         "workload": name, "T": T, "path": {1: "stream", 2: "grouped"}.get(path, path),
         "ms_per_step": ms_step, "tokens_per_s": T / (ms_step * 1e-3),
         "graph": {"ms_per_step": ms_graph, "tokens_per_s": T / (ms_graph * 1e-3)},
+        "ffn_layer": {"ms_per_step": ms_ffn, "tokens_per_s": T / (ms_ffn * 1e-3),
+                      "note": "moe_ffn_layer: the block with all five feed-forward norms and the residual"},
         "experts_touched": n_active, "max_rows_per_expert": int(cnt.max()),
         "block_bytes": work["bytes"], "block_flops": work["flops"],
         "block_gbs": work["bytes"] / (ms_step * 1e-3) / 1e9,
@@ -261,7 +282,8 @@ def run_workload(name, steps, warmup, layers, dev, ev: HipEvents, log):
     }
     res["block_hbm_frac"] = res["block_gbs"] / HBM_PEAK_GBS
     res["block_mfma_frac"] = res["block_tflops"] / MFMA_BF16_PEAK_TFLOPS
-    log(f"[bench] {name}: {ms_step * 1e3:.1f} us/step ({ms_graph * 1e3:.1f} replayed from a graph), "
+    log(f"[bench] {name}: {ms_step * 1e3:.1f} us/step ({ms_graph * 1e3:.1f} replayed from a graph; "
+        f"with the FFN norms and residual {ms_ffn * 1e3:.1f}), "
         f"{res['tokens_per_s']:.0f} tok/s, "
         f"{res['block_gbs']:.0f} GB/s, dominant {dom_name} {dom_ms * 1e3:.1f} us, stages {res['stages_us']} "
         f"GB/s {res['stages_gbs']}")
@@ -396,6 +418,7 @@ def main():
                    "layers_cycled": args.layers, "path": primary["path"]},
         "roofline": roof,
         "graph": primary["graph"],
+        "ffn_layer": primary["ffn_layer"],
         "block": {k: primary[k] for k in ("block_bytes", "block_gbs", "block_hbm_frac", "block_flops",
                                           "block_tflops", "block_mfma_frac", "experts_touched",
                                           "stages_us", "stages_gbs", "dominant")},
@@ -403,7 +426,8 @@ def main():
     if args.workload == "decode" and not args.no_prefill:
         pre = run_workload("prefill", max(10, args.steps // 4), max(3, args.warmup // 4), args.layers,
                            dev, ev, log)
-        out["prefill"] = {k: pre[k] for k in ("T", "path", "ms_per_step", "tokens_per_s", "graph", "block_gbs",
+        out["prefill"] = {k: pre[k] for k in ("T", "path", "ms_per_step", "tokens_per_s", "graph", "ffn_layer",
+                                              "block_gbs",
                                               "block_hbm_frac", "block_tflops", "block_mfma_frac",
                                               "experts_touched", "stages_us", "stages_gbs", "dominant")}
         out["prefill"]["roofline"] = roofline_for(pre, "mfma")

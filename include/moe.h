@@ -197,8 +197,9 @@ typedef struct moe_ffn_norms {
  * add, and out is rounded once to bf16. h, out [T, H] bf16 (out may not alias
  * h); n as above (NULL: every norm absent, the residual kept); ws as for
  * moe_block (moe_ffn_workspace_bytes: its size); dbg as for moe_block, its
- * routing being that of x_m. Errors as for moe_block, plus MOE_ERR_ALIGN for a
- * misaligned gain. */
+ * routing being that of x_m. hidden <= 16384. Errors as for moe_block, plus
+ * MOE_ERR_ALIGN for a misaligned gain and MOE_ERR_UNSUPPORTED for a larger
+ * hidden size. */
 size_t moe_ffn_workspace_bytes(const moe_dims* d, int32_t T);
 int moe_ffn_layer(const moe_dims* d, const moe_weights* w, const moe_ffn_norms* n, const void* h,
                   int32_t T, void* out, moe_debug* dbg, void* ws, size_t ws_bytes, hipStream_t stream);

@@ -6,9 +6,9 @@
 //   out = h + N_post(N_post_dense(dense) + N_post_moe(moe)),
 // the branches run on x_d = bf16(N_pre_dense(h)) and x_m = bf16(N_pre_moe(h)),
 // N_g(v) = v / sqrt(mean(v^2) + eps) * g per token (absent gain: no norm).
-// Both kernels take one token row per workgroup: the row's sums of squares are
-// workgroup reductions in a fixed order, and everything stays fp32 until the
-// single rounding of each output.
+// Both kernels take one token row per workgroup (hidden sizes up to kFMaxH):
+// the row's sums of squares are workgroup reductions in a fixed order, and
+// everything stays fp32 until the single rounding of each output.
 #include "common.h"
 #include "kernels.h"
 #include "topk.h"
@@ -17,19 +17,28 @@ namespace moe {
 
 namespace {
 
-constexpr int kFT = 256;  // threads per token row
-constexpr int kFWaves = kFT / kWave;
+// A workgroup of NT threads per token row holds the row in registers, kFR
+// four-value pieces a thread: hidden sizes up to 4 kFR NT. Small batches take
+// 1024 threads a row (more loads in flight for few rows), larger ones 256 (more
+// rows resident per CU).
+constexpr int kFR = 4;
+constexpr int kFMaxH = 4 * kFR * 1024;
 
-// the workgroup's sum of one value per thread (wavefront sums, then the
-// wavefronts in order); every thread gets it
-__device__ __forceinline__ float row_sum(float v, float* red) {
-    v = wave_sum<kWave>(v);
+// the workgroup's sums of two values per thread (wavefront sums, then the
+// wavefronts in order); every thread gets them
+template <int NT>
+__device__ __forceinline__ float2 row_sum2(float a, float b, float2* red) {
+    a = wave_sum<kWave>(a);
+    b = wave_sum<kWave>(b);
     __syncthreads();  // red is free (a previous sum has been read)
-    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = make_float2(a, b);
     __syncthreads();
-    float s = red[0];
+    float2 s = red[0];
 #pragma unroll
-    for (int w = 1; w < kFWaves; ++w) s += red[w];
+    for (int w = 1; w < NT / kWave; ++w) {
+        s.x += red[w].x;
+        s.y += red[w].y;
+    }
     return s;
 }
 
@@ -37,48 +46,53 @@ __device__ __forceinline__ float inv_rms(float ss, int H, float eps) {
     return 1.0f / sqrtf(ss / (float)H + eps);
 }
 
-// x_d, x_m of token blockIdx.x (each only if its gain is given)
-__global__ __launch_bounds__(kFT) void ffn_prenorm_kernel(const uint16_t* __restrict__ h, int H,
+// x_d, x_m of token blockIdx.x (each only if its gain is given). Each thread
+// holds its (at most kFR) four-value pieces of the row in registers: the row
+// is read once.
+template <int NT>
+__global__ __launch_bounds__(NT) void ffn_prenorm_kernel(const uint16_t* __restrict__ h, int H,
                                                           const uint16_t* __restrict__ gd,
                                                           const uint16_t* __restrict__ gm, float eps,
                                                           uint16_t* __restrict__ xd, uint16_t* __restrict__ xm) {
-    __shared__ float red[kFWaves];
+    __shared__ float2 red[NT / kWave];
     const int64_t base = (int64_t)blockIdx.x * H;
-    const uint4* row = reinterpret_cast<const uint4*>(h + base);
-    const int n8 = H >> 3;
+    const uint2* row = reinterpret_cast<const uint2*>(h + base);
+    const int n4 = H >> 2;
+    uint2 v[kFR];
     float ss = 0.f;
-    for (int c = threadIdx.x; c < n8; c += kFT) {
-        float f[8];
-        unpack8(row[c], f);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ss += f[i] * f[i];
+    for (int q = 0; q < kFR; ++q) {
+        const int c = threadIdx.x + q * NT;
+        v[q] = c < n4 ? row[c] : make_uint2(0u, 0u);
+        const float f0 = bf16_lo(v[q].x), f1 = bf16_hi(v[q].x), f2 = bf16_lo(v[q].y), f3 = bf16_hi(v[q].y);
+        ss += f0 * f0 + f1 * f1 + f2 * f2 + f3 * f3;
     }
-    const float rn = inv_rms(row_sum(ss, red), H, eps);
-    for (int c = threadIdx.x; c < n8; c += kFT) {
-        float f[8];
-        unpack8(row[c], f);
+    const float rn = inv_rms(row_sum2<NT>(ss, 0.f, red).x, H, eps);
+#pragma unroll
+    for (int q = 0; q < kFR; ++q) {
+        const int c = threadIdx.x + q * NT;
+        if (c >= n4) continue;
+        const float f0 = bf16_lo(v[q].x), f1 = bf16_hi(v[q].x), f2 = bf16_lo(v[q].y), f3 = bf16_hi(v[q].y);
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const uint16_t* g = b ? gm : gd;
             uint16_t* dst = b ? xm : xd;
             if (!g) continue;  // uniform
-            float gv[8];
-            unpack8(reinterpret_cast<const uint4*>(g)[c], gv);
-            uint32_t o[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                o[i] = pack_bf16x2(f[2 * i] * rn * gv[2 * i], f[2 * i + 1] * rn * gv[2 * i + 1]);
-            reinterpret_cast<uint4*>(dst + base)[c] = make_uint4(o[0], o[1], o[2], o[3]);
+            const uint2 gv = reinterpret_cast<const uint2*>(g)[c];
+            reinterpret_cast<uint2*>(dst + base)[c] =
+                make_uint2(pack_bf16x2(f0 * rn * bf16_lo(gv.x), f1 * rn * bf16_hi(gv.x)),
+                           pack_bf16x2(f2 * rn * bf16_lo(gv.y), f3 * rn * bf16_hi(gv.y)));
         }
     }
 }
 
 // out for token t = blockIdx.x. The MoE branch of the token is the sum over
 // k (in k order) of its rows rows[inv_row[t K + k]]: fp32 rows times topk_w
-// (F32ROWS) or bf16 rows already weighted. LDS holds the fp32 dense and MoE
-// rows, then their normed sum.
-template <bool F32ROWS>
-__global__ __launch_bounds__(kFT) void ffn_post_kernel(const uint16_t* __restrict__ h,
+// (F32ROWS) or bf16 rows already weighted. Each thread keeps its (at most
+// kFR) four-value pieces of the dense and MoE rows in registers; the two
+// branches' sums of squares are one reduction, their normed sum's another.
+template <int NT, bool F32ROWS>
+__global__ __launch_bounds__(NT) void ffn_post_kernel(const uint16_t* __restrict__ h,
                                                        const float* __restrict__ dense,
                                                        const void* __restrict__ rows,
                                                        const int32_t* __restrict__ inv_row,
@@ -87,10 +101,10 @@ __global__ __launch_bounds__(kFT) void ffn_post_kernel(const uint16_t* __restric
                                                        const uint16_t* __restrict__ gpm,
                                                        const uint16_t* __restrict__ gp, float eps,
                                                        uint16_t* __restrict__ out) {
-    extern __shared__ float buf[];  // [2][H]
-    __shared__ float red[kFWaves];
+    __shared__ float2 red[NT / kWave];
     const int t = blockIdx.x;
     const int64_t base = (int64_t)t * H;
+    const int n4 = H >> 2;
     int p[kMaxTopK];
     float wk[kMaxTopK];
 #pragma unroll
@@ -98,10 +112,16 @@ __global__ __launch_bounds__(kFT) void ffn_post_kernel(const uint16_t* __restric
         p[k] = inv_row[(int64_t)t * K + min(k, K - 1)];
         wk[k] = F32ROWS ? topk_w[(int64_t)t * K + min(k, K - 1)] : 1.f;
     }
+    float d[kFR][4], m[kFR][4];
     float ssd = 0.f, ssm = 0.f;
-    for (int c = threadIdx.x * 4; c < H; c += kFT * 4) {
-        const float4 d = *reinterpret_cast<const float4*>(dense + base + c);
-        float m[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < kFR; ++q) {
+        const int c4 = threadIdx.x + q * NT;
+        const int c = min(c4, n4 - 1) * 4;  // past the row: a repeat of its last piece, never stored
+        const float4 dv = *reinterpret_cast<const float4*>(dense + base + c);
+        d[q][0] = dv.x; d[q][1] = dv.y; d[q][2] = dv.z; d[q][3] = dv.w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m[q][i] = 0.f;
 #pragma unroll
         for (int k = 0; k < kMaxTopK; ++k) {
             if (k < K) {
@@ -117,42 +137,69 @@ __global__ __launch_bounds__(kFT) void ffn_post_kernel(const uint16_t* __restric
                     r[2] = bf16_lo(v.y); r[3] = bf16_hi(v.y);
                 }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) m[i] += F32ROWS ? wk[k] * r[i] : r[i];
+                for (int i = 0; i < 4; ++i) m[q][i] += F32ROWS ? wk[k] * r[i] : r[i];
             }
         }
-        buf[c] = d.x; buf[c + 1] = d.y; buf[c + 2] = d.z; buf[c + 3] = d.w;
-        ssd += d.x * d.x + d.y * d.y + d.z * d.z + d.w * d.w;
+        if (c4 < n4) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            buf[H + c + i] = m[i];
-            ssm += m[i] * m[i];
+            for (int i = 0; i < 4; ++i) {
+                ssd += d[q][i] * d[q][i];
+                ssm += m[q][i] * m[q][i];
+            }
         }
     }
-    __syncthreads();  // the rows in LDS are read below by other threads than wrote them
-    const float rnd = gpd ? inv_rms(row_sum(ssd, red), H, eps) : 1.f;
-    const float rnm = gpm ? inv_rms(row_sum(ssm, red), H, eps) : 1.f;
-    float sss = 0.f;
-    for (int c = threadIdx.x; c < H; c += kFT) {
-        const float gd = gpd ? bf16_to_f32(gpd[c]) : 1.f;
-        const float gm = gpm ? bf16_to_f32(gpm[c]) : 1.f;
-        const float s = buf[c] * rnd * gd + buf[H + c] * rnm * gm;
-        buf[c] = s;
-        sss += s * s;
+    float rnd = 1.f, rnm = 1.f;
+    if (gpd || gpm) {  // uniform
+        const float2 ss = row_sum2<NT>(ssd, ssm, red);
+        if (gpd) rnd = inv_rms(ss.x, H, eps);
+        if (gpm) rnm = inv_rms(ss.y, H, eps);
     }
-    const float rns = gp ? inv_rms(row_sum(sss, red), H, eps) : 1.f;
-    for (int c = threadIdx.x; c < H; c += kFT) {
-        const float g = gp ? bf16_to_f32(gp[c]) : 1.f;
-        const float hv = bf16_to_f32(h[base + c]);
-        out[base + c] = f32_to_bf16(hv + buf[c] * rns * g);
+    float sss = 0.f;
+#pragma unroll
+    for (int q = 0; q < kFR; ++q) {
+        const int c4 = threadIdx.x + q * NT;
+        const int c = min(c4, n4 - 1) * 4;
+        const uint2 gdv = gpd ? *reinterpret_cast<const uint2*>(gpd + c) : make_uint2(0x3F803F80u, 0x3F803F80u);
+        const uint2 gmv = gpm ? *reinterpret_cast<const uint2*>(gpm + c) : make_uint2(0x3F803F80u, 0x3F803F80u);
+        const float gdf[4] = {bf16_lo(gdv.x), bf16_hi(gdv.x), bf16_lo(gdv.y), bf16_hi(gdv.y)};
+        const float gmf[4] = {bf16_lo(gmv.x), bf16_hi(gmv.x), bf16_lo(gmv.y), bf16_hi(gmv.y)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            d[q][i] = d[q][i] * rnd * gdf[i] + m[q][i] * rnm * gmf[i];  // the branches' sum
+            if (c4 < n4) sss += d[q][i] * d[q][i];
+        }
+    }
+    const float rns = gp ? inv_rms(row_sum2<NT>(sss, 0.f, red).x, H, eps) : 1.f;
+#pragma unroll
+    for (int q = 0; q < kFR; ++q) {
+        const int c4 = threadIdx.x + q * NT;
+        if (c4 >= n4) continue;
+        const int c = c4 * 4;
+        const uint2 gv = gp ? *reinterpret_cast<const uint2*>(gp + c) : make_uint2(0x3F803F80u, 0x3F803F80u);
+        const uint2 hv = *reinterpret_cast<const uint2*>(h + base + c);
+        const float g[4] = {bf16_lo(gv.x), bf16_hi(gv.x), bf16_lo(gv.y), bf16_hi(gv.y)};
+        const float hf[4] = {bf16_lo(hv.x), bf16_hi(hv.x), bf16_lo(hv.y), bf16_hi(hv.y)};
+        *reinterpret_cast<uint2*>(out + base + c) =
+            make_uint2(pack_bf16x2(hf[0] + d[q][0] * rns * g[0], hf[1] + d[q][1] * rns * g[1]),
+                       pack_bf16x2(hf[2] + d[q][2] * rns * g[2], hf[3] + d[q][3] * rns * g[3]));
     }
 }
 
 }  // namespace
 
+namespace {
+// threads per token row for a launch of T rows of H values
+int ffn_threads(int T, int H) { return (T >= 512 && H <= 4 * kFR * 256) ? 256 : 1024; }
+}  // namespace
+
 hipError_t launch_ffn_prenorm(const uint16_t* h, int T, int H, const uint16_t* gd, const uint16_t* gm, float eps,
                               uint16_t* xd, uint16_t* xm, hipStream_t stream) {
     if (T <= 0 || (!gd && !gm)) return hipSuccess;
-    hipLaunchKernelGGL(ffn_prenorm_kernel, dim3(T), dim3(kFT), 0, stream, h, H, gd, gm, eps, xd, xm);
+    if (H > kFMaxH) return hipErrorInvalidValue;
+    if (ffn_threads(T, H) == 256)
+        hipLaunchKernelGGL(ffn_prenorm_kernel<256>, dim3(T), dim3(256), 0, stream, h, H, gd, gm, eps, xd, xm);
+    else
+        hipLaunchKernelGGL(ffn_prenorm_kernel<1024>, dim3(T), dim3(1024), 0, stream, h, H, gd, gm, eps, xd, xm);
     return hipGetLastError();
 }
 
@@ -161,13 +208,19 @@ hipError_t launch_ffn_post(const uint16_t* h, const float* dense, const void* ro
                            const uint16_t* gpd, const uint16_t* gpm, const uint16_t* gp, float eps, uint16_t* out,
                            hipStream_t stream) {
     if (T <= 0) return hipSuccess;
-    const size_t lds = (size_t)2 * H * sizeof(float);
-    if (f32_rows)
-        hipLaunchKernelGGL(ffn_post_kernel<true>, dim3(T), dim3(kFT), lds, stream, h, dense, rows, inv_row, topk_w,
-                           H, K, gpd, gpm, gp, eps, out);
-    else
-        hipLaunchKernelGGL(ffn_post_kernel<false>, dim3(T), dim3(kFT), lds, stream, h, dense, rows, inv_row, topk_w,
-                           H, K, gpd, gpm, gp, eps, out);
+    if (H > kFMaxH) return hipErrorInvalidValue;
+#define MOE_FFN_POST(NT, F32)                                                                              \
+    hipLaunchKernelGGL((ffn_post_kernel<NT, F32>), dim3(T), dim3(NT), 0, stream, h, dense, rows, inv_row, \
+                       topk_w, H, K, gpd, gpm, gp, eps, out)
+    const bool small = ffn_threads(T, H) == 256;
+    if (f32_rows) {
+        if (small) MOE_FFN_POST(256, true);
+        else MOE_FFN_POST(1024, true);
+    } else {
+        if (small) MOE_FFN_POST(256, false);
+        else MOE_FFN_POST(1024, false);
+    }
+#undef MOE_FFN_POST
     return hipGetLastError();
 }
 

@@ -440,6 +440,8 @@ int moe_ffn_layer(const moe_dims* d, const moe_weights* w, const moe_ffn_norms* 
                   void* out, moe_debug* dbg, void* ws, size_t ws_bytes, hipStream_t stream) {
     int rc;
     if ((rc = check_dims(d)) || (rc = check_T(T)) || (rc = check_weights(w)) || (rc = check_tiled(w))) return rc;
+    if (d->hidden > 16384)
+        return fail(MOE_ERR_UNSUPPORTED, "hidden=%d: the feed-forward norms take hidden <= 16384", d->hidden);
     moe_ffn_norms none{};
     if (!n) n = &none;
     const void* gains[] = {n->pre_dense, n->pre_moe, n->post_dense, n->post_moe, n->post};

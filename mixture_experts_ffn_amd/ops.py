@@ -270,6 +270,33 @@ class BlockCall:
         return self.y
 
 
+class FfnCall:
+    """moe_ffn_layer with its arguments marshalled once, for repeated calls on
+    the same tensors."""
+
+    def __init__(self, dims: BlockDims, weights: LayerWeights, norms: Optional[FfnNorms], h: torch.Tensor,
+                 out=None, workspace=None):
+        self.h = _dev(h, "h")
+        self.T = h.shape[0]
+        self.out = out if out is not None else torch.empty((self.T, dims.hidden), dtype=torch.bfloat16,
+                                                           device=h.device)
+        need = moe_ffn_workspace_bytes(dims, self.T)
+        self.ws = _dev(workspace if workspace is not None
+                       else torch.empty(need, dtype=torch.uint8, device=h.device), "workspace")
+        self.weights, self.norms = weights, norms  # keep the tensors alive
+        self._dims = dims.c()
+        self._w = weights.c()
+        self._n = norms.c() if norms is not None else None
+
+    def __call__(self, debug: Optional[MoeDebug] = None, stream=None) -> torch.Tensor:
+        rc = _lib().moe_ffn_layer(ctypes.byref(self._dims), ctypes.byref(self._w),
+                                  ctypes.byref(self._n) if self._n is not None else None, self.h.data_ptr(),
+                                  self.T, self.out.data_ptr(), ctypes.byref(debug) if debug is not None else None,
+                                  self.ws.data_ptr(), self.ws.numel(), _stream(stream))
+        _check(rc, "moe_ffn_layer")
+        return self.out
+
+
 def new_debug(path: int = _abi.MOE_PATH_AUTO, **outputs) -> MoeDebug:
     """A moe_debug struct; keyword arguments name device tensors for its outputs."""
     d = MoeDebug()
