@@ -246,6 +246,26 @@ def run_workload(name, steps, warmup, layers, dev, ev: HipEvents, log):
     ms_ffn = (time.perf_counter() - t_f) * 1e3 / steps
     del ffn_calls
 
+    # a prompt longer than one prefill chunk: the same steps through the
+    # chunked driver (consecutive chunks of the default size, one workspace)
+    chunked = None
+    from mixture_experts_ffn_amd import moe_prefill_chunk_tokens, moe_prefill_chunked, moe_prefill_workspace_bytes
+    C = moe_prefill_chunk_tokens(0)
+    if T > C:
+        ws_c = torch.empty(moe_prefill_workspace_bytes(dims, C), dtype=torch.uint8, device=dev)
+        for i in range(warmup):
+            moe_prefill_chunked(dims, copies[i % layers], None, xd, C, out=y, workspace=ws_c)
+        torch.cuda.synchronize()
+        t_c = time.perf_counter()
+        for i in range(steps):
+            moe_prefill_chunked(dims, copies[i % layers], None, xd, C, out=y, workspace=ws_c)
+        torch.cuda.synchronize()
+        ms_c = (time.perf_counter() - t_c) * 1e3 / steps
+        chunked = {"ms_per_step": ms_c, "tokens_per_s": T / (ms_c * 1e-3), "chunk": C,
+                   "workspace_bytes": ws_c.numel(), "unchunked_workspace_bytes": ws.numel(),
+                   "note": "moe_prefill_chunked: the block over consecutive chunks, one chunk's workspace"}
+        del ws_c
+
     # dominant kernel: HIP events on the library's stream around that kernel in
     # every step of a second timed run (an event marker costs a few us of
     # stream time, so it is kept out of the run above)
@@ -270,6 +290,7 @@ def run_workload(name, steps, warmup, layers, dev, ev: HipEvents, log):
         "graph": {"ms_per_step": ms_graph, "tokens_per_s": T / (ms_graph * 1e-3)},
         "ffn_layer": {"ms_per_step": ms_ffn, "tokens_per_s": T / (ms_ffn * 1e-3),
                       "note": "moe_ffn_layer: the block with all five feed-forward norms and the residual"},
+        **({"chunked": chunked} if chunked else {}),
         "experts_touched": n_active, "max_rows_per_expert": int(cnt.max()),
         "block_bytes": work["bytes"], "block_flops": work["flops"],
         "block_gbs": work["bytes"] / (ms_step * 1e-3) / 1e9,
@@ -283,7 +304,8 @@ def run_workload(name, steps, warmup, layers, dev, ev: HipEvents, log):
     res["block_hbm_frac"] = res["block_gbs"] / HBM_PEAK_GBS
     res["block_mfma_frac"] = res["block_tflops"] / MFMA_BF16_PEAK_TFLOPS
     log(f"[bench] {name}: {ms_step * 1e3:.1f} us/step ({ms_graph * 1e3:.1f} replayed from a graph; "
-        f"with the FFN norms and residual {ms_ffn * 1e3:.1f}), "
+        f"with the FFN norms and residual {ms_ffn * 1e3:.1f}"
+        + (f"; in {C}-token chunks {chunked['ms_per_step'] * 1e3:.1f}" if chunked else "") + "), "
         f"{res['tokens_per_s']:.0f} tok/s, "
         f"{res['block_gbs']:.0f} GB/s, dominant {dom_name} {dom_ms * 1e3:.1f} us, stages {res['stages_us']} "
         f"GB/s {res['stages_gbs']}")

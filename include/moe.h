@@ -204,6 +204,30 @@ size_t moe_ffn_workspace_bytes(const moe_dims* d, int32_t T);
 int moe_ffn_layer(const moe_dims* d, const moe_weights* w, const moe_ffn_norms* n, const void* h,
                   int32_t T, void* out, moe_debug* dbg, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Chunked prefill ([TT] "Configurable knobs": a long prompt is prefilled in
+ * bounded token chunks, 16384 by default, the size snapped to a multiple of the
+ * 1024-token sliding window and capped at 32768, so that peak prefill memory
+ * does not grow with the prompt).
+ * moe_prefill_chunk_tokens: the chunk size used for a requested one: <= 0 gives
+ * 16384; otherwise rounded down to a multiple of 1024, at least 1024 and at
+ * most 32768. Host arithmetic only.
+ * moe_prefill_workspace_bytes: workspace for chunks of that size (the layer's,
+ * which covers the block's), 0 on invalid dims.
+ * moe_prefill_chunked: runs consecutive chunks of h [T, H] (the last one
+ * ragged) through the block on `stream`, one after another, reusing ws.
+ * n == NULL: out = moe_block(h) per chunk; n != NULL: out = moe_ffn_layer(h, n)
+ * per chunk. Each token's result depends only on that token, so the output
+ * equals the per-chunk calls bit for bit; each chunk takes the path moe_block
+ * would take at its size. out [T, H] bf16, may not alias h. ws must hold
+ * moe_prefill_workspace_bytes(d, chunk) bytes for chunk =
+ * moe_prefill_chunk_tokens(chunk_tokens) (less when T is smaller: the
+ * workspace of min(T, chunk) tokens). Errors as for moe_ffn_layer. */
+int32_t moe_prefill_chunk_tokens(int32_t chunk_tokens);
+size_t moe_prefill_workspace_bytes(const moe_dims* d, int32_t chunk_tokens);
+int moe_prefill_chunked(const moe_dims* d, const moe_weights* w, const moe_ffn_norms* n, const void* h,
+                        int32_t T, int32_t chunk_tokens, void* out, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
 /* Per-row symmetric int8 quantisation of a bf16 matrix [rows, cols], as the
  * int8 build quantises the fused expert weights when it loads them ([INT8]
  * "How it works"): scale[r] = max_c |w[r,c]| / 127 (fp32), q[r,c] =

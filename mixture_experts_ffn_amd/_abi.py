@@ -72,6 +72,7 @@ class MoeFfnNorms(ctypes.Structure):
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_block", "dense_mlp",
            "moe_ffn_workspace_bytes", "moe_ffn_layer",
+           "moe_prefill_chunk_tokens", "moe_prefill_workspace_bytes", "moe_prefill_chunked",
            "moe_quantize_int8", "moe_tile_weights", "moe_last_error")
 
 _lib = None
@@ -102,6 +103,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.moe_ffn_layer.argtypes = [P(MoeDims), P(MoeWeights), P(MoeFfnNorms), vp, i32, vp, P(MoeDebug), vp, sz,
                                   vp]
     lib.moe_ffn_layer.restype = ctypes.c_int
+    lib.moe_prefill_chunk_tokens.argtypes = [i32]
+    lib.moe_prefill_chunk_tokens.restype = i32
+    lib.moe_prefill_workspace_bytes.argtypes = [P(MoeDims), i32]
+    lib.moe_prefill_workspace_bytes.restype = sz
+    lib.moe_prefill_chunked.argtypes = [P(MoeDims), P(MoeWeights), P(MoeFfnNorms), vp, i32, i32, vp, vp, sz, vp]
+    lib.moe_prefill_chunked.restype = ctypes.c_int
     lib.moe_quantize_int8.argtypes = [vp, i64, i32, vp, vp, vp]
     lib.moe_quantize_int8.restype = ctypes.c_int
     lib.moe_tile_weights.argtypes = [vp, i64, i32, i32, vp, vp]

@@ -1,5 +1,6 @@
 // Host side of libmoe_ffn.so: argument checks, workspace carving, path
 // selection and kernel launches for the C ABI declared in include/moe.h.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -34,6 +35,11 @@ size_t up256(size_t b) { return (b + 255) & ~size_t(255); }
 // runs; below it, the per-expert dot-product router and a separate top-k,
 // which spread a small batch over more workgroups.
 constexpr int kRouterMfmaMinT = 64;
+constexpr int kFfnMaxHidden = 16384;  // the norm kernels hold a row in registers
+// chunked prefill: default and largest chunk, and the sliding window the size is a multiple of
+constexpr int32_t kPrefillChunkDefault = 16384;
+constexpr int32_t kPrefillChunkMax = 32768;
+constexpr int32_t kSlidingWindow = 1024;
 
 // Workspace layout at a given T (byte offsets into ws).
 struct Layout {
@@ -200,6 +206,33 @@ struct FfnLayout {
 };
 FfnLayout ffn_layout(const moe_dims& d, int64_t T) {
     return {make_layout(d, T).total + 2 * up256((size_t)T * d.hidden * 2)};
+}
+
+// Checks shared by moe_ffn_layer and moe_prefill_chunked (the workspace size
+// is each caller's own). layer: the norm kernels run (n may still be NULL).
+int check_layer_args(const moe_dims* d, const moe_weights* w, const moe_ffn_norms* n, bool layer, const void* h,
+                     int32_t T, const void* out, const void* ws) {
+    int rc;
+    if ((rc = check_dims(d)) || (rc = check_T(T)) || (rc = check_weights(w)) || (rc = check_tiled(w))) return rc;
+    if (layer && d->hidden > kFfnMaxHidden)
+        return fail(MOE_ERR_UNSUPPORTED, "hidden=%d: the feed-forward norms take hidden <= %d", d->hidden,
+                    kFfnMaxHidden);
+    if (n) {
+        const void* gains[] = {n->pre_dense, n->pre_moe, n->post_dense, n->post_moe, n->post};
+        const char* names[] = {"pre_dense", "pre_moe", "post_dense", "post_moe", "post"};
+        for (int i = 0; i < 5; ++i)
+            if (gains[i] && !aligned(gains[i], 16))
+                return fail(MOE_ERR_ALIGN, "norm gain %s is not 16-byte aligned", names[i]);
+        if (!(n->eps >= 0.f) || n->eps > 1.f) return fail(MOE_ERR_SHAPE, "norm eps=%g must be in [0, 1]", (double)n->eps);
+    }
+    if (T > 0) {  // empty batch: h, out and ws may be NULL
+        CHECK_PTR(h, "h", 16);
+        CHECK_PTR(out, "out", 16);
+        if (out == h) return fail(MOE_ERR_SHAPE, "out may not alias h");
+        if (!ws) return fail(MOE_ERR_NULL, "workspace is NULL");
+        if (!aligned(ws, 256)) return fail(MOE_ERR_ALIGN, "workspace must be 256-byte aligned");
+    }
+    return MOE_OK;
 }
 
 // The block's pipeline. The router and the experts read x, the dense MLP xd;
@@ -439,27 +472,51 @@ size_t moe_ffn_workspace_bytes(const moe_dims* d, int32_t T) {
 int moe_ffn_layer(const moe_dims* d, const moe_weights* w, const moe_ffn_norms* n, const void* h, int32_t T,
                   void* out, moe_debug* dbg, void* ws, size_t ws_bytes, hipStream_t stream) {
     int rc;
-    if ((rc = check_dims(d)) || (rc = check_T(T)) || (rc = check_weights(w)) || (rc = check_tiled(w))) return rc;
-    if (d->hidden > 16384)
-        return fail(MOE_ERR_UNSUPPORTED, "hidden=%d: the feed-forward norms take hidden <= 16384", d->hidden);
+    if ((rc = check_layer_args(d, w, n, true, h, T, out, ws))) return rc;
     moe_ffn_norms none{};
     if (!n) n = &none;
-    const void* gains[] = {n->pre_dense, n->pre_moe, n->post_dense, n->post_moe, n->post};
-    const char* names[] = {"pre_dense", "pre_moe", "post_dense", "post_moe", "post"};
-    for (int i = 0; i < 5; ++i)
-        if (gains[i] && !aligned(gains[i], 16)) return fail(MOE_ERR_ALIGN, "norm gain %s is not 16-byte aligned", names[i]);
-    if (!(n->eps >= 0.f) || n->eps > 1.f) return fail(MOE_ERR_SHAPE, "norm eps=%g must be in [0, 1]", (double)n->eps);
-    if (T > 0) {  // empty batch: h, out and ws may be NULL
-        CHECK_PTR(h, "h", 16);
-        CHECK_PTR(out, "out", 16);
-        if (out == h) return fail(MOE_ERR_SHAPE, "out may not alias h");
-        if (!ws) return fail(MOE_ERR_NULL, "workspace is NULL");
-        if (!aligned(ws, 256)) return fail(MOE_ERR_ALIGN, "workspace must be 256-byte aligned");
+    if (T > 0) {
         const size_t need = ffn_layout(*d, T).total;
         if (ws_bytes < need)
             return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed at T=%d", ws_bytes, need, T);
     }
     return block_impl(d, w, h, h, T, out, n, h, dbg, ws, stream);
+}
+
+int32_t moe_prefill_chunk_tokens(int32_t chunk_tokens) {
+    if (chunk_tokens <= 0) return kPrefillChunkDefault;
+    const int32_t c = chunk_tokens / kSlidingWindow * kSlidingWindow;
+    return c < kSlidingWindow ? kSlidingWindow : (c > kPrefillChunkMax ? kPrefillChunkMax : c);
+}
+
+size_t moe_prefill_workspace_bytes(const moe_dims* d, int32_t chunk_tokens) {
+    if (check_dims(d) != MOE_OK) return 0;
+    return ffn_layout(*d, moe_prefill_chunk_tokens(chunk_tokens)).total;
+}
+
+int moe_prefill_chunked(const moe_dims* d, const moe_weights* w, const moe_ffn_norms* n, const void* h,
+                        int32_t T, int32_t chunk_tokens, void* out, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+    int rc;
+    if ((rc = check_layer_args(d, w, n, n != nullptr, h, T, out, ws))) return rc;
+    const int32_t C = moe_prefill_chunk_tokens(chunk_tokens);
+    if (T > 0) {  // the chunks have two sizes at most: the first's and the ragged last one's
+        auto need_at = [&](int32_t t) { return n ? ffn_layout(*d, t).total : make_layout(*d, t).total; };
+        const int32_t first = T < C ? T : C, last = T - (T - 1) / C * C;
+        const size_t need = std::max(need_at(first), need_at(last));
+        if (ws_bytes < need)
+            return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed for chunks of %d tokens", ws_bytes,
+                        need, first);
+    }
+    g_err[0] = 0;
+    const size_t row = (size_t)d->hidden * 2;
+    for (int32_t t0 = 0; t0 < T; t0 += C) {
+        const int32_t tc = T - t0 < C ? T - t0 : C;
+        const void* hc = static_cast<const char*>(h) + (size_t)t0 * row;
+        void* oc = static_cast<char*>(out) + (size_t)t0 * row;
+        if ((rc = block_impl(d, w, hc, hc, tc, oc, n, n ? hc : nullptr, nullptr, ws, stream))) return rc;
+    }
+    return MOE_OK;
 }
 
 int dense_mlp(const moe_dims* d, const void* dense_gate_up, const void* dense_down, const void* x,

@@ -199,6 +199,39 @@ def moe_ffn_layer(dims: BlockDims, weights: LayerWeights, norms: Optional[FfnNor
     return out
 
 
+def moe_prefill_chunk_tokens(chunk_tokens: int = 0) -> int:
+    """The chunk size the chunked prefill uses for a requested one (0: the default)."""
+    return int(_lib().moe_prefill_chunk_tokens(int(chunk_tokens)))
+
+
+def moe_prefill_workspace_bytes(dims: BlockDims, chunk_tokens: int = 0) -> int:
+    n = _lib().moe_prefill_workspace_bytes(ctypes.byref(dims.c()), int(chunk_tokens))
+    if n == 0:
+        raise MoEError(_abi.MOE_ERR_SHAPE, "moe_prefill_workspace_bytes", _lib().moe_last_error().decode())
+    return n
+
+
+def moe_prefill_chunked(dims: BlockDims, weights: LayerWeights, norms: Optional[FfnNorms], h: torch.Tensor,
+                        chunk_tokens: int = 0, out=None, workspace=None, stream=None) -> torch.Tensor:
+    """Chunked prefill: consecutive chunks of h through the block (norms None)
+    or the layer's FFN (norms given), reusing one chunk's workspace."""
+    h = _dev(h, "h")
+    T = h.shape[0]
+    if out is None:
+        out = torch.empty((T, dims.hidden), dtype=torch.bfloat16, device=h.device)
+    if workspace is None:
+        workspace = torch.empty(moe_prefill_workspace_bytes(dims, chunk_tokens), dtype=torch.uint8,
+                                device=h.device)
+    ws = _dev(workspace, "workspace")
+    cn = norms.c() if norms is not None else None
+    rc = _lib().moe_prefill_chunked(ctypes.byref(dims.c()), ctypes.byref(weights.c()),
+                                    ctypes.byref(cn) if cn is not None else None, h.data_ptr(), T,
+                                    int(chunk_tokens), _dev(out, "out").data_ptr(), ws.data_ptr(), ws.numel(),
+                                    _stream(stream))
+    _check(rc, "moe_prefill_chunked")
+    return out
+
+
 def moe_quantize_int8(w: torch.Tensor, q=None, scale=None, stream=None):
     """Per-row symmetric int8 of a bf16 tensor [..., cols]: returns (q int8, scale fp32 [...])."""
     w = _dev(w, "w")

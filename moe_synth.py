@@ -77,6 +77,10 @@ WORKLOADS = {
                             note="real shape, int8 per-channel experts, T=8"),
     "int8_prefill": Workload("int8_prefill", REAL, 4096, 4, int8=True,
                              note="real shape, int8 per-channel experts, T=4096"),
+    "mtp_decode": Workload("mtp_decode", REAL, 40, 1,
+                           note="real shape, multi-token decode: 8 sequences x 5 tokens"),
+    "long_prefill": Workload("long_prefill", REAL, 40960, 2,
+                             note="real shape, a 40960-token prompt prefilled in 16384-token chunks"),
 }
 
 

@@ -193,3 +193,54 @@ def test_ffn_layer_argument_errors(L):
     # an empty batch is a valid no-op, with or without gains
     assert call(T=0, h=None, out=None, ws=None, ws_bytes=0) == _abi.MOE_OK
     assert call(n=None, T=0, h=None, out=None, ws=None, ws_bytes=0) == _abi.MOE_OK
+
+
+def test_prefill_chunk_size_rule(L):
+    """The chunk size of the chunked prefill ([TT] "Configurable knobs": 16384
+    tokens by default, snapped to a multiple of the 1024-token sliding window,
+    capped at 32768). Host arithmetic only."""
+    cases = {0: 16384, -7: 16384, 1: 1024, 1023: 1024, 1024: 1024, 2047: 1024, 2048: 2048,
+             5000: 4096, 16384: 16384, 16385: 16384, 32768: 32768, 40000: 32768, 2 ** 31 - 1: 32768}
+    for req, want in cases.items():
+        assert L.moe_prefill_chunk_tokens(req) == want, req
+    d = _real()
+    for req in (0, 1500, 40000):
+        c = L.moe_prefill_chunk_tokens(req)
+        assert L.moe_prefill_workspace_bytes(ctypes.byref(d), req) == L.moe_ffn_workspace_bytes(ctypes.byref(d), c)
+    bad = _abi.MoeDims(2816, 128, 9, 704, 2112, 1e-6)
+    assert L.moe_prefill_workspace_bytes(ctypes.byref(bad), 0) == 0
+
+
+def test_prefill_chunked_argument_errors(L):
+    """moe_prefill_chunked checks everything before it launches: the block's
+    arguments, the gains (with norms), and a workspace that must hold the
+    largest chunk, which is less than the whole prompt's."""
+    d = _real()
+    T, C = 5000, 2048
+    ws_chunk = L.moe_prefill_workspace_bytes(ctypes.byref(d), C)
+    ws_block = L.moe_workspace_bytes(ctypes.byref(d), C)
+    assert ws_chunk < L.moe_ffn_workspace_bytes(ctypes.byref(d), T)
+    norms = _abi.MoeFfnNorms(FAKE, FAKE, FAKE, FAKE, FAKE, 1e-6)
+    ok = dict(h=FAKE, T=T, out=FAKE + (1 << 26), ws=FAKE, ws_bytes=ws_chunk)
+
+    def call(n=norms, w=None, chunk=C, **kw):
+        a = dict(ok, **kw)
+        w = w or _weights()
+        return L.moe_prefill_chunked(ctypes.byref(d), ctypes.byref(w), ctypes.byref(n) if n is not None else None,
+                                     a["h"], a["T"], chunk, a["out"], a["ws"], a["ws_bytes"], None)
+
+    assert call(h=None) == _abi.MOE_ERR_NULL
+    assert call(out=None) == _abi.MOE_ERR_NULL
+    assert call(ws=None) == _abi.MOE_ERR_NULL
+    assert call(out=FAKE) == _abi.MOE_ERR_SHAPE              # out aliases h
+    assert call(T=-1) == _abi.MOE_ERR_SHAPE
+    assert call(ws=FAKE + 16) == _abi.MOE_ERR_ALIGN
+    assert call(ws_bytes=ws_chunk - 1) == _abi.MOE_ERR_WORKSPACE
+    assert call(ws_bytes=ws_block) == _abi.MOE_ERR_WORKSPACE  # the layer needs its branch inputs too
+    assert call(chunk=4096, ws_bytes=ws_chunk) == _abi.MOE_ERR_WORKSPACE
+    assert call(n=_abi.MoeFfnNorms(FAKE, FAKE, FAKE, FAKE, FAKE + 4, 1e-6)) == _abi.MOE_ERR_ALIGN
+    assert b"post" in L.moe_last_error()
+    assert call(w=_weights(layout=_abi.MOE_LAYOUT_ROWS)) == _abi.MOE_ERR_UNSUPPORTED
+    # an empty prompt is a valid no-op
+    assert call(T=0, h=None, out=None, ws=None, ws_bytes=0) == _abi.MOE_OK
+    assert call(n=None, T=0, h=None, out=None, ws=None, ws_bytes=0) == _abi.MOE_OK

@@ -15,15 +15,17 @@ import torch
 
 import moe_synth
 import oracle
-from mixture_experts_ffn_amd import (MOE_PATH_GROUPED, MOE_PATH_STREAM, BlockCall, FfnNorms, MoEError,
-                                     dense_mlp, moe_block, moe_ffn_layer, moe_quantize_int8, moe_route,
-                                     moe_tile_weights, moe_workspace_bytes, new_debug)
+from mixture_experts_ffn_amd import (MOE_PATH_AUTO, MOE_PATH_GROUPED, MOE_PATH_STREAM, BlockCall, FfnNorms,
+                                     MoEError, dense_mlp, moe_block, moe_ffn_layer, moe_prefill_chunk_tokens,
+                                     moe_prefill_chunked, moe_prefill_workspace_bytes, moe_quantize_int8,
+                                     moe_route, moe_tile_weights, moe_workspace_bytes, new_debug)
 from gpu_util import (REL_BF16, REL_INT8, bf16_dev, check_routing, compare_y, dims_of,
                       oracle_int8_weights, routing_for, to_np, upload, y_f64)
 
 pytestmark = pytest.mark.gpu
 
 _CACHE = {}
+_WCACHE = {}
 
 
 def say(*a):
@@ -38,10 +40,17 @@ def dev():
 
 
 def inputs(name, dev, tokens=None):
+    """(workload, oracle weights, x, device weights, device x). Workloads that
+    draw the same weights (same shape, seed and variant) share one upload."""
     key = (name, tokens)
     if key not in _CACHE:
-        wl, w, x = moe_synth.make_inputs(name, tokens)
-        lw = upload(w, dev, int8=wl.int8)
+        wl = moe_synth.WORKLOADS[name]
+        wkey = (wl.shape, wl.seed, wl.skew, wl.int8)
+        if wkey not in _WCACHE:
+            w = moe_synth.make_weights(wl.shape, wl.seed, wl.skew)
+            _WCACHE[wkey] = (w, upload(w, dev, int8=wl.int8))
+        w, lw = _WCACHE[wkey]
+        x = moe_synth.make_tokens(wl.shape, wl.seed, wl.tokens if tokens is None else tokens)
         _CACHE[key] = (wl, w, x, lw, bf16_dev(x, dev))
     return _CACHE[key]
 
@@ -162,7 +171,8 @@ PATH_CASES = [("tiny", MOE_PATH_STREAM), ("tiny", MOE_PATH_GROUPED),
               ("decode", MOE_PATH_STREAM), ("decode", MOE_PATH_GROUPED),
               ("prefill", MOE_PATH_GROUPED), ("skew", MOE_PATH_GROUPED),
               ("int8_decode", MOE_PATH_STREAM), ("int8_decode", MOE_PATH_GROUPED),
-              ("int8_prefill", MOE_PATH_GROUPED)]
+              ("int8_prefill", MOE_PATH_GROUPED),
+              ("mtp_decode", MOE_PATH_STREAM), ("mtp_decode", MOE_PATH_GROUPED)]
 
 
 @pytest.mark.parametrize("name,path", PATH_CASES)
@@ -333,6 +343,19 @@ def test_graph_replay(dev, name, path):
 FFN_SETS = {"all": oracle.FFN_NORMS, "post_only": ("post",), "pre_moe": ("pre_moe", "post_moe"), "none": ()}
 
 
+def ffn_gains(H, which, dev, eps=1e-5):
+    """Seeded bf16 gains 1 + 0.1 N for the norms in FFN_SETS[which] (the rest
+    absent): (the oracle's dict, the library's FfnNorms)."""
+    rng = np.random.default_rng(7)
+    gains = {k: moe_synth.f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal(H)).astype(np.float32))
+             for k in oracle.FFN_NORMS}
+    sel = FFN_SETS[which]
+    norms_np = {**{k: (gains[k] if k in sel else None) for k in oracle.FFN_NORMS}, "eps": eps}
+    norms = FfnNorms(**{k: (torch.from_numpy(gains[k].view(np.int16)).view(torch.bfloat16).to(dev)
+                            if k in sel else None) for k in oracle.FFN_NORMS}, eps=eps)
+    return norms_np, norms
+
+
 @pytest.mark.parametrize("name,path,which", [
     ("tiny", MOE_PATH_STREAM, "all"), ("tiny", MOE_PATH_GROUPED, "all"), ("tiny", MOE_PATH_GROUPED, "none"),
     ("decode", MOE_PATH_STREAM, "all"), ("decode", MOE_PATH_STREAM, "post_only"),
@@ -346,14 +369,7 @@ def test_ffn_layer(dev, name, path, which):
     s = wl.shape
     K, H = s.top_k, s.hidden
     say(f"case: ffn layer {name} path={path} norms={which}")
-    rng = np.random.default_rng(7)
-    gains = {k: moe_synth.f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal(H)).astype(np.float32))
-             for k in oracle.FFN_NORMS}
-    sel = FFN_SETS[which]
-    eps = 1e-5
-    norms_np = {**{k: (gains[k] if k in sel else None) for k in oracle.FFN_NORMS}, "eps": eps}
-    norms = FfnNorms(**{k: (torch.from_numpy(gains[k].view(np.int16)).view(torch.bfloat16).to(dev)
-                            if k in sel else None) for k in oracle.FFN_NORMS}, eps=eps)
+    norms_np, norms = ffn_gains(H, which, dev)
     T = xd.shape[0]
     out_t = dict(topk_idx=torch.empty((T, K), dtype=torch.int32, device=dev),
                  topk_w=torch.empty((T, K), dtype=torch.float32, device=dev))
@@ -379,3 +395,55 @@ def test_ffn_layer(dev, name, path, which):
     cos = float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
     assert rel <= bound and cos >= 1.0 - bound * bound / 2, f"branches: rel-L2 {rel:.3g} (bound {bound:.3g}), cos {cos:.6f}"
 
+
+
+CHUNK_CASES = [("tiny", 2048 + 77, 1024, None), ("tiny", 2048 + 20, 1500, "all"),
+               ("long_prefill", None, 0, None), ("prefill", 2048 + 5, 1024, "all")]
+
+
+@pytest.mark.parametrize("name,T,chunk,which", CHUNK_CASES)
+def test_prefill_chunked(dev, name, T, chunk, which):
+    """moe_prefill_chunked: bit for bit the per-chunk calls of the block (or the
+    layer), whose routing then serves the comparison with the oracle on sampled
+    tokens, spread over every chunk. Chunks of 1024 tokens with a ragged last
+    one of 77 or 5 tokens (the 5-token one takes the streaming path), 1500
+    snapped down to 1024, and the real 40960-token prompt in the default
+    16384-token chunks."""
+    wl, w, x, lw, xd = inputs(name, dev, T)
+    s = wl.shape
+    T, K, H = x.shape[0], s.top_k, s.hidden
+    C = moe_prefill_chunk_tokens(chunk)
+    assert C == (16384 if chunk <= 0 else max(1024, min(32768, chunk // 1024 * 1024)))
+    say(f"case: chunked prefill {name} T={T} chunk={C} norms={which}")
+    norms_np, norms = ffn_gains(H, which, dev) if which else (None, None)
+    ws = torch.empty(moe_prefill_workspace_bytes(dims_of(s), chunk), dtype=torch.uint8, device=dev)
+    out = moe_prefill_chunked(dims_of(s), lw, norms, xd, chunk, workspace=ws)
+    # the same chunks one call each, with their routing
+    ref_out = torch.empty_like(out)
+    gi = np.empty((T, K), np.int32)
+    gw = np.empty((T, K), np.float32)
+    for t0 in range(0, T, C):
+        t1 = min(T, t0 + C)
+        o = dict(topk_idx=torch.empty((t1 - t0, K), dtype=torch.int32, device=dev),
+                 topk_w=torch.empty((t1 - t0, K), dtype=torch.float32, device=dev))
+        dbg = new_debug(MOE_PATH_AUTO, **o)
+        if norms is None:
+            ref_out[t0:t1] = moe_block(dims_of(s), lw, xd[t0:t1], debug=dbg)
+        else:
+            ref_out[t0:t1] = moe_ffn_layer(dims_of(s), lw, norms, xd[t0:t1], debug=dbg)
+        torch.cuda.synchronize()
+        gi[t0:t1], gw[t0:t1] = to_np(o["topk_idx"]), to_np(o["topk_w"])
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), "chunked != per-chunk calls"
+    toks = sample_tokens(T, n=32, seed=11)
+    # the layer routes its MoE branch's input, the pre-normed h
+    ref_r = (oracle_route(wl, w, x[toks]) if norms is None
+             else oracle.ffn_layer(x[toks], w, norms_np, K, s.rms_eps)[1])
+    check_routing(gi[toks], gw[toks], ref_r, w["per_expert_scale"])
+    r = routing_for(gi[toks], ref_r, w["per_expert_scale"])
+    if norms is None:
+        ref, _ = oracle.moe_block(x[toks], w, K, s.rms_eps, routing=r)
+    else:
+        ref, _ = oracle.ffn_layer(x[toks], w, norms_np, K, s.rms_eps, routing=r)
+    cos, rel = compare_y(y_f64(out)[toks], ref, REL_BF16)
+    say(f"  tokens checked {len(toks)}  cos {cos:.7f}  rel-L2 {rel:.3e}")
