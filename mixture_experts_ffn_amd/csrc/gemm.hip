@@ -71,9 +71,35 @@ __host__ __device__ __forceinline__ int n_tiles_of(const GemmArgs& p) {
 __host__ __device__ __forceinline__ int mtile_cap(const GemmArgs& p) {
     return p.mtile_group ? p.max_mtiles : (p.M_dense + BM - 1) / BM;
 }
+// The dense problem's M-tiles are cut into gm groups (gm | kXcds). Its units
+// (M-tile, N-tile) are ordered by group, then N-tile, then M-tile, and each XCD
+// runs one contiguous, equal share of them, about kXcdSlots at a time: such a
+// pass reads each of its M-tiles' rows and N-tiles' weights (tiles of equal
+// size, BM = BN) from HBM once, the other blocks of the pass finding them in
+// the XCD's L2. gm minimises the tiles the passes read: at T = 2048 (8 M-tiles)
+// 4 M-tiles x 4-5 N-tiles per XCD instead of 1 x 17 (weights read 8 times).
+constexpr int kXcdSlots = 32;  // blocks in flight per XCD: 32 CUs, one block each
+template <int MODE>
+__host__ __device__ __forceinline__ int dense_groups(const GemmArgs& p) {
+    const int m_total = (p.M_dense + BM - 1) / BM;
+    const int share = (m_total * n_tiles_of<MODE>(p) + kXcds - 1) / kXcds;
+    const int pass = min(share, kXcdSlots), passes = (share + pass - 1) / pass;
+    int best = 1, best_cost = 0;
+    for (int g = 1; g <= kXcds; g *= 2) {
+        const int m_in = (m_total + g - 1) / g, pm = min(m_in, pass);
+        const int cost = passes * (pm + (pass + pm - 1) / pm);
+        if (g == 1 || cost < best_cost) {
+            best = g;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
 template <int MODE>
 __host__ __device__ __forceinline__ int blocks_of(const GemmArgs& p) {
-    return kXcds * ((mtile_cap(p) + kXcds - 1) / kXcds) * n_tiles_of<MODE>(p);
+    if (p.mtile_group) return kXcds * ((p.max_mtiles + kXcds - 1) / kXcds) * n_tiles_of<MODE>(p);
+    const int units = ((p.M_dense + BM - 1) / BM) * n_tiles_of<MODE>(p);
+    return kXcds * ((units + kXcds - 1) / kXcds);
 }
 
 // tiled-layout tile (16 weight rows) holding the wavefront's column tile j
@@ -260,9 +286,8 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
     const int n_nt = n_tiles_of<MODE>(p);
 
     // XCD-aware mapping (gemm_expert_blocks): the routed experts' tile of this
-    // block comes precomputed from the grouping; the dense problem's XCD x
-    // owns M-tiles [x * chunk, (x + 1) * chunk) and runs them, per N-tile, back
-    // to back, so an N-tile's weights come from HBM once per XCD.
+    // block comes precomputed from the grouping; the dense problem's units are
+    // shared out as dense_groups describes.
     int group = 0, row0, rows_valid, nt;
     if (p.tiles) {
         const int2 te = p.tiles[b];
@@ -273,13 +298,14 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
         nt = te.y >> 18;
     } else {
         const int m_total = (p.M_dense + BM - 1) / BM;
-        const int chunk = (m_total + kXcds - 1) / kXcds;
-        const int xcd = b % kXcds, local = b / kXcds;
-        const int c0 = xcd * chunk, c1 = min(c0 + chunk, m_total);
-        if (c0 + local / n_nt >= c1) return;
-        const int rl = c1 - c0;
-        nt = local / rl;
-        const int mt = c0 + (local - nt * rl);
+        const int units = m_total * n_nt, share = (units + kXcds - 1) / kXcds;
+        const int u = (b % kXcds) * share + b / kXcds;  // block b runs on XCD b % kXcds
+        if (b / kXcds >= share || u >= units) return;
+        const int gm = dense_groups<MODE>(p), mc = (m_total + gm - 1) / gm;
+        const int mg = u / (mc * n_nt), r = u - mg * mc * n_nt;  // every group but the last holds mc
+        const int m_in = min(mc, m_total - mg * mc);
+        nt = r / m_in;
+        const int mt = mg * mc + (r - nt * m_in);
         row0 = mt * BM;
         rows_valid = min(BM, p.M_dense - row0);
     }
