@@ -30,6 +30,8 @@ What the block computes (one input x feeds router, experts and dense MLP):
   experts -- [INF2] "How it works (the recipe)", first bullet.
 * int8 experts -- [INT8] intro and "How it works": per-channel symmetric int8
   expert weights, every other weight bf16.
+* fp8 experts -- the vLLM recipe page ("Gemma 4 26B-A4B IT"), ``variants`` ›
+  fp8: E4M3 expert weights with dynamic per-token activation quantisation.
 
 Precision. Everything is float64 except where the pages fix a precision: the
 router's softmax works on fp32 logits ([ONNX] row "Router"), so the logits are
@@ -44,7 +46,11 @@ scale is a per-channel vector; top-k selects by logit, descending, ties going
 to the lower expert index, and emits the experts in that order; gate rows come
 before up rows in a gate_up matrix; the dense MLP has the same GeGLU form as an
 expert; int8 scales are per output channel, ``max|w|/127``, rounding half to
-even.
+even. fp8: E4M3 in its OCP form without infinities (bias 7, largest finite
+448); weight scales per output channel and activation scales per token (per
+row of each expert linear's input), both ``amax/448`` in fp32, codes rounded
+half to even in fp32; the expert's h is rounded to bf16, as on the bf16 path,
+before it is quantised; router and dense MLP stay bf16.
 """
 from __future__ import annotations
 
@@ -57,6 +63,7 @@ __all__ = [
     "permute_pairs", "expert_ffn", "dense_mlp", "moe_part", "moe_block", "masked_dense_block",
     "quantize_int8", "dequantize_int8", "brute_force_block", "NEAR_TIE",
     "round_bf16", "rms_norm_scaled", "FFN_NORMS", "ffn_layer",
+    "FP8_MAX", "fp8_e4m3_encode", "fp8_e4m3_decode", "quantize_fp8", "dequantize_fp8", "expert_ffn_fp8",
 ]
 
 #: logit gap under which a top-k decision is reported as a near-tie
@@ -211,6 +218,16 @@ def _expert_weights(weights, e, dtype):
     return weights["expert_gate_up"][e], weights["expert_down"][e]
 
 
+def _expert(weights, e, dtype):
+    """Expert e as a function of its input rows, in the given weight format."""
+    if dtype == "fp8":
+        return lambda rows: expert_ffn_fp8(rows, weights["expert_gate_up_f8"][e],
+                                           weights["expert_gate_up_f8_scale"][e],
+                                           weights["expert_down_f8"][e], weights["expert_down_f8_scale"][e])
+    gu, dn = _expert_weights(weights, e, dtype)
+    return lambda rows: expert_ffn(rows, gu, dn)
+
+
 def moe_part(x, weights, top_k, eps, expert_dtype="bf16", routing=None):
     """moe = sum_k w[t,k] * expert_{e[t,k]}(x_t), added in k order (the sparse
     top-k form of the MoE branch). Returns ``(moe [T,H] float64, routing)``;
@@ -224,8 +241,7 @@ def moe_part(x, weights, top_k, eps, expert_dtype="bf16", routing=None):
     contrib = np.zeros((T, K, x64.shape[1]))
     for e in np.unique(idx):
         tk = np.argwhere(idx == e)                 # (token, slot) pairs routed to e
-        gu, dn = _expert_weights(weights, int(e), expert_dtype)
-        out = expert_ffn(x64[tk[:, 0]], gu, dn)
+        out = _expert(weights, int(e), expert_dtype)(x64[tk[:, 0]])
         contrib[tk[:, 0], tk[:, 1]] = w[tk[:, 0], tk[:, 1]][:, None] * out
     moe = np.zeros_like(x64)
     for k in range(K):                             # k order
@@ -239,7 +255,9 @@ def moe_block(x, weights, top_k, eps, expert_dtype="bf16", routing=None):
     ``weights`` uses the keys of ``moe_synth.make_weights``; for
     ``expert_dtype="int8"`` it must also hold ``expert_gate_up_q``,
     ``expert_gate_up_scale``, ``expert_down_q``, ``expert_down_scale``
-    (see ``quantize_int8``). ``routing`` may supply a precomputed ``route``
+    (see ``quantize_int8``); for ``"fp8"`` ``expert_gate_up_f8``,
+    ``expert_gate_up_f8_scale``, ``expert_down_f8``, ``expert_down_f8_scale``
+    (see ``quantize_fp8``). ``routing`` may supply a precomputed ``route``
     result (or one with a different but equally valid index set).
     Returns ``(y [T,H] float64, routing)``.
     """
@@ -309,8 +327,7 @@ def masked_dense_block(x, weights, top_k, eps, expert_dtype="bf16", routing=None
     np.put_along_axis(mask, idx.astype(np.int64), w, axis=1)   # scatter the top-k weights
     y = dense_mlp(x64, weights["dense_gate_up"], weights["dense_down"])
     for e in range(E):
-        gu, dn = _expert_weights(weights, e, expert_dtype)
-        y = y + mask[:, e:e + 1] * expert_ffn(x64, gu, dn)
+        y = y + mask[:, e:e + 1] * _expert(weights, e, expert_dtype)(x64)
     return y, routing
 
 
@@ -342,6 +359,76 @@ def dequantize_int8(q, scale):
 # brute force: the same definition with explicit Python loops and no BLAS,
 # for a handful of tokens of the small workload.
 # --------------------------------------------------------------------------
+# --------------------------------------------------------------------------
+# fp8 experts: the vLLM recipe page ("Gemma 4 26B-A4B IT"), ``variants`` ›
+# fp8 -- E4M3 expert weights, activations quantised per token at run time.
+# E4M3 (OCP, no infinities): sign, 4 exponent bits with bias 7, 3 mantissa
+# bits; exponent field 0 holds the subnormals m * 2^-9; S.1111.111 is NaN, so
+# the largest finite value is 1.75 * 2^8 = 448.
+# --------------------------------------------------------------------------
+FP8_MAX = 448.0
+
+
+def fp8_e4m3_encode(v):
+    """float32 values -> E4M3 codes (uint8): the nearest representable value,
+    ties to the even code; magnitudes past 448 saturate to 448."""
+    a64 = np.asarray(v, dtype=np.float32).astype(np.float64)      # exact
+    sign = np.signbit(a64).astype(np.int64) << 7
+    a = np.abs(a64)
+    code = np.zeros(a.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6
+    # below the smallest normal: multiples of 2^-9 (code 8 is 2^-6 itself)
+    code[sub] = np.rint(a[sub] * 512.0).astype(np.int64)          # rint: half to even
+    m, ex = np.frexp(a[~sub])                                      # a = m 2^ex, m in [0.5, 1)
+    e = ex.astype(np.int64) - 1
+    mant = np.rint((2.0 * m - 1.0) * 8.0).astype(np.int64)        # exact operands
+    e = np.where(mant == 8, e + 1, e)
+    mant = np.where(mant == 8, 0, mant)
+    code[~sub] = np.minimum(((e + 7) << 3) | mant, 0x7E)           # saturate at 448
+    return (code | sign).astype(np.uint8)
+
+
+def fp8_e4m3_decode(codes):
+    """E4M3 codes -> float64 values (NaN for S.1111.111)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    e, m = (c >> 3) & 0xF, c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return np.where(c & 0x80, -mag, mag)
+
+
+def quantize_fp8(v):
+    """Per-row E4M3 quantisation of a [..., rows, cols] tensor (bf16 bits or
+    floats): scale = max|v| / 448 in fp32, code = encode(v / scale) with the
+    division in fp32; an all-zero row gets scale 0 and codes 0. Serves the
+    weights (rows = output channels) and the activations (rows = tokens)."""
+    a = np.asarray(v)
+    v32 = bf16_to_f64(a).astype(np.float32) if a.dtype == np.uint16 else a.astype(np.float32)
+    amax = np.max(np.abs(v32), axis=-1, keepdims=True)
+    scale = (amax / np.float32(FP8_MAX)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    q = fp8_e4m3_encode((v32 / safe).astype(np.float32))
+    q = np.where(scale > 0, q, 0).astype(np.uint8)
+    return q, scale[..., 0].astype(np.float32)
+
+
+def dequantize_fp8(q, scale):
+    return fp8_e4m3_decode(q) * np.asarray(scale, dtype=np.float64)[..., None]
+
+
+def expert_ffn_fp8(x_rows, gu_q, gu_scale, dn_q, dn_scale):
+    """An fp8 expert on input rows x [n, H] (bf16 values): each row quantised
+    per token, the GeGLU on the dequantised rows and weights, h rounded to bf16
+    and quantised per row, then the down projection."""
+    x32 = _f64(x_rows).astype(np.float32)                          # bf16 values: exact
+    xq = dequantize_fp8(*quantize_fp8(x32))
+    gu = dequantize_fp8(gu_q, gu_scale)
+    I = gu.shape[0] // 2
+    h = round_bf16(gelu_tanh(xq @ gu[:I].T) * (xq @ gu[I:].T))
+    hq = dequantize_fp8(*quantize_fp8(h.astype(np.float32)))       # bf16 values: exact
+    return hq @ dequantize_fp8(dn_q, dn_scale).T
+
+
 def brute_force_block(x, weights, top_k, eps, tokens):
     """y for the listed token indices, computed element by element in float64."""
     X = _f64(x)

@@ -321,6 +321,114 @@ def test_int8_block_equals_block_on_dequantised_weights(tiny):
     assert rel < 2e-2
 
 
+# ---------------------------------------------------------------- fp8 (E4M3)
+# the vLLM recipe page ("Gemma 4 26B-A4B IT"), variants > fp8: E4M3 weights,
+# dynamic per-token activation quantisation
+
+
+def _fp8_table():
+    """Every finite E4M3 code and its value, built from numpy's float16: an
+    E4M3 code's bits placed at the top of a float16 (sign at bit 15, exponent
+    and mantissa at bits 7..13) are that code's value times 2^-8, subnormals
+    included (the two formats' exponent biases differ by 8)."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    c = codes.astype(np.uint16)
+    h = (((c & 0x80) << 8) | ((c & 0x7F) << 7)).astype(np.uint16).view(np.float16)
+    return codes, h.astype(np.float64) * 256.0
+
+
+def test_fp8_decode_against_float16_placement():
+    codes, vals = _fp8_table()
+    np.testing.assert_array_equal(oracle.fp8_e4m3_decode(codes), vals)
+    assert oracle.fp8_e4m3_decode(np.array([0x7E]))[0] == 448.0
+    assert oracle.fp8_e4m3_decode(np.array([0x01]))[0] == 2.0 ** -9
+    assert np.isnan(oracle.fp8_e4m3_decode(np.array([0x7F, 0xFF]))).all()
+
+
+def test_fp8_encode_golden():
+    v = np.array([0.0, -0.0, 1.0, -2.0, 448.0, 2.0 ** -9, 2.0 ** -6, 7 * 2.0 ** -9,
+                  1.0625, 1.1875, 1.125, 464.0, 500.0, 2.0 ** -10, 1.5 * 2.0 ** -9], dtype=np.float32)
+    # 1.0625, 1.1875, 464, 2^-10 and 1.5 2^-9 lie halfway: ties go to the even code
+    want = [0x00, 0x80, 0x38, 0xC0, 0x7E, 0x01, 0x08, 0x07, 0x38, 0x3A, 0x39, 0x7E, 0x7E, 0x00, 0x02]
+    assert oracle.fp8_e4m3_encode(v).tolist() == want
+
+
+def test_fp8_encode_is_nearest_by_brute_force():
+    """Against a search over every finite value: the nearest, ties to the even
+    code (magnitudes up to 464, the midpoint past 448)."""
+    codes, vals = _fp8_table()
+    rng = np.random.default_rng(3)
+    v = np.concatenate([rng.uniform(-464, 464, 4000), rng.uniform(-0.02, 0.02, 4000),
+                        vals[np.isfinite(vals)], (vals[:-1] + vals[1:]) / 2]).astype(np.float32)
+    got = oracle.fp8_e4m3_encode(v)
+    dist = np.abs(vals[None, :] - v.astype(np.float64)[:, None])
+    best = dist.min(axis=1, keepdims=True)
+    cand = dist == best
+    for i in range(v.size):
+        c = codes[cand[i]]
+        if c.size > 1:   # a tie: the even mantissa (for +-0 the sign of v)
+            c = c[(c & 1) == 0]
+            if c.size > 1:
+                c = c[(c >> 7) == np.signbit(v[i])]
+        assert got[i] == c[0], (v[i], got[i], c)
+
+
+def test_fp8_quantisation_bounds():
+    rng = np.random.default_rng(4)
+    w = moe_synth.f32_to_bf16_bits((0.02 * rng.standard_normal((64, 256))).astype(np.float32))
+    q, s = oracle.quantize_fp8(w)
+    w64 = oracle.bf16_to_f64(w)
+    amax = np.abs(w64).max(axis=1)
+    np.testing.assert_array_equal(s, (amax.astype(np.float32) / np.float32(448)).astype(np.float32))
+    dq = oracle.dequantize_fp8(q, s)
+    # the largest element lands on +-448 scale; every element within half a step
+    # (2^-4 relative for normals, 2^-10 scale below 2^-6 scale)
+    assert np.all(np.abs(oracle.fp8_e4m3_decode(q)).max(axis=1) == 448.0)
+    step = np.maximum(np.abs(dq) * 2.0 ** -4, 2.0 ** -10 * s[:, None])
+    assert np.all(np.abs(dq - w64) <= step * (1 + 1e-6))
+    zq, zs = oracle.quantize_fp8(np.zeros((2, 5), dtype=np.float32))
+    assert (zs == 0).all() and (zq == 0).all()
+
+
+def _fp8_weights(w):
+    wq = dict(w)
+    wq["expert_gate_up_f8"], wq["expert_gate_up_f8_scale"] = oracle.quantize_fp8(w["expert_gate_up"])
+    wq["expert_down_f8"], wq["expert_down_f8_scale"] = oracle.quantize_fp8(w["expert_down"])
+    return wq
+
+
+def test_fp8_block_sparse_equals_masked_dense_and_tracks_bf16(tiny):
+    wl, w, x = tiny
+    wq = _fp8_weights(w)
+    y8, r = oracle.moe_block(x, wq, 4, 1e-6, expert_dtype="fp8")
+    ym, _ = oracle.masked_dense_block(x, wq, 4, 1e-6, expert_dtype="fp8", routing=r)
+    np.testing.assert_allclose(y8, ym, rtol=1e-12, atol=1e-13)
+    # quantisation noise of three 3-bit-mantissa roundings: visible, but small
+    yb, _ = oracle.moe_block(x, w, 4, 1e-6, routing=r)
+    yd = oracle.dense_mlp(x, w["dense_gate_up"], w["dense_down"])
+    rel = np.linalg.norm((y8 - yd) - (yb - yd)) / np.linalg.norm(yb - yd)
+    assert 1e-3 < rel < 0.12, rel
+
+
+def test_fp8_expert_activation_quantisation_is_per_token(tiny):
+    """Each token's row is quantised on its own: a token's output does not
+    depend on the other rows, and scaling a row by a power of two scales its
+    quantised input exactly (the codes stay, the scale doubles)."""
+    wl, w, x = tiny
+    wq = _fp8_weights(w)
+    e = 3
+    args = (wq["expert_gate_up_f8"][e], wq["expert_gate_up_f8_scale"][e],
+            wq["expert_down_f8"][e], wq["expert_down_f8_scale"][e])
+    rows = oracle.bf16_to_f64(x[:6])
+    full = oracle.expert_ffn_fp8(rows, *args)
+    for t in (0, 5):
+        np.testing.assert_allclose(oracle.expert_ffn_fp8(rows[t:t + 1], *args)[0], full[t], rtol=1e-12, atol=1e-15)
+    q1, s1 = oracle.quantize_fp8(rows.astype(np.float32))
+    q2, s2 = oracle.quantize_fp8((2 * rows).astype(np.float32))
+    np.testing.assert_array_equal(q1, q2)
+    np.testing.assert_array_equal(s2, 2 * s1)
+
+
 # ---------------------------------------------------------------- accumulation
 def test_fp16_accumulation_loses_accuracy_at_real_hidden():
     """Negative control for the ONNX export card, "MoE dispatch: why this
