@@ -127,6 +127,8 @@ def stage_work(stage: str, shape, T, n_active, int8):
                       2 * TK * I * H + 2 * T * Id * H,
                       f"{n_active} experts' down ({dn_w} B each) + h + rows + dense down + hd + fp32 dense out"),
         "combine": (T * H * 4 + TK * H * 2 + TK * 4 + y, TK * H, "fp32 dense out + expert rows + y"),
+        "act_quant": (2 * x + T * 4, 0, "x read, its E4M3 carriers written, per-token scales"),
+        "h_quant": (2 * TK * I * 2 + TK * 12, 0, "h read and rewritten as E4M3 carriers, row scales and factors"),
     }
     return table[stage]
 
@@ -160,6 +162,10 @@ def run_workload(name, steps, warmup, layers, dev, ev: HipEvents, log):
     if wl.int8:
         base.expert_gate_up, base.gate_up_scale = moe_quantize_int8(base.expert_gate_up)
         base.expert_down, base.down_scale = moe_quantize_int8(base.expert_down)
+    if wl.fp8:
+        from mixture_experts_ffn_amd import moe_quantize_fp8
+        base.expert_gate_up, base.gate_up_scale = moe_quantize_fp8(base.expert_gate_up)
+        base.expert_down, base.down_scale = moe_quantize_fp8(base.expert_down)
     base = tile_layer(base)  # the block reads its matrices in the tiled layout
     copies = [base]
     for _ in range(layers - 1):
@@ -282,8 +288,9 @@ def run_workload(name, steps, warmup, layers, dev, ev: HipEvents, log):
     torch.cuda.synchronize()
     dom_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs]))
 
-    work = algorithmic(s, T, n_active, wl.int8)
-    dbytes, dflops, dunits = stage_work(dom_name, s, T, n_active, wl.int8)
+    byte_w = wl.int8 or wl.fp8  # one byte a weight plus fp32 row scales
+    work = algorithmic(s, T, n_active, byte_w)
+    dbytes, dflops, dunits = stage_work(dom_name, s, T, n_active, byte_w)
     res = {
         "workload": name, "T": T, "path": {1: "stream", 2: "grouped"}.get(path, path),
         "ms_per_step": ms_step, "tokens_per_s": T / (ms_step * 1e-3),
@@ -296,7 +303,7 @@ def run_workload(name, steps, warmup, layers, dev, ev: HipEvents, log):
         "block_gbs": work["bytes"] / (ms_step * 1e-3) / 1e9,
         "block_tflops": work["flops"] / (ms_step * 1e-3) / 1e12,
         "stages_us": {n: round(float(t) * 1e3, 2) for n, t in zip(stage_names, per_stage)},
-        "stages_gbs": {n: round(stage_work(n, s, T, n_active, wl.int8)[0] / (float(t) * 1e-3) / 1e9, 1)
+        "stages_gbs": {n: round(stage_work(n, s, T, n_active, byte_w)[0] / (float(t) * 1e-3) / 1e9, 1)
                        for n, t in zip(stage_names, per_stage)},
         "dominant": {"kernel": dom_name, "avg_us": dom_ms * 1e3, "bytes": dbytes, "flops": dflops,
                      "units": dunits},

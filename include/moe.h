@@ -14,6 +14,7 @@
  *          canonical inference metadata", table "Truthful graph contracts"
  *          (rows "Mixture of Experts", "MoE topology", "Router") and
  *          "MoE dispatch: why this export uses the vectorized unfused path"
+ *   [VLLM] "Gemma 4 26B-A4B IT" (vLLM recipe), its "variants" list, fp8 entry
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -62,6 +63,8 @@ extern "C" {
 /* expert weight storage */
 #define MOE_DTYPE_BF16 0
 #define MOE_DTYPE_INT8 1  /* [INT8]: per-output-channel symmetric int8 + fp32 scale */
+#define MOE_DTYPE_FP8  2  /* [VLLM] fp8 variant: E4M3 codes + fp32 per-output-channel scale; the
+                             experts' inputs are quantised per token inside the block */
 
 /* how moe_block computes the routed experts */
 #define MOE_PATH_AUTO    0  /* streaming when T <= the streaming limit, else grouped */
@@ -112,11 +115,11 @@ typedef struct moe_weights {
     const void*  router_w;          /* [E, H]   bf16 */
     const float* per_expert_scale;  /* [E]      fp32 */
     const float* logit_bias;        /* [E]      fp32, or NULL for none */
-    const void*  expert_gate_up;    /* [E, 2I, H]  bf16, or int8 if expert_dtype == INT8 */
+    const void*  expert_gate_up;    /* [E, 2I, H]  bf16, or int8 / E4M3 codes (1 byte) per expert_dtype */
     const void*  expert_down;       /* [E, H, I]   bf16, or int8 */
     int32_t      expert_dtype;      /* MOE_DTYPE_* */
-    const float* gate_up_scale;     /* [E, 2I] fp32 per-row scales (INT8 only; else ignored) */
-    const float* down_scale;        /* [E, H]  fp32 per-row scales (INT8 only; else ignored) */
+    const float* gate_up_scale;     /* [E, 2I] fp32 per-row scales (INT8 and FP8; else ignored) */
+    const float* down_scale;        /* [E, H]  fp32 per-row scales (INT8 and FP8; else ignored) */
     const void*  dense_gate_up;     /* [2Id, H] bf16 */
     const void*  dense_down;        /* [H, Id]  bf16 */
     int32_t      layout;            /* MOE_LAYOUT_TILED (MOE_LAYOUT_ROWS is rejected) */
@@ -237,8 +240,20 @@ int moe_prefill_chunked(const moe_dims* d, const moe_weights* w, const moe_ffn_n
 int moe_quantize_int8(const void* w_bf16, int64_t rows, int32_t cols, int8_t* q, float* scale,
                       hipStream_t stream);
 
+/* Per-row E4M3 quantisation of a bf16 matrix [rows, cols] ([VLLM] "variants",
+ * fp8: E4M3 weights with dynamic per-token activation quantisation; the E4M3
+ * format is the OCP one without infinities: bias 7, largest finite 448):
+ * scale[r] = max_c |w[r,c]| / 448 (fp32), q[r,c] = the E4M3 code nearest to
+ * w[r,c] / scale[r] (fp32 division), ties to the even code; an all-zero row
+ * gets scale 0 and codes 0. cols % 8 == 0, rows >= 0. Writes q [rows, cols]
+ * (one byte each) and scale [rows] fp32. With expert_dtype = MOE_DTYPE_FP8 the
+ * block quantises the experts' inputs the same way, per token: x before the
+ * gate/up projection, h (rounded to bf16) before the down projection. */
+int moe_quantize_fp8(const void* w_bf16, int64_t rows, int32_t cols, uint8_t* q, float* scale,
+                     hipStream_t stream);
+
 /* Re-lays a row-major matrix into MOE_LAYOUT_TILED (see above): src [rows, cols]
- * of dtype MOE_DTYPE_BF16 or MOE_DTYPE_INT8 -> dst, same size, a different
+ * of dtype MOE_DTYPE_BF16, MOE_DTYPE_INT8 or MOE_DTYPE_FP8 -> dst, same size, a different
  * buffer. An [E, rows, cols] stack of expert matrices is one matrix of E * rows
  * rows. rows % 16 == 0, cols % 64 == 0, rows >= 0. Pure data movement: the
  * values are the same bits. */

@@ -30,6 +30,7 @@ MOE_MAX_EXPERTS = 256
 MOE_MAX_TOPK = 8
 MOE_DTYPE_BF16 = 0
 MOE_DTYPE_INT8 = 1
+MOE_DTYPE_FP8 = 2
 MOE_PATH_AUTO = 0
 MOE_PATH_STREAM = 1
 MOE_PATH_GROUPED = 2
@@ -73,7 +74,7 @@ class MoeFfnNorms(ctypes.Structure):
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_block", "dense_mlp",
            "moe_ffn_workspace_bytes", "moe_ffn_layer",
            "moe_prefill_chunk_tokens", "moe_prefill_workspace_bytes", "moe_prefill_chunked",
-           "moe_quantize_int8", "moe_tile_weights", "moe_last_error")
+           "moe_quantize_int8", "moe_quantize_fp8", "moe_tile_weights", "moe_last_error")
 
 _lib = None
 
@@ -111,6 +112,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.moe_prefill_chunked.restype = ctypes.c_int
     lib.moe_quantize_int8.argtypes = [vp, i64, i32, vp, vp, vp]
     lib.moe_quantize_int8.restype = ctypes.c_int
+    lib.moe_quantize_fp8.argtypes = [vp, i64, i32, vp, vp, vp]
+    lib.moe_quantize_fp8.restype = ctypes.c_int
     lib.moe_tile_weights.argtypes = [vp, i64, i32, i32, vp, vp]
     lib.moe_tile_weights.restype = ctypes.c_int
     lib.moe_last_error.argtypes = []

@@ -98,4 +98,46 @@ __device__ __forceinline__ void lds_barrier() {
     raw_barrier();
 }
 
+// ---- E4M3 (fp8 experts: the recipe page's fp8 variant) -------------------
+// E4M3 in its OCP form without infinities: sign, 4 exponent bits (bias 7), 3
+// mantissa bits; exponent field 0 holds the subnormals m 2^-9; the largest
+// finite value is 448. The kernels carry E4M3 values as bf16 holding value *
+// 2^-8 and fold 2^8 per operand into the scales.
+
+// nearest E4M3 code of an fp32 value, ties to the even code, saturating at 448
+__device__ __forceinline__ uint32_t fp8_e4m3_code(float v) {
+    const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+    const float a = fabsf(v);
+    uint32_t c;
+    if (a < 0.015625f) {  // below 2^-6: multiples of 2^-9 (code 8 is 2^-6 itself)
+        c = (uint32_t)rintf(a * 512.f);
+    } else {
+        const uint32_t au = __float_as_uint(a);
+        int e = (int)(au >> 23) - 127;
+        uint32_t m = (au >> 20) & 7u;
+        const uint32_t rest = au & 0xFFFFFu;  // the 20 bits below the kept mantissa
+        if (rest > 0x80000u || (rest == 0x80000u && (m & 1u))) ++m;
+        if (m == 8u) {
+            m = 0u;
+            ++e;
+        }
+        c = min(((uint32_t)(e + 7) << 3) | m, 0x7Eu);
+    }
+    return c | sign;
+}
+
+// an E4M3 code's bits placed at the top of a half (sign to bit 15, exponent
+// and mantissa to bits 7..13) are exactly its value * 2^-8, subnormals
+// included (the exponent biases differ by 8); widened to fp32 and, with at
+// most 4 significant bits, cut to bf16 without rounding. (Code 0x7F, a NaN,
+// never produced by the quantisers, would read as 480.)
+__device__ __forceinline__ uint32_t fp8_as_bf16_bits(uint32_t c) {
+    const float f = (float)__builtin_bit_cast(_Float16, (unsigned short)(((c & 0x80u) << 8) | ((c & 0x7Fu) << 7)));
+    return __float_as_uint(f) >> 16;
+}
+// two E4M3 codes (bytes sh and sh + 8 of a word) -> packed bf16 pair (value * 2^-8)
+__device__ __forceinline__ uint32_t fp8pair_to_bf16(uint32_t word, int sh) {
+    return fp8_as_bf16_bits((word >> sh) & 0xFFu) | (fp8_as_bf16_bits((word >> (sh + 8)) & 0xFFu) << 16);
+}
+
 }  // namespace moe

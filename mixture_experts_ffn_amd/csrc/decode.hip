@@ -62,17 +62,17 @@ __device__ __forceinline__ uint2 ld_nt8(const void* p) {
 }
 // 8 weights at element offset `col` of a weight matrix: 16 bytes of bf16, or
 // 8 bytes of int8 kept in .x/.y
-template <bool INT8>
+template <int WQ>
 __device__ __forceinline__ uint4 load_w8(const void* w, int64_t col) {
-    if (INT8) {
+    if (WQ) {
         const uint2 v = ld_nt8(reinterpret_cast<const int8_t*>(w) + col);
         return make_uint4(v.x, v.y, 0u, 0u);
     }
     return ld_nt16(reinterpret_cast<const uint16_t*>(w) + col);
 }
-template <bool INT8>
+template <int WQ>
 __device__ __forceinline__ void unpack_w8(const uint4& v, float* f) {
-    if (INT8) unpack8_i8(make_uint2(v.x, v.y), f);
+    if (WQ) unpack8_i8(make_uint2(v.x, v.y), f);
     else unpack8(v, f);
 }
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
@@ -103,9 +103,9 @@ __device__ __forceinline__ uint4 i8x8_to_bf16(const uint4& v) {
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 // weights as packed bf16, whatever their storage
-template <bool INT8>
+template <int WQ>
 __device__ __forceinline__ uint4 as_bf16(const uint4& v) {
-    if (INT8) return i8x8_to_bf16(v);
+    if (WQ) return i8x8_to_bf16(v);
     return v;
 }
 
@@ -135,27 +135,35 @@ __device__ __forceinline__ void i8x16_to_bf16(const uint4& v, uint4& lo, uint4& 
     lo = i8x8_to_bf16(make_uint4(v.x, v.y, 0u, 0u));
     hi = i8x8_to_bf16(make_uint4(v.z, v.w, 0u, 0u));
 }
+// 16 E4M3 codes (one tiled-layout piece) -> two groups of 8 bf16 (value * 2^-8, exact)
+__device__ __forceinline__ void f8x16_to_bf16(const uint4& v, uint4& lo, uint4& hi) {
+    lo = make_uint4(fp8pair_to_bf16(v.x, 0), fp8pair_to_bf16(v.x, 16), fp8pair_to_bf16(v.y, 0),
+                    fp8pair_to_bf16(v.y, 16));
+    hi = make_uint4(fp8pair_to_bf16(v.z, 0), fp8pair_to_bf16(v.z, 16), fp8pair_to_bf16(v.w, 0),
+                    fp8pair_to_bf16(v.w, 16));
+}
 
 // One K-step of a lane's piece of a tile (bf16: two 16-byte halves, 8 k each;
-// int8: one 16-byte piece, 16 k) dotted with the 16 matching x values.
+// int8 or E4M3: one 16-byte piece, 16 k) dotted with the 16 matching x values.
 // OPAQUE (int8): the piece is made opaque before it is widened, so that the
 // compiler widens it where it is used instead of hoisting every step's widened
 // copy (twice the registers) out of the caller's loop over tokens.
-template <bool INT8, bool OPAQUE = false>
-__device__ __forceinline__ float piece_dot(const uint4 (&w)[INT8 ? 1 : 2], const uint16_t* xp,
+template <int WQ, bool OPAQUE = false>
+__device__ __forceinline__ float piece_dot(const uint4 (&w)[WQ ? 1 : 2], const uint16_t* xp,
                                            float acc) {
     const uint4 x0 = *reinterpret_cast<const uint4*>(xp);
     const uint4 x1 = *reinterpret_cast<const uint4*>(xp + 8);
-    if (INT8) {
+    if (WQ) {
         uint4 v = w[0];
         if (OPAQUE) asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
         uint4 lo, hi;
-        i8x16_to_bf16(v, lo, hi);
+        if (WQ == 2) f8x16_to_bf16(v, lo, hi);
+        else i8x16_to_bf16(v, lo, hi);
         acc = dot8_bf16(lo, x0, acc);
         return dot8_bf16(hi, x1, acc);
     }
     acc = dot8_bf16(w[0], x0, acc);
-    return dot8_bf16(w[INT8 ? 0 : 1], x1, acc);
+    return dot8_bf16(w[WQ ? 0 : 1], x1, acc);
 }
 
 // sum of the four lanes holding one row of a tile (lanes r, r+16, r+32, r+48)
@@ -164,37 +172,37 @@ __device__ __forceinline__ float tile_row_sum(float v) {
     return v + __shfl_xor(v, 32, kWave);
 }
 
-template <bool INT8>
-constexpr int kTileBytes = INT8 ? 1024 : 2048;
+template <int WQ>
+constexpr int kTileBytes = WQ ? 1024 : 2048;
 
 // Load steps kt0 .. kt0 + NS - 1 (clamped to the last step nk - 1) of this
 // lane's pieces of a tile whose step 0 starts at `tile`; all loads issued at once.
-template <int NS, bool INT8>
+template <int NS, int WQ>
 __device__ __forceinline__ void tile_load(const char* tile, int kt0, int nk, int lane,
-                                          uint4 (&w)[NS][INT8 ? 1 : 2]) {
+                                          uint4 (&w)[NS][WQ ? 1 : 2]) {
     const char* p = tile + lane * 16;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        const int64_t off = (int64_t)min(kt0 + s, nk - 1) * kTileBytes<INT8>;
+        const int64_t off = (int64_t)min(kt0 + s, nk - 1) * kTileBytes<WQ>;
         w[s][0] = ld_nt16(p + off);
-        if (!INT8) w[s][INT8 ? 0 : 1] = ld_nt16(p + off + 1024);
+        if (!WQ) w[s][WQ ? 0 : 1] = ld_nt16(p + off + 1024);
     }
 }
 
 // tile_load of two tiles at once, their loads interleaved step by step (so
 // that step s of both has landed once 2 (s + 1) of them have).
-template <int NS, bool INT8>
+template <int NS, int WQ>
 __device__ __forceinline__ void tile_load2(const char* ta, const char* tb, int kt0, int nk, int lane,
-                                           uint4 (&wa)[NS][INT8 ? 1 : 2], uint4 (&wb)[NS][INT8 ? 1 : 2]) {
+                                           uint4 (&wa)[NS][WQ ? 1 : 2], uint4 (&wb)[NS][WQ ? 1 : 2]) {
     const char* pa = ta + lane * 16;
     const char* pb = tb + lane * 16;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        const int64_t off = (int64_t)min(kt0 + s, nk - 1) * kTileBytes<INT8>;
+        const int64_t off = (int64_t)min(kt0 + s, nk - 1) * kTileBytes<WQ>;
         wa[s][0] = ld_nt16(pa + off);
-        if (!INT8) wa[s][INT8 ? 0 : 1] = ld_nt16(pa + off + 1024);
+        if (!WQ) wa[s][WQ ? 0 : 1] = ld_nt16(pa + off + 1024);
         wb[s][0] = ld_nt16(pb + off);
-        if (!INT8) wb[s][INT8 ? 0 : 1] = ld_nt16(pb + off + 1024);
+        if (!WQ) wb[s][WQ ? 0 : 1] = ld_nt16(pb + off + 1024);
     }
 }
 
@@ -204,7 +212,7 @@ __device__ __forceinline__ void tile_load2(const char* ta, const char* tb, int k
 // p the grouped row. Wavefront w takes NS of the half's K-steps from
 // kb + w NS (steps past the half contribute 0); only the half's columns of x
 // are staged.
-template <int NS, bool INT8>
+template <int NS, int WQ>
 __device__ __forceinline__ void gateup_half_item(const uint16_t* __restrict__ x, int H, const void* W, int inter,
                                                  int hc, int half, const int32_t* toks, int n_rows,
                                                  int64_t half_stride, float* __restrict__ part, uint4* xs,
@@ -214,10 +222,10 @@ __device__ __forceinline__ void gateup_half_item(const uint16_t* __restrict__ x,
     const int kb = half * hk, kt0 = kb + wave * NS, ke = kb + hk;
     const int n_steps = max(0, min(NS, ke - kt0));
     const char* Wb = reinterpret_cast<const char*>(W);
-    uint4 wg[NS][INT8 ? 1 : 2], wu[NS][INT8 ? 1 : 2];
+    uint4 wg[NS][WQ ? 1 : 2], wu[NS][WQ ? 1 : 2];
     // loads clamped to the half's last step
-    tile_load<NS, INT8>(Wb + (int64_t)hc * nk * kTileBytes<INT8>, kt0, ke, lane, wg);
-    tile_load<NS, INT8>(Wb + (int64_t)(inter / 16 + hc) * nk * kTileBytes<INT8>, kt0, ke, lane, wu);
+    tile_load<NS, WQ>(Wb + (int64_t)hc * nk * kTileBytes<WQ>, kt0, ke, lane, wg);
+    tile_load<NS, WQ>(Wb + (int64_t)(inter / 16 + hc) * nk * kTileBytes<WQ>, kt0, ke, lane, wu);
     const int len8 = hk * 8;  // 16-byte chunks of x per token in the half
     constexpr int kPer = (kPass * 4 * NS * 8 + kThreads - 1) / kThreads;
     for (int pass = 0; pass < n_rows; pass += kPass) {
@@ -246,8 +254,8 @@ __device__ __forceinline__ void gateup_half_item(const uint16_t* __restrict__ x,
 #pragma unroll
             for (int st = 0; st < NS; ++st)
                 if (st < n_steps) {
-                    ag = piece_dot<INT8>(wg[st], xr + st * 64, ag);
-                    au = piece_dot<INT8>(wu[st], xr + st * 64, au);
+                    ag = piece_dot<WQ>(wg[st], xr + st * 64, ag);
+                    au = piece_dot<WQ>(wu[st], xr + st * 64, au);
                 }
             ag = tile_row_sum(ag);
             au = tile_row_sum(au);
@@ -477,7 +485,7 @@ __device__ __forceinline__ void dense_finish(const StreamArgs& a, int blk) {
 // Items of (touched expert, 16 h columns, half of the K range): twice as many
 // workgroups of half the bytes, so that the last ones in flight finish sooner.
 // Writes fp32 partial sums (hpart); the down kernel forms h from them.
-template <int NS, bool INT8>
+template <int NS, int WQ>
 __global__ __launch_bounds__(kThreads) void decode_experts_gateup_kernel(StreamArgs a) {
     extern __shared__ uint4 xs[];
     __shared__ float red[kWaves * kPass * 2 * 16];
@@ -494,9 +502,10 @@ __global__ __launch_bounds__(kThreads) void decode_experts_gateup_kernel(StreamA
     const int e = a.active[slot];
     const int p0 = a.offsets[e], n = a.offsets[e + 1] - p0;
     const int64_t wstride = (int64_t)2 * a.I * a.H;
-    const void* W = INT8 ? (const void*)((const int8_t*)a.gu + e * wstride)
+    const void* W = WQ ? (const void*)((const int8_t*)a.gu + e * wstride)
                          : (const void*)((const uint16_t*)a.gu + e * wstride);
-    gateup_half_item<NS, INT8>(a.x, a.H, W, a.I, hc, half, a.perm_token + p0, n,
+    // E4M3 experts read x quantised per token (bf16 carrier of value * 2^-8)
+    gateup_half_item<NS, WQ>(WQ == 2 ? a.xq : a.x, a.H, W, a.I, hc, half, a.perm_token + p0, n,
                                (int64_t)a.T * a.K * 2 * a.I, a.hpart + (int64_t)p0 * 2 * a.I, xs, red);
 }
 
@@ -651,7 +660,7 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(StreamArgs 
 // h = gelu_tanh(gate) * up, gate and up each the sum of the two halves' fp32
 // partial sums (times the int8 column scales), rounded to bf16. Loads are
 // unconditional (indices clamped into range); only the LDS stores are predicated.
-template <int KPER, bool INT8>
+template <int KPER, int WQ>
 __device__ __forceinline__ void stage_h(const StreamArgs& a, int p0, int n, const float* gs, uint4* hs) {
     const int I = a.I, hc8 = I >> 3;
     const int64_t half = (int64_t)a.T * a.K * 2 * I;
@@ -675,7 +684,7 @@ __device__ __forceinline__ void stage_h(const StreamArgs& a, int p0, int n, cons
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             float g_lo = gv[2 * j], g_hi = gv[2 * j + 1], u_lo = uv[2 * j], u_hi = uv[2 * j + 1];
-            if (INT8) {
+            if (WQ) {
                 g_lo *= gs[c + 2 * j];
                 g_hi *= gs[c + 2 * j + 1];
                 u_lo *= gs[I + c + 2 * j];
@@ -688,23 +697,77 @@ __device__ __forceinline__ void stage_h(const StreamArgs& a, int p0, int n, cons
     }
 }
 
+// ---------------------------------------------------------------- K3b
+// E4M3 experts: h of each routed pair (grouped row p) from the two K halves'
+// partial sums, times the gate/up column scales and the token's activation
+// scale (times 2^16: the two operands' bf16 carriers hold value * 2^-8),
+// h = gelu_tanh(gate) * up rounded to bf16, then quantised per row (max |h| /
+// 448, codes round half to even: the recipe page's per-token activation
+// quantisation) into a.h as bf16 carriers, the row scale times 2^16 into
+// a.h_scale. Workgroup b takes the rows of active expert b, a wavefront a row;
+// a lane holds NC 8-column chunks.
+template <int NC>
+__global__ __launch_bounds__(kThreads) void decode_hquant_kernel(StreamArgs a) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if ((int)blockIdx.x >= *a.n_active) return;
+    const int e = a.active[blockIdx.x];
+    const int p0 = a.offsets[e], p1 = a.offsets[e + 1];
+    const int I = a.I, hc8 = I >> 3;
+    const int64_t half = (int64_t)a.T * a.K * 2 * I;
+    const float* gs = a.gu_scale + (int64_t)e * 2 * I;
+    for (int p = p0 + wave; p < p1; p += kWaves) {  // uniform per wavefront
+        const float rs = a.x_scale[a.perm_token[p]] * 65536.f;
+        const float* g0 = a.hpart + (int64_t)p * 2 * I;
+        float hv[NC][8];
+        float amax = 0.f;
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+            const int c = min(lane + j * kWave, hc8 - 1) * 8;  // clamped: repeats a chunk, same max
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float g = (g0[c + i] + g0[half + c + i]) * gs[c + i] * rs;
+                const float u = (g0[I + c + i] + g0[half + I + c + i]) * gs[I + c + i] * rs;
+                hv[j][i] = bf16_to_f32(f32_to_bf16(gelu_tanh(g) * u));  // h rounded to bf16
+                amax = fmaxf(amax, fabsf(hv[j][i]));
+            }
+        }
+        amax = wave_max<kWave>(amax);
+        const float s = amax / 448.0f;
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+            const int cc = lane + j * kWave;
+            if (cc < hc8) {
+                uint32_t o[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t c0 = s > 0.f ? fp8_e4m3_code(hv[j][2 * i] / s) : 0u;
+                    const uint32_t c1 = s > 0.f ? fp8_e4m3_code(hv[j][2 * i + 1] / s) : 0u;
+                    o[i] = fp8_as_bf16_bits(c0) | (fp8_as_bf16_bits(c1) << 16);
+                }
+                reinterpret_cast<uint4*>(a.h + (int64_t)p * I)[cc] = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        }
+        if (lane == 0) a.h_scale[p] = s * 65536.f;
+    }
+}
+
 // ---------------------------------------------------------------- K4
 // Down projections. A wavefront reads K-steps [kt0, kt0 + n_steps) (n_steps <=
 // NS) of one 16-row tile of a tiled [H, inter] matrix and dots them with the
 // token rows of h (or hd) staged in LDS; returns, in lanes 0..15, the partial
 // sum of row lane of the tile for token n of the pass.
-template <int NS, bool INT8>
-__device__ __forceinline__ float down_dot(const uint4 (&w)[NS][INT8 ? 1 : 2], const uint16_t* hrow,
+template <int NS, int WQ>
+__device__ __forceinline__ float down_dot(const uint4 (&w)[NS][WQ ? 1 : 2], const uint16_t* hrow,
                                           int kt0, int n_steps, int lane) {
     const uint16_t* hp = hrow + kt0 * 64 + (lane >> 4) * 16;
     float acc = 0.f;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-        if (s < n_steps) acc = piece_dot<INT8, true>(w[s], hp + s * 64, acc);
+        if (s < n_steps) acc = piece_dot<WQ, true>(w[s], hp + s * 64, acc);
     return tile_row_sum(acc);
 }
 
-template <int NS, bool INT8>
+template <int NS, int WQ>
 __global__ __launch_bounds__(kThreads) void decode_down_kernel(StreamArgs a) {
     extern __shared__ uint4 hs[];  // [kPass][max(I, Id)] bf16
     __shared__ float red[kWaves * kPass * 16];
@@ -720,24 +783,29 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(StreamArgs a) {
         const int e = a.active[slot];
         const int p0 = a.offsets[e], n_rows = a.offsets[e + 1] - p0;
         const int64_t wstride = (int64_t)a.H * a.I;
-        const char* W = INT8 ? (const char*)((const int8_t*)a.dw + e * wstride)
+        const char* W = WQ ? (const char*)((const int8_t*)a.dw + e * wstride)
                              : (const char*)((const uint16_t*)a.dw + e * wstride);
         const int nk = a.I >> 6, tile = g * kWaves + wave;
-        uint4 w[NS][INT8 ? 1 : 2];
-        tile_load<NS, INT8>(W + (int64_t)tile * nk * kTileBytes<INT8>, 0, nk, lane, w);
-        const float sc = INT8 ? a.dw_scale[(int64_t)e * a.H + tile * 16 + (lane & 15)] : 1.f;
+        uint4 w[NS][WQ ? 1 : 2];
+        tile_load<NS, WQ>(W + (int64_t)tile * nk * kTileBytes<WQ>, 0, nk, lane, w);
+        const float sc = WQ ? a.dw_scale[(int64_t)e * a.H + tile * 16 + (lane & 15)] : 1.f;
         const int hc8 = a.I >> 3;
-        const float* gs = INT8 ? a.gu_scale + (int64_t)e * 2 * a.I : nullptr;
+        const float* gs = WQ ? a.gu_scale + (int64_t)e * 2 * a.I : nullptr;
         for (int pass = 0; pass < n_rows; pass += kPass) {
             const int nt = min(kPass, n_rows - pass);
             __syncthreads();
-            stage_h<(kPass * 128 + kThreads - 1) / kThreads, INT8>(a, p0 + pass, nt * hc8, gs, hs);
+            if (WQ == 2)  // E4M3: rows of h already formed and quantised (decode_hquant_kernel)
+                stage_rows<(kPass * 128 + kThreads - 1) / kThreads>(
+                    reinterpret_cast<const uint4*>(a.h + (int64_t)(p0 + pass) * a.I), nt * hc8, hs);
+            else
+                stage_h<(kPass * 128 + kThreads - 1) / kThreads, WQ>(a, p0 + pass, nt * hc8, gs, hs);
             __syncthreads();
 #pragma unroll 1
             for (int n = 0; n < nt; ++n) {
-                const float v = down_dot<NS, INT8>(w, reinterpret_cast<const uint16_t*>(hs + n * hc8), 0,
+                const float v = down_dot<NS, WQ>(w, reinterpret_cast<const uint16_t*>(hs + n * hc8), 0,
                                                    nk, lane);
-                if (lane < 16) a.part[(int64_t)(p0 + pass + n) * a.H + tile * 16 + lane] = v * sc;
+                const float hsc = WQ == 2 ? a.h_scale[p0 + pass + n] : 1.f;
+                if (lane < 16) a.part[(int64_t)(p0 + pass + n) * a.H + tile * 16 + lane] = v * sc * hsc;
             }
         }
     } else {
@@ -819,15 +887,17 @@ hipError_t launch_front_ns(const StreamArgs& a, const uint16_t* scale, const uin
 }
 
 template <int NJ>
-hipError_t launch_experts_nj(const StreamArgs& a, bool int8, hipStream_t stream) {
+hipError_t launch_experts_nj(const StreamArgs& a, int wq, hipStream_t stream) {
     const int n_fin = a.with_dense ? (a.T * a.Id + kThreads - 1) / kThreads : 0;
     const int blocks = n_fin + a.max_active * (a.I / 16) * 2;
     if (blocks <= 0) return hipSuccess;
     const size_t lds = (size_t)kPass * (a.H / 2) * sizeof(uint16_t);
-    if (int8)
-        hipLaunchKernelGGL((decode_experts_gateup_kernel<NJ, true>), dim3(blocks), dim3(kThreads), lds, stream, a);
+    if (wq == 2)
+        hipLaunchKernelGGL((decode_experts_gateup_kernel<NJ, 2>), dim3(blocks), dim3(kThreads), lds, stream, a);
+    else if (wq == 1)
+        hipLaunchKernelGGL((decode_experts_gateup_kernel<NJ, 1>), dim3(blocks), dim3(kThreads), lds, stream, a);
     else
-        hipLaunchKernelGGL((decode_experts_gateup_kernel<NJ, false>), dim3(blocks), dim3(kThreads), lds, stream, a);
+        hipLaunchKernelGGL((decode_experts_gateup_kernel<NJ, 0>), dim3(blocks), dim3(kThreads), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -881,14 +951,14 @@ hipError_t launch_decode_route(const StreamArgs& a, const float* lpart, const fl
     }
 }
 
-hipError_t launch_decode_experts_gateup(const StreamArgs& a, bool int8, hipStream_t stream) {
+hipError_t launch_decode_experts_gateup(const StreamArgs& a, int wq, hipStream_t stream) {
     // K-steps per wavefront: half of the H / 64 steps over four wavefronts
-#define CALL(n) launch_experts_nj<n>(a, int8, stream)
+#define CALL(n) launch_experts_nj<n>(a, wq, stream)
     MOE_NJ_SWITCH((a.H / 128 + kWaves - 1) / kWaves, CALL)
 #undef CALL
 }
 
-hipError_t launch_decode_down(const StreamArgs& a, bool int8, hipStream_t stream) {
+hipError_t launch_decode_down(const StreamArgs& a, int wq, hipStream_t stream) {
     // K-steps a wavefront holds: a whole expert tile (I / 64) or a quarter of
     // a dense tile (Id / 256, rounded up)
     const int need = max(a.I / 64, (a.Id / 64 + kWaves - 1) / kWaves);
@@ -898,8 +968,9 @@ hipError_t launch_decode_down(const StreamArgs& a, bool int8, hipStream_t stream
     const dim3 grid(blocks), block(kThreads);
 #define LAUNCH(N)                                                                                   \
     do {                                                                                            \
-        if (int8) hipLaunchKernelGGL((decode_down_kernel<N, true>), grid, block, lds, stream, a);   \
-        else hipLaunchKernelGGL((decode_down_kernel<N, false>), grid, block, lds, stream, a);       \
+        if (wq == 2) hipLaunchKernelGGL((decode_down_kernel<N, 2>), grid, block, lds, stream, a);   \
+        else if (wq == 1) hipLaunchKernelGGL((decode_down_kernel<N, 1>), grid, block, lds, stream, a); \
+        else hipLaunchKernelGGL((decode_down_kernel<N, 0>), grid, block, lds, stream, a);            \
         return hipGetLastError();                                                                   \
     } while (0)
     if (need <= 2) LAUNCH(2);
@@ -910,6 +981,21 @@ hipError_t launch_decode_down(const StreamArgs& a, bool int8, hipStream_t stream
     if (need <= 16) LAUNCH(16);
 #undef LAUNCH
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_hquant(const StreamArgs& a, hipStream_t stream) {
+    const int blocks = a.max_active;
+    if (blocks <= 0) return hipSuccess;
+    const int nc = (a.I / 8 + kWave - 1) / kWave;  // 8-column chunks per lane
+#define LAUNCH(N)                                                                                    \
+    do {                                                                                             \
+        hipLaunchKernelGGL(decode_hquant_kernel<N>, dim3(blocks), dim3(kThreads), 0, stream, a);     \
+        return hipGetLastError();                                                                    \
+    } while (0)
+    if (nc <= 1) LAUNCH(1);
+    if (nc <= 2) LAUNCH(2);
+#undef LAUNCH
+    return hipErrorInvalidValue;  // expert_inter <= 1024 on the streaming path
 }
 
 hipError_t launch_decode_combine(const StreamArgs& a, hipStream_t stream) {

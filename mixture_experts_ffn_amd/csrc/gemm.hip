@@ -130,19 +130,19 @@ constexpr int kAStageElems = BM * BK;  // bf16 elements per LDS stage of A
 
 // One K-step of the wavefront's B fragments: bf16 q[2 j + s] = column tile j,
 // 8 k of sub-step s; int8 q[j] = column tile j, all 16 k.
-template <bool INT8>
+template <int WQ>
 struct BStep {
-    v4u q[INT8 ? 2 : 4];
+    v4u q[WQ ? 2 : 4];
 };
-template <bool INT8>
-constexpr int kBLoads = INT8 ? 2 : 4;
+template <int WQ>
+constexpr int kBLoads = WQ ? 2 : 4;
 
 // bp[j]: this lane's 16-byte piece of K-step 0 of the wavefront's tile j; a
 // K-step is one tile (2 KB bf16: sub-step s at + 1024 s; 1 KB int8), so every
 // load of the wavefront reads one contiguous 1 KB
-template <bool INT8>
-__device__ __forceinline__ void b_load(const char* const (&bp)[2], int kt, BStep<INT8>& r) {
-    if (INT8) {
+template <int WQ>
+__device__ __forceinline__ void b_load(const char* const (&bp)[2], int kt, BStep<WQ>& r) {
+    if (WQ) {
         const int64_t off = (int64_t)kt * 1024;
 #pragma unroll
         for (int j = 0; j < 2; ++j) r.q[j] = *reinterpret_cast<const v4u*>(bp[j] + off);
@@ -156,17 +156,21 @@ __device__ __forceinline__ void b_load(const char* const (&bp)[2], int kt, BStep
     }
 }
 
-template <bool INT8>
-__device__ __forceinline__ bf16x8_t b_frag(const BStep<INT8>& r, int j, int s) {
+template <int WQ>
+__device__ __forceinline__ bf16x8_t b_frag(const BStep<WQ>& r, int j, int s) {
     v4u v;
-    if (INT8) {
+    if (WQ) {
         // the piece made opaque here, so that each fragment is widened where it
         // is used rather than all of them ahead (registers the loop lacks)
         v4u w = r.q[j & 1];
         asm volatile("" : "+v"(w));
         const unsigned w0 = s ? w.z : w.x, w1 = s ? w.w : w.y;
-        v = v4u{i8pair_to_bf16(w0, 0), i8pair_to_bf16(w0, 16), i8pair_to_bf16(w1, 0),
-                i8pair_to_bf16(w1, 16)};
+        if (WQ == 2)  // E4M3 codes: bf16 of value * 2^-8
+            v = v4u{fp8pair_to_bf16(w0, 0), fp8pair_to_bf16(w0, 16), fp8pair_to_bf16(w1, 0),
+                    fp8pair_to_bf16(w1, 16)};
+        else
+            v = v4u{i8pair_to_bf16(w0, 0), i8pair_to_bf16(w0, 16), i8pair_to_bf16(w1, 0),
+                    i8pair_to_bf16(w1, 16)};
     } else {
         v = r.q[(2 * j + s) & 3];
     }
@@ -193,12 +197,12 @@ __device__ __forceinline__ void a_dma(const char* const (&ap)[kADma], int kt, ui
 // the lane), B from registers. Slabs go in groups of four: the group's A
 // fragments are read before its MFMAs, so that the LDS latency is paid once
 // per group rather than once per fragment.
-template <bool INT8, int NSL>
-__device__ __forceinline__ void mma_step(const uint16_t* As, const BStep<INT8>& rb, int lane,
+template <int WQ, int NSL>
+__device__ __forceinline__ void mma_step(const uint16_t* As, const BStep<WQ>& rb, int lane,
                                          f32x4_t (&acc)[kSlabs][2]) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-        const bf16x8_t b0 = b_frag<INT8>(rb, 0, s), b1 = b_frag<INT8>(rb, 1, s);
+        const bf16x8_t b0 = b_frag<WQ>(rb, 0, s), b1 = b_frag<WQ>(rb, 1, s);
         const int c = (lane >> 4) * 2 + s;
 #pragma unroll
         for (int g = 0; g < NSL; g += 4) {
@@ -241,32 +245,32 @@ constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 
 // also waits for every B load issued before it.) a_dma pins the order of the
 // loads against compiler scheduling; loads past the last K-step repeat the
 // last one, so every step issues the same loads.
-template <bool INT8, int NSL>
+template <int WQ, int NSL>
 __device__ __forceinline__ void k_loop(const char* const (&ap)[kADma], const char* const (&bp)[2], int nk,
                                        const Lds& L, int wave, int lane, f32x4_t (&acc)[kSlabs][2]) {
-    constexpr int kB = NSL > 0 ? kBLoads<INT8> : 0;
+    constexpr int kB = NSL > 0 ? kBLoads<WQ> : 0;
     constexpr int kWait = wait_vm_lgkm0((kDepth - 2) * (kADma + kB));
     static_assert((kDepth - 2) * (kADma + kB) < 64, "vmcnt range");
     static_assert(kDepth == 4, "four stages and slots below");
     const int last = nk - 1;
-    BStep<INT8> rb0, rb1, rb2, rb3;
+    BStep<WQ> rb0, rb1, rb2, rb3;
     uint16_t* const S0 = L.a[0];
     uint16_t* const S1 = L.a[1];
     uint16_t* const S2 = L.a[2];
     uint16_t* const S3 = L.a[3];
     a_dma(ap, 0, S0, wave);
-    if (NSL > 0) b_load<INT8>(bp, 0, rb0);
+    if (NSL > 0) b_load<WQ>(bp, 0, rb0);
     a_dma(ap, min(1, last), S1, wave);
-    if (NSL > 0) b_load<INT8>(bp, min(1, last), rb1);
+    if (NSL > 0) b_load<WQ>(bp, min(1, last), rb1);
     a_dma(ap, min(2, last), S2, wave);
-    if (NSL > 0) b_load<INT8>(bp, min(2, last), rb2);
+    if (NSL > 0) b_load<WQ>(bp, min(2, last), rb2);
 #define MOE_GEMM_STEP(U, SA, RB, SN, RN)                                    \
     __builtin_amdgcn_s_waitcnt(kWait);                                      \
     raw_barrier();                                                          \
     a_dma(ap, min(kt + (U) + kDepth - 1, last), SN, wave);                  \
     if (NSL > 0) {                                                          \
-        b_load<INT8>(bp, min(kt + (U) + kDepth - 1, last), RN);             \
-        if (kt + (U) < nk) mma_step<INT8, NSL>(SA, RB, lane, acc);          \
+        b_load<WQ>(bp, min(kt + (U) + kDepth - 1, last), RN);             \
+        if (kt + (U) < nk) mma_step<WQ, NSL>(SA, RB, lane, acc);          \
     }
     for (int kt = 0; kt < nk; kt += kDepth) {
         MOE_GEMM_STEP(0, S0, rb0, S3, rb3)
@@ -279,7 +283,7 @@ __device__ __forceinline__ void k_loop(const char* const (&ap)[kADma], const cha
     raw_barrier();
 }
 
-template <int MODE, bool INT8>
+template <int MODE, int WQ>
 __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& L) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wn = wave;
@@ -326,7 +330,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
     // 16 (l / 16)) in the tiled layout; A rows of this wavefront's DMA share
     const char* bp[2];
     {
-        const int esz = INT8 ? 1 : 2;
+        const int esz = WQ ? 1 : 2;
         const char* B = (const char*)p.B + (int64_t)group * p.b_group_stride * esz;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
@@ -345,7 +349,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
     // loop: int8 column scales of this lane's columns, router weight of row tid
     const int col_l = lane & 15;
     float sc0 = 1.f, sc1 = 1.f, row_wt = 1.f;
-    if (INT8) {
+    if (WQ) {
         const float* bs = p.b_scale + (int64_t)group * p.scale_group_stride;
         if (MODE == MODE_GATEUP) {
             const int hc = min(nt * kHalfN + wn * 16 + col_l, p.n_out - 1);
@@ -358,24 +362,36 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
     }
     if (MODE == MODE_DOWN && !p.Cf && tid < BM)
         row_wt = tid >= rows_valid ? 0.f : p.row_w ? p.row_w[row0 + tid] : 1.f;
+    // fp8 gate/up: the per-token scale of each A row, times 2^16 (the 2^-8 of
+    // each operand's bf16 carrier)
+    if (MODE == MODE_GATEUP && WQ == 2 && tid < BM) {
+        const int rr = min(tid, rows_valid - 1);
+        const int64_t arow = p.a_rows ? p.a_rows[row0 + rr] : (int64_t)(row0 + rr);
+        row_wt = p.a_scale[arow] * 65536.f;
+    }
     switch (nsl) {  // uniform per wavefront
-        case 0: k_loop<INT8, 0>(ap, bp, nk, L, wave, lane, acc); break;
-        case 4: k_loop<INT8, 4>(ap, bp, nk, L, wave, lane, acc); break;
-        case 8: k_loop<INT8, 8>(ap, bp, nk, L, wave, lane, acc); break;
-        case 12: k_loop<INT8, 12>(ap, bp, nk, L, wave, lane, acc); break;
-        default: k_loop<INT8, 16>(ap, bp, nk, L, wave, lane, acc); break;
+        case 0: k_loop<WQ, 0>(ap, bp, nk, L, wave, lane, acc); break;
+        case 4: k_loop<WQ, 4>(ap, bp, nk, L, wave, lane, acc); break;
+        case 8: k_loop<WQ, 8>(ap, bp, nk, L, wave, lane, acc); break;
+        case 12: k_loop<WQ, 12>(ap, bp, nk, L, wave, lane, acc); break;
+        default: k_loop<WQ, 16>(ap, bp, nk, L, wave, lane, acc); break;
     }
 
     // epilogue: acc[i][jj][v] is C[row = 16 i + 4 (lane>>4) + v][column tile jj, lane&15]
     if (MODE == MODE_GATEUP) {
         // the h tile [BM][128] bf16, rows 128 h .. + 128 staged in A stage h (32 KB each)
         const int hl = wn * 16 + col_l;  // column within the 128-wide h tile
+        if (WQ == 2) {
+            if (tid < BM) L.rw[tid] = row_wt;
+            lds_barrier();
+        }
 #pragma unroll
         for (int i = 0; i < kSlabs; ++i)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int r = i * 16 + (lane >> 4) * 4 + v;
-                const float g = acc[i][0][v] * sc0, u = acc[i][1][v] * sc1;
+                const float rs = WQ == 2 ? L.rw[r] : 1.f;
+                const float g = acc[i][0][v] * sc0 * rs, u = acc[i][1][v] * sc1 * rs;
                 L.a[i >> 3][(r & 127) * kHalfN + hl] = f32_to_bf16(gelu_tanh(g) * u);
             }
         lds_barrier();
@@ -427,7 +443,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
     }
 }
 
-template <int MODE, bool INT8_0, bool INT8_1>
+template <int MODE, int WQ_0, int WQ_1>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p0, GemmArgs p1, int split) {
     // four LDS stages of A (256 x 64 bf16, 32 KB each; after the K loop, the
     // epilogue's staging) and the tile's router weights
@@ -438,18 +454,18 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p0, GemmArgs p1
     __shared__ float rw[BM];
     const Lds L{{st0, st1, st2, st3}, rw};
     const int b = blockIdx.x;
-    if (b < split) gemm_block<MODE, INT8_0>(p0, b, L);
-    else gemm_block<MODE, INT8_1>(p1, b - split, L);
+    if (b < split) gemm_block<MODE, WQ_0>(p0, b, L);
+    else gemm_block<MODE, WQ_1>(p1, b - split, L);
 }
 
 // first and second problem back to back in one grid (each a whole number of
 // XCD rounds, so block b of either runs on XCD b % 8)
-template <int MODE, bool INT8_0, bool INT8_1>
+template <int MODE, int WQ_0, int WQ_1>
 hipError_t launch(const GemmArgs& first, const GemmArgs* second, hipStream_t stream) {
     const int b0 = blocks_of<MODE>(first);
     const int b1 = second ? blocks_of<MODE>(*second) : 0;
     if (b0 + b1 <= 0) return hipSuccess;
-    hipLaunchKernelGGL((gemm_kernel<MODE, INT8_0, INT8_1>), dim3((unsigned)(b0 + b1)), dim3(kThreads),
+    hipLaunchKernelGGL((gemm_kernel<MODE, WQ_0, WQ_1>), dim3((unsigned)(b0 + b1)), dim3(kThreads),
                        0, stream, first, second ? *second : first, b0);
     return hipGetLastError();
 }
@@ -488,28 +504,37 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_gemm_gateup(const GemmArgs& experts, const GemmArgs* dense, bool int8,
+// wq: the experts' weight format (0 bf16, 1 int8, 2 E4M3); the dense problem is bf16
+hipError_t launch_gemm_gateup(const GemmArgs& experts, const GemmArgs* dense, int wq,
                               hipStream_t stream) {
     // the dense problem first: its tiles hold full 256-row M-tiles and run
     // longest, so the shorter expert tiles fill the end of the launch
-    if (!dense) return int8 ? launch<MODE_GATEUP, true, true>(experts, nullptr, stream)
-                            : launch<MODE_GATEUP, false, false>(experts, nullptr, stream);
-    return int8 ? launch<MODE_GATEUP, false, true>(*dense, &experts, stream)
-                : launch<MODE_GATEUP, false, false>(*dense, &experts, stream);
-}
-hipError_t launch_gemm_down(const GemmArgs& experts, const GemmArgs* dense, bool int8,
-                            hipStream_t stream) {
-    // the dense problem first: its blocks run a longer reduction. With int8
-    // experts the two run as two launches (one kernel holding both loops would
-    // need more registers than a wavefront has).
-    if (!dense) return int8 ? launch<MODE_DOWN, true, true>(experts, nullptr, stream)
-                            : launch<MODE_DOWN, false, false>(experts, nullptr, stream);
-    if (int8) {
-        const hipError_t e = launch<MODE_DOWN, false, false>(*dense, nullptr, stream);
-        if (e != hipSuccess) return e;
-        return launch<MODE_DOWN, true, true>(experts, nullptr, stream);
+    if (!dense) {
+        if (wq == 2) return launch<MODE_GATEUP, 2, 2>(experts, nullptr, stream);
+        return wq ? launch<MODE_GATEUP, 1, 1>(experts, nullptr, stream)
+                  : launch<MODE_GATEUP, 0, 0>(experts, nullptr, stream);
     }
-    return launch<MODE_DOWN, false, false>(*dense, &experts, stream);
+    if (wq == 2) return launch<MODE_GATEUP, 0, 2>(*dense, &experts, stream);
+    return wq ? launch<MODE_GATEUP, 0, 1>(*dense, &experts, stream)
+              : launch<MODE_GATEUP, 0, 0>(*dense, &experts, stream);
+}
+hipError_t launch_gemm_down(const GemmArgs& experts, const GemmArgs* dense, int wq,
+                            hipStream_t stream) {
+    // the dense problem first: its blocks run a longer reduction. With 1-byte
+    // expert weights the two run as two launches (one kernel holding both loops
+    // would need more registers than a wavefront has).
+    if (!dense) {
+        if (wq == 2) return launch<MODE_DOWN, 2, 2>(experts, nullptr, stream);
+        return wq ? launch<MODE_DOWN, 1, 1>(experts, nullptr, stream)
+                  : launch<MODE_DOWN, 0, 0>(experts, nullptr, stream);
+    }
+    if (wq) {
+        const hipError_t e = launch<MODE_DOWN, 0, 0>(*dense, nullptr, stream);
+        if (e != hipSuccess) return e;
+        return wq == 2 ? launch<MODE_DOWN, 2, 2>(experts, nullptr, stream)
+                       : launch<MODE_DOWN, 1, 1>(experts, nullptr, stream);
+    }
+    return launch<MODE_DOWN, 0, 0>(*dense, &experts, stream);
 }
 hipError_t launch_combine(const float* dense_out, const uint16_t* rows, const int32_t* inv_row,
                           int T, int H, int K, uint16_t* y, hipStream_t stream) {

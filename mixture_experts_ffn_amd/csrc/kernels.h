@@ -78,6 +78,7 @@ struct GemmArgs {
     const int32_t* a_rows;                    // gather: A row of grouped row p is a_rows[p]; null = p
     const void* B; int64_t b_group_stride; int64_t ldb;  // weights [groups][rows][ldb]
     const float* b_scale; int64_t scale_group_stride;    // int8 per-row scales, null for bf16
+    const float* a_scale;                     // fp8 gate/up: per-token scale of A's rows (by source row)
     int K;                                    // reduction length
     int n_out;                                // output columns
     int up_off;                               // gate/up: B row of the first up row
@@ -91,10 +92,10 @@ struct GemmArgs {
     const int2* tiles;                        // grouped: the tile of every block (PermuteOut::tiles)
 };
 // gate/up + GELU of the experts, and of `dense` (bf16, may be null), in one launch
-hipError_t launch_gemm_gateup(const GemmArgs& experts, const GemmArgs* dense, bool int8,
+hipError_t launch_gemm_gateup(const GemmArgs& experts, const GemmArgs* dense, int wq,
                               hipStream_t stream);
 // down of the experts (weighted bf16 rows) and of `dense` (fp32, may be null), in one launch
-hipError_t launch_gemm_down(const GemmArgs& experts, const GemmArgs* dense, bool int8,
+hipError_t launch_gemm_down(const GemmArgs& experts, const GemmArgs* dense, int wq,
                             hipStream_t stream);
 // y[t] = dense_out[t] + sum_k rows[inv_row[t*K + k]], in k order, rounded once to bf16
 hipError_t launch_combine(const float* dense_out, const uint16_t* rows, const int32_t* inv_row,
@@ -105,6 +106,8 @@ struct StreamArgs {
     int T, H, I, Id, K, E;
     const uint16_t* x;                        // router and experts input
     const uint16_t* xd;                       // dense MLP input
+    // E4M3 experts: x quantised per token (bf16 carriers of value * 2^-8) and its per-token scales
+    const uint16_t* xq; const float* x_scale;
     // experts
     const void* gu; const float* gu_scale;   // [E][2I][H]
     const void* dw; const float* dw_scale;   // [E][H][I]
@@ -118,6 +121,7 @@ struct StreamArgs {
     const uint16_t* dgu; const uint16_t* ddw;
     // intermediates and output
     uint16_t* h;    // [T*K][I]
+    float* h_scale; // E4M3 experts: scale of each row of h (grouped order), times 2^16
     uint16_t* hd;   // [T][Id]
     uint16_t* y;    // [T][H]
     // fp32 partial outputs of K4: expert rows [T*K][H] (grouped order), dense [T][H]
@@ -142,9 +146,11 @@ hipError_t launch_decode_route(const StreamArgs& a, const float* lpart, const fl
                                hipStream_t stream);
 // K3: the dense gate/up finish (dgu_part -> hd, if a.with_dense), then the gate/up of the
 // touched experts -> fp32 partial sums of the two halves of K (hpart)
-hipError_t launch_decode_experts_gateup(const StreamArgs& a, bool int8, hipStream_t stream);
+hipError_t launch_decode_experts_gateup(const StreamArgs& a, int wq, hipStream_t stream);
 // K4: h from hpart, down of the touched experts and of the dense MLP -> fp32 partial rows
-hipError_t launch_decode_down(const StreamArgs& a, bool int8, hipStream_t stream);
+hipError_t launch_decode_down(const StreamArgs& a, int wq, hipStream_t stream);
+// E4M3 experts: h of every routed pair formed and quantised per row (a.h, a.h_scale)
+hipError_t launch_decode_hquant(const StreamArgs& a, hipStream_t stream);
 // K5: y = dense + sum_k w_k * expert rows (k order) -> bf16
 hipError_t launch_decode_combine(const StreamArgs& a, hipStream_t stream);
 
@@ -154,6 +160,12 @@ hipError_t launch_tile_weights(const void* src, int64_t rows, int cols, bool int
                                hipStream_t stream);
 hipError_t launch_quantize_int8(const uint16_t* w, int64_t rows, int cols, int8_t* q, float* scale,
                                 hipStream_t stream);
+// E4M3 per row: weights -> codes + scales; activations -> bf16 carriers of
+// value * 2^-8 + scales (+ mul_out = mul_in * scale * 2^16 when mul_out is set)
+hipError_t launch_quantize_fp8(const uint16_t* w, int64_t rows, int cols, uint8_t* q, float* scale,
+                               hipStream_t stream);
+hipError_t launch_act_quant_fp8(const uint16_t* x, int64_t rows, int cols, uint16_t* xq, float* scale,
+                                const float* mul_in, float* mul_out, hipStream_t stream);
 
 // ---- the layer's feed-forward norms around the block (ffn.hip) ----------------
 // x_d = bf16(N_gd(h)), x_m = bf16(N_gm(h)) per token (only those whose gain is given)

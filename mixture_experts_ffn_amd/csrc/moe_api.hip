@@ -45,7 +45,7 @@ constexpr int32_t kSlidingWindow = 1024;
 struct Layout {
     size_t logits, partial, topk_idx, topk_w, pair_rank, tile_counts, counts, offsets, active, n_active;
     size_t perm_token, perm_w, inv_row, mtile_group, mtile_row0, n_mtiles, gemm_tiles[2], h, hd, rows;
-    size_t dout, part, dpart, dgu_part, lpart, ss_part, hpart, total;
+    size_t dout, part, dpart, dgu_part, lpart, ss_part, hpart, xq, xscale, hscale, wrow, total;
     int max_mtiles;
 };
 
@@ -93,6 +93,12 @@ Layout make_layout(const moe_dims& d, int64_t T) {
     L.lpart = take(Ts * moe::kFrontSplit * E * 4);
     L.ss_part = take(Ts * moe::kFrontSplit * 4);
     L.hpart = take(2 * Ts * K * 2 * d.expert_inter * 4);
+    // E4M3 experts: x quantised per token and its scales; h's per-row scales and
+    // the down projection's row factors (router weight x scale x 2^16)
+    L.xq = take(T * d.hidden * 2);
+    L.xscale = take(T * 4);
+    L.hscale = take(TK * 4);
+    L.wrow = take(TK * 4);
     L.total = off;
     return L;
 }
@@ -151,9 +157,9 @@ int check_weights(const moe_weights* w) {
     if (w->logit_bias && !aligned(w->logit_bias, 4)) return fail(MOE_ERR_ALIGN, "logit_bias misaligned");
     CHECK_PTR(w->expert_gate_up, "expert_gate_up", 16);
     CHECK_PTR(w->expert_down, "expert_down", 16);
-    if (w->expert_dtype != MOE_DTYPE_BF16 && w->expert_dtype != MOE_DTYPE_INT8)
+    if (w->expert_dtype != MOE_DTYPE_BF16 && w->expert_dtype != MOE_DTYPE_INT8 && w->expert_dtype != MOE_DTYPE_FP8)
         return fail(MOE_ERR_UNSUPPORTED, "expert_dtype=%d", w->expert_dtype);
-    if (w->expert_dtype == MOE_DTYPE_INT8) {
+    if (w->expert_dtype != MOE_DTYPE_BF16) {
         CHECK_PTR(w->gate_up_scale, "gate_up_scale", 4);
         CHECK_PTR(w->down_scale, "down_scale", 4);
     }
@@ -245,6 +251,9 @@ int check_layer_args(const moe_dims* d, const moe_weights* w, const moe_ffn_norm
 // Arguments are checked by the callers.
 int block_impl(const moe_dims* d, const moe_weights* w, const void* x, const void* xd_in, int32_t T, void* y,
                const moe_ffn_norms* norms, const void* hres, moe_debug* dbg, void* ws, hipStream_t stream) {
+    // the per-row E4M3 quantisers hold a row in registers
+    if (w->expert_dtype == MOE_DTYPE_FP8 && (d->hidden > 16384 || d->expert_inter > 16384))
+        return fail(MOE_ERR_UNSUPPORTED, "E4M3 experts take hidden and expert_inter <= 16384");
     int path = dbg ? dbg->path : MOE_PATH_AUTO;
     if (path != MOE_PATH_AUTO && path != MOE_PATH_STREAM && path != MOE_PATH_GROUPED)
         return fail(MOE_ERR_UNSUPPORTED, "unknown path %d", path);
@@ -262,7 +271,8 @@ int block_impl(const moe_dims* d, const moe_weights* w, const void* x, const voi
     if (T == 0) return MOE_OK;
 
     const Layout L = make_layout(*d, T);
-    const bool int8 = w->expert_dtype == MOE_DTYPE_INT8;
+    // experts' weight format for the kernels: 0 bf16, 1 int8, 2 E4M3
+    const int wq = w->expert_dtype == MOE_DTYPE_FP8 ? 2 : w->expert_dtype == MOE_DTYPE_INT8 ? 1 : 0;
     const int H = d->hidden, E = d->num_experts, K = d->top_k, I = d->expert_inter, Id = d->dense_inter;
     int32_t* topk_idx = at<int32_t>(ws, L.topk_idx);
     float* topk_w = at<float>(ws, L.topk_w);
@@ -322,6 +332,14 @@ int block_impl(const moe_dims* d, const moe_weights* w, const void* x, const voi
         sa.dgu_part = at<float>(ws, L.dgu_part);
         sa.hpart = at<float>(ws, L.hpart);
         sa.with_dense = 1;  // the dense MLP's items ride along in K2, K3 and K4
+        if (wq == 2) {
+            sa.xq = at<uint16_t>(ws, L.xq);
+            sa.x_scale = at<float>(ws, L.xscale);
+            HIP_TRY(st.begin("act_quant"), "event record");
+            HIP_TRY(moe::launch_act_quant_fp8(xb, T, H, at<uint16_t>(ws, L.xq), at<float>(ws, L.xscale), nullptr,
+                                              nullptr, stream),
+                    "act_quant launch");
+        }
         HIP_TRY(st.begin("decode_front"), "event record");
         float* lpart = at<float>(ws, L.lpart);
         float* ss_part = at<float>(ws, L.ss_part);
@@ -333,9 +351,14 @@ int block_impl(const moe_dims* d, const moe_weights* w, const void* x, const voi
                                          topk_idx, topk_w, stream),
                 "decode_route launch");
         HIP_TRY(st.begin("decode_experts_gateup"), "event record");
-        HIP_TRY(moe::launch_decode_experts_gateup(sa, int8, stream), "decode_experts_gateup launch");
+        HIP_TRY(moe::launch_decode_experts_gateup(sa, wq, stream), "decode_experts_gateup launch");
+        if (wq == 2) {
+            sa.h_scale = at<float>(ws, L.hscale);
+            HIP_TRY(st.begin("h_quant"), "event record");
+            HIP_TRY(moe::launch_decode_hquant(sa, stream), "decode_hquant launch");
+        }
         HIP_TRY(st.begin("decode_down"), "event record");
-        HIP_TRY(moe::launch_decode_down(sa, int8, stream), "decode_down launch");
+        HIP_TRY(moe::launch_decode_down(sa, wq, stream), "decode_down launch");
         if (norms) {
             HIP_TRY(st.begin("ffn_post"), "event record");
             HIP_TRY(moe::launch_ffn_post((const uint16_t*)hres, sa.dpart, sa.part, true, po.inv_row, topk_w, T, H,
@@ -356,10 +379,19 @@ int block_impl(const moe_dims* d, const moe_weights* w, const void* x, const voi
         HIP_TRY(moe::launch_permute(topk_idx, topk_w, pair_rank, T, K, E, moe::kGemmBM, po, stream),
                 "permute launch");
         moe::GemmArgs g{};
-        // experts gate/up + GELU: gathered rows of x
+        // experts gate/up + GELU: gathered rows of x (E4M3 experts: of x
+        // quantised per token, with the token scales applied before the GELU)
         g.A = xb; g.lda = H; g.a_rows = po.perm_token;
+        if (wq == 2) {
+            HIP_TRY(st.begin("act_quant"), "event record");
+            HIP_TRY(moe::launch_act_quant_fp8(xb, T, H, at<uint16_t>(ws, L.xq), at<float>(ws, L.xscale), nullptr,
+                                              nullptr, stream),
+                    "act_quant launch");
+            g.A = at<uint16_t>(ws, L.xq);
+            g.a_scale = at<float>(ws, L.xscale);
+        }
         g.B = w->expert_gate_up; g.b_group_stride = (int64_t)2 * I * H; g.ldb = H;
-        g.b_scale = int8 ? w->gate_up_scale : nullptr; g.scale_group_stride = 2 * I;
+        g.b_scale = wq ? w->gate_up_scale : nullptr; g.scale_group_stride = 2 * I;
         g.K = H; g.n_out = I; g.up_off = I;
         g.mtile_group = po.mtile_group; g.mtile_row0 = po.mtile_row0; g.n_mtiles = po.n_mtiles;
         g.group_end = po.offsets; g.max_mtiles = L.max_mtiles; g.tiles = po.tiles[0];
@@ -369,22 +401,31 @@ int block_impl(const moe_dims* d, const moe_weights* w, const void* x, const voi
         gd.A = xdb; gd.lda = H; gd.B = w->dense_gate_up; gd.ldb = H; gd.K = H;
         gd.n_out = Id; gd.up_off = Id; gd.M_dense = T; gd.C = hd; gd.ldc = Id;
         HIP_TRY(st.begin("gemm_gateup"), "event record");
-        HIP_TRY(moe::launch_gemm_gateup(g, &gd, int8, stream), "gemm_gateup launch");
+        HIP_TRY(moe::launch_gemm_gateup(g, &gd, wq, stream), "gemm_gateup launch");
         // experts down, weighted rows
         moe::GemmArgs gw{};
         gw.A = h; gw.lda = I; gw.B = w->expert_down; gw.b_group_stride = (int64_t)H * I; gw.ldb = I;
-        gw.b_scale = int8 ? w->down_scale : nullptr; gw.scale_group_stride = H;
+        gw.b_scale = wq ? w->down_scale : nullptr; gw.scale_group_stride = H;
         gw.K = I; gw.n_out = H;
         gw.mtile_group = po.mtile_group; gw.mtile_row0 = po.mtile_row0; gw.n_mtiles = po.n_mtiles;
         gw.group_end = po.offsets; gw.max_mtiles = L.max_mtiles; gw.tiles = po.tiles[1];
         gw.C = rows; gw.ldc = H; gw.row_w = po.perm_w;
+        if (wq == 2) {
+            // h quantised per row in place; each row's factor becomes router
+            // weight x scale x 2^16
+            HIP_TRY(st.begin("h_quant"), "event record");
+            HIP_TRY(moe::launch_act_quant_fp8(h, (int64_t)T * K, I, h, at<float>(ws, L.hscale), po.perm_w,
+                                              at<float>(ws, L.wrow), stream),
+                    "h_quant launch");
+            gw.row_w = at<float>(ws, L.wrow);
+        }
         // dense down (fp32), in the same launch
         float* dout = at<float>(ws, L.dout);
         moe::GemmArgs gc{};
         gc.A = hd; gc.lda = Id; gc.B = w->dense_down; gc.ldb = Id; gc.K = Id; gc.n_out = H;
         gc.M_dense = T; gc.Cf = dout; gc.ldc = H;
         HIP_TRY(st.begin("gemm_down"), "event record");
-        HIP_TRY(moe::launch_gemm_down(gw, &gc, int8, stream), "gemm_down launch");
+        HIP_TRY(moe::launch_gemm_down(gw, &gc, wq, stream), "gemm_down launch");
         if (norms) {
             HIP_TRY(st.begin("ffn_post"), "event record");
             HIP_TRY(moe::launch_ffn_post((const uint16_t*)hres, dout, rows, false, po.inv_row, nullptr, T, H, K,
@@ -547,18 +588,18 @@ int dense_mlp(const moe_dims* d, const void* dense_gate_up, const void* dense_do
         sa.dgu_part = at<float>(ws, L.dgu_part);
         HIP_TRY(moe::launch_decode_front(sa, nullptr, nullptr, nullptr, nullptr, stream),
                 "decode_front launch");
-        HIP_TRY(moe::launch_decode_experts_gateup(sa, false, stream), "dense finish launch");
-        HIP_TRY(moe::launch_decode_down(sa, false, stream), "decode_down launch");
+        HIP_TRY(moe::launch_decode_experts_gateup(sa, 0, stream), "dense finish launch");
+        HIP_TRY(moe::launch_decode_down(sa, 0, stream), "decode_down launch");
         HIP_TRY(moe::launch_decode_combine(sa, stream), "decode_combine launch");
     } else {
         moe::GemmArgs gd{};
         gd.A = (const uint16_t*)x; gd.lda = H; gd.B = dense_gate_up; gd.ldb = H; gd.K = H;
         gd.n_out = Id; gd.up_off = Id; gd.M_dense = T; gd.C = hd; gd.ldc = Id;
-        HIP_TRY(moe::launch_gemm_gateup(gd, nullptr, false, stream), "gemm_gateup dense launch");
+        HIP_TRY(moe::launch_gemm_gateup(gd, nullptr, 0, stream), "gemm_gateup dense launch");
         moe::GemmArgs gc{};
         gc.A = hd; gc.lda = Id; gc.B = dense_down; gc.ldb = Id; gc.K = Id; gc.n_out = H;
         gc.M_dense = T; gc.C = (uint16_t*)y; gc.ldc = H;
-        HIP_TRY(moe::launch_gemm_down(gc, nullptr, false, stream), "gemm_down dense launch");
+        HIP_TRY(moe::launch_gemm_down(gc, nullptr, 0, stream), "gemm_down dense launch");
     }
     return MOE_OK;
 }
@@ -578,9 +619,23 @@ int moe_quantize_int8(const void* w_bf16, int64_t rows, int32_t cols, int8_t* q,
     return MOE_OK;
 }
 
+int moe_quantize_fp8(const void* w_bf16, int64_t rows, int32_t cols, uint8_t* q, float* scale,
+                     hipStream_t stream) {
+    if (rows < 0 || rows > ((int64_t)1 << 32) || cols <= 0 || cols % 8)
+        return fail(MOE_ERR_SHAPE, "rows=%lld cols=%d (need rows >= 0, cols > 0, cols %% 8 == 0)",
+                    (long long)rows, cols);
+    CHECK_PTR(w_bf16, "w", 16);
+    CHECK_PTR(q, "q", 16);
+    CHECK_PTR(scale, "scale", 4);
+    g_err[0] = 0;
+    if (rows == 0) return MOE_OK;
+    HIP_TRY(moe::launch_quantize_fp8((const uint16_t*)w_bf16, rows, cols, q, scale, stream), "quantize launch");
+    return MOE_OK;
+}
+
 int moe_tile_weights(const void* src, int64_t rows, int32_t cols, int32_t dtype, void* dst,
                      hipStream_t stream) {
-    if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_INT8)
+    if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_INT8 && dtype != MOE_DTYPE_FP8)
         return fail(MOE_ERR_UNSUPPORTED, "dtype %d", dtype);
     if (rows < 0 || rows % 16 || cols <= 0 || cols % 64)
         return fail(MOE_ERR_SHAPE, "rows=%lld cols=%d (need rows %% 16 == 0, cols %% 64 == 0)",
@@ -590,7 +645,7 @@ int moe_tile_weights(const void* src, int64_t rows, int32_t cols, int32_t dtype,
     if (src == dst) return fail(MOE_ERR_SHAPE, "src and dst must be different buffers");
     g_err[0] = 0;
     if (rows == 0) return MOE_OK;
-    HIP_TRY(moe::launch_tile_weights(src, rows, cols, dtype == MOE_DTYPE_INT8, dst, stream),
+    HIP_TRY(moe::launch_tile_weights(src, rows, cols, dtype != MOE_DTYPE_BF16, dst, stream),
             "tile launch");
     return MOE_OK;
 }

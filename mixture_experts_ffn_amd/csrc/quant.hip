@@ -51,4 +51,121 @@ hipError_t launch_quantize_int8(const uint16_t* w, int64_t rows, int cols, int8_
     return hipGetLastError();
 }
 
+// ---- E4M3 (the recipe page's fp8 variant: E4M3 weights, activations
+// quantised per token at run time). scale = max|v| / 448 in fp32 (IEEE
+// division); code = nearest E4M3 of v / scale, ties to the even code; an
+// all-zero row gets scale 0 and codes 0.
+
+// weights: one wavefront a row of a bf16 [rows, cols] matrix -> codes + scale
+__global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t* __restrict__ w, int64_t rows,
+                                                           int cols, uint8_t* __restrict__ q,
+                                                           float* __restrict__ scale) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + wave;
+    if (r >= rows) return;
+    const uint4* src = reinterpret_cast<const uint4*>(w + r * cols);
+    const int nc = cols >> 3;
+    float amax = 0.f;
+    for (int c = lane; c < nc; c += kWave) {
+        float f[8];
+        unpack8(src[c], f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    }
+    amax = wave_max<kWave>(amax);
+    const float s = amax / 448.0f;
+    if (lane == 0) scale[r] = s;
+    uint2* dst = reinterpret_cast<uint2*>(q + r * cols);
+    for (int c = lane; c < nc; c += kWave) {
+        float f[8];
+        unpack8(src[c], f);
+        uint32_t b[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) b[i] = s > 0.f ? fp8_e4m3_code(f[i] / s) : 0u;
+        dst[c] = make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
+                            b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
+    }
+}
+
+// activations: one wavefront a row of a bf16 [rows, cols] matrix, the row
+// held in registers (NC 8-value chunks a lane, all loads issued at once) ->
+// the row's codes as bf16 carriers (value * 2^-8) in xq (xq == x allowed: a
+// row is read whole before it is written), its scale, and (mul_out) mul_in[r]
+// * scale[r] * 2^16, the factor the down projection's rows take
+template <int NC>
+__global__ __launch_bounds__(256) void act_quant_fp8_kernel(const uint16_t* x, int64_t rows, int cols,
+                                                            uint16_t* xq, float* __restrict__ scale,
+                                                            const float* __restrict__ mul_in,
+                                                            float* __restrict__ mul_out) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + wave;
+    if (r >= rows) return;
+    const uint4* src = reinterpret_cast<const uint4*>(x + r * cols);
+    uint4* dst = reinterpret_cast<uint4*>(xq + r * cols);
+    const int nc = cols >> 3;
+    uint4 v[NC];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) v[j] = src[min(lane + j * kWave, nc - 1)];  // clamped: same max
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        float f[8];
+        unpack8(v[j], f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    }
+    amax = wave_max<kWave>(amax);
+    const float s = amax / 448.0f;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        const int c = lane + j * kWave;
+        if (c < nc) {
+            float f[8];
+            unpack8(v[j], f);
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t c0 = s > 0.f ? fp8_e4m3_code(f[2 * i] / s) : 0u;
+                const uint32_t c1 = s > 0.f ? fp8_e4m3_code(f[2 * i + 1] / s) : 0u;
+                o[i] = fp8_as_bf16_bits(c0) | (fp8_as_bf16_bits(c1) << 16);
+            }
+            dst[c] = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    }
+    if (lane == 0) {
+        scale[r] = s;
+        if (mul_out) mul_out[r] = mul_in[r] * s * 65536.f;
+    }
+}
+
+hipError_t launch_quantize_fp8(const uint16_t* w, int64_t rows, int cols, uint8_t* q, float* scale,
+                               hipStream_t stream) {
+    const int64_t blocks = (rows + 3) / 4;
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(quantize_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w, rows, cols, q,
+                       scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_act_quant_fp8(const uint16_t* x, int64_t rows, int cols, uint16_t* xq, float* scale,
+                                const float* mul_in, float* mul_out, hipStream_t stream) {
+    const int64_t blocks = (rows + 3) / 4;
+    if (blocks <= 0) return hipSuccess;
+    const int nc = (cols / 8 + kWave - 1) / kWave;  // 8-value chunks a lane
+#define LAUNCH(N)                                                                                          \
+    do {                                                                                                   \
+        hipLaunchKernelGGL(act_quant_fp8_kernel<N>, dim3((unsigned)blocks), dim3(256), 0, stream, x, rows, \
+                           cols, xq, scale, mul_in, mul_out);                                              \
+        return hipGetLastError();                                                                          \
+    } while (0)
+    if (nc <= 2) LAUNCH(2);
+    if (nc <= 4) LAUNCH(4);
+    if (nc <= 6) LAUNCH(6);
+    if (nc <= 8) LAUNCH(8);
+    if (nc <= 16) LAUNCH(16);
+    if (nc <= 32) LAUNCH(32);
+#undef LAUNCH
+    return hipErrorInvalidValue;  // cols <= 16384
+}
+
 }  // namespace moe

@@ -45,18 +45,18 @@ class LayerWeights:
     router_scale: torch.Tensor            # [H] bf16
     router_w: torch.Tensor                # [E, H] bf16
     per_expert_scale: torch.Tensor        # [E] fp32
-    expert_gate_up: torch.Tensor          # [E, 2I, H] bf16 or int8
-    expert_down: torch.Tensor             # [E, H, I] bf16 or int8
+    expert_gate_up: torch.Tensor          # [E, 2I, H] bf16, int8, or E4M3 codes (float8_e4m3fn or uint8)
+    expert_down: torch.Tensor             # [E, H, I] same format
     dense_gate_up: torch.Tensor           # [2Id, H] bf16
     dense_down: torch.Tensor              # [H, Id] bf16
     logit_bias: Optional[torch.Tensor] = None   # [E] fp32
-    gate_up_scale: Optional[torch.Tensor] = None  # [E, 2I] fp32 (int8)
-    down_scale: Optional[torch.Tensor] = None     # [E, H] fp32 (int8)
+    gate_up_scale: Optional[torch.Tensor] = None  # [E, 2I] fp32 (int8, E4M3)
+    down_scale: Optional[torch.Tensor] = None     # [E, H] fp32 (int8, E4M3)
     layout: int = _abi.MOE_LAYOUT_ROWS            # of the four expert / dense matrices
 
     @property
     def expert_dtype(self) -> int:
-        return _abi.MOE_DTYPE_INT8 if self.expert_gate_up.dtype == torch.int8 else _abi.MOE_DTYPE_BF16
+        return _weight_format(self.expert_gate_up.dtype)
 
     def c(self) -> MoeWeights:
         def ptr(t):
@@ -232,6 +232,31 @@ def moe_prefill_chunked(dims: BlockDims, weights: LayerWeights, norms: Optional[
     return out
 
 
+def _weight_format(dt) -> int:
+    if dt == torch.bfloat16:
+        return _abi.MOE_DTYPE_BF16
+    if dt == torch.int8:
+        return _abi.MOE_DTYPE_INT8
+    if dt in (torch.uint8, torch.float8_e4m3fn):
+        return _abi.MOE_DTYPE_FP8
+    raise TypeError(f"expert weights must be bf16, int8 or E4M3 codes (float8_e4m3fn / uint8), got {dt}")
+
+
+def moe_quantize_fp8(w: torch.Tensor, q=None, scale=None, stream=None):
+    """Per-row E4M3 of a bf16 tensor [..., cols]: returns (codes float8_e4m3fn, scale fp32 [...])."""
+    w = _dev(w, "w")
+    cols = w.shape[-1]
+    rows = w.numel() // cols
+    if q is None:
+        q = torch.empty(w.shape, dtype=torch.float8_e4m3fn, device=w.device)
+    if scale is None:
+        scale = torch.empty(w.shape[:-1], dtype=torch.float32, device=w.device)
+    rc = _lib().moe_quantize_fp8(w.data_ptr(), rows, cols, _dev(q, "q").data_ptr(),
+                                 _dev(scale, "scale").data_ptr(), _stream(stream))
+    _check(rc, "moe_quantize_fp8")
+    return q, scale
+
+
 def moe_quantize_int8(w: torch.Tensor, q=None, scale=None, stream=None):
     """Per-row symmetric int8 of a bf16 tensor [..., cols]: returns (q int8, scale fp32 [...])."""
     w = _dev(w, "w")
@@ -252,12 +277,7 @@ def moe_tile_weights(w: torch.Tensor, out=None, stream=None) -> torch.Tensor:
     (all leading dimensions stacked as rows). Same shape and dtype; the data is
     re-laid into 16 x 64 tiles (include/moe.h, MOE_LAYOUT_TILED)."""
     w = _dev(w, "w")
-    if w.dtype == torch.bfloat16:
-        dtype = _abi.MOE_DTYPE_BF16
-    elif w.dtype == torch.int8:
-        dtype = _abi.MOE_DTYPE_INT8
-    else:
-        raise TypeError(f"w must be bf16 or int8, got {w.dtype}")
+    dtype = _weight_format(w.dtype)
     cols = w.shape[-1]
     rows = w.numel() // cols
     if out is None:

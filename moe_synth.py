@@ -64,6 +64,7 @@ class Workload:
     seed: int
     skew: bool = False
     int8: bool = False
+    fp8: bool = False
     note: str = ""
 
 
@@ -77,6 +78,10 @@ WORKLOADS = {
                             note="real shape, int8 per-channel experts, T=8"),
     "int8_prefill": Workload("int8_prefill", REAL, 4096, 4, int8=True,
                              note="real shape, int8 per-channel experts, T=4096"),
+    "fp8_decode": Workload("fp8_decode", REAL, 8, 5, fp8=True,
+                           note="real shape, E4M3 experts with per-token activation quantisation, T=8"),
+    "fp8_prefill": Workload("fp8_prefill", REAL, 2048, 5, fp8=True,
+                            note="real shape, E4M3 experts with per-token activation quantisation, T=2048"),
     "mtp_decode": Workload("mtp_decode", REAL, 40, 1,
                            note="real shape, multi-token decode: 8 sequences x 5 tokens"),
     "long_prefill": Workload("long_prefill", REAL, 40960, 2,

@@ -6,7 +6,7 @@ import torch
 
 import moe_synth
 import oracle
-from mixture_experts_ffn_amd import BlockDims, LayerWeights, moe_quantize_int8, tile_layer
+from mixture_experts_ffn_amd import BlockDims, LayerWeights, moe_quantize_fp8, moe_quantize_int8, tile_layer
 
 COS_MIN = 0.9999
 REL_BF16 = 1e-2
@@ -27,10 +27,10 @@ def f32_dev(a, dev):
     return None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
 
 
-def upload(w: dict, dev, int8: bool = False) -> LayerWeights:
+def upload(w: dict, dev, int8: bool = False, fp8: bool = False) -> LayerWeights:
     """Device copy of a generated layer, its expert and dense matrices in the
-    tiled layout the block reads. int8 experts are quantised on the GPU by the
-    library's own quantiser (row-major), then tiled."""
+    tiled layout the block reads. int8 and E4M3 experts are quantised on the GPU
+    by the library's own quantisers (row-major), then tiled."""
     gu = bf16_dev(w["expert_gate_up"], dev)
     dn = bf16_dev(w["expert_down"], dev)
     lw = LayerWeights(
@@ -42,6 +42,10 @@ def upload(w: dict, dev, int8: bool = False) -> LayerWeights:
         lw.expert_gate_up, lw.gate_up_scale = moe_quantize_int8(gu)
         lw.expert_down, lw.down_scale = moe_quantize_int8(dn)
         del gu, dn
+    if fp8:
+        lw.expert_gate_up, lw.gate_up_scale = moe_quantize_fp8(gu)
+        lw.expert_down, lw.down_scale = moe_quantize_fp8(dn)
+        del gu, dn
     return tile_layer(lw)
 
 
@@ -50,6 +54,22 @@ def oracle_int8_weights(w: dict) -> dict:
     wq["expert_gate_up_q"], wq["expert_gate_up_scale"] = oracle.quantize_int8(w["expert_gate_up"])
     wq["expert_down_q"], wq["expert_down_scale"] = oracle.quantize_int8(w["expert_down"])
     return wq
+
+
+def oracle_fp8_weights(w: dict) -> dict:
+    wq = dict(w)
+    wq["expert_gate_up_f8"], wq["expert_gate_up_f8_scale"] = oracle.quantize_fp8(w["expert_gate_up"])
+    wq["expert_down_f8"], wq["expert_down_f8_scale"] = oracle.quantize_fp8(w["expert_down"])
+    return wq
+
+
+def oracle_weights(wl, w: dict):
+    """(the oracle's weights, its expert_dtype) for a workload's format."""
+    if wl.int8:
+        return oracle_int8_weights(w), "int8"
+    if wl.fp8:
+        return oracle_fp8_weights(w), "fp8"
+    return w, "bf16"
 
 
 def check_routing(gpu_idx: np.ndarray, gpu_w: np.ndarray, ref: dict, pes: np.ndarray):
@@ -93,6 +113,8 @@ def compare_y(y_gpu: np.ndarray, y_ref: np.ndarray, rel_max: float):
 def to_np(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).cpu().numpy()
     return t.cpu().numpy()
 
 

@@ -17,10 +17,11 @@ import moe_synth
 import oracle
 from mixture_experts_ffn_amd import (MOE_PATH_AUTO, MOE_PATH_GROUPED, MOE_PATH_STREAM, BlockCall, FfnNorms,
                                      MoEError, dense_mlp, moe_block, moe_ffn_layer, moe_prefill_chunk_tokens,
-                                     moe_prefill_chunked, moe_prefill_workspace_bytes, moe_quantize_int8,
+                                     moe_prefill_chunked, moe_prefill_workspace_bytes, moe_quantize_fp8,
+                                     moe_quantize_int8,
                                      moe_route, moe_tile_weights, moe_workspace_bytes, new_debug)
 from gpu_util import (REL_BF16, REL_INT8, bf16_dev, check_routing, compare_y, dims_of,
-                      oracle_int8_weights, routing_for, to_np, upload, y_f64)
+                      oracle_int8_weights, oracle_weights, routing_for, to_np, upload, y_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,10 +46,10 @@ def inputs(name, dev, tokens=None):
     key = (name, tokens)
     if key not in _CACHE:
         wl = moe_synth.WORKLOADS[name]
-        wkey = (wl.shape, wl.seed, wl.skew, wl.int8)
+        wkey = (wl.shape, wl.seed, wl.skew, wl.int8, wl.fp8)
         if wkey not in _WCACHE:
             w = moe_synth.make_weights(wl.shape, wl.seed, wl.skew)
-            _WCACHE[wkey] = (w, upload(w, dev, int8=wl.int8))
+            _WCACHE[wkey] = (w, upload(w, dev, int8=wl.int8, fp8=wl.fp8))
         w, lw = _WCACHE[wkey]
         x = moe_synth.make_tokens(wl.shape, wl.seed, wl.tokens if tokens is None else tokens)
         _CACHE[key] = (wl, w, x, lw, bf16_dev(x, dev))
@@ -94,7 +95,7 @@ def _tiled_reference(w: np.ndarray) -> np.ndarray:
     all lanes, then 8..15; int8 tiles store each lane's 16 positions together."""
     rows, cols = w.shape
     out = np.empty(w.size, dtype=w.dtype)
-    tb = 1024 if w.dtype == np.int8 else 2048
+    tb = 1024 if w.dtype.itemsize == 1 else 2048
     esz = w.dtype.itemsize
     for r in range(rows):
         for c in range(cols):
@@ -112,7 +113,7 @@ def _tiled_reference(w: np.ndarray) -> np.ndarray:
 def _tiled(w: np.ndarray) -> np.ndarray:
     """Vectorised form of _tiled_reference (checked against it below)."""
     rows, cols = w.shape
-    if w.dtype == np.int8:  # (ti, r, tj, g, pos) -> (ti, tj, g, r, pos)
+    if w.dtype.itemsize == 1:  # int8 or E4M3 codes: (ti, r, tj, g, pos) -> (ti, tj, g, r, pos)
         return w.reshape(rows // 16, 16, cols // 64, 4, 16).transpose(0, 2, 3, 1, 4).ravel()
     # (ti, r, tj, g, h, e) -> (ti, tj, h, g, r, e)
     return w.reshape(rows // 16, 16, cols // 64, 4, 2, 8).transpose(0, 2, 4, 3, 1, 5).ravel()
@@ -134,6 +135,34 @@ def test_tile_weights_layout(dev, dtype, shape):
     ref = _tiled_reference(w.reshape(-1, shape[-1]))
     np.testing.assert_array_equal(got, ref)
     np.testing.assert_array_equal(_tiled(w.reshape(-1, shape[-1])), ref)
+
+
+def test_quantize_fp8_bit_exact(dev):
+    """The E4M3 quantiser: codes and scales bit for bit against the oracle's,
+    on real-shape expert weights and on rows built to hit ties, subnormal codes
+    and zero rows."""
+    say("case: fp8 quantiser, real-shape expert weights (seed 5)")
+    wl, w, x, lw, xd = inputs("fp8_decode", dev)
+    q_ref, s_ref = oracle.quantize_fp8(w["expert_gate_up"][:16])
+    q, s = moe_quantize_fp8(bf16_dev(w["expert_gate_up"][:16], dev))
+    np.testing.assert_array_equal(to_np(q), q_ref)
+    np.testing.assert_array_equal(to_np(s).view(np.uint32), s_ref.view(np.uint32))
+    # the full layer as uploaded for the block (quantised, then tiled)
+    qd_ref, sd_ref = oracle.quantize_fp8(w["expert_down"])
+    np.testing.assert_array_equal(to_np(lw.expert_down).ravel(), _tiled(qd_ref.reshape(-1, qd_ref.shape[-1])))
+    np.testing.assert_array_equal(to_np(lw.down_scale).view(np.uint32), sd_ref.view(np.uint32))
+    # rows whose scale is a power of two (max 448 * 2^k): every value is exact
+    # in fp32 after the division, so halfway cases stay halfway
+    rng = np.random.default_rng(9)
+    grid = np.array([0.0, 2.0 ** -10, 1.5 * 2.0 ** -9, 2.0 ** -7, 1.0625, 1.1875, 3.25, 100.0, 300.0],
+                    dtype=np.float32)
+    rows = np.stack([np.concatenate([[448.0], rng.choice(grid, 63) * rng.choice([-1, 1], 63)]) * 2.0 ** k
+                     for k in range(-8, 8)] + [np.zeros(64)]).astype(np.float32)
+    bits = moe_synth.f32_to_bf16_bits(rows)
+    q2_ref, s2_ref = oracle.quantize_fp8(bits)
+    q2, s2 = moe_quantize_fp8(bf16_dev(bits, dev))
+    np.testing.assert_array_equal(to_np(q2), q2_ref)
+    np.testing.assert_array_equal(to_np(s2).view(np.uint32), s2_ref.view(np.uint32))
 
 
 def test_quantize_int8_bit_exact(dev):
@@ -172,7 +201,8 @@ PATH_CASES = [("tiny", MOE_PATH_STREAM), ("tiny", MOE_PATH_GROUPED),
               ("prefill", MOE_PATH_GROUPED), ("skew", MOE_PATH_GROUPED),
               ("int8_decode", MOE_PATH_STREAM), ("int8_decode", MOE_PATH_GROUPED),
               ("int8_prefill", MOE_PATH_GROUPED),
-              ("mtp_decode", MOE_PATH_STREAM), ("mtp_decode", MOE_PATH_GROUPED)]
+              ("mtp_decode", MOE_PATH_STREAM), ("mtp_decode", MOE_PATH_GROUPED),
+              ("fp8_decode", MOE_PATH_STREAM), ("fp8_decode", MOE_PATH_GROUPED), ("fp8_prefill", MOE_PATH_GROUPED)]
 
 
 @pytest.mark.parametrize("name,path", PATH_CASES)
@@ -191,10 +221,9 @@ def test_block_parity(dev, name, path):
     # block output on sampled tokens
     toks = sample_tokens(T)
     r = routing_for(dbg["topk_idx"][toks], {k: v[toks] for k, v in ref.items()}, w["per_expert_scale"])
-    ow = oracle_int8_weights(w) if wl.int8 else w
-    y_ref, _ = oracle.moe_block(x[toks], ow, s.top_k, s.rms_eps,
-                                expert_dtype="int8" if wl.int8 else "bf16", routing=r)
-    cos, rel = compare_y(y_f64(y)[toks], y_ref, REL_INT8 if wl.int8 else REL_BF16)
+    ow, fmt = oracle_weights(wl, w)
+    y_ref, _ = oracle.moe_block(x[toks], ow, s.top_k, s.rms_eps, expert_dtype=fmt, routing=r)
+    cos, rel = compare_y(y_f64(y)[toks], y_ref, REL_BF16 if fmt == "bf16" else REL_INT8)
     say(f"  tokens checked {len(toks)}  cos {cos:.7f}  rel-L2 {rel:.3e}")
 
 
@@ -208,7 +237,7 @@ def test_skew_routing_collapses_to_few_experts(dev):
     assert counts.max() > 8 * x.shape[0] * wl.shape.top_k / wl.shape.num_experts
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode", "int8_decode"])
+@pytest.mark.parametrize("name", ["tiny", "decode", "int8_decode", "fp8_decode"])
 def test_stream_and_grouped_paths_agree(dev, name):
     wl, w, x, lw, xd = inputs(name, dev)
     say(f"case: paths agree {name}")
