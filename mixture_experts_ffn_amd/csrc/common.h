@@ -102,7 +102,7 @@ __device__ __forceinline__ void lds_barrier() {
 // E4M3 in its OCP form without infinities: sign, 4 exponent bits (bias 7), 3
 // mantissa bits; exponent field 0 holds the subnormals m 2^-9; the largest
 // finite value is 448. The kernels carry E4M3 values as bf16 holding value *
-// 2^-8 and fold 2^8 per operand into the scales.
+// 2^-8 (half carriers) and fold 2^8 per operand into the scales.
 
 // nearest E4M3 code of an fp32 value, ties to the even code, saturating at 448
 __device__ __forceinline__ uint32_t fp8_e4m3_code(float v) {
@@ -128,16 +128,54 @@ __device__ __forceinline__ uint32_t fp8_e4m3_code(float v) {
 
 // an E4M3 code's bits placed at the top of a half (sign to bit 15, exponent
 // and mantissa to bits 7..13) are exactly its value * 2^-8, subnormals
-// included (the exponent biases differ by 8); widened to fp32 and, with at
-// most 4 significant bits, cut to bf16 without rounding. (Code 0x7F, a NaN,
-// never produced by the quantisers, would read as 480.)
-__device__ __forceinline__ uint32_t fp8_as_bf16_bits(uint32_t c) {
-    const float f = (float)__builtin_bit_cast(_Float16, (unsigned short)(((c & 0x80u) << 8) | ((c & 0x7Fu) << 7)));
-    return __float_as_uint(f) >> 16;
+// included (the exponent biases differ by 8): the half carrier of a code. (Code
+// 0x7F, a NaN, never produced by the quantisers, would read as 480.)
+__device__ __forceinline__ uint32_t fp8_as_f16_bits(uint32_t c) { return ((c & 0x80u) << 8) | ((c & 0x7Fu) << 7); }
+// two E4M3 codes (bytes sh / 8 and sh / 8 + 1 of a word) -> a packed pair of half carriers
+__device__ __forceinline__ uint32_t fp8pair_to_f16(uint32_t word, int sh) {
+    const uint32_t p = ((word >> sh) & 0xFFu) | (((word >> sh) << 8) & 0xFF0000u);  // bytes to 0 and 2
+    return ((p & 0x007F007Fu) << 7) | ((p & 0x00800080u) << 8);
 }
-// two E4M3 codes (bytes sh and sh + 8 of a word) -> packed bf16 pair (value * 2^-8)
-__device__ __forceinline__ uint32_t fp8pair_to_bf16(uint32_t word, int sh) {
-    return fp8_as_bf16_bits((word >> sh) & 0xFFu) | (fp8_as_bf16_bits((word >> (sh + 8)) & 0xFFu) << 16);
+
+// One wavefront quantises a bf16 row of nc 8-value chunks (nc <= 64 NC) to
+// E4M3 per row: scale = max|x| / 448 (fp32, IEEE division), codes the nearest
+// to x / scale, ties to even, written as half carriers to xq (xq == x allowed:
+// the row is held in registers, all loads issued before any store). Returns
+// the scale (0 for an all-zero row, whose codes are 0).
+template <int NC>
+__device__ __forceinline__ float fp8_quantize_row(const uint16_t* x, uint16_t* xq, int nc, int lane) {
+    const uint4* src = reinterpret_cast<const uint4*>(x);
+    uint4* dst = reinterpret_cast<uint4*>(xq);
+    uint4 v[NC];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) v[j] = src[min(lane + j * kWave, nc - 1)];  // clamped: same max
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        float f[8];
+        unpack8(v[j], f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    }
+    amax = wave_max<kWave>(amax);
+    const float s = amax / 448.0f;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        const int c = lane + j * kWave;
+        if (c < nc) {
+            float f[8];
+            unpack8(v[j], f);
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t c0 = s > 0.f ? fp8_e4m3_code(f[2 * i] / s) : 0u;
+                const uint32_t c1 = s > 0.f ? fp8_e4m3_code(f[2 * i + 1] / s) : 0u;
+                o[i] = fp8_as_f16_bits(c0) | (fp8_as_f16_bits(c1) << 16);
+            }
+            dst[c] = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    }
+    return s;
 }
 
 }  // namespace moe

@@ -135,16 +135,26 @@ __device__ __forceinline__ void i8x16_to_bf16(const uint4& v, uint4& lo, uint4& 
     lo = i8x8_to_bf16(make_uint4(v.x, v.y, 0u, 0u));
     hi = i8x8_to_bf16(make_uint4(v.z, v.w, 0u, 0u));
 }
-// 16 E4M3 codes (one tiled-layout piece) -> two groups of 8 bf16 (value * 2^-8, exact)
-__device__ __forceinline__ void f8x16_to_bf16(const uint4& v, uint4& lo, uint4& hi) {
-    lo = make_uint4(fp8pair_to_bf16(v.x, 0), fp8pair_to_bf16(v.x, 16), fp8pair_to_bf16(v.y, 0),
-                    fp8pair_to_bf16(v.y, 16));
-    hi = make_uint4(fp8pair_to_bf16(v.z, 0), fp8pair_to_bf16(v.z, 16), fp8pair_to_bf16(v.w, 0),
-                    fp8pair_to_bf16(v.w, 16));
+// 16 E4M3 codes (one tiled-layout piece) -> two groups of 8 half carriers (value * 2^-8, exact)
+__device__ __forceinline__ void f8x16_to_f16(const uint4& v, uint4& lo, uint4& hi) {
+    lo = make_uint4(fp8pair_to_f16(v.x, 0), fp8pair_to_f16(v.x, 16), fp8pair_to_f16(v.y, 0),
+                    fp8pair_to_f16(v.y, 16));
+    hi = make_uint4(fp8pair_to_f16(v.z, 0), fp8pair_to_f16(v.z, 16), fp8pair_to_f16(v.w, 0),
+                    fp8pair_to_f16(v.w, 16));
+}
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+// acc + a.lo*b.lo + a.hi*b.hi on packed halves (v_dot2_f32_f16: the products of
+// two half carriers of E4M3 values are exact in fp32)
+__device__ __forceinline__ float dot8_f16(const uint4& a, const uint4& b, float acc) {
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a.x), __builtin_bit_cast(f16x2_t, b.x), acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a.y), __builtin_bit_cast(f16x2_t, b.y), acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a.z), __builtin_bit_cast(f16x2_t, b.z), acc, false);
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a.w), __builtin_bit_cast(f16x2_t, b.w), acc, false);
 }
 
 // One K-step of a lane's piece of a tile (bf16: two 16-byte halves, 8 k each;
-// int8 or E4M3: one 16-byte piece, 16 k) dotted with the 16 matching x values.
+// int8 or E4M3: one 16-byte piece, 16 k) dotted with the 16 matching x values
+// (for E4M3 the half carriers of x).
 // OPAQUE (int8): the piece is made opaque before it is widened, so that the
 // compiler widens it where it is used instead of hoisting every step's widened
 // copy (twice the registers) out of the caller's loop over tokens.
@@ -157,8 +167,12 @@ __device__ __forceinline__ float piece_dot(const uint4 (&w)[WQ ? 1 : 2], const u
         uint4 v = w[0];
         if (OPAQUE) asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
         uint4 lo, hi;
-        if (WQ == 2) f8x16_to_bf16(v, lo, hi);
-        else i8x16_to_bf16(v, lo, hi);
+        if (WQ == 2) {  // E4M3: half carriers on both sides
+            f8x16_to_f16(v, lo, hi);
+            acc = dot8_f16(lo, x0, acc);
+            return dot8_f16(hi, x1, acc);
+        }
+        i8x16_to_bf16(v, lo, hi);
         acc = dot8_bf16(lo, x0, acc);
         return dot8_bf16(hi, x1, acc);
     }
@@ -450,12 +464,21 @@ __global__ __launch_bounds__(kThreads) void decode_front_kernel(StreamArgs a, co
     __shared__ float red[kWaves * 512 + kWaves * 16];
     const int n_router = wr ? ((a.E + 15) / 16) * kFrontSplit : 0;
     const int b = blockIdx.x;
+    const int n_dense = a.with_dense && a.front_dense ? (a.Id / 16) * kFrontSplit : 0;
     if (b < n_router) {
         const int nt = b / kFrontSplit, ks = b - nt * kFrontSplit;
         router_part<NS>(a.x, a.H, scale, wr, a.E, nt, ks, a.T, lpart, ss_part, red);
-    } else {
+    } else if (b < n_router + n_dense) {
         const int i = b - n_router, hc = i / kFrontSplit, ks = i - hc * kFrontSplit;
         dense_gateup_part<NS>(a.xd, a.H, a.dgu, a.Id, hc, ks, a.T, a.dgu_part, red, (int)threadIdx.x);
+    } else {
+        // E4M3 experts: x quantised per token, a wavefront a token (hidden <= 3072: 6 chunks a lane)
+        const int t = (b - n_router - n_dense) * kWaves + ((int)threadIdx.x >> 6);
+        if (t < a.T) {
+            const float s = fp8_quantize_row<6>(a.x + (int64_t)t * a.H, a.xq + (int64_t)t * a.H, a.H >> 3,
+                                                (int)threadIdx.x & 63);
+            if ((threadIdx.x & 63) == 0) a.x_scale[t] = s;
+        }
     }
 }
 
@@ -504,7 +527,7 @@ __global__ __launch_bounds__(kThreads) void decode_experts_gateup_kernel(StreamA
     const int64_t wstride = (int64_t)2 * a.I * a.H;
     const void* W = WQ ? (const void*)((const int8_t*)a.gu + e * wstride)
                          : (const void*)((const uint16_t*)a.gu + e * wstride);
-    // E4M3 experts read x quantised per token (bf16 carrier of value * 2^-8)
+    // E4M3 experts read x quantised per token (half carriers of value * 2^-8)
     gateup_half_item<NS, WQ>(WQ == 2 ? a.xq : a.x, a.H, W, a.I, hc, half, a.perm_token + p0, n,
                                (int64_t)a.T * a.K * 2 * a.I, a.hpart + (int64_t)p0 * 2 * a.I, xs, red);
 }
@@ -700,10 +723,10 @@ __device__ __forceinline__ void stage_h(const StreamArgs& a, int p0, int n, cons
 // ---------------------------------------------------------------- K3b
 // E4M3 experts: h of each routed pair (grouped row p) from the two K halves'
 // partial sums, times the gate/up column scales and the token's activation
-// scale (times 2^16: the two operands' bf16 carriers hold value * 2^-8),
+// scale (times 2^16: the two operands' half carriers hold value * 2^-8),
 // h = gelu_tanh(gate) * up rounded to bf16, then quantised per row (max |h| /
 // 448, codes round half to even: the recipe page's per-token activation
-// quantisation) into a.h as bf16 carriers, the row scale times 2^16 into
+// quantisation) into a.h as half carriers, the row scale times 2^16 into
 // a.h_scale. Workgroup b takes the rows of active expert b, a wavefront a row;
 // a lane holds NC 8-column chunks.
 template <int NC>
@@ -742,7 +765,7 @@ __global__ __launch_bounds__(kThreads) void decode_hquant_kernel(StreamArgs a) {
                 for (int i = 0; i < 4; ++i) {
                     const uint32_t c0 = s > 0.f ? fp8_e4m3_code(hv[j][2 * i] / s) : 0u;
                     const uint32_t c1 = s > 0.f ? fp8_e4m3_code(hv[j][2 * i + 1] / s) : 0u;
-                    o[i] = fp8_as_bf16_bits(c0) | (fp8_as_bf16_bits(c1) << 16);
+                    o[i] = fp8_as_f16_bits(c0) | (fp8_as_f16_bits(c1) << 16);
                 }
                 reinterpret_cast<uint4*>(a.h + (int64_t)p * I)[cc] = make_uint4(o[0], o[1], o[2], o[3]);
             }
@@ -879,7 +902,8 @@ template <int NS>
 hipError_t launch_front_ns(const StreamArgs& a, const uint16_t* scale, const uint16_t* wr, float* lpart,
                            float* ss_part, hipStream_t stream) {
     const int n_router = wr ? ((a.E + 15) / 16) * kFrontSplit : 0;
-    const int blocks = n_router + (a.with_dense && a.front_dense ? (a.Id / 16) * kFrontSplit : 0);
+    const int n_quant = a.xq ? (a.T + kWaves - 1) / kWaves : 0;  // E4M3 experts: x quantised per token
+    const int blocks = n_router + (a.with_dense && a.front_dense ? (a.Id / 16) * kFrontSplit : 0) + n_quant;
     if (blocks <= 0) return hipSuccess;
     hipLaunchKernelGGL(decode_front_kernel<NS>, dim3(blocks), dim3(kThreads), 0, stream, a, scale, wr, lpart,
                        ss_part);

@@ -125,6 +125,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 // native 4 x u32 vector (a first-class type that stays in registers)
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kAStageElems = BM * BK;  // bf16 elements per LDS stage of A
 
@@ -165,9 +166,9 @@ __device__ __forceinline__ bf16x8_t b_frag(const BStep<WQ>& r, int j, int s) {
         v4u w = r.q[j & 1];
         asm volatile("" : "+v"(w));
         const unsigned w0 = s ? w.z : w.x, w1 = s ? w.w : w.y;
-        if (WQ == 2)  // E4M3 codes: bf16 of value * 2^-8
-            v = v4u{fp8pair_to_bf16(w0, 0), fp8pair_to_bf16(w0, 16), fp8pair_to_bf16(w1, 0),
-                    fp8pair_to_bf16(w1, 16)};
+        if (WQ == 2)  // E4M3 codes: half carriers (value * 2^-8), bit placement only
+            v = v4u{fp8pair_to_f16(w0, 0), fp8pair_to_f16(w0, 16), fp8pair_to_f16(w1, 0),
+                    fp8pair_to_f16(w1, 16)};
         else
             v = v4u{i8pair_to_bf16(w0, 0), i8pair_to_bf16(w0, 16), i8pair_to_bf16(w1, 0),
                     i8pair_to_bf16(w1, 16)};
@@ -212,8 +213,17 @@ __device__ __forceinline__ void mma_step(const uint16_t* As, const BStep<WQ>& rb
                 af[i] = *reinterpret_cast<const bf16x8_t*>(As + swz((g + i) * 16 + (lane & 15), c));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                acc[g + i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], b0, acc[g + i][0], 0, 0, 0);
-                acc[g + i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], b1, acc[g + i][1], 0, 0, 0);
+                if (WQ == 2) {  // E4M3: half carriers in A and B, f16 MFMAs (exact products)
+                    acc[g + i][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, af[i]),
+                                                                           __builtin_bit_cast(f16x8_t, b0),
+                                                                           acc[g + i][0], 0, 0, 0);
+                    acc[g + i][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, af[i]),
+                                                                           __builtin_bit_cast(f16x8_t, b1),
+                                                                           acc[g + i][1], 0, 0, 0);
+                } else {
+                    acc[g + i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], b0, acc[g + i][0], 0, 0, 0);
+                    acc[g + i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], b1, acc[g + i][1], 0, 0, 0);
+                }
             }
             // DS reads first, then the MFMAs, in one scheduling group each
             __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -363,7 +373,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
     if (MODE == MODE_DOWN && !p.Cf && tid < BM)
         row_wt = tid >= rows_valid ? 0.f : p.row_w ? p.row_w[row0 + tid] : 1.f;
     // fp8 gate/up: the per-token scale of each A row, times 2^16 (the 2^-8 of
-    // each operand's bf16 carrier)
+    // each operand's half carrier)
     if (MODE == MODE_GATEUP && WQ == 2 && tid < BM) {
         const int rr = min(tid, rows_valid - 1);
         const int64_t arow = p.a_rows ? p.a_rows[row0 + rr] : (int64_t)(row0 + rr);

@@ -106,8 +106,8 @@ struct StreamArgs {
     int T, H, I, Id, K, E;
     const uint16_t* x;                        // router and experts input
     const uint16_t* xd;                       // dense MLP input
-    // E4M3 experts: x quantised per token (bf16 carriers of value * 2^-8) and its per-token scales
-    const uint16_t* xq; const float* x_scale;
+    // E4M3 experts: x quantised per token (half carriers of value * 2^-8) and its per-token scales
+    uint16_t* xq; float* x_scale;  // written by decode_front's last workgroups
     // experts
     const void* gu; const float* gu_scale;   // [E][2I][H]
     const void* dw; const float* dw_scale;   // [E][H][I]
@@ -160,7 +160,7 @@ hipError_t launch_tile_weights(const void* src, int64_t rows, int cols, bool int
                                hipStream_t stream);
 hipError_t launch_quantize_int8(const uint16_t* w, int64_t rows, int cols, int8_t* q, float* scale,
                                 hipStream_t stream);
-// E4M3 per row: weights -> codes + scales; activations -> bf16 carriers of
+// E4M3 per row: weights -> codes + scales; activations -> half carriers of
 // value * 2^-8 + scales (+ mul_out = mul_in * scale * 2^16 when mul_out is set)
 hipError_t launch_quantize_fp8(const uint16_t* w, int64_t rows, int cols, uint8_t* q, float* scale,
                                hipStream_t stream);

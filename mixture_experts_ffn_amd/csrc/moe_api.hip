@@ -332,13 +332,9 @@ int block_impl(const moe_dims* d, const moe_weights* w, const void* x, const voi
         sa.dgu_part = at<float>(ws, L.dgu_part);
         sa.hpart = at<float>(ws, L.hpart);
         sa.with_dense = 1;  // the dense MLP's items ride along in K2, K3 and K4
-        if (wq == 2) {
+        if (wq == 2) {  // quantised per token by decode_front's last workgroups
             sa.xq = at<uint16_t>(ws, L.xq);
             sa.x_scale = at<float>(ws, L.xscale);
-            HIP_TRY(st.begin("act_quant"), "event record");
-            HIP_TRY(moe::launch_act_quant_fp8(xb, T, H, at<uint16_t>(ws, L.xq), at<float>(ws, L.xscale), nullptr,
-                                              nullptr, stream),
-                    "act_quant launch");
         }
         HIP_TRY(st.begin("decode_front"), "event record");
         float* lpart = at<float>(ws, L.lpart);

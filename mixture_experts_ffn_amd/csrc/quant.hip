@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t* __res
 
 // activations: one wavefront a row of a bf16 [rows, cols] matrix, the row
 // held in registers (NC 8-value chunks a lane, all loads issued at once) ->
-// the row's codes as bf16 carriers (value * 2^-8) in xq (xq == x allowed: a
+// the row's codes as half carriers (value * 2^-8) in xq (xq == x allowed: a
 // row is read whole before it is written), its scale, and (mul_out) mul_in[r]
 // * scale[r] * 2^16, the factor the down projection's rows take
 template <int NC>
@@ -100,38 +100,7 @@ __global__ __launch_bounds__(256) void act_quant_fp8_kernel(const uint16_t* x, i
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t r = (int64_t)blockIdx.x * 4 + wave;
     if (r >= rows) return;
-    const uint4* src = reinterpret_cast<const uint4*>(x + r * cols);
-    uint4* dst = reinterpret_cast<uint4*>(xq + r * cols);
-    const int nc = cols >> 3;
-    uint4 v[NC];
-#pragma unroll
-    for (int j = 0; j < NC; ++j) v[j] = src[min(lane + j * kWave, nc - 1)];  // clamped: same max
-    float amax = 0.f;
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-        float f[8];
-        unpack8(v[j], f);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-    }
-    amax = wave_max<kWave>(amax);
-    const float s = amax / 448.0f;
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-        const int c = lane + j * kWave;
-        if (c < nc) {
-            float f[8];
-            unpack8(v[j], f);
-            uint32_t o[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t c0 = s > 0.f ? fp8_e4m3_code(f[2 * i] / s) : 0u;
-                const uint32_t c1 = s > 0.f ? fp8_e4m3_code(f[2 * i + 1] / s) : 0u;
-                o[i] = fp8_as_bf16_bits(c0) | (fp8_as_bf16_bits(c1) << 16);
-            }
-            dst[c] = make_uint4(o[0], o[1], o[2], o[3]);
-        }
-    }
+    const float s = fp8_quantize_row<NC>(x + r * cols, xq + r * cols, cols >> 3, lane);
     if (lane == 0) {
         scale[r] = s;
         if (mul_out) mul_out[r] = mul_in[r] * s * 65536.f;
