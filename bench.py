@@ -451,6 +451,7 @@ def main():
         "roofline": roof,
         "graph": primary["graph"],
         "ffn_layer": primary["ffn_layer"],
+        **({"chunked": primary["chunked"]} if "chunked" in primary else {}),
         "block": {k: primary[k] for k in ("block_bytes", "block_gbs", "block_hbm_frac", "block_flops",
                                           "block_tflops", "block_mfma_frac", "experts_touched",
                                           "stages_us", "stages_gbs", "dominant")},
