@@ -338,7 +338,8 @@ def test_empty_batch_and_errors(dev):
 
 
 @pytest.mark.parametrize("name,path", [("tiny", MOE_PATH_STREAM), ("tiny", MOE_PATH_GROUPED),
-                                       ("decode", MOE_PATH_STREAM)])
+                                       ("decode", MOE_PATH_STREAM), ("fp8_decode", MOE_PATH_STREAM),
+                                       ("fp8_decode", MOE_PATH_GROUPED)])
 def test_graph_replay(dev, name, path):
     """The block captured into a HIP graph: every replay, with eager calls of
     the block on other tokens (same workspace) and synchronisations between
@@ -388,7 +389,9 @@ def ffn_gains(H, which, dev, eps=1e-5):
 @pytest.mark.parametrize("name,path,which", [
     ("tiny", MOE_PATH_STREAM, "all"), ("tiny", MOE_PATH_GROUPED, "all"), ("tiny", MOE_PATH_GROUPED, "none"),
     ("decode", MOE_PATH_STREAM, "all"), ("decode", MOE_PATH_STREAM, "post_only"),
-    ("decode", MOE_PATH_GROUPED, "pre_moe"), ("prefill", MOE_PATH_GROUPED, "all")])
+    ("decode", MOE_PATH_GROUPED, "pre_moe"), ("prefill", MOE_PATH_GROUPED, "all"),
+    ("int8_decode", MOE_PATH_STREAM, "all"), ("fp8_decode", MOE_PATH_STREAM, "all"),
+    ("fp8_decode", MOE_PATH_GROUPED, "pre_moe")])
 def test_ffn_layer(dev, name, path, which):
     """moe_ffn_layer against the oracle's ffn_layer. Routing as in the block
     tests (on the MoE branch's input); the output compared whole and, since
@@ -408,17 +411,19 @@ def test_ffn_layer(dev, name, path, which):
     assert dbg.path_taken == path
     toks = np.arange(T) if T <= 64 else sample_tokens(T, n=16, seed=5)
     gi, gw = to_np(out_t["topk_idx"])[toks], to_np(out_t["topk_w"])[toks]
-    _, ref_r = oracle.ffn_layer(x[toks], w, norms_np, K, s.rms_eps)
+    ow, fmt = oracle_weights(wl, w)
+    rel_max = REL_BF16 if fmt == "bf16" else REL_INT8
+    _, ref_r = oracle.ffn_layer(x[toks], ow, norms_np, K, s.rms_eps, expert_dtype=fmt)
     check_routing(gi, gw, ref_r, w["per_expert_scale"])
-    ref, _ = oracle.ffn_layer(x[toks], w, norms_np, K, s.rms_eps,
+    ref, _ = oracle.ffn_layer(x[toks], ow, norms_np, K, s.rms_eps, expert_dtype=fmt,
                               routing=routing_for(gi, ref_r, w["per_expert_scale"]))
     got = y_f64(out)[toks]
     h64 = oracle.bf16_to_f64(x[toks])
-    compare_y(got, ref, REL_BF16)
+    compare_y(got, ref, rel_max)
     # the branches' part alone: its rel-L2 error may grow by the output's rounding
     # (2^-9 of |out| per element) and its cosine falls accordingly (1 - rel^2 / 2)
     branch_ref = ref - h64
-    bound = REL_BF16 + 2.0**-9 * np.linalg.norm(ref) / np.linalg.norm(branch_ref)
+    bound = rel_max + 2.0**-9 * np.linalg.norm(ref) / np.linalg.norm(branch_ref)
     a, b = (got - h64).ravel(), branch_ref.ravel()
     rel = float(np.linalg.norm(a - b) / np.linalg.norm(b))
     cos = float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
@@ -427,7 +432,8 @@ def test_ffn_layer(dev, name, path, which):
 
 
 CHUNK_CASES = [("tiny", 2048 + 77, 1024, None), ("tiny", 2048 + 20, 1500, "all"),
-               ("long_prefill", None, 0, None), ("prefill", 2048 + 5, 1024, "all")]
+               ("long_prefill", None, 0, None), ("prefill", 2048 + 5, 1024, "all"),
+               ("fp8_prefill", 2048 + 5, 1024, None)]
 
 
 @pytest.mark.parametrize("name,T,chunk,which", CHUNK_CASES)
@@ -466,13 +472,14 @@ def test_prefill_chunked(dev, name, T, chunk, which):
     assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), "chunked != per-chunk calls"
     toks = sample_tokens(T, n=32, seed=11)
     # the layer routes its MoE branch's input, the pre-normed h
+    ow, fmt = oracle_weights(wl, w)
     ref_r = (oracle_route(wl, w, x[toks]) if norms is None
-             else oracle.ffn_layer(x[toks], w, norms_np, K, s.rms_eps)[1])
+             else oracle.ffn_layer(x[toks], ow, norms_np, K, s.rms_eps, expert_dtype=fmt)[1])
     check_routing(gi[toks], gw[toks], ref_r, w["per_expert_scale"])
     r = routing_for(gi[toks], ref_r, w["per_expert_scale"])
     if norms is None:
-        ref, _ = oracle.moe_block(x[toks], w, K, s.rms_eps, routing=r)
+        ref, _ = oracle.moe_block(x[toks], ow, K, s.rms_eps, expert_dtype=fmt, routing=r)
     else:
-        ref, _ = oracle.ffn_layer(x[toks], w, norms_np, K, s.rms_eps, routing=r)
-    cos, rel = compare_y(y_f64(out)[toks], ref, REL_BF16)
+        ref, _ = oracle.ffn_layer(x[toks], ow, norms_np, K, s.rms_eps, expert_dtype=fmt, routing=r)
+    cos, rel = compare_y(y_f64(out)[toks], ref, REL_BF16 if fmt == "bf16" else REL_INT8)
     say(f"  tokens checked {len(toks)}  cos {cos:.7f}  rel-L2 {rel:.3e}")
