@@ -31,13 +31,6 @@ __device__ __forceinline__ void unpack8(const uint4& v, float* f) {
     f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
     f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
 }
-// 8 int8 held in a uint2 -> 8 floats (exact)
-__device__ __forceinline__ void unpack8_i8(const uint2& v, float* f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f[i] = (float)(int8_t)((v.x >> (8 * i)) & 0xFF);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f[4 + i] = (float)(int8_t)((v.y >> (8 * i)) & 0xFF);
-}
 
 // Products s*w of 8 bf16 pairs (packed two per word) are exact in fp32 (16
 // significant bits); each is split into a bf16 hi (its truncation) and a bf16

@@ -34,6 +34,10 @@
 //      topology"), without atomics.
 // int8 experts (int8 experts card, "How it works") are read as int8, widened
 // exactly in registers, and their per-row scale multiplies the dot product.
+// E4M3 experts (the vLLM recipe's fp8 variant) are widened to half carriers by
+// bit placement and dotted with x quantised per token (decode_front's last
+// workgroups); h is formed and quantised per routed row by decode_hquant.
+// The template parameter WQ names the experts' format: 0 bf16, 1 int8, 2 E4M3.
 #include "common.h"
 #include "kernels.h"
 #include "topk.h"
@@ -50,30 +54,10 @@ constexpr int kRouteThreads = 1024;
 constexpr int kMaxPairs = MOE_STREAM_MAX_TOKENS * MOE_MAX_TOPK;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint4 ld_nt16(const void* p) {
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
     return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ uint2 ld_nt8(const void* p) {
-    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
-    return make_uint2(v.x, v.y);
-}
-// 8 weights at element offset `col` of a weight matrix: 16 bytes of bf16, or
-// 8 bytes of int8 kept in .x/.y
-template <int WQ>
-__device__ __forceinline__ uint4 load_w8(const void* w, int64_t col) {
-    if (WQ) {
-        const uint2 v = ld_nt8(reinterpret_cast<const int8_t*>(w) + col);
-        return make_uint4(v.x, v.y, 0u, 0u);
-    }
-    return ld_nt16(reinterpret_cast<const uint16_t*>(w) + col);
-}
-template <int WQ>
-__device__ __forceinline__ void unpack_w8(const uint4& v, float* f) {
-    if (WQ) unpack8_i8(make_uint2(v.x, v.y), f);
-    else unpack8(v, f);
 }
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 
@@ -101,19 +85,6 @@ __device__ __forceinline__ uint4 i8x8_to_bf16(const uint4& v) {
         o[q] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
     }
     return make_uint4(o[0], o[1], o[2], o[3]);
-}
-// weights as packed bf16, whatever their storage
-template <int WQ>
-__device__ __forceinline__ uint4 as_bf16(const uint4& v) {
-    if (WQ) return i8x8_to_bf16(v);
-    return v;
-}
-
-__device__ __forceinline__ float dot8(const float* a, const float* b) {
-    float s = a[0] * b[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) s += a[i] * b[i];
-    return s;
 }
 
 // Copy n (1 <= n <= KPER * 256) contiguous 16-byte chunks into LDS; loads are
@@ -155,7 +126,7 @@ __device__ __forceinline__ float dot8_f16(const uint4& a, const uint4& b, float 
 // One K-step of a lane's piece of a tile (bf16: two 16-byte halves, 8 k each;
 // int8 or E4M3: one 16-byte piece, 16 k) dotted with the 16 matching x values
 // (for E4M3 the half carriers of x).
-// OPAQUE (int8): the piece is made opaque before it is widened, so that the
+// OPAQUE (1-byte weights): the piece is made opaque before it is widened, so that the
 // compiler widens it where it is used instead of hoisting every step's widened
 // copy (twice the registers) out of the caller's loop over tokens.
 template <int WQ, bool OPAQUE = false>

@@ -11,7 +11,10 @@
 // A rows may be gathered (the tokens of an expert, in grouped order), so the
 // routed pairs are computed without copying x. int8 weights (int8 experts card,
 // "How it works") are widened to bf16 exactly in registers and their per-row
-// fp32 scales are applied in the epilogue. combine_kernel then adds, per token,
+// fp32 scales are applied in the epilogue; E4M3 weights (the vLLM recipe's fp8
+// variant) become half carriers by bit placement and meet A rows quantised per
+// token in f16 MFMAs, the activation scale applied per row in the epilogue.
+// The template parameter WQ names the format: 0 bf16, 1 int8, 2 E4M3. combine_kernel then adds, per token,
 // the dense output and its K weighted expert rows (ONNX export card, "Truthful
 // graph contracts", row "MoE topology": dense + moe).
 //
@@ -130,7 +133,7 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 constexpr int kAStageElems = BM * BK;  // bf16 elements per LDS stage of A
 
 // One K-step of the wavefront's B fragments: bf16 q[2 j + s] = column tile j,
-// 8 k of sub-step s; int8 q[j] = column tile j, all 16 k.
+// 8 k of sub-step s; 1-byte (int8, E4M3) q[j] = column tile j, all 16 k.
 template <int WQ>
 struct BStep {
     v4u q[WQ ? 2 : 4];
@@ -139,7 +142,7 @@ template <int WQ>
 constexpr int kBLoads = WQ ? 2 : 4;
 
 // bp[j]: this lane's 16-byte piece of K-step 0 of the wavefront's tile j; a
-// K-step is one tile (2 KB bf16: sub-step s at + 1024 s; 1 KB int8), so every
+// K-step is one tile (2 KB bf16: sub-step s at + 1024 s; 1 KB int8 or E4M3), so every
 // load of the wavefront reads one contiguous 1 KB
 template <int WQ>
 __device__ __forceinline__ void b_load(const char* const (&bp)[2], int kt, BStep<WQ>& r) {
@@ -356,7 +359,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
         ap[q] = reinterpret_cast<const char*>(p.A + arow * p.lda + c * 8);
     }
     // epilogue operands, loaded now so that their latency hides behind the K
-    // loop: int8 column scales of this lane's columns, router weight of row tid
+    // loop: 1-byte formats' column scales of this lane's columns, router weight of row tid
     const int col_l = lane & 15;
     float sc0 = 1.f, sc1 = 1.f, row_wt = 1.f;
     if (WQ) {
