@@ -258,12 +258,13 @@ constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 
 // also waits for every B load issued before it.) a_dma pins the order of the
 // loads against compiler scheduling; loads past the last K-step repeat the
 // last one, so every step issues the same loads.
-template <int WQ, int NSL>
+template <int WQ, int NSL, bool ADMA>
 __device__ __forceinline__ void k_loop(const char* const (&ap)[kADma], const char* const (&bp)[2], int nk,
                                        const Lds& L, int wave, int lane, f32x4_t (&acc)[kSlabs][2]) {
+    constexpr int kA = ADMA ? kADma : 0;
     constexpr int kB = NSL > 0 ? kBLoads<WQ> : 0;
-    constexpr int kWait = wait_vm_lgkm0((kDepth - 2) * (kADma + kB));
-    static_assert((kDepth - 2) * (kADma + kB) < 64, "vmcnt range");
+    constexpr int kWait = wait_vm_lgkm0((kDepth - 2) * (kA + kB));
+    static_assert((kDepth - 2) * (kA + kB) < 64, "vmcnt range");
     static_assert(kDepth == 4, "four stages and slots below");
     const int last = nk - 1;
     BStep<WQ> rb0, rb1, rb2, rb3;
@@ -271,16 +272,16 @@ __device__ __forceinline__ void k_loop(const char* const (&ap)[kADma], const cha
     uint16_t* const S1 = L.a[1];
     uint16_t* const S2 = L.a[2];
     uint16_t* const S3 = L.a[3];
-    a_dma(ap, 0, S0, wave);
+    if (ADMA) a_dma(ap, 0, S0, wave);
     if (NSL > 0) b_load<WQ>(bp, 0, rb0);
-    a_dma(ap, min(1, last), S1, wave);
+    if (ADMA) a_dma(ap, min(1, last), S1, wave);
     if (NSL > 0) b_load<WQ>(bp, min(1, last), rb1);
-    a_dma(ap, min(2, last), S2, wave);
+    if (ADMA) a_dma(ap, min(2, last), S2, wave);
     if (NSL > 0) b_load<WQ>(bp, min(2, last), rb2);
 #define MOE_GEMM_STEP(U, SA, RB, SN, RN)                                    \
     __builtin_amdgcn_s_waitcnt(kWait);                                      \
     raw_barrier();                                                          \
-    a_dma(ap, min(kt + (U) + kDepth - 1, last), SN, wave);                  \
+    if (ADMA) a_dma(ap, min(kt + (U) + kDepth - 1, last), SN, wave);        \
     if (NSL > 0) {                                                          \
         b_load<WQ>(bp, min(kt + (U) + kDepth - 1, last), RN);             \
         if (kt + (U) < nk) mma_step<WQ, NSL>(SA, RB, lane, acc);          \
@@ -382,13 +383,24 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
         const int64_t arow = p.a_rows ? p.a_rows[row0 + rr] : (int64_t)(row0 + rr);
         row_wt = p.a_scale[arow] * 65536.f;
     }
+    // A rows the MFMAs read: the valid slabs rounded up to groups of four (the
+    // same for every wavefront); a wavefront whose 32 DMA rows all lie past them
+    // moves no A (its wait counts are its own loads, so they differ by template)
+    const int rows_read = (n_slabs + 3) / 4 * 64;
+    const bool adma = wave * kADma * 8 < rows_read;
+#define MOE_K_LOOP(N)                                                      \
+    do {                                                                   \
+        if (adma) k_loop<WQ, N, true>(ap, bp, nk, L, wave, lane, acc);     \
+        else k_loop<WQ, N, false>(ap, bp, nk, L, wave, lane, acc);         \
+    } while (0)
     switch (nsl) {  // uniform per wavefront
-        case 0: k_loop<WQ, 0>(ap, bp, nk, L, wave, lane, acc); break;
-        case 4: k_loop<WQ, 4>(ap, bp, nk, L, wave, lane, acc); break;
-        case 8: k_loop<WQ, 8>(ap, bp, nk, L, wave, lane, acc); break;
-        case 12: k_loop<WQ, 12>(ap, bp, nk, L, wave, lane, acc); break;
-        default: k_loop<WQ, 16>(ap, bp, nk, L, wave, lane, acc); break;
+        case 0: MOE_K_LOOP(0); break;
+        case 4: MOE_K_LOOP(4); break;
+        case 8: MOE_K_LOOP(8); break;
+        case 12: MOE_K_LOOP(12); break;
+        default: MOE_K_LOOP(16); break;
     }
+#undef MOE_K_LOOP
 
     // epilogue: acc[i][jj][v] is C[row = 16 i + 4 (lane>>4) + v][column tile jj, lane&15]
     if (MODE == MODE_GATEUP) {
