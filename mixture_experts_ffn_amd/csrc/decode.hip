@@ -434,22 +434,25 @@ __global__ __launch_bounds__(kThreads) void decode_front_kernel(StreamArgs a, co
                                                                float* ss_part) {
     __shared__ float red[kWaves * 512 + kWaves * 16];
     const int n_router = wr ? ((a.E + 15) / 16) * kFrontSplit : 0;
-    const int b = blockIdx.x;
     const int n_dense = a.with_dense && a.front_dense ? (a.Id / 16) * kFrontSplit : 0;
-    if (b < n_router) {
-        const int nt = b / kFrontSplit, ks = b - nt * kFrontSplit;
-        router_part<NS>(a.x, a.H, scale, wr, a.E, nt, ks, a.T, lpart, ss_part, red);
-    } else if (b < n_router + n_dense) {
-        const int i = b - n_router, hc = i / kFrontSplit, ks = i - hc * kFrontSplit;
-        dense_gateup_part<NS>(a.xd, a.H, a.dgu, a.Id, hc, ks, a.T, a.dgu_part, red, (int)threadIdx.x);
-    } else {
-        // E4M3 experts: x quantised per token, a wavefront a token (hidden <= 3072: 6 chunks a lane)
-        const int t = (b - n_router - n_dense) * kWaves + ((int)threadIdx.x >> 6);
+    // E4M3 experts: the workgroups that quantise x per token come first (the
+    // longest of the launch, so they start first)
+    const int n_quant = a.xq ? (a.T + kWaves - 1) / kWaves : 0;
+    const int b = (int)blockIdx.x - n_quant;
+    if (b < 0) {
+        // a wavefront a token (hidden <= 3072: 6 chunks a lane)
+        const int t = (int)blockIdx.x * kWaves + ((int)threadIdx.x >> 6);
         if (t < a.T) {
             const float s = fp8_quantize_row<6>(a.x + (int64_t)t * a.H, a.xq + (int64_t)t * a.H, a.H >> 3,
                                                 (int)threadIdx.x & 63);
             if ((threadIdx.x & 63) == 0) a.x_scale[t] = s;
         }
+    } else if (b < n_router) {
+        const int nt = b / kFrontSplit, ks = b - nt * kFrontSplit;
+        router_part<NS>(a.x, a.H, scale, wr, a.E, nt, ks, a.T, lpart, ss_part, red);
+    } else if (b < n_router + n_dense) {
+        const int i = b - n_router, hc = i / kFrontSplit, ks = i - hc * kFrontSplit;
+        dense_gateup_part<NS>(a.xd, a.H, a.dgu, a.Id, hc, ks, a.T, a.dgu_part, red, (int)threadIdx.x);
     }
 }
 
