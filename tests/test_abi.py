@@ -244,3 +244,35 @@ def test_prefill_chunked_argument_errors(L):
     # an empty prompt is a valid no-op
     assert call(T=0, h=None, out=None, ws=None, ws_bytes=0) == _abi.MOE_OK
     assert call(n=None, T=0, h=None, out=None, ws=None, ws_bytes=0) == _abi.MOE_OK
+
+
+def test_fp8_argument_errors(L):
+    """E4M3 experts: the scales are required, hidden and expert_inter are
+    limited to 16384 (the per-row quantisers hold a row in registers), the
+    quantiser checks its shape, and every error comes before any launch."""
+    d = _real()
+    T = 8
+    ws = L.moe_workspace_bytes(ctypes.byref(d), T)
+
+    def block(w, dims=d):
+        return L.moe_block(ctypes.byref(dims), ctypes.byref(w), FAKE, T, FAKE + (1 << 20), None, FAKE,
+                           L.moe_workspace_bytes(ctypes.byref(dims), T), None)
+
+    fp8 = dict(expert_dtype=_abi.MOE_DTYPE_FP8)
+    assert block(_weights(**fp8)) == _abi.MOE_ERR_NULL                       # scales missing
+    assert b"gate_up_scale" in L.moe_last_error()
+    assert block(_weights(**fp8, gate_up_scale=FAKE)) == _abi.MOE_ERR_NULL   # down_scale missing
+    assert block(_weights(**fp8, gate_up_scale=FAKE + 2, down_scale=FAKE)) == _abi.MOE_ERR_ALIGN
+    assert block(_weights(expert_dtype=3, gate_up_scale=FAKE, down_scale=FAKE)) == _abi.MOE_ERR_UNSUPPORTED
+    wide = _abi.MoeDims(16640, 128, 8, 704, 2112, 1e-6)
+    assert block(_weights(**fp8, gate_up_scale=FAKE, down_scale=FAKE), wide) == _abi.MOE_ERR_UNSUPPORTED
+    assert b"16384" in L.moe_last_error()
+    # the quantiser: shape and pointer checks, and an empty matrix is a no-op
+    assert L.moe_quantize_fp8(FAKE, 4, 12, FAKE, FAKE, None) == _abi.MOE_ERR_SHAPE   # cols % 8
+    assert L.moe_quantize_fp8(FAKE, -1, 16, FAKE, FAKE, None) == _abi.MOE_ERR_SHAPE
+    assert L.moe_quantize_fp8(None, 4, 16, FAKE, FAKE, None) == _abi.MOE_ERR_NULL
+    assert L.moe_quantize_fp8(FAKE, 4, 16, FAKE + 8, FAKE, None) == _abi.MOE_ERR_ALIGN
+    assert L.moe_quantize_fp8(FAKE, 0, 16, FAKE, FAKE, None) == _abi.MOE_OK
+    # E4M3 tiles are 1-byte tiles
+    assert L.moe_tile_weights(FAKE, 16, 64, _abi.MOE_DTYPE_FP8, FAKE, None) == _abi.MOE_ERR_SHAPE  # src == dst
+    assert L.moe_tile_weights(FAKE, 0, 64, _abi.MOE_DTYPE_FP8, FAKE + 64, None) == _abi.MOE_OK
