@@ -276,3 +276,19 @@ def test_fp8_argument_errors(L):
     # E4M3 tiles are 1-byte tiles
     assert L.moe_tile_weights(FAKE, 16, 64, _abi.MOE_DTYPE_FP8, FAKE, None) == _abi.MOE_ERR_SHAPE  # src == dst
     assert L.moe_tile_weights(FAKE, 0, 64, _abi.MOE_DTYPE_FP8, FAKE + 64, None) == _abi.MOE_OK
+
+
+def test_no_fallback_missing_library_and_host_tensors(tmp_path):
+    """There is no other implementation: a missing library raises at load time,
+    and host tensors are refused by the binding instead of being computed on
+    the CPU."""
+    import torch
+    from mixture_experts_ffn_amd import BlockDims, moe_block, moe_ffn_layer, moe_prefill_chunked
+    with pytest.raises(RuntimeError, match="missing"):
+        _abi.load_library(str(tmp_path / "libmoe_ffn.so"))
+    dims = BlockDims(512, 16, 4, 128, 384)
+    x = torch.zeros((8, 512), dtype=torch.bfloat16)
+    for call in (lambda: moe_block(dims, None, x), lambda: moe_ffn_layer(dims, None, None, x),
+                 lambda: moe_prefill_chunked(dims, None, None, x)):
+        with pytest.raises(ValueError, match="device tensor"):
+            call()
