@@ -19,7 +19,7 @@ struct RouterSplit {
     int slice_steps;  // 64-wide K-steps per slice
 };
 RouterSplit router_split(int T, int H, int E);
-// partial: router_split(T, H, E).slices * T * E fp32
+// partial: router_split(T, H, E).slices * T * (E + 1) fp32 (logit sums, then sums of squares)
 hipError_t launch_router_mfma(const uint16_t* x, const uint16_t* scale, const uint16_t* w,
                               const float* bias, const float* pes, int T, int H, int E, int K,
                               float eps, int32_t* topk_idx, float* topk_w, float* partial,

@@ -63,8 +63,8 @@ Layout make_layout(const moe_dims& d, int64_t T) {
     L.max_mtiles = (int)((TK + BM - 1) / BM + (E < TK ? E : TK));
     // fp32 logits: only moe_route's small-batch router stages them
     L.logits = take((T <= kRouterMfmaMinT ? T : 0) * E * 4);
-    // MFMA router's partial sums (every T: the grouped path uses it at any size)
-    L.partial = take(T > 0 ? (size_t)moe::router_split((int)T, d.hidden, (int)E).slices * T * E * 4 : 0);
+    // MFMA router's partial sums and sums of squares (every T: the grouped path uses it at any size)
+    L.partial = take(T > 0 ? (size_t)moe::router_split((int)T, d.hidden, (int)E).slices * T * (E + 1) * 4 : 0);
     L.topk_idx = take(TK * 4);
     L.topk_w = take(TK * 4);
     L.pair_rank = take(TK * 4);

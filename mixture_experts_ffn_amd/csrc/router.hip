@@ -116,10 +116,12 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
 //   them in 16-wide column tiles) and one slice of the hidden dimension; it
 //   issues the loads of up to NS K-steps at once (no load waits on another),
 //   then splits, stages through LDS and multiplies step by step. The sums of
-//   each slice go to partial[slice][t][e].
+//   each slice go to partial[slice][t][e], and the slice's sum of squares of
+//   each token row (from the x chunks it stages) to ss_partial[slice][t].
 // router_finish_kernel: one wavefront per token adds the slices in order (the
-//   same order for every run), applies the RMSNorm factor, the H^-0.5 and the
-//   bias, and runs the softmax / top-k.
+//   same order for every run), applies the RMSNorm factor from the slices'
+//   sums of squares (x is not read again), the H^-0.5 and the bias, and runs
+//   the softmax / top-k.
 namespace {
 
 constexpr int kRT = 32;  // tokens per workgroup: two 16-row MFMA tiles
@@ -163,7 +165,7 @@ template <int NQ, int NS>
 __global__ __launch_bounds__(kRThreads) void router_partial_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ scale,
     const uint16_t* __restrict__ w, int T, int H, int E, int slice_steps,
-    float* __restrict__ partial) {
+    float* __restrict__ partial, float* __restrict__ ss_partial) {
     constexpr int kMaxE = 32 * NQ, kMaxCT = kMaxE / 64;  // column tiles per wave
     // per stage: x tile [32][64], hi and lo tiles [32 NQ][64] (bf16)
     __shared__ __attribute__((aligned(16))) uint16_t xs[2][kRT * kRK];
@@ -191,6 +193,7 @@ __global__ __launch_bounds__(kRThreads) void router_partial_kernel(
 #pragma unroll
         for (int j = 0; j < kMaxCT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    float ss = 0.f;  // this thread's share of the slice's sum of squares of its token row
     int step = 0;  // steps multiplied so far (selects the LDS buffer)
     for (int c0 = kb; c0 < ke; c0 += NS) {
         RStage<NQ> st[NS];
@@ -201,6 +204,12 @@ __global__ __launch_bounds__(kRThreads) void router_partial_kernel(
             if (c0 + i < ke) {  // uniform
                 const int buf = (step + i) & 1;
                 *reinterpret_cast<v4u*>(&xs[buf][rswz(xr_row, cc)]) = st[i].x;
+                {
+                    float f[8];
+                    unpack8(make_uint4(st[i].x[0], st[i].x[1], st[i].x[2], st[i].x[3]), f);
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) ss += f[k] * f[k];
+                }
 #pragma unroll
                 for (int q = 0; q < NQ; ++q) {
                     const int r = xr_row + 32 * q;
@@ -240,6 +249,13 @@ __global__ __launch_bounds__(kRThreads) void router_partial_kernel(
         step += NS;
     }
 
+    // the row's sum of squares over the slice: the 8 threads of a row are
+    // consecutive lanes (tid & 7), added in a fixed order
+    ss += __shfl_xor(ss, 1, kWave);
+    ss += __shfl_xor(ss, 2, kWave);
+    ss += __shfl_xor(ss, 4, kWave);
+    if (cc == 0 && xr_row < nt) ss_partial[(int64_t)blockIdx.y * T + t0 + xr_row] = ss;
+
     float* out = partial + (int64_t)blockIdx.y * T * E;
 #pragma unroll
     for (int j = 0; j < kMaxCT; ++j) {
@@ -260,7 +276,7 @@ __global__ __launch_bounds__(kRThreads) void router_partial_kernel(
 }  // namespace
 
 __global__ __launch_bounds__(256) void router_finish_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ partial, int S,
+    const float* __restrict__ partial, const float* __restrict__ ss_partial, int S,
     const float* __restrict__ bias, const float* __restrict__ pes, int T, int H, int E, int K,
     float eps, float inv_sqrt_h, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -275,15 +291,8 @@ __global__ __launch_bounds__(256) void router_finish_kernel(
             for (int sl = 0; sl < S; ++sl) a += partial[((int64_t)sl * T + t) * E + e];
         lv[j] = a;
     }
-    float q = 0.f;  // sum of squares of x_t
-    const uint16_t* row = x + (int64_t)t * H;
-    for (int k = lane * 8; k < H; k += kWave * 8) {
-        float f[8];
-        unpack8(*reinterpret_cast<const uint4*>(row + k), f);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) q += f[i] * f[i];
-    }
-    q = wave_sum<kWave>(q);
+    float q = 0.f;  // sum of squares of x_t: the slices' shares, in slice order
+    for (int sl = 0; sl < S; ++sl) q += ss_partial[(int64_t)sl * T + t];
     const float f = (1.0f / sqrtf(q / (float)H + eps)) * inv_sqrt_h;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -324,13 +333,15 @@ hipError_t launch_router_mfma(const uint16_t* x, const uint16_t* scale, const ui
     const float inv_sqrt_h = (float)(1.0 / __builtin_sqrt((double)H));
     const RouterSplit rs = router_split(T, H, E);
     const dim3 grid((T + kRT - 1) / kRT, rs.slices);
+    // partial: the slices' logit sums [S][T][E], then their sums of squares [S][T]
+    float* ss_partial = partial + (int64_t)rs.slices * T * E;
     if (E <= 128)
         hipLaunchKernelGGL((router_partial_kernel<4, 6>), grid, dim3(kRThreads), 0, stream, x, scale,
-                           w, T, H, E, rs.slice_steps, partial);
+                           w, T, H, E, rs.slice_steps, partial, ss_partial);
     else
         hipLaunchKernelGGL((router_partial_kernel<8, 3>), grid, dim3(kRThreads), 0, stream, x, scale,
-                           w, T, H, E, rs.slice_steps, partial);
-    hipLaunchKernelGGL(router_finish_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, x, partial,
+                           w, T, H, E, rs.slice_steps, partial, ss_partial);
+    hipLaunchKernelGGL(router_finish_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, partial, ss_partial,
                        rs.slices, bias, pes, T, H, E, K, eps, inv_sqrt_h, topk_idx, topk_w);
     return hipGetLastError();
 }
