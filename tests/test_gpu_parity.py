@@ -483,3 +483,47 @@ def test_prefill_chunked(dev, name, T, chunk, which):
         ref, _ = oracle.ffn_layer(x[toks], ow, norms_np, K, s.rms_eps, expert_dtype=fmt, routing=r)
     cos, rel = compare_y(y_f64(out)[toks], ref, REL_BF16 if fmt == "bf16" else REL_INT8)
     say(f"  tokens checked {len(toks)}  cos {cos:.7f}  rel-L2 {rel:.3e}")
+
+
+# ---------------------------------------------------------------- seeded random shapes
+def _random_cases(n=8, seed=2024):
+    """Small shapes drawn once from a fixed seed: hidden a multiple of 256 up to
+    1024, 2..64 experts, top-k up to min(8, E), intermediates multiples of 64,
+    ragged T from 1 to 300, each in the three expert formats."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        E = int(rng.integers(2, 65))
+        shape = moe_synth.BlockShape(hidden=256 * int(rng.integers(1, 5)), num_experts=E,
+                                     top_k=int(rng.integers(1, min(8, E) + 1)),
+                                     expert_inter=64 * int(rng.integers(1, 5)),
+                                     dense_inter=64 * int(rng.integers(1, 5)))
+        T = int(rng.choice([1, 7, 33, 64, 65, 129, 300]))
+        cases.append((i, shape, T, ("bf16", "int8", "fp8")[i % 3]))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: f"r{c[0]}-{c[3]}-T{c[2]}")
+def test_random_shapes(dev, case):
+    """moe_block on both paths (the streaming one where T <= 64) against the
+    oracle on every token, at shapes none of the workloads has."""
+    i, shape, T, fmt = case
+    say(f"case: random shape {i}: {shape} T={T} experts {fmt}")
+    w = moe_synth.make_weights(shape, 100 + i)
+    x = moe_synth.make_tokens(shape, 100 + i, T)
+    lw = upload(w, dev, int8=fmt == "int8", fp8=fmt == "fp8")
+    xd = bf16_dev(x, dev)
+    wl = moe_synth.Workload(f"random{i}", shape, T, 100 + i, int8=fmt == "int8", fp8=fmt == "fp8")
+    ref_r = oracle_route(wl, w, x)
+    ow, ofmt = oracle_weights(wl, w)
+    paths = [MOE_PATH_GROUPED] + ([MOE_PATH_STREAM] if T <= 64 else [])
+    for path in paths:
+        y, dbg = run_block(wl, lw, xd, path)
+        check_routing(dbg["topk_idx"], dbg["topk_w"], ref_r, w["per_expert_scale"])
+        p = oracle.permute_pairs(dbg["topk_idx"], shape.num_experts)
+        for k in ("counts", "offsets", "perm_token", "inv_row"):
+            np.testing.assert_array_equal(dbg[k], p[k], err_msg=k)
+        r = routing_for(dbg["topk_idx"], ref_r, w["per_expert_scale"])
+        y_ref, _ = oracle.moe_block(x, ow, shape.top_k, shape.rms_eps, expert_dtype=ofmt, routing=r)
+        cos, rel = compare_y(y_f64(y), y_ref, REL_BF16 if ofmt == "bf16" else REL_INT8)
+        say(f"  path {path}: cos {cos:.7f}  rel-L2 {rel:.3e}")
