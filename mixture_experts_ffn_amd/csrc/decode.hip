@@ -428,6 +428,52 @@ __device__ __forceinline__ void router_part(const uint16_t* __restrict__ x, int 
 // Router items first (ceil(E / 16) x kFrontSplit), then the dense gate/up
 // items (Id / 16 x kFrontSplit) if with_dense and front_dense (else the
 // routing launch runs them).
+// E4M3 experts: token t's row of x quantised per row (max |x| / 448, codes
+// round half to even) into a.xq as half carriers, its scale into a.x_scale[t].
+// The whole workgroup takes the row: lane l of wavefront w holds 8-value
+// chunks l + 64 (w + 4 j) (hidden <= 3072: two a lane), the maximum goes
+// through DPP and then LDS.
+__device__ __forceinline__ void quantize_token_fp8(const StreamArgs& a, int t, float* red) {
+    constexpr int NC = 2;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nc = a.H >> 3;
+    const uint4* src = reinterpret_cast<const uint4*>(a.x + (int64_t)t * a.H);
+    uint4* dst = reinterpret_cast<uint4*>(a.xq + (int64_t)t * a.H);
+    uint4 v[NC];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) v[j] = src[min(lane + kWave * (wave + kWaves * j), nc - 1)];  // clamped: same max
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        float f[8];
+        unpack8(v[j], f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    }
+    amax = wave_max<kWave>(amax);
+    if (lane == 0) red[wave] = amax;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) amax = fmaxf(amax, red[w]);
+    const float s = amax / 448.0f;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        const int c = lane + kWave * (wave + kWaves * j);
+        if (c < nc) {
+            float f[8];
+            unpack8(v[j], f);
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t c0 = s > 0.f ? fp8_e4m3_code(f[2 * i] / s) : 0u;
+                const uint32_t c1 = s > 0.f ? fp8_e4m3_code(f[2 * i + 1] / s) : 0u;
+                o[i] = fp8_as_f16_bits(c0) | (fp8_as_f16_bits(c1) << 16);
+            }
+            dst[c] = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    }
+    if (threadIdx.x == 0) a.x_scale[t] = s;
+}
+
 template <int NS>
 __global__ __launch_bounds__(kThreads) void decode_front_kernel(StreamArgs a, const uint16_t* scale,
                                                                const uint16_t* wr, float* lpart,
@@ -436,17 +482,11 @@ __global__ __launch_bounds__(kThreads) void decode_front_kernel(StreamArgs a, co
     const int n_router = wr ? ((a.E + 15) / 16) * kFrontSplit : 0;
     const int n_dense = a.with_dense && a.front_dense ? (a.Id / 16) * kFrontSplit : 0;
     // E4M3 experts: the workgroups that quantise x per token come first (the
-    // longest of the launch, so they start first)
-    const int n_quant = a.xq ? (a.T + kWaves - 1) / kWaves : 0;
+    // longest of the launch, so they start first), one a token
+    const int n_quant = a.xq ? a.T : 0;
     const int b = (int)blockIdx.x - n_quant;
     if (b < 0) {
-        // a wavefront a token (hidden <= 3072: 6 chunks a lane)
-        const int t = (int)blockIdx.x * kWaves + ((int)threadIdx.x >> 6);
-        if (t < a.T) {
-            const float s = fp8_quantize_row<6>(a.x + (int64_t)t * a.H, a.xq + (int64_t)t * a.H, a.H >> 3,
-                                                (int)threadIdx.x & 63);
-            if ((threadIdx.x & 63) == 0) a.x_scale[t] = s;
-        }
+        quantize_token_fp8(a, (int)blockIdx.x, red);
     } else if (b < n_router) {
         const int nt = b / kFrontSplit, ks = b - nt * kFrontSplit;
         router_part<NS>(a.x, a.H, scale, wr, a.E, nt, ks, a.T, lpart, ss_part, red);
@@ -876,7 +916,7 @@ template <int NS>
 hipError_t launch_front_ns(const StreamArgs& a, const uint16_t* scale, const uint16_t* wr, float* lpart,
                            float* ss_part, hipStream_t stream) {
     const int n_router = wr ? ((a.E + 15) / 16) * kFrontSplit : 0;
-    const int n_quant = a.xq ? (a.T + kWaves - 1) / kWaves : 0;  // E4M3 experts: x quantised per token
+    const int n_quant = a.xq ? a.T : 0;  // E4M3 experts: x quantised per token, a workgroup each
     const int blocks = n_router + (a.with_dense && a.front_dense ? (a.Id / 16) * kFrontSplit : 0) + n_quant;
     if (blocks <= 0) return hipSuccess;
     hipLaunchKernelGGL(decode_front_kernel<NS>, dim3(blocks), dim3(kThreads), 0, stream, a, scale, wr, lpart,
