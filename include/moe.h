@@ -182,7 +182,7 @@ int dense_mlp(const moe_dims* d, const void* dense_gate_up, const void* dense_do
  * that position. N_g(v) = v / sqrt(mean(v^2) + eps) * g, per token, in fp32. */
 typedef struct moe_ffn_norms {
     const void* pre_dense;   /* dense MLP branch input */
-    const void* pre_moe;     /* MoE branch input (router and experts) */
+    const void* pre_moe;     /* MoE branch input (the experts; the router reads h) */
     const void* post_dense;  /* dense MLP branch output */
     const void* post_moe;    /* MoE branch output */
     const void* post;        /* their sum, before the residual */
@@ -195,12 +195,14 @@ typedef struct moe_ffn_norms {
  * topology": post_ff_norm(dense + moe) + residual):
  *   out = h + N_post(N_post_dense(dense(x_d)) + N_post_moe(moe(x_m))),
  *   x_d = bf16(N_pre_dense(h)), x_m = bf16(N_pre_moe(h)),
- * dense and moe as in moe_block (router, top-k, experts on x_m; the dense MLP on
- * x_d); the branch outputs stay fp32 through the post-norms and the residual
- * add, and out is rounded once to bf16. h, out [T, H] bf16 (out may not alias
- * h); n as above (NULL: every norm absent, the residual kept); ws as for
- * moe_block (moe_ffn_workspace_bytes: its size); dbg as for moe_block, its
- * routing being that of x_m. hidden <= 16384. Errors as for moe_block, plus
+ * dense and moe as in moe_block (the experts on x_m, the dense MLP on x_d), the
+ * router on h itself: its own first step is a scale-free RMSNorm ([ONNX] row
+ * "Router"), the norm of a router that reads the un-normalised stream. The
+ * branch outputs stay fp32 through the post-norms and the residual add, and
+ * out is rounded once to bf16. h, out [T, H] bf16 (out may not alias h); n as
+ * above (NULL: every norm absent, the residual kept); ws as for moe_block
+ * (moe_ffn_workspace_bytes: its size); dbg as for moe_block, its routing being
+ * that of h. hidden <= 16384. Errors as for moe_block, plus
  * MOE_ERR_ALIGN for a misaligned gain and MOE_ERR_UNSUPPORTED for a larger
  * hidden size. */
 size_t moe_ffn_workspace_bytes(const moe_dims* d, int32_t T);

@@ -489,7 +489,7 @@ __global__ __launch_bounds__(kThreads) void decode_front_kernel(StreamArgs a, co
         quantize_token_fp8(a, (int)blockIdx.x, red);
     } else if (b < n_router) {
         const int nt = b / kFrontSplit, ks = b - nt * kFrontSplit;
-        router_part<NS>(a.x, a.H, scale, wr, a.E, nt, ks, a.T, lpart, ss_part, red);
+        router_part<NS>(a.xr, a.H, scale, wr, a.E, nt, ks, a.T, lpart, ss_part, red);
     } else if (b < n_router + n_dense) {
         const int i = b - n_router, hc = i / kFrontSplit, ks = i - hc * kFrontSplit;
         dense_gateup_part<NS>(a.xd, a.H, a.dgu, a.Id, hc, ks, a.T, a.dgu_part, red, (int)threadIdx.x);

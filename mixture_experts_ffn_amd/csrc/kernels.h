@@ -104,7 +104,8 @@ hipError_t launch_combine(const float* dense_out, const uint16_t* rows, const in
 // ---- small-batch path (decode.hip) ----------------------------------------
 struct StreamArgs {
     int T, H, I, Id, K, E;
-    const uint16_t* x;                        // router and experts input
+    const uint16_t* x;                        // experts input
+    const uint16_t* xr;                       // router input
     const uint16_t* xd;                       // dense MLP input
     // E4M3 experts: x quantised per token (half carriers of value * 2^-8) and its per-token scales
     uint16_t* xq; float* x_scale;  // written by decode_front's last workgroups

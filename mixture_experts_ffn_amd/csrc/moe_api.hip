@@ -35,6 +35,9 @@ size_t up256(size_t b) { return (b + 255) & ~size_t(255); }
 // runs; below it, the per-expert dot-product router and a separate top-k,
 // which spread a small batch over more workgroups.
 constexpr int kRouterMfmaMinT = 64;
+// the small-batch router stages 8 token rows in LDS (16 * hidden bytes); wider
+// rows take the MFMA router, whose LDS does not grow with hidden
+constexpr int kRouterLogitsMaxHidden = 4096;
 constexpr int kFfnMaxHidden = 16384;  // the norm kernels hold a row in registers
 // chunked prefill: default and largest chunk, and the sliding window the size is a multiple of
 constexpr int32_t kPrefillChunkDefault = 16384;
@@ -62,7 +65,7 @@ Layout make_layout(const moe_dims& d, int64_t T) {
     const int64_t BM = moe::kGemmBM;
     L.max_mtiles = (int)((TK + BM - 1) / BM + (E < TK ? E : TK));
     // fp32 logits: only moe_route's small-batch router stages them
-    L.logits = take((T <= kRouterMfmaMinT ? T : 0) * E * 4);
+    L.logits = take((T <= kRouterMfmaMinT && d.hidden <= kRouterLogitsMaxHidden ? T : 0) * E * 4);
     // MFMA router's partial sums and sums of squares (every T: the grouped path uses it at any size)
     L.partial = take(T > 0 ? (size_t)moe::router_split((int)T, d.hidden, (int)E).slices * T * (E + 1) * 4 : 0);
     L.topk_idx = take(TK * 4);
@@ -245,9 +248,10 @@ int check_layer_args(const moe_dims* d, const moe_weights* w, const moe_ffn_norm
     return MOE_OK;
 }
 
-// The block's pipeline. The router and the experts read x, the dense MLP xd;
-// without norms y = dense + moe (moe_block), with them (moe_ffn_layer) the
-// last stage forms y = h + N_post(N_post_dense(dense) + N_post_moe(moe)).
+// The block's pipeline. The router reads x as given, the experts x or its
+// MoE pre-norm, the dense MLP x or its dense pre-norm; without norms y = dense
+// + moe (moe_block), with them (moe_ffn_layer) the last stage forms
+// y = h + N_post(N_post_dense(dense) + N_post_moe(moe)).
 // Arguments are checked by the callers.
 int block_impl(const moe_dims* d, const moe_weights* w, const void* x, const void* xd_in, int32_t T, void* y,
                const moe_ffn_norms* norms, const void* hres, moe_debug* dbg, void* ws, hipStream_t stream) {
@@ -299,6 +303,9 @@ int block_impl(const moe_dims* d, const moe_weights* w, const void* x, const voi
     uint16_t* rows = at<uint16_t>(ws, L.rows);
     const uint16_t* xb = (const uint16_t*)x;
     const uint16_t* xdb = (const uint16_t*)xd_in;
+    // the router normalises its own input (a scale-free RMSNorm), so it reads
+    // the un-normalised stream even where the experts read a pre-norm of it
+    const uint16_t* xr = (const uint16_t*)x;
     const uint16_t* g_pd = norms ? (const uint16_t*)norms->post_dense : nullptr;
     const uint16_t* g_pm = norms ? (const uint16_t*)norms->post_moe : nullptr;
     const uint16_t* g_p = norms ? (const uint16_t*)norms->post : nullptr;
@@ -319,7 +326,7 @@ int block_impl(const moe_dims* d, const moe_weights* w, const void* x, const voi
     if (path == MOE_PATH_STREAM) {
         moe::StreamArgs sa{};
         sa.T = T; sa.H = H; sa.I = I; sa.Id = Id; sa.K = K; sa.E = E;
-        sa.x = xb; sa.xd = xdb;
+        sa.x = xb; sa.xr = xr; sa.xd = xdb;
         sa.gu = w->expert_gate_up; sa.gu_scale = w->gate_up_scale;
         sa.dw = w->expert_down; sa.dw_scale = w->down_scale;
         sa.counts = po.counts; sa.offsets = po.offsets; sa.active = po.active; sa.n_active = po.n_active;
@@ -366,7 +373,7 @@ int block_impl(const moe_dims* d, const moe_weights* w, const void* x, const voi
         }
     } else {
         HIP_TRY(st.begin("router"), "event record");
-        HIP_TRY(moe::launch_router_mfma(xb, (const uint16_t*)w->router_scale,
+        HIP_TRY(moe::launch_router_mfma(xr, (const uint16_t*)w->router_scale,
                                         (const uint16_t*)w->router_w, w->logit_bias,
                                         w->per_expert_scale, T, H, E, K, d->rms_eps, topk_idx,
                                         topk_w, at<float>(ws, L.partial), stream),
@@ -474,7 +481,7 @@ int moe_route(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
     CHECK_PTR(topk_w, "topk_w", 4);
     if ((rc = check_ws(d, T, ws, ws_bytes))) return rc;
     const Layout L = make_layout(*d, T);
-    if (T > kRouterMfmaMinT) {
+    if (T > kRouterMfmaMinT || d->hidden > kRouterLogitsMaxHidden) {
         HIP_TRY(moe::launch_router_mfma((const uint16_t*)x, (const uint16_t*)w->router_scale,
                                         (const uint16_t*)w->router_w, w->logit_bias,
                                         w->per_expert_scale, T, d->hidden, d->num_experts, d->top_k,
@@ -577,7 +584,7 @@ int dense_mlp(const moe_dims* d, const void* dense_gate_up, const void* dense_do
     if (T <= stream_limit() && stream_fits(*d)) {
         moe::StreamArgs sa{};
         sa.T = T; sa.H = H; sa.I = d->expert_inter; sa.Id = Id; sa.K = d->top_k; sa.E = d->num_experts;
-        sa.x = (const uint16_t*)x; sa.xd = sa.x; sa.max_active = 0; sa.with_dense = 1; sa.front_dense = 1;
+        sa.x = (const uint16_t*)x; sa.xr = sa.x; sa.xd = sa.x; sa.max_active = 0; sa.with_dense = 1; sa.front_dense = 1;
         sa.dgu = (const uint16_t*)dense_gate_up; sa.ddw = (const uint16_t*)dense_down;
         sa.hd = hd; sa.y = (uint16_t*)y;
         sa.part = at<float>(ws, L.part); sa.dpart = at<float>(ws, L.dpart);

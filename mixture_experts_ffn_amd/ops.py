@@ -58,6 +58,31 @@ class LayerWeights:
     def expert_dtype(self) -> int:
         return _weight_format(self.expert_gate_up.dtype)
 
+    def check(self, dims: "BlockDims"):
+        """Every tensor's shape and dtype against dims, and one device for all."""
+        H, E, I, Id = dims.hidden, dims.num_experts, dims.expert_inter, dims.dense_inter
+        bf, f32 = (torch.bfloat16,), (torch.float32,)
+        _want(self.router_scale, "router_scale", (H,), bf)
+        _want(self.router_w, "router_w", (E, H), bf)
+        _want(self.per_expert_scale, "per_expert_scale", (E,), f32)
+        if self.logit_bias is not None:
+            _want(self.logit_bias, "logit_bias", (E,), f32)
+        fmt = (torch.bfloat16, torch.int8) + _ONE_BYTE
+        _want(self.expert_gate_up, "expert_gate_up", (E, 2 * I, H), fmt)
+        dn_fmt = (torch.uint8, torch.float8_e4m3fn) if self.expert_gate_up.dtype in (torch.uint8,
+                                                                                    torch.float8_e4m3fn) \
+            else (self.expert_gate_up.dtype,)
+        _want(self.expert_down, "expert_down", (E, H, I), dn_fmt)
+        if self.expert_gate_up.dtype != torch.bfloat16:
+            if self.gate_up_scale is None or self.down_scale is None:
+                raise ValueError("1-byte expert weights need gate_up_scale and down_scale")
+            _want(self.gate_up_scale, "gate_up_scale", (E, 2 * I), f32)
+            _want(self.down_scale, "down_scale", (E, H), f32)
+        _want(self.dense_gate_up, "dense_gate_up", (2 * Id, H), bf)
+        _want(self.dense_down, "dense_down", (H, Id), bf)
+        _same_device(*[(k, v) for k, v in vars(self).items() if isinstance(v, torch.Tensor)])
+        return self
+
     def c(self) -> MoeWeights:
         def ptr(t):
             return None if t is None else _dev(t, "weight").data_ptr()
@@ -79,6 +104,54 @@ def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
+
+
+_ONE_BYTE = (torch.int8, torch.uint8, torch.float8_e4m3fn)
+
+
+def _want(t, name: str, shape, dtypes) -> torch.Tensor:
+    """Shape and dtype of an argument against what the dims imply (checked
+    before the device, so that a mismatch raises wherever the tensor lives)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {list(dtypes)}")
+    return t
+
+
+def _tokens(x, name: str, hidden: int) -> int:
+    """T of an activation [T, hidden] bf16."""
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if x.dim() != 2 or x.shape[1] != hidden:
+        raise ValueError(f"{name} has shape {tuple(x.shape)}, expected (T, {hidden})")
+    _want(x, name, x.shape, (torch.bfloat16,))
+    return int(x.shape[0])
+
+
+def _same_device(*named):
+    devs = {t.device for _, t in named if t is not None}
+    if len(devs) > 1:
+        raise ValueError("arguments live on different devices: "
+                         + ", ".join(f"{n} on {t.device}" for n, t in named if t is not None))
+
+
+def _debug_outputs(debug, dims: "BlockDims", T: int):
+    """The device outputs a debug struct made by new_debug() names must hold
+    what the block writes into them."""
+    outs = getattr(debug, "_outputs", None) if debug is not None else None
+    if not outs:
+        return []
+    K, E = dims.top_k, dims.num_experts
+    need = {"topk_idx": (T * K, torch.int32), "topk_w": (T * K, torch.float32), "counts": (E, torch.int32),
+            "offsets": (E + 1, torch.int32), "perm_token": (T * K, torch.int32), "inv_row": (T * K, torch.int32)}
+    for k, t in outs.items():
+        n, dt = need[k]
+        if t.dtype != dt or t.numel() < n:
+            raise ValueError(f"debug output {k} must hold at least {n} {dt} values (has {t.numel()} {t.dtype})")
+    return list(outs.items())
 
 
 def _stream(stream) -> int:
@@ -109,8 +182,14 @@ def _workspace(dims, T, device, workspace):
 def moe_route(dims: BlockDims, weights: LayerWeights, x: torch.Tensor, topk_idx=None,
               topk_w=None, workspace=None, stream=None):
     """Router alone: returns (topk_idx [T,K] int32, topk_w [T,K] fp32)."""
+    T = _tokens(x, "x", dims.hidden)
+    weights.check(dims)
+    if topk_idx is not None:
+        _want(topk_idx, "topk_idx", (T, dims.top_k), (torch.int32,))
+    if topk_w is not None:
+        _want(topk_w, "topk_w", (T, dims.top_k), (torch.float32,))
+    _same_device(("x", x), ("router_w", weights.router_w), ("topk_idx", topk_idx), ("topk_w", topk_w))
     x = _dev(x, "x")
-    T = x.shape[0]
     if topk_idx is None:
         topk_idx = torch.empty((T, dims.top_k), dtype=torch.int32, device=x.device)
     if topk_w is None:
@@ -126,8 +205,12 @@ def moe_route(dims: BlockDims, weights: LayerWeights, x: torch.Tensor, topk_idx=
 def moe_block(dims: BlockDims, weights: LayerWeights, x: torch.Tensor, y=None,
               debug: Optional[MoeDebug] = None, workspace=None, stream=None) -> torch.Tensor:
     """The whole block: y = dense(x) + sum_k w_k expert_k(x) (bf16 [T, H])."""
+    T = _tokens(x, "x", dims.hidden)
+    weights.check(dims)
+    if y is not None:
+        _want(y, "y", (T, dims.hidden), (torch.bfloat16,))
+    _same_device(("x", x), ("router_w", weights.router_w), ("y", y), *_debug_outputs(debug, dims, T))
     x = _dev(x, "x")
-    T = x.shape[0]
     if y is None:
         y = torch.empty((T, dims.hidden), dtype=torch.bfloat16, device=x.device)
     ws, _ = _workspace(dims, T, x.device, workspace)
@@ -141,8 +224,13 @@ def moe_block(dims: BlockDims, weights: LayerWeights, x: torch.Tensor, y=None,
 def dense_mlp(dims: BlockDims, dense_gate_up: torch.Tensor, dense_down: torch.Tensor,
               x: torch.Tensor, y=None, workspace=None, stream=None) -> torch.Tensor:
     """The shared dense MLP alone (bf16 [T, H])."""
+    T = _tokens(x, "x", dims.hidden)
+    _want(dense_gate_up, "dense_gate_up", (2 * dims.dense_inter, dims.hidden), (torch.bfloat16,))
+    _want(dense_down, "dense_down", (dims.hidden, dims.dense_inter), (torch.bfloat16,))
+    if y is not None:
+        _want(y, "y", (T, dims.hidden), (torch.bfloat16,))
+    _same_device(("x", x), ("dense_gate_up", dense_gate_up), ("dense_down", dense_down), ("y", y))
     x = _dev(x, "x")
-    T = x.shape[0]
     if y is None:
         y = torch.empty((T, dims.hidden), dtype=torch.bfloat16, device=x.device)
     ws, _ = _workspace(dims, T, x.device, workspace)
@@ -164,6 +252,15 @@ class FfnNorms:
     post: Optional[torch.Tensor] = None
     eps: float = 1e-6
 
+    def check(self, dims: "BlockDims"):
+        for k in ("pre_dense", "pre_moe", "post_dense", "post_moe", "post"):
+            if getattr(self, k) is not None:
+                _want(getattr(self, k), k, (dims.hidden,), (torch.bfloat16,))
+        return self
+
+    def tensors(self):
+        return [(k, getattr(self, k)) for k in ("pre_dense", "pre_moe", "post_dense", "post_moe", "post")]
+
     def c(self) -> _abi.MoeFfnNorms:
         def p(t, name):
             return None if t is None else _dev(t, name).data_ptr()
@@ -182,9 +279,16 @@ def moe_ffn_workspace_bytes(dims: BlockDims, T: int) -> int:
 def moe_ffn_layer(dims: BlockDims, weights: LayerWeights, norms: Optional[FfnNorms], h: torch.Tensor,
                   out=None, debug: Optional[MoeDebug] = None, workspace=None, stream=None) -> torch.Tensor:
     """The layer's FFN: out = h + N_post(N_post_dense(dense(x_d)) + N_post_moe(moe(x_m)))
-    with x_d, x_m the pre-normed h (bf16 [T, H] in and out)."""
+    with x_d, x_m the pre-normed h and the router on h (bf16 [T, H] in and out)."""
+    T = _tokens(h, "h", dims.hidden)
+    weights.check(dims)
+    if norms is not None:
+        norms.check(dims)
+    if out is not None:
+        _want(out, "out", (T, dims.hidden), (torch.bfloat16,))
+    _same_device(("h", h), ("router_w", weights.router_w), ("out", out),
+                 *(norms.tensors() if norms is not None else []), *_debug_outputs(debug, dims, T))
     h = _dev(h, "h")
-    T = h.shape[0]
     if out is None:
         out = torch.empty((T, dims.hidden), dtype=torch.bfloat16, device=h.device)
     need = moe_ffn_workspace_bytes(dims, T)
@@ -215,8 +319,15 @@ def moe_prefill_chunked(dims: BlockDims, weights: LayerWeights, norms: Optional[
                         chunk_tokens: int = 0, out=None, workspace=None, stream=None) -> torch.Tensor:
     """Chunked prefill: consecutive chunks of h through the block (norms None)
     or the layer's FFN (norms given), reusing one chunk's workspace."""
+    T = _tokens(h, "h", dims.hidden)
+    weights.check(dims)
+    if norms is not None:
+        norms.check(dims)
+    if out is not None:
+        _want(out, "out", (T, dims.hidden), (torch.bfloat16,))
+    _same_device(("h", h), ("router_w", weights.router_w), ("out", out),
+                 *(norms.tensors() if norms is not None else []))
     h = _dev(h, "h")
-    T = h.shape[0]
     if out is None:
         out = torch.empty((T, dims.hidden), dtype=torch.bfloat16, device=h.device)
     if workspace is None:
@@ -244,6 +355,12 @@ def _weight_format(dt) -> int:
 
 def moe_quantize_fp8(w: torch.Tensor, q=None, scale=None, stream=None):
     """Per-row E4M3 of a bf16 tensor [..., cols]: returns (codes float8_e4m3fn, scale fp32 [...])."""
+    _want(w, "w", w.shape, (torch.bfloat16,))
+    if q is not None:
+        _want(q, "q", w.shape, (torch.uint8, torch.float8_e4m3fn))
+    if scale is not None:
+        _want(scale, "scale", w.shape[:-1], (torch.float32,))
+    _same_device(("w", w), ("q", q), ("scale", scale))
     w = _dev(w, "w")
     cols = w.shape[-1]
     rows = w.numel() // cols
@@ -259,6 +376,12 @@ def moe_quantize_fp8(w: torch.Tensor, q=None, scale=None, stream=None):
 
 def moe_quantize_int8(w: torch.Tensor, q=None, scale=None, stream=None):
     """Per-row symmetric int8 of a bf16 tensor [..., cols]: returns (q int8, scale fp32 [...])."""
+    _want(w, "w", w.shape, (torch.bfloat16,))
+    if q is not None:
+        _want(q, "q", w.shape, (torch.int8,))
+    if scale is not None:
+        _want(scale, "scale", w.shape[:-1], (torch.float32,))
+    _same_device(("w", w), ("q", q), ("scale", scale))
     w = _dev(w, "w")
     cols = w.shape[-1]
     rows = w.numel() // cols
@@ -276,8 +399,11 @@ def moe_tile_weights(w: torch.Tensor, out=None, stream=None) -> torch.Tensor:
     """Tiled-layout copy of a row-major bf16 or int8 matrix [..., rows, cols]
     (all leading dimensions stacked as rows). Same shape and dtype; the data is
     re-laid into 16 x 64 tiles (include/moe.h, MOE_LAYOUT_TILED)."""
-    w = _dev(w, "w")
     dtype = _weight_format(w.dtype)
+    if out is not None:
+        _want(out, "out", w.shape, (w.dtype,))
+    _same_device(("w", w), ("out", out))
+    w = _dev(w, "w")
     cols = w.shape[-1]
     rows = w.numel() // cols
     if out is None:
@@ -305,6 +431,12 @@ class BlockCall:
 
     def __init__(self, dims: BlockDims, weights: LayerWeights, x: torch.Tensor, y=None,
                  workspace=None):
+        T = _tokens(x, "x", dims.hidden)
+        weights.check(dims)
+        if y is not None:
+            _want(y, "y", (T, dims.hidden), (torch.bfloat16,))
+        _same_device(("x", x), ("router_w", weights.router_w), ("y", y))
+        self.dims = dims
         self.x = _dev(x, "x")
         self.T = x.shape[0]
         self.y = y if y is not None else torch.empty((self.T, dims.hidden), dtype=torch.bfloat16,
@@ -315,6 +447,7 @@ class BlockCall:
         self._w = weights.c()
 
     def __call__(self, debug: Optional[MoeDebug] = None, stream=None) -> torch.Tensor:
+        _same_device(("x", self.x), *_debug_outputs(debug, self.dims, self.T))
         rc = _lib().moe_block(ctypes.byref(self._dims), ctypes.byref(self._w), self.x.data_ptr(),
                               self.T, self.y.data_ptr(),
                               ctypes.byref(debug) if debug is not None else None,
@@ -329,6 +462,15 @@ class FfnCall:
 
     def __init__(self, dims: BlockDims, weights: LayerWeights, norms: Optional[FfnNorms], h: torch.Tensor,
                  out=None, workspace=None):
+        T = _tokens(h, "h", dims.hidden)
+        weights.check(dims)
+        if norms is not None:
+            norms.check(dims)
+        if out is not None:
+            _want(out, "out", (T, dims.hidden), (torch.bfloat16,))
+        _same_device(("h", h), ("router_w", weights.router_w), ("out", out),
+                     *(norms.tensors() if norms is not None else []))
+        self.dims = dims
         self.h = _dev(h, "h")
         self.T = h.shape[0]
         self.out = out if out is not None else torch.empty((self.T, dims.hidden), dtype=torch.bfloat16,
@@ -342,6 +484,7 @@ class FfnCall:
         self._n = norms.c() if norms is not None else None
 
     def __call__(self, debug: Optional[MoeDebug] = None, stream=None) -> torch.Tensor:
+        _same_device(("h", self.h), *_debug_outputs(debug, self.dims, self.T))
         rc = _lib().moe_ffn_layer(ctypes.byref(self._dims), ctypes.byref(self._w),
                                   ctypes.byref(self._n) if self._n is not None else None, self.h.data_ptr(),
                                   self.T, self.out.data_ptr(), ctypes.byref(debug) if debug is not None else None,
@@ -354,6 +497,10 @@ def new_debug(path: int = _abi.MOE_PATH_AUTO, **outputs) -> MoeDebug:
     """A moe_debug struct; keyword arguments name device tensors for its outputs."""
     d = MoeDebug()
     d.path = path
+    allowed = ("topk_idx", "topk_w", "counts", "offsets", "perm_token", "inv_row")
     for k, t in outputs.items():
+        if k not in allowed:
+            raise ValueError(f"unknown debug output {k} (one of {allowed})")
         setattr(d, k, _dev(t, k).data_ptr())
+    d._outputs = dict(outputs)  # sizes are checked against T at each call
     return d

@@ -49,8 +49,10 @@ expert; int8 scales are per output channel, ``max|w|/127``, rounding half to
 even. fp8: E4M3 in its OCP form without infinities (bias 7, largest finite
 448); weight scales per output channel and activation scales per token (per
 row of each expert linear's input), both ``amax/448`` in fp32, codes rounded
-half to even in fp32; the expert's h is rounded to bf16, as on the bf16 path,
-before it is quantised; router and dense MLP stay bf16.
+half to even in fp32; the expert's h is quantised from its bf16 value (the
+activations between operators of a bf16 model are bf16 tensors); router and
+dense MLP stay bf16. In the layer (``ffn_layer``) the router reads the
+un-normalised residual stream, the experts their branch's pre-normed input.
 """
 from __future__ import annotations
 
@@ -300,13 +302,20 @@ def ffn_layer(h, weights, norms, top_k, eps, expert_dtype="bf16", routing=None):
     x_d = N_pre_dense(h) and x_m = N_pre_moe(h) rounded to bf16 (the block's
     input precision); N_k is ``rms_norm_scaled`` with ``norms[k]`` (None: no
     norm at that position) and ``norms["eps"]``. ``eps`` is the router's.
-    Returns ``(out [T,H] float64, routing)``; routing is that of x_m.
+
+    The router reads the residual stream h itself, not x_m: its own first step
+    is a scale-free RMSNorm ([ONNX] row "Router"), the step a router needs
+    when its input has not been normalised; the experts read x_m.
+    Returns ``(out [T,H] float64, routing)``; routing is that of h.
     """
     h64 = _f64(h)
     ne = norms["eps"]
     xd = h64 if norms["pre_dense"] is None else round_bf16(rms_norm_scaled(h64, norms["pre_dense"], ne))
     xm = h64 if norms["pre_moe"] is None else round_bf16(rms_norm_scaled(h64, norms["pre_moe"], ne))
     dense = dense_mlp(xd, weights["dense_gate_up"], weights["dense_down"])
+    if routing is None:
+        routing = route(h64, weights["router_scale"], weights["router_w"], weights["per_expert_scale"], top_k,
+                        eps, weights.get("logit_bias"))
     moe, routing = moe_part(xm, weights, top_k, eps, expert_dtype, routing)
     s = rms_norm_scaled(dense, norms["post_dense"], ne) + rms_norm_scaled(moe, norms["post_moe"], ne)
     return h64 + rms_norm_scaled(s, norms["post"], ne), routing
@@ -419,7 +428,14 @@ def dequantize_fp8(q, scale):
 def expert_ffn_fp8(x_rows, gu_q, gu_scale, dn_q, dn_scale):
     """An fp8 expert on input rows x [n, H] (bf16 values): each row quantised
     per token, the GeGLU on the dequantised rows and weights, h rounded to bf16
-    and quantised per row, then the down projection."""
+    and quantised per row, then the down projection.
+
+    Reading (the recipe page fixes only "dynamic per-token activation
+    quantization"): an activation is quantised from the tensor the model holds
+    between its operators, which in a bf16 model is a bf16 tensor. x arrives in
+    bf16; h, the GeGLU's output and the down projection's input, is such a
+    tensor too, so it is rounded to bf16 before its per-row quantisation. (On
+    the bf16 path nothing is quantised and the oracle keeps h exact.)"""
     x32 = _f64(x_rows).astype(np.float32)                          # bf16 values: exact
     xq = dequantize_fp8(*quantize_fp8(x32))
     gu = dequantize_fp8(gu_q, gu_scale)

@@ -278,6 +278,22 @@ def test_fp8_argument_errors(L):
     assert L.moe_tile_weights(FAKE, 0, 64, _abi.MOE_DTYPE_FP8, FAKE + 64, None) == _abi.MOE_OK
 
 
+def _host_layer(dims, fmt="bf16"):
+    """A layer of host tensors with the shapes and dtypes dims imply."""
+    import torch
+    from mixture_experts_ffn_amd import LayerWeights
+    H, E, I, Id = dims.hidden, dims.num_experts, dims.expert_inter, dims.dense_inter
+    bf = torch.bfloat16
+    ex = {"bf16": bf, "int8": torch.int8, "fp8": torch.float8_e4m3fn}[fmt]
+    lw = LayerWeights(router_scale=torch.zeros(H, dtype=bf), router_w=torch.zeros((E, H), dtype=bf),
+                      per_expert_scale=torch.ones(E), expert_gate_up=torch.zeros((E, 2 * I, H), dtype=ex),
+                      expert_down=torch.zeros((E, H, I), dtype=ex), dense_gate_up=torch.zeros((2 * Id, H), dtype=bf),
+                      dense_down=torch.zeros((H, Id), dtype=bf))
+    if fmt != "bf16":
+        lw.gate_up_scale, lw.down_scale = torch.ones((E, 2 * I)), torch.ones((E, H))
+    return lw
+
+
 def test_no_fallback_missing_library_and_host_tensors(tmp_path):
     """There is no other implementation: a missing library raises at load time,
     and host tensors are refused by the binding instead of being computed on
@@ -287,8 +303,74 @@ def test_no_fallback_missing_library_and_host_tensors(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         _abi.load_library(str(tmp_path / "libmoe_ffn.so"))
     dims = BlockDims(512, 16, 4, 128, 384)
+    lw = _host_layer(dims)
     x = torch.zeros((8, 512), dtype=torch.bfloat16)
-    for call in (lambda: moe_block(dims, None, x), lambda: moe_ffn_layer(dims, None, None, x),
-                 lambda: moe_prefill_chunked(dims, None, None, x)):
+    for call in (lambda: moe_block(dims, lw, x), lambda: moe_ffn_layer(dims, lw, None, x),
+                 lambda: moe_prefill_chunked(dims, lw, None, x)):
         with pytest.raises(ValueError, match="device tensor"):
             call()
+
+
+def test_binding_checks_shapes_dtypes_and_devices():
+    """The C ABI receives bare pointers, so the binding checks every tensor
+    against the dims before any call: a mismatch raises instead of becoming an
+    out-of-bounds access on the device. Host tensors suffice: these checks come
+    before the device check."""
+    import dataclasses
+    import torch
+    from mixture_experts_ffn_amd import (BlockCall, BlockDims, FfnNorms, dense_mlp, moe_block, moe_ffn_layer,
+                                         moe_quantize_int8, moe_route, moe_tile_weights)
+    dims = BlockDims(256, 4, 2, 64, 64)
+    bf = torch.bfloat16
+    x = torch.zeros((8, 256), dtype=bf)
+    good = _host_layer(dims)
+
+    def raises(fn, match):
+        with pytest.raises((ValueError, TypeError), match=match):
+            fn()
+
+    # the activations
+    raises(lambda: moe_block(dims, good, torch.zeros((8, 128), dtype=bf)), r"expected \(T, 256\)")
+    raises(lambda: moe_block(dims, good, torch.zeros((8, 256))), "dtype")
+    raises(lambda: moe_block(dims, good, torch.zeros(256, dtype=bf)), "shape")
+    raises(lambda: moe_block(dims, good, x, y=torch.zeros((8, 128), dtype=bf)), "y has shape")
+    raises(lambda: moe_block(dims, good, x, y=torch.zeros((8, 256))), "y has dtype")
+    # every weight against the dims
+    bad = {"router_scale": torch.zeros(128, dtype=bf), "router_w": torch.zeros((4, 128), dtype=bf),
+           "per_expert_scale": torch.ones(3), "logit_bias": torch.zeros(5),
+           "expert_gate_up": torch.zeros((4, 64, 256), dtype=bf), "expert_down": torch.zeros((4, 256, 32), dtype=bf),
+           "dense_gate_up": torch.zeros((64, 256), dtype=bf), "dense_down": torch.zeros((256, 32), dtype=bf)}
+    for k, v in bad.items():
+        raises(lambda: moe_block(dims, dataclasses.replace(good, **{k: v}), x), k)
+    raises(lambda: moe_block(dims, dataclasses.replace(good, per_expert_scale=torch.ones(4, dtype=torch.float64)),
+                             x), "per_expert_scale has dtype")
+    # 1-byte experts: scales present and of the right shape; down in the same format
+    q8 = _host_layer(dims, "int8")
+    raises(lambda: moe_block(dims, dataclasses.replace(q8, down_scale=None), x), "down_scale")
+    raises(lambda: moe_block(dims, dataclasses.replace(q8, gate_up_scale=torch.ones((4, 64))), x), "gate_up_scale")
+    raises(lambda: moe_block(dims, dataclasses.replace(q8, expert_down=torch.zeros((4, 256, 64), dtype=bf)), x),
+           "expert_down has dtype")
+    # the router alone, the dense MLP alone, the layer
+    raises(lambda: moe_route(dims, good, x, topk_idx=torch.zeros((8, 3), dtype=torch.int32)), "topk_idx")
+    raises(lambda: moe_route(dims, good, x, topk_w=torch.zeros((8, 2), dtype=bf)), "topk_w")
+    raises(lambda: dense_mlp(dims, good.dense_gate_up, torch.zeros((256, 128), dtype=bf), x), "dense_down")
+    raises(lambda: moe_ffn_layer(dims, good, FfnNorms(post=torch.zeros(128, dtype=bf)), x), "post has shape")
+    raises(lambda: moe_ffn_layer(dims, good, None, x, out=torch.zeros((4, 256), dtype=bf)), "out has shape")
+    raises(lambda: BlockCall(dims, good, torch.zeros((8, 512), dtype=bf)), "shape")
+    # load-time helpers
+    raises(lambda: moe_quantize_int8(torch.zeros((4, 64))), "dtype")
+    raises(lambda: moe_quantize_int8(torch.zeros((4, 64), dtype=bf), scale=torch.ones(3)), "scale has shape")
+    raises(lambda: moe_tile_weights(torch.zeros((16, 64), dtype=bf), out=torch.zeros((16, 64), dtype=torch.int8)),
+           "out has")
+    # debug outputs too small for T * K
+    from mixture_experts_ffn_amd.ops import _debug_outputs
+    dbg = _abi.MoeDebug()
+    dbg._outputs = {"topk_idx": torch.zeros(8, dtype=torch.int32)}
+    raises(lambda: _debug_outputs(dbg, dims, 8), "topk_idx must hold at least 16")
+    dbg._outputs = {"offsets": torch.zeros(4, dtype=torch.int32)}
+    raises(lambda: _debug_outputs(dbg, dims, 8), "offsets must hold at least 5")
+    dbg._outputs = {"topk_w": torch.zeros(16, dtype=torch.int32)}
+    raises(lambda: _debug_outputs(dbg, dims, 8), "topk_w")
+    # all tensors on one device
+    if torch.cuda.is_available():
+        raises(lambda: moe_block(dims, good, x.cuda()), "different devices")

@@ -3,9 +3,12 @@
 Integer results (top-k indices, counts, offsets, grouped order, inverse rows,
 int8 codes) must match bit for bit; near-ties of the router (logit gap under
 1e-6) are flagged and then checked for validity instead. The block output must
-reach cosine >= 0.9999 and relative L2 <= 1e-2 (bf16) or 2e-2 (int8 experts).
+reach cosine >= 0.9999 and relative L2 <= 1e-2 (bf16) or 2e-2 (int8 and E4M3
+experts), pooled over the tokens compared and for each token on its own.
 Real-shape workloads are checked at their full sizes, in the configuration
-the bench times, on sampled tokens (the block is token-independent).
+the bench times: every token up to T = 2048; at T = 4096 and 16384 the tokens
+of the first and last grouped row of every 128 rows of each expert (so every
+GEMM M-tile has checked rows) plus a random sample.
 """
 import sys
 
@@ -68,6 +71,42 @@ def sample_tokens(T, n=24, seed=0):
     rng = np.random.default_rng(seed)
     s = set(rng.choice(T, size=n - 2, replace=False).tolist()) | {0, T - 1}
     return np.array(sorted(s))
+
+
+#: every token is compared with the oracle up to this batch size
+FULL_CHECK_T = 2048
+#: above it, the first and last grouped row of every run of this many rows of
+#: each expert (a multiple of the GEMM's 256-row M-tiles and of their halves)
+SEGMENT_ROWS = 128
+
+
+def block_check_tokens(T, dbg, n_random=24, seed=0):
+    """Tokens whose y the block tests compare: all of them up to FULL_CHECK_T;
+    beyond, the tokens of the first and last grouped row of every SEGMENT_ROWS
+    rows of each expert (through the GPU's own offsets and perm_token, so that
+    every M-tile of every expert GEMM block, partial last tiles included, has
+    rows checked) plus a random sample."""
+    if T <= FULL_CHECK_T:
+        return np.arange(T)
+    off, perm = dbg["offsets"], dbg["perm_token"]
+    rows = set()
+    for e in range(len(off) - 1):
+        for r0 in range(int(off[e]), int(off[e + 1]), SEGMENT_ROWS):
+            rows.add(r0)
+            rows.add(min(r0 + SEGMENT_ROWS, int(off[e + 1])) - 1)
+    toks = {int(perm[r]) for r in rows} | set(sample_tokens(T, n_random, seed).tolist())
+    return np.array(sorted(toks))
+
+
+def compare_per_token(y_gpu, y_ref, rel_max):
+    """Beside the pooled cosine and rel-L2: every token's own rel-L2 within the
+    same bar. Returns the largest."""
+    a = y_gpu.astype(np.float64)
+    b = y_ref.astype(np.float64)
+    rel = np.linalg.norm(a - b, axis=1) / np.linalg.norm(b, axis=1)
+    worst = int(np.argmax(rel))
+    assert rel[worst] <= rel_max, f"token row {worst}: rel-L2 {rel[worst]:.3g} > {rel_max}"
+    return float(rel[worst])
 
 
 def run_block(wl, lw, xd, path):
@@ -196,6 +235,20 @@ def test_route_parity(dev, name):
     say(f"  flagged near-ties: {n_flag} of {x.shape[0]}")
 
 
+def test_route_parity_wide_rows(dev):
+    """moe_route on a small batch of rows wider than the small-batch router
+    stages in LDS: it takes the MFMA router instead of failing at launch."""
+    s = moe_synth.BlockShape(hidden=12288, num_experts=64, top_k=8, expert_inter=64, dense_inter=64)
+    wl = moe_synth.Workload("wide", s, 8, 31)
+    w = moe_synth.make_weights(s, 31)
+    x = moe_synth.make_tokens(s, 31, 8)
+    say("case: moe_route hidden=12288 T=8")
+    lw = upload(w, dev)
+    idx, wt = moe_route(dims_of(s), lw, bf16_dev(x, dev))
+    torch.cuda.synchronize()
+    check_routing(to_np(idx), to_np(wt), oracle_route(wl, w, x), w["per_expert_scale"])
+
+
 PATH_CASES = [("tiny", MOE_PATH_STREAM), ("tiny", MOE_PATH_GROUPED),
               ("decode", MOE_PATH_STREAM), ("decode", MOE_PATH_GROUPED),
               ("prefill", MOE_PATH_GROUPED), ("skew", MOE_PATH_GROUPED),
@@ -218,13 +271,15 @@ def test_block_parity(dev, name, path):
     p = oracle.permute_pairs(dbg["topk_idx"], s.num_experts)
     for k in ("counts", "offsets", "perm_token", "inv_row"):
         np.testing.assert_array_equal(dbg[k], p[k], err_msg=k)
-    # block output on sampled tokens
-    toks = sample_tokens(T)
+    # block output: every token up to T = 2048, beyond that rows of every M-tile
+    toks = block_check_tokens(T, dbg)
     r = routing_for(dbg["topk_idx"][toks], {k: v[toks] for k, v in ref.items()}, w["per_expert_scale"])
     ow, fmt = oracle_weights(wl, w)
     y_ref, _ = oracle.moe_block(x[toks], ow, s.top_k, s.rms_eps, expert_dtype=fmt, routing=r)
-    cos, rel = compare_y(y_f64(y)[toks], y_ref, REL_BF16 if fmt == "bf16" else REL_INT8)
-    say(f"  tokens checked {len(toks)}  cos {cos:.7f}  rel-L2 {rel:.3e}")
+    bar = REL_BF16 if fmt == "bf16" else REL_INT8
+    cos, rel = compare_y(y_f64(y)[toks], y_ref, bar)
+    worst = compare_per_token(y_f64(y)[toks], y_ref, bar)
+    say(f"  tokens checked {len(toks)}  cos {cos:.7f}  rel-L2 {rel:.3e}  worst token rel-L2 {worst:.3e}")
 
 
 def test_skew_routing_collapses_to_few_experts(dev):
@@ -276,9 +331,9 @@ def test_dense_mlp_parity(dev, name, T):
     xs = xd[:T].contiguous()
     y = dense_mlp(dims_of(wl.shape), lw.dense_gate_up, lw.dense_down, xs)
     torch.cuda.synchronize()
-    toks = sample_tokens(T)
-    y_ref = oracle.dense_mlp(x[:T][toks], w["dense_gate_up"], w["dense_down"])
-    compare_y(y_f64(y)[toks], y_ref, REL_BF16)
+    y_ref = oracle.dense_mlp(x[:T], w["dense_gate_up"], w["dense_down"])
+    compare_y(y_f64(y), y_ref, REL_BF16)
+    compare_per_token(y_f64(y), y_ref, REL_BF16)
 
 
 EDGE = {
@@ -317,10 +372,11 @@ def test_ragged_real_shape(dev, T):
     y, dbg = run_block(wl, lw, xs, MOE_PATH_GROUPED)
     ref = oracle_route(wl, w, x[:T])
     check_routing(dbg["topk_idx"], dbg["topk_w"], ref, w["per_expert_scale"])
-    toks = sample_tokens(T, n=12, seed=T)
+    toks = block_check_tokens(T, dbg)
     r = routing_for(dbg["topk_idx"][toks], {k: v[toks] for k, v in ref.items()}, w["per_expert_scale"])
     y_ref, _ = oracle.moe_block(x[:T][toks], w, 8, 1e-6, routing=r)
     compare_y(y_f64(y)[toks], y_ref, REL_BF16)
+    compare_per_token(y_f64(y)[toks], y_ref, REL_BF16)
 
 
 def test_empty_batch_and_errors(dev):
@@ -394,7 +450,7 @@ def ffn_gains(H, which, dev, eps=1e-5):
     ("fp8_decode", MOE_PATH_GROUPED, "pre_moe")])
 def test_ffn_layer(dev, name, path, which):
     """moe_ffn_layer against the oracle's ffn_layer. Routing as in the block
-    tests (on the MoE branch's input); the output compared whole and, since
+    tests (on the residual h); the output compared whole and, since
     the residual dominates it, also minus h, with the rounding of the output
     to bf16 (half an ulp, 2^-9 relative) added to the bound."""
     wl, w, x, lw, xd = inputs(name, dev)
@@ -409,7 +465,7 @@ def test_ffn_layer(dev, name, path, which):
     out = moe_ffn_layer(dims_of(s), lw, norms, xd, debug=dbg)
     torch.cuda.synchronize()
     assert dbg.path_taken == path
-    toks = np.arange(T) if T <= 64 else sample_tokens(T, n=16, seed=5)
+    toks = np.arange(T) if T <= FULL_CHECK_T else sample_tokens(T, n=64, seed=5)
     gi, gw = to_np(out_t["topk_idx"])[toks], to_np(out_t["topk_w"])[toks]
     ow, fmt = oracle_weights(wl, w)
     rel_max = REL_BF16 if fmt == "bf16" else REL_INT8
@@ -470,8 +526,8 @@ def test_prefill_chunked(dev, name, T, chunk, which):
         gi[t0:t1], gw[t0:t1] = to_np(o["topk_idx"]), to_np(o["topk_w"])
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), "chunked != per-chunk calls"
-    toks = sample_tokens(T, n=32, seed=11)
-    # the layer routes its MoE branch's input, the pre-normed h
+    toks = sample_tokens(T, n=64, seed=11)
+    # the layer routes the residual h (the router normalises it itself)
     ow, fmt = oracle_weights(wl, w)
     ref_r = (oracle_route(wl, w, x[toks]) if norms is None
              else oracle.ffn_layer(x[toks], ow, norms_np, K, s.rms_eps, expert_dtype=fmt)[1])

@@ -429,6 +429,30 @@ def test_fp8_expert_activation_quantisation_is_per_token(tiny):
     np.testing.assert_array_equal(s2, 2 * s1)
 
 
+def test_fp8_expert_golden():
+    """A hand-derived fp8 expert (tests/golden/fp8_expert.json): the codes of x
+    and of the weights, and the output, which depends on h being rounded to
+    bf16 and then quantised per row (the fixture records what either slip
+    would give instead)."""
+    with open(os.path.join(HERE, "golden", "fp8_expert.json")) as f:
+        ex = json.load(f)
+    x = np.array(ex["x"], dtype=np.float32)
+    gu = np.array(ex["gate_up"], dtype=np.float32)
+    dn = np.array(ex["down"], dtype=np.float32)
+    xq, xs = oracle.quantize_fp8(x)
+    np.testing.assert_array_equal(xq[0], ex["x_codes"])
+    assert xs[0] == ex["scale"]
+    guq, gus = oracle.quantize_fp8(gu)
+    np.testing.assert_array_equal(guq, ex["gate_up_codes"])
+    assert (gus == ex["scale"]).all()
+    dnq, dns = oracle.quantize_fp8(dn)
+    np.testing.assert_array_equal(dns, [ex["scale"], ex["scale"], 0.0, 0.0, 0.0])
+    y = oracle.expert_ffn_fp8(x, guq, gus, dnq, dns)
+    np.testing.assert_array_equal(y[0], ex["expected_y"])
+    assert not np.array_equal(ex["expected_y"], ex["if_h_not_rounded_to_bf16"])
+    assert not np.array_equal(ex["expected_y"], ex["if_h_not_quantised"])
+
+
 # ---------------------------------------------------------------- accumulation
 def test_fp16_accumulation_loses_accuracy_at_real_hidden():
     """Negative control for the ONNX export card, "MoE dispatch: why this
@@ -491,20 +515,42 @@ def test_ffn_layer_without_norms_is_residual_plus_block(tiny):
     np.testing.assert_array_equal(out, oracle.bf16_to_f64(x) + y)
 
 
-def test_ffn_layer_equal_pre_norms_feed_router_and_both_branches(tiny):
+def test_ffn_layer_equal_pre_norms_feed_both_branches(tiny):
     """Equal pre-norm gains on both branches: the layer is the residual plus
-    the block run on the normalised input rounded to bf16, and the router
-    reads that input."""
+    the block run on the normalised input rounded to bf16, routed on the
+    residual h itself."""
     wl, w, x = tiny
     K, eps = wl.shape.top_k, wl.shape.rms_eps
     g = oracle.round_bf16(1.0 + 0.1 * np.random.default_rng(2).standard_normal(wl.shape.hidden))
     norms = {**NO_NORMS, "pre_dense": g, "pre_moe": g, "eps": 1e-5}
     out, r = oracle.ffn_layer(x, w, norms, K, eps)
-    xn = oracle.round_bf16(oracle.rms_normalise(x, 1e-5) * g[None, :])
-    r_ref = oracle.route(xn, w["router_scale"], w["router_w"], w["per_expert_scale"], K, eps)
+    r_ref = oracle.route(x, w["router_scale"], w["router_w"], w["per_expert_scale"], K, eps)
     np.testing.assert_array_equal(r["topk_idx"], r_ref["topk_idx"])
+    np.testing.assert_array_equal(r["topk_w"], r_ref["topk_w"])
+    xn = oracle.round_bf16(oracle.rms_normalise(x, 1e-5) * g[None, :])
     y, _ = oracle.moe_block(xn, w, K, eps, routing=r)
     np.testing.assert_array_equal(out, oracle.bf16_to_f64(x) + y)
+
+
+def test_ffn_layer_routing_ignores_the_pre_norms(tiny):
+    """The router reads the un-normalised residual: its choice and weights do
+    not move with the pre-norm gains, while the MoE branch's output does; and
+    since the router's own norm is scale-free, scaling h by a power of two
+    leaves the routing unchanged."""
+    wl, w, x = tiny
+    K, eps = wl.shape.top_k, wl.shape.rms_eps
+    H = wl.shape.hidden
+    rng = np.random.default_rng(12)
+    g1 = oracle.round_bf16(1.0 + 0.3 * rng.standard_normal(H))
+    g2 = oracle.round_bf16(1.0 + 0.3 * rng.standard_normal(H))
+    a, ra = oracle.ffn_layer(x, w, {**NO_NORMS, "pre_moe": g1}, K, eps)
+    b, rb = oracle.ffn_layer(x, w, {**NO_NORMS, "pre_moe": g2}, K, eps)
+    np.testing.assert_array_equal(ra["topk_idx"], rb["topk_idx"])
+    np.testing.assert_array_equal(ra["topk_w"], rb["topk_w"])
+    assert np.max(np.abs(a - b)) > 1e-3
+    _, r4 = oracle.ffn_layer(oracle.bf16_to_f64(x) * 4.0, w, {**NO_NORMS, "pre_moe": g1}, K, 0.0)
+    _, r1 = oracle.ffn_layer(x, w, {**NO_NORMS, "pre_moe": g1}, K, 0.0)
+    np.testing.assert_array_equal(r4["topk_idx"], r1["topk_idx"])
 
 
 def test_ffn_layer_moe_branch_alone(tiny):
@@ -543,8 +589,8 @@ def test_ffn_layer_post_norms_act_per_branch(tiny):
 
 
 def test_ffn_layer_pre_norms_act_per_branch(tiny):
-    """A pre-norm on the MoE branch only: the router and experts read the
-    normalised input, the dense MLP the raw one."""
+    """A pre-norm on the MoE branch only: the experts read the normalised
+    input, the dense MLP and the router the raw one."""
     wl, w, x = tiny
     K, eps = wl.shape.top_k, wl.shape.rms_eps
     g = oracle.round_bf16(1.0 + 0.1 * np.random.default_rng(4).standard_normal(wl.shape.hidden))
@@ -553,5 +599,5 @@ def test_ffn_layer_pre_norms_act_per_branch(tiny):
     moe, _ = oracle.moe_part(xn, w, K, eps, routing=r)
     dense = oracle.dense_mlp(x, w["dense_gate_up"], w["dense_down"])
     np.testing.assert_array_equal(out, oracle.bf16_to_f64(x) + (dense + moe))
-    r_ref = oracle.route(xn, w["router_scale"], w["router_w"], w["per_expert_scale"], K, eps)
+    r_ref = oracle.route(x, w["router_scale"], w["router_w"], w["per_expert_scale"], K, eps)
     np.testing.assert_array_equal(r["topk_idx"], r_ref["topk_idx"])
