@@ -2,6 +2,7 @@
 """Benchmark of the hybrid MoE FFN block on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+                    [--secondary prefill,skew,...|none] [--cpu-seconds S]
 
 A step is one pass of the whole block (router, grouping, experts, dense MLP,
 combine) over one batch of seeded synthetic tokens, on one layer's weights.
@@ -13,8 +14,17 @@ last-level cache. Inputs are resident in HBM before timing starts.
 Prints ONE JSON line. ``value`` is tokens/s of the primary workload (decode,
 T=8, by default); the dominant kernel's roofline is measured live with HIP
 events recorded on the library's stream around that kernel in every timed
-step. The prefill (T=2048) numbers the metric also names are reported under
-``prefill``. ``cpu_baseline`` times the CPU oracle on a bounded sample.
+step. The other workloads (prefill T=2048, the skewed T=16384 chunk, int8
+experts at T=8 and T=4096, E4M3 experts at T=8 and T=2048) follow under
+``secondary``, each with its step time, block fractions and the roofline of
+its own dominant kernel; ``targets`` says for each configuration whether its
+stated target is met. ``cpu_baseline`` times the CPU oracle on a bounded
+token sample of every workload, on the same weights.
+
+Bytes are algorithmic: the weights of the touched experts, the dense MLP and
+the router read once, x read once and y written once. Intermediates (h, the
+weighted expert rows, the dense intermediate and output, partial sums) are
+implementation traffic, reported per stage as ``impl_bytes``.
 """
 from __future__ import annotations
 
@@ -95,56 +105,78 @@ def algorithmic(shape: moe_synth.BlockShape, T: int, n_active: int, int8: bool):
     return {"bytes": bytes_total, "flops": flops, "gu_expert": gu_expert, "dn_expert": dn_expert}
 
 
-def stage_work(stage: str, shape, T, n_active, int8):
-    """Algorithmic bytes and FLOPs of one launch of a stage's kernel, with the
-    units it processes (weights of the touched experts read once, activations
-    and outputs once; no re-reads, no padding)."""
+def stage_work(stage: str, shape, T, n_active, byte_w):
+    """(algorithmic bytes, FLOPs, units, implementation bytes) of one launch of
+    a stage's kernel. Algorithmic bytes are the weights the kernel streams
+    (touched experts, dense MLP, router: each read once), plus x if it reads x
+    and y if it writes y; intermediates are implementation bytes."""
     H, E, K, I, Id = shape.hidden, shape.num_experts, shape.top_k, shape.expert_inter, shape.dense_inter
     TK = T * K
-    wb = 1 if int8 else 2
-    gu_w = 2 * I * H * wb + (2 * I * 4 if int8 else 0)
-    dn_w = H * I * wb + (H * 4 if int8 else 0)
-    router_w = E * H * 2 + H * 2
+    wb = 1 if byte_w else 2
+    gu_w = 2 * I * H * wb + (2 * I * 4 if byte_w else 0)
+    dn_w = H * I * wb + (H * 4 if byte_w else 0)
+    router_w = E * H * 2 + H * 2 + E * 4
+    dgu_w, ddn_w = 2 * Id * H * 2, H * Id * 2
     x, y = T * H * 2, T * H * 2
+    S = 4  # K-slices of the streaming path's partial sums
     table = {
-        "decode_front": (router_w + 2 * Id * H * 2 + x + 4 * T * (E + 1) * 4 + 4 * T * 2 * Id * 4,
-                         2 * T * E * H + 2 * T * H * 2 * Id,
-                         "router weights + dense gate_up + x + 4 K-slices of partial logits and dense sums"),
-        "decode_route": (4 * T * (E + 1) * 4 + E * 4 + TK * 20 + 4 * T * 2 * Id * 4 + T * Id * 2, 0,
-                         "partial logits + routing tables + dense partial sums + hd"),
-        "decode_experts_gateup": (n_active * gu_w + x + TK * I * 2, 2 * TK * H * 2 * I,
-                                  f"{n_active} experts' gate_up ({gu_w} B each) + x + h"),
-        "decode_down": (n_active * dn_w + H * Id * 2 + TK * I * 2 + T * Id * 2,
-                        2 * TK * I * H + 2 * T * Id * H,
-                        f"{n_active} experts' down ({dn_w} B each) + dense down + h + hd"),
-        "decode_combine": ((TK + T) * H * 4 + y, 2 * TK * H, "fp32 partial rows + y"),
-        "router": (router_w + x + E * 4 + TK * 8, 2 * T * E * H, "router weights + x + top-k"),
-        "permute": (TK * 8 + TK * 12 + E * 8, 0, "top-k + grouping tables"),
-        "gemm_gateup": (n_active * gu_w + 2 * Id * H * 2 + x + TK * I * 2 + T * Id * 2,
+        "decode_front": (router_w + x, 2 * T * E * H,
+                         "router weights + x", S * T * (E + 1) * 4),
+        "decode_route": (dgu_w + x, 2 * T * H * 2 * Id,
+                         "dense gate_up + x (beside the routing workgroup)",
+                         S * T * (E + 1) * 4 + TK * 20 + S * T * 2 * Id * 4),
+        "decode_experts_gateup": (n_active * gu_w + x, 2 * TK * H * 2 * I,
+                                  f"{n_active} experts' gate_up ({gu_w} B each) + x",
+                                  S * T * 2 * Id * 4 + T * Id * 2 + 2 * TK * 2 * I * 4),
+        "decode_down": (n_active * dn_w + ddn_w, 2 * TK * I * H + 2 * T * Id * H,
+                        f"{n_active} experts' down ({dn_w} B each) + dense down",
+                        2 * TK * 2 * I * 4 + T * Id * 2 + (TK + T) * H * 4),
+        "h_quant": (0, 0, "h of every routed pair, quantised per row", 2 * TK * 2 * I * 4 + TK * I * 2 + TK * 8),
+        "decode_combine": (y, 2 * TK * H, "y", (TK + T) * H * 4 + TK * 8),
+        "router": (router_w + x, 2 * T * E * H, "router weights + x", TK * 8),
+        "permute": (0, 0, "grouping tables", TK * 8 + TK * 12 + E * 8),
+        "act_quant": (x, 0, "x", T * H * 2 + T * 4),
+        "gemm_gateup": (n_active * gu_w + dgu_w + x,
                         2 * TK * H * 2 * I + 2 * T * H * 2 * Id,
-                        f"{n_active} experts' gate_up ({gu_w} B each) + dense gate_up + x + h + hd"),
-        "gemm_down": (n_active * dn_w + TK * I * 2 + TK * H * 2 + H * Id * 2 + T * Id * 2 + T * H * 4,
-                      2 * TK * I * H + 2 * T * Id * H,
-                      f"{n_active} experts' down ({dn_w} B each) + h + rows + dense down + hd + fp32 dense out"),
-        "combine": (T * H * 4 + TK * H * 2 + TK * 4 + y, TK * H, "fp32 dense out + expert rows + y"),
-        "act_quant": (2 * x + T * 4, 0, "x read, its E4M3 carriers written, per-token scales"),
-        "h_quant": (2 * TK * I * 2 + TK * 12, 0, "h read and rewritten as E4M3 carriers, row scales and factors"),
+                        f"{n_active} experts' gate_up ({gu_w} B each) + dense gate_up + x",
+                        TK * I * 2 + T * Id * 2),
+        "gemm_down": (n_active * dn_w + ddn_w, 2 * TK * I * H + 2 * T * Id * H,
+                      f"{n_active} experts' down ({dn_w} B each) + dense down",
+                      TK * I * 2 + T * Id * 2 + TK * H * 2 + T * H * 4),
+        "combine": (y, TK * H, "y", T * H * 4 + TK * H * 2 + TK * 4),
     }
+    if stage == "h_quant" and T > 64:  # the grouped path's in-place pass over h
+        return (0, 0, "h quantised per row in place", 2 * TK * I * 2 + TK * 12)
     return table[stage]
 
 
 # ---------------------------------------------------------------- workloads
-def run_workload(name, steps, warmup, layers, dev, ev: HipEvents, log):
+_WCACHE = {}
+
+
+def host_inputs(name):
+    """(workload, numpy weights, x) of a workload; workloads that draw the same
+    weights (shape, seed, skew) share one draw."""
+    wl = moe_synth.WORKLOADS[name]
+    key = (wl.shape, wl.seed, wl.skew)
+    if key not in _WCACHE:
+        _WCACHE.clear()  # one layer's weights on the host at a time
+        _WCACHE[key] = moe_synth.make_weights(wl.shape, wl.seed, wl.skew)
+    return wl, _WCACHE[key], moe_synth.make_tokens(wl.shape, wl.seed, wl.tokens)
+
+
+def run_workload(name, steps, warmup, layers, dev, ev: HipEvents, log, extras=True):
+    """Times the block on one workload. extras: also the graph replay, the
+    layer's FFN around the block, and the chunked prefill where T exceeds a
+    chunk."""
     import torch
     from mixture_experts_ffn_amd import BlockCall, moe_quantize_int8, new_debug, tile_layer, _abi
     from mixture_experts_ffn_amd.ops import BlockDims, LayerWeights
 
-    wl = moe_synth.WORKLOADS[name]
+    t0 = time.time()
+    wl, w, x = host_inputs(name)
     s = wl.shape
     T = wl.tokens
-    t0 = time.time()
-    w = moe_synth.make_weights(s, wl.seed, wl.skew)
-    x = moe_synth.make_tokens(s, wl.seed, T)
     log(f"[bench] {name}: generated inputs in {time.time() - t0:.1f}s")
 
     def bf(a):
@@ -158,7 +190,6 @@ def run_workload(name, steps, warmup, layers, dev, ev: HipEvents, log):
                         expert_gate_up=bf(w["expert_gate_up"]), expert_down=bf(w["expert_down"]),
                         dense_gate_up=bf(w["dense_gate_up"]), dense_down=bf(w["dense_down"]),
                         logit_bias=f32(w["logit_bias"]))
-    del w
     if wl.int8:
         base.expert_gate_up, base.gate_up_scale = moe_quantize_int8(base.expert_gate_up)
         base.expert_down, base.down_scale = moe_quantize_int8(base.expert_down)
@@ -216,61 +247,69 @@ def run_workload(name, steps, warmup, layers, dev, ev: HipEvents, log):
     elapsed = time.perf_counter() - t_start
     ms_step = elapsed * 1e3 / steps
 
-    # the same steps replayed from a HIP graph holding one call per weight copy
-    # (reported beside the eager time; `value` stays the eager rate)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for c in calls:
-            c()
-    torch.cuda.synchronize()
-    graph.replay()
-    torch.cuda.synchronize()
-    reps = max(1, steps // layers)
-    t_g = time.perf_counter()
-    for _ in range(reps):
+    res = {"workload": name, "T": T, "path": {1: "stream", 2: "grouped"}.get(path, path),
+           "ms_per_step": ms_step, "tokens_per_s": T / (ms_step * 1e-3)}
+    note = ""
+    if extras:
+        # the same steps replayed from a HIP graph holding one call per weight
+        # copy (reported beside the eager time; `value` stays the eager rate)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for c in calls:
+                c()
+        torch.cuda.synchronize()
         graph.replay()
-    torch.cuda.synchronize()
-    ms_graph = (time.perf_counter() - t_g) * 1e3 / (reps * layers)
-    del graph
+        torch.cuda.synchronize()
+        reps = max(1, steps // layers)
+        t_g = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        ms_graph = (time.perf_counter() - t_g) * 1e3 / (reps * layers)
+        del graph
+        res["graph"] = {"ms_per_step": ms_graph, "tokens_per_s": T / (ms_graph * 1e-3)}
 
-    # the layer's FFN around the block (all five feed-forward norms present):
-    # the same steps through moe_ffn_layer, for the cost of the norms and residual
-    from mixture_experts_ffn_amd import FfnCall, FfnNorms
-    rng = np.random.default_rng(wl.seed)
-    gains = {k: bf(moe_synth.f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal(s.hidden)).astype(np.float32)))
-             for k in ("pre_dense", "pre_moe", "post_dense", "post_moe", "post")}
-    norms = FfnNorms(**gains, eps=1e-6)
-    out_ffn = torch.empty_like(y)
-    ffn_calls = [FfnCall(dims, c, norms, xd, out=out_ffn) for c in copies]
-    for i in range(warmup):
-        ffn_calls[i % layers]()
-    torch.cuda.synchronize()
-    t_f = time.perf_counter()
-    for i in range(steps):
-        ffn_calls[i % layers]()
-    torch.cuda.synchronize()
-    ms_ffn = (time.perf_counter() - t_f) * 1e3 / steps
-    del ffn_calls
-
-    # a prompt longer than one prefill chunk: the same steps through the
-    # chunked driver (consecutive chunks of the default size, one workspace)
-    chunked = None
-    from mixture_experts_ffn_amd import moe_prefill_chunk_tokens, moe_prefill_chunked, moe_prefill_workspace_bytes
-    C = moe_prefill_chunk_tokens(0)
-    if T > C:
-        ws_c = torch.empty(moe_prefill_workspace_bytes(dims, C), dtype=torch.uint8, device=dev)
+        # the layer's FFN around the block (all five feed-forward norms present):
+        # the same steps through moe_ffn_layer, for the cost of the norms and residual
+        from mixture_experts_ffn_amd import FfnCall, FfnNorms
+        rng = np.random.default_rng(wl.seed)
+        gains = {k: bf(moe_synth.f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal(s.hidden)).astype(np.float32)))
+                 for k in ("pre_dense", "pre_moe", "post_dense", "post_moe", "post")}
+        norms = FfnNorms(**gains, eps=1e-6)
+        out_ffn = torch.empty_like(y)
+        ffn_calls = [FfnCall(dims, c, norms, xd, out=out_ffn) for c in copies]
         for i in range(warmup):
-            moe_prefill_chunked(dims, copies[i % layers], None, xd, C, out=y, workspace=ws_c)
+            ffn_calls[i % layers]()
         torch.cuda.synchronize()
-        t_c = time.perf_counter()
+        t_f = time.perf_counter()
         for i in range(steps):
-            moe_prefill_chunked(dims, copies[i % layers], None, xd, C, out=y, workspace=ws_c)
+            ffn_calls[i % layers]()
         torch.cuda.synchronize()
-        ms_c = (time.perf_counter() - t_c) * 1e3 / steps
-        chunked = {"ms_per_step": ms_c, "tokens_per_s": T / (ms_c * 1e-3), "chunk": C,
-                   "workspace_bytes": ws_c.numel(), "unchunked_workspace_bytes": ws.numel(),
-                   "note": "moe_prefill_chunked: the block over consecutive chunks, one chunk's workspace"}
-        del ws_c
+        ms_ffn = (time.perf_counter() - t_f) * 1e3 / steps
+        del ffn_calls
+        res["ffn_layer"] = {"ms_per_step": ms_ffn, "tokens_per_s": T / (ms_ffn * 1e-3),
+                            "note": "moe_ffn_layer: the block with all five feed-forward norms and the residual"}
+        note = f"; {ms_graph * 1e3:.1f} replayed from a graph; with the FFN norms and residual {ms_ffn * 1e3:.1f}"
+
+        # a prompt longer than one prefill chunk: the same steps through the
+        # chunked driver (consecutive chunks of the default size, one workspace)
+        from mixture_experts_ffn_amd import (moe_prefill_chunk_tokens, moe_prefill_chunked,
+                                             moe_prefill_workspace_bytes)
+        C = moe_prefill_chunk_tokens(0)
+        if T > C:
+            ws_c = torch.empty(moe_prefill_workspace_bytes(dims, C), dtype=torch.uint8, device=dev)
+            for i in range(warmup):
+                moe_prefill_chunked(dims, copies[i % layers], None, xd, C, out=y, workspace=ws_c)
+            torch.cuda.synchronize()
+            t_c = time.perf_counter()
+            for i in range(steps):
+                moe_prefill_chunked(dims, copies[i % layers], None, xd, C, out=y, workspace=ws_c)
+            torch.cuda.synchronize()
+            ms_c = (time.perf_counter() - t_c) * 1e3 / steps
+            res["chunked"] = {"ms_per_step": ms_c, "tokens_per_s": T / (ms_c * 1e-3), "chunk": C,
+                              "workspace_bytes": ws_c.numel(), "unchunked_workspace_bytes": ws.numel(),
+                              "note": "moe_prefill_chunked: the block over consecutive chunks, one chunk's workspace"}
+            del ws_c
 
     # dominant kernel: HIP events on the library's stream around that kernel in
     # every step of a second timed run (an event marker costs a few us of
@@ -290,32 +329,27 @@ def run_workload(name, steps, warmup, layers, dev, ev: HipEvents, log):
 
     byte_w = wl.int8 or wl.fp8  # one byte a weight plus fp32 row scales
     work = algorithmic(s, T, n_active, byte_w)
-    dbytes, dflops, dunits = stage_work(dom_name, s, T, n_active, byte_w)
-    res = {
-        "workload": name, "T": T, "path": {1: "stream", 2: "grouped"}.get(path, path),
-        "ms_per_step": ms_step, "tokens_per_s": T / (ms_step * 1e-3),
-        "graph": {"ms_per_step": ms_graph, "tokens_per_s": T / (ms_graph * 1e-3)},
-        "ffn_layer": {"ms_per_step": ms_ffn, "tokens_per_s": T / (ms_ffn * 1e-3),
-                      "note": "moe_ffn_layer: the block with all five feed-forward norms and the residual"},
-        **({"chunked": chunked} if chunked else {}),
+    dbytes, dflops, dunits, dimpl = stage_work(dom_name, s, T, n_active, byte_w)
+    sw = {n: stage_work(n, s, T, n_active, byte_w) for n in stage_names}
+    res.update({
         "experts_touched": n_active, "max_rows_per_expert": int(cnt.max()),
         "block_bytes": work["bytes"], "block_flops": work["flops"],
         "block_gbs": work["bytes"] / (ms_step * 1e-3) / 1e9,
         "block_tflops": work["flops"] / (ms_step * 1e-3) / 1e12,
         "stages_us": {n: round(float(t) * 1e3, 2) for n, t in zip(stage_names, per_stage)},
-        "stages_gbs": {n: round(stage_work(n, s, T, n_active, byte_w)[0] / (float(t) * 1e-3) / 1e9, 1)
-                       for n, t in zip(stage_names, per_stage)},
+        "stages_gbs": {n: round(sw[n][0] / (float(t) * 1e-3) / 1e9, 1) for n, t in zip(stage_names, per_stage)},
+        "impl_bytes": {n: sw[n][3] for n in stage_names},
         "dominant": {"kernel": dom_name, "avg_us": dom_ms * 1e3, "bytes": dbytes, "flops": dflops,
-                     "units": dunits},
-    }
+                     "units": dunits, "impl_bytes": dimpl},
+    })
     res["block_hbm_frac"] = res["block_gbs"] / HBM_PEAK_GBS
     res["block_mfma_frac"] = res["block_tflops"] / MFMA_BF16_PEAK_TFLOPS
-    log(f"[bench] {name}: {ms_step * 1e3:.1f} us/step ({ms_graph * 1e3:.1f} replayed from a graph; "
-        f"with the FFN norms and residual {ms_ffn * 1e3:.1f}"
-        + (f"; in {C}-token chunks {chunked['ms_per_step'] * 1e3:.1f}" if chunked else "") + "), "
-        f"{res['tokens_per_s']:.0f} tok/s, "
-        f"{res['block_gbs']:.0f} GB/s, dominant {dom_name} {dom_ms * 1e3:.1f} us, stages {res['stages_us']} "
-        f"GB/s {res['stages_gbs']}")
+    log(f"[bench] {name}: {ms_step * 1e3:.1f} us/step{note}"
+        + (f"; in {res['chunked']['chunk']}-token chunks {res['chunked']['ms_per_step'] * 1e3:.1f}"
+           if "chunked" in res else "") + "), "
+        f"{res['tokens_per_s']:.0f} tok/s, block {res['block_gbs']:.0f} GB/s ({res['block_hbm_frac']:.3f} HBM, "
+        f"{res['block_mfma_frac']:.3f} MFMA), dominant {dom_name} {dom_ms * 1e3:.1f} us, "
+        f"stages {res['stages_us']} GB/s {res['stages_gbs']}")
     del calls, copies, base
     torch.cuda.empty_cache()
     return res
@@ -324,8 +358,8 @@ def run_workload(name, steps, warmup, layers, dev, ev: HipEvents, log):
 def roofline_for(res, bound=None):
     """Roofline of the dominant kernel. bound None: the roof that binds it, the
     larger of its algorithmic bytes at the HBM peak and its FLOPs at the MFMA
-    peak (bf16: int8 experts are widened to bf16 before their MFMAs). The other
-    roof's fraction is reported beside it."""
+    peak (bf16: int8 and E4M3 experts are widened to 16-bit operands before
+    their MFMAs). The other roof's fraction is reported beside it."""
     d = res["dominant"]
     sec = d["avg_us"] * 1e-6
     hbm = {"bound": "hbm", "achieved": d["bytes"] / sec / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
@@ -358,31 +392,94 @@ def measured_traffic(kernel, workload):
     return None
 
 
-def cpu_baseline(name, budget_s, log):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+# the stated target of each configuration: (block measure, bar)
+TARGETS = {
+    "decode": ("block_hbm_frac", 0.70),
+    "prefill": ("block_mfma_frac", 0.55),
+    "skew": ("block_mfma_frac", 0.55),
+    "int8_decode": ("block_hbm_frac", 0.70),
+    "int8_prefill": ("block_mfma_frac", 0.55),
+}
+TARGET_NOTES = {
+    "prefill": "not reachable: at 0.55 MFMA the block would stream its 1.58 GB faster than the 8 TB/s HBM peak "
+               "(the cap is 0.541); block_hbm_frac is the binding roof",
+}
+
+
+def targets_of(results):
+    out = []
+    for r in results:
+        if r["workload"] in TARGETS:
+            key, bar = TARGETS[r["workload"]]
+            t = {"workload": r["workload"], "measure": key, "value": round(r[key], 4), "target": bar,
+                 "met": bool(r[key] >= bar)}
+            if r["workload"] in TARGET_NOTES:
+                t["note"] = TARGET_NOTES[r["workload"]]
+                t["block_hbm_frac"] = round(r["block_hbm_frac"], 4)
+            out.append(t)
+    return out
+
+
+class _LazyQuantised(dict):
+    """Per-expert quantised weights for the oracle, made on first use (a
+    load-time step: warmed before timing)."""
+
+    def __init__(self, src, quant, part):
+        super().__init__()
+        self.src, self.quant, self.part = src, quant, part
+
+    def __getitem__(self, e):
+        if e not in self:
+            dict.__setitem__(self, e, self.quant(self.src[e])[self.part])
+        return dict.__getitem__(self, e)
+
+
+def cpu_baseline(name, budget_s, log, tokens=None):
+    """The oracle, as it stands, on a bounded token sample of the same
+    workload (same seeded weights), on the host's cores."""
     import oracle
     from threadpoolctl import threadpool_info, threadpool_limits
-    wl = moe_synth.WORKLOADS[name]
+    wl, w, x_all = host_inputs(name)
     s = wl.shape
-    T = min(wl.tokens, 8)
-    w = moe_synth.make_weights(s, wl.seed, wl.skew)
-    x = moe_synth.make_tokens(s, wl.seed, wl.tokens)[:T]
+    # the sample: a decode batch as it is; a few tokens of the larger ones (the
+    # E4M3 oracle decodes every touched expert's codes on each call, so fewer)
+    if tokens is None:
+        tokens = 2 if wl.fp8 else 8 if (wl.tokens <= 64 or wl.int8) else 32
+    T = min(wl.tokens, tokens)
+    x = x_all[:T]
+    fmt = "int8" if wl.int8 else "fp8" if wl.fp8 else "bf16"
+    ow = dict(w)
+    if fmt == "int8":
+        for k, src in (("expert_gate_up", w["expert_gate_up"]), ("expert_down", w["expert_down"])):
+            ow[k + "_q"] = _LazyQuantised(src, oracle.quantize_int8, 0)
+            ow[k + "_scale"] = _LazyQuantised(src, oracle.quantize_int8, 1)
+    elif fmt == "fp8":
+        for k, src in (("expert_gate_up", w["expert_gate_up"]), ("expert_down", w["expert_down"])):
+            ow[k + "_f8"] = _LazyQuantised(src, oracle.quantize_fp8, 0)
+            ow[k + "_f8_scale"] = _LazyQuantised(src, oracle.quantize_fp8, 1)
     cores = min(os.cpu_count() or 1, 16)   # the box's CPU share for one GPU
     with threadpool_limits(limits=cores):
         used = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        oracle.moe_block(x, ow, s.top_k, s.rms_eps, expert_dtype=fmt)  # warm: quantised experts made here
         n = 0
         t0 = time.perf_counter()
         while True:
-            oracle.moe_block(x, w, s.top_k, s.rms_eps)
+            oracle.moe_block(x, ow, s.top_k, s.rms_eps, expert_dtype=fmt)
             n += 1
             if time.perf_counter() - t0 >= budget_s:
                 break
         dt = time.perf_counter() - t0
     v = n * T / dt
-    log(f"[bench] cpu oracle: {n} calls x {T} tokens in {dt:.1f}s -> {v:.2f} tok/s on {used} threads")
+    log(f"[bench] cpu oracle {name}: {n} calls x {T} tokens in {dt:.1f}s -> {v:.2f} tok/s on {used} threads")
     return {"value": v, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
-            "sample": f"{n} oracle calls of the {name} workload's first {T} tokens (fp64 numpy, "
+            "sample": f"{n} oracle calls of the {name} workload's first {T} tokens ({fmt} experts, fp64 numpy, "
                       f"same seeded weights), {dt:.1f} s"}
+
+
+SECONDARY_DEFAULT = ("prefill", "skew", "int8_decode", "int8_prefill", "fp8_decode", "fp8_prefill")
+SECONDARY_KEYS = ("T", "path", "ms_per_step", "tokens_per_s", "graph", "ffn_layer", "chunked", "block_bytes",
+                  "block_gbs", "block_hbm_frac", "block_flops", "block_tflops", "block_mfma_frac",
+                  "experts_touched", "max_rows_per_expert", "stages_us", "stages_gbs", "impl_bytes", "dominant")
 
 
 def main():
@@ -392,8 +489,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode", choices=sorted(moe_synth.WORKLOADS))
     ap.add_argument("--layers", type=int, default=4, help="distinct weight copies cycled per step")
-    ap.add_argument("--no-prefill", action="store_true", help="skip the T=2048 secondary line")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0 = skip)")
+    ap.add_argument("--secondary", default=",".join(SECONDARY_DEFAULT),
+                    help="comma-separated workloads reported under 'secondary' ('none': only the primary)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="oracle time budget for the primary workload (0 = skip every oracle timing)")
+    ap.add_argument("--cpu-seconds-secondary", type=float, default=4.0,
+                    help="oracle time budget for each secondary workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (the known-size kernel that "
                          "scales rocprofv3's FETCH_SIZE / WRITE_SIZE to bytes), then exit")
@@ -424,9 +525,13 @@ def main():
     load_library()
     dev = torch.device("cuda:0")
     ev = HipEvents()
+    cpu = {}
 
     primary = run_workload(args.workload, args.steps, args.warmup, args.layers, dev, ev, log)
+    if args.cpu_seconds > 0:
+        cpu[args.workload] = cpu_baseline(args.workload, args.cpu_seconds, log)
     roof = roofline_for(primary)
+    wl = moe_synth.WORKLOADS[args.workload]
     out = {
         "metric": METRIC,
         "value": primary["tokens_per_s"],
@@ -440,32 +545,37 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",  # bf16 operands, fp32 accumulation (MFMA or v_dot2 with fp32 sums)
         "data": "synthetic: seeded random tokens and random-init weights of the real block shape",
-        "config": {"workload": f"{args.workload}: {moe_synth.WORKLOADS[args.workload].note}",
-                   "T": primary["T"], "hidden": 2816 if args.workload != "tiny" else 512,
-                   "experts": moe_synth.WORKLOADS[args.workload].shape.num_experts,
-                   "top_k": moe_synth.WORKLOADS[args.workload].shape.top_k,
-                   "expert_inter": moe_synth.WORKLOADS[args.workload].shape.expert_inter,
-                   "dense_inter": moe_synth.WORKLOADS[args.workload].shape.dense_inter,
-                   "seed": moe_synth.WORKLOADS[args.workload].seed,
-                   "layers_cycled": args.layers, "path": primary["path"]},
+        "config": {"workload": f"{args.workload}: {wl.note}", "T": primary["T"], "hidden": wl.shape.hidden,
+                   "experts": wl.shape.num_experts, "top_k": wl.shape.top_k,
+                   "expert_inter": wl.shape.expert_inter, "dense_inter": wl.shape.dense_inter,
+                   "seed": wl.seed, "layers_cycled": args.layers, "path": primary["path"]},
         "roofline": roof,
-        "graph": primary["graph"],
-        "ffn_layer": primary["ffn_layer"],
-        **({"chunked": primary["chunked"]} if "chunked" in primary else {}),
         "block": {k: primary[k] for k in ("block_bytes", "block_gbs", "block_hbm_frac", "block_flops",
                                           "block_tflops", "block_mfma_frac", "experts_touched",
-                                          "stages_us", "stages_gbs", "dominant")},
+                                          "stages_us", "stages_gbs", "impl_bytes", "dominant")},
+        **{k: primary[k] for k in ("graph", "ffn_layer", "chunked") if k in primary},
     }
-    if args.workload == "decode" and not args.no_prefill:
-        pre = run_workload("prefill", max(10, args.steps // 4), max(3, args.warmup // 4), args.layers,
-                           dev, ev, log)
-        out["prefill"] = {k: pre[k] for k in ("T", "path", "ms_per_step", "tokens_per_s", "graph", "ffn_layer",
-                                              "block_gbs",
-                                              "block_hbm_frac", "block_tflops", "block_mfma_frac",
-                                              "experts_touched", "stages_us", "stages_gbs", "dominant")}
-        out["prefill"]["roofline"] = roofline_for(pre)
-    if args.cpu_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds, log)
+    results = [primary]
+    secondary = {}
+    names = [] if args.secondary == "none" else [n for n in args.secondary.split(",") if n and n != args.workload]
+    for name in names:
+        steps = max(10, args.steps // 4) if moe_synth.WORKLOADS[name].tokens > 64 else max(20, args.steps // 2)
+        r = run_workload(name, steps, max(3, args.warmup // 4), args.layers, dev, ev, log,
+                         extras=(name == "prefill"))
+        if args.cpu_seconds > 0 and args.cpu_seconds_secondary > 0:
+            cpu[name] = cpu_baseline(name, args.cpu_seconds_secondary, log)
+        sec = {k: r[k] for k in SECONDARY_KEYS if k in r}
+        sec["steps"] = steps
+        sec["roofline"] = roofline_for(r)
+        secondary[name] = sec
+        results.append(r)
+    if secondary:
+        out["secondary"] = secondary
+    out["targets"] = targets_of(results)
+    if cpu:
+        out["cpu_baseline"] = dict(cpu[args.workload]) if args.workload in cpu else None
+        if out["cpu_baseline"] is not None:
+            out["cpu_baseline"]["per_config"] = {k: v for k, v in cpu.items() if k != args.workload}
     else:
         out["cpu_baseline"] = None
     out["context"] = PAGE_CONTEXT
