@@ -170,6 +170,25 @@ int moe_route(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
 int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T, void* y,
               moe_debug* dbg, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_block without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Its kernels use the library's own scratch array, of
+ * MOE_NOALLOC_SCRATCH_BYTES per device, which each device the library runs on
+ * holds from the library's load until the process ends; nothing is allocated
+ * or freed on any call. The array's device address is looked up once per
+ * device, on the first call made with that device current. Arguments, result,
+ * path choice and errors are those of moe_block, and so is the output, bit for
+ * bit. A batch whose workspace (moe_workspace_bytes) exceeds the array is
+ * refused with MOE_ERR_WORKSPACE before anything is launched: at the real
+ * shape that admits every decode-sized batch (T <= 64) and grouped batches of
+ * about 400 tokens. Every call on one device shares its array and leaves its
+ * intermediates there (no kernel relies on what an earlier call left): calls
+ * that overlap on one device, from several streams or threads, race and must
+ * be serialised by the caller. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32 << 20)
+int moe_block_noalloc(const moe_dims* d, const moe_weights* w, const void* x, int32_t T, void* y,
+                      moe_debug* dbg, hipStream_t stream);
+
 /* The shared dense MLP alone ([ONNX] row "MoE topology"): y [T, H] bf16 =
  * dense_down @ (gelu_tanh(gate @ x) * (up @ x)), with dense_gate_up [2Id, H]
  * (gate rows first) and dense_down [H, Id], all bf16 and in MOE_LAYOUT_TILED. Uses d->hidden and

@@ -71,7 +71,9 @@ class MoeFfnNorms(ctypes.Structure):
                 ("post", ctypes.c_void_p), ("eps", ctypes.c_float)]
 
 
-EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_block", "dense_mlp",
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_block", "moe_block_noalloc", "dense_mlp",
            "moe_ffn_workspace_bytes", "moe_ffn_layer",
            "moe_prefill_chunk_tokens", "moe_prefill_workspace_bytes", "moe_prefill_chunked",
            "moe_quantize_int8", "moe_quantize_fp8", "moe_tile_weights", "moe_last_error")
@@ -97,6 +99,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.moe_route.restype = ctypes.c_int
     lib.moe_block.argtypes = [P(MoeDims), P(MoeWeights), vp, i32, vp, P(MoeDebug), vp, sz, vp]
     lib.moe_block.restype = ctypes.c_int
+    lib.moe_block_noalloc.argtypes = [P(MoeDims), P(MoeWeights), vp, i32, vp, P(MoeDebug), vp]
+    lib.moe_block_noalloc.restype = ctypes.c_int
     lib.dense_mlp.argtypes = [P(MoeDims), vp, vp, vp, i32, vp, vp, sz, vp]
     lib.dense_mlp.restype = ctypes.c_int
     lib.moe_ffn_workspace_bytes.argtypes = [P(MoeDims), i32]

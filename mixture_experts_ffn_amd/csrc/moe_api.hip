@@ -5,9 +5,17 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "kernels.h"
+
+// The workspace of moe_block_noalloc: a fixed array that the code object
+// brings to every device the library runs on (each device holds its own copy,
+// at its own address, until the process ends). Host code never uses this
+// name as a device address: it reads each device's address once with
+// hipGetSymbolAddress and passes that to the kernels.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -212,6 +220,27 @@ struct Stages {
 
 template <typename T>
 T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current and kept for the later ones.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(void** out) {
+    int dev = -1;
+    HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address on device %d", dev);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
 
 // moe_ffn_layer's workspace: the block's, then the two branches' bf16 inputs
 struct FfnLayout {
@@ -509,6 +538,23 @@ int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
         CHECK_PTR(y, "y", 16);
         if ((rc = check_ws(d, T, ws, ws_bytes))) return rc;
     }
+    return block_impl(d, w, x, x, T, y, nullptr, nullptr, dbg, ws, stream);
+}
+
+int moe_block_noalloc(const moe_dims* d, const moe_weights* w, const void* x, int32_t T, void* y,
+                      moe_debug* dbg, hipStream_t stream) {
+    int rc;
+    if ((rc = check_dims(d)) || (rc = check_T(T)) || (rc = check_weights(w)) || (rc = check_tiled(w))) return rc;
+    if (T == 0) return block_impl(d, w, x, x, T, y, nullptr, nullptr, dbg, nullptr, stream);
+    CHECK_PTR(x, "x", 16);
+    CHECK_PTR(y, "y", 16);
+    const size_t need = make_layout(*d, T).total;
+    if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+        return fail(MOE_ERR_WORKSPACE,
+                    "moe_block_noalloc: T=%d needs %zu bytes of scratch, more than the %zu the library holds "
+                    "(moe_block with a workspace takes any size)", T, need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if ((rc = scratch_of_current_device(&ws))) return rc;
     return block_impl(d, w, x, x, T, y, nullptr, nullptr, dbg, ws, stream);
 }
 

@@ -221,6 +221,21 @@ def moe_block(dims: BlockDims, weights: LayerWeights, x: torch.Tensor, y=None,
     return y
 
 
+def moe_block_noalloc(dims: BlockDims, weights: LayerWeights, x: torch.Tensor, y: torch.Tensor,
+                      debug: Optional[MoeDebug] = None, stream=None) -> torch.Tensor:
+    """moe_block on the library's own scratch array: no workspace, nothing
+    allocated (y must be given). Calls that overlap on one device race."""
+    T = _tokens(x, "x", dims.hidden)
+    weights.check(dims)
+    _want(y, "y", (T, dims.hidden), (torch.bfloat16,))
+    _same_device(("x", x), ("router_w", weights.router_w), ("y", y), *_debug_outputs(debug, dims, T))
+    rc = _lib().moe_block_noalloc(ctypes.byref(dims.c()), ctypes.byref(weights.c()), _dev(x, "x").data_ptr(), T,
+                                  _dev(y, "y").data_ptr(), ctypes.byref(debug) if debug is not None else None,
+                                  _stream(stream))
+    _check(rc, "moe_block_noalloc")
+    return y
+
+
 def dense_mlp(dims: BlockDims, dense_gate_up: torch.Tensor, dense_down: torch.Tensor,
               x: torch.Tensor, y=None, workspace=None, stream=None) -> torch.Tensor:
     """The shared dense MLP alone (bf16 [T, H])."""
