@@ -11,10 +11,12 @@
 // A rows may be gathered (the tokens of an expert, in grouped order), so the
 // routed pairs are computed without copying x. int8 weights (int8 experts card,
 // "How it works") are widened to bf16 exactly in registers and their per-row
-// fp32 scales are applied in the epilogue; E4M3 weights (the vLLM recipe's fp8
-// variant) become half carriers by bit placement and meet A rows quantised per
-// token in f16 MFMAs, the activation scale applied per row in the epilogue.
-// The template parameter WQ names the format: 0 bf16, 1 int8, 2 E4M3. combine_kernel then adds, per token,
+// fp32 scales are applied in the epilogue. E4M3 weights (the vLLM recipe's fp8
+// variant) meet A rows quantised per token to E4M3 bytes in gfx950's fp8 MFMA
+// (16x16x128, twice the bf16 rate: a K-step there is 128 codes, 128 bytes a
+// row, the bytes a bf16 K-step of 64 moves), both scales applied per row and
+// column in the epilogue. The template parameter WQ names the format: 0 bf16,
+// 1 int8, 2 E4M3. combine_kernel then adds, per token,
 // the dense output and its K weighted expert rows (ONNX export card, "Truthful
 // graph contracts", row "MoE topology": dense + moe).
 //
@@ -128,25 +130,38 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 // native 4 x u32 vector (a first-class type that stays in registers)
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kAStageElems = BM * BK;  // bf16 elements per LDS stage of A
 
 // One K-step of the wavefront's B fragments: bf16 q[2 j + s] = column tile j,
-// 8 k of sub-step s; 1-byte (int8, E4M3) q[j] = column tile j, all 16 k.
+// 8 k of sub-step s; int8 q[j] = column tile j, all 16 k; E4M3 q[2 j + s] =
+// column tile j, the 16 codes of 64-wide tile s of the 128-wide K-step.
 template <int WQ>
 struct BStep {
-    v4u q[WQ ? 2 : 4];
+    v4u q[WQ == 1 ? 2 : 4];
 };
 template <int WQ>
-constexpr int kBLoads = WQ ? 2 : 4;
+constexpr int kBLoads = WQ == 1 ? 2 : 4;
+typedef int v8i __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ v8i cat8(const v4u& a, const v4u& b) {
+    return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+}
 
-// bp[j]: this lane's 16-byte piece of K-step 0 of the wavefront's tile j; a
-// K-step is one tile (2 KB bf16: sub-step s at + 1024 s; 1 KB int8 or E4M3), so every
-// load of the wavefront reads one contiguous 1 KB
+// bp[j]: this lane's 16-byte piece of tile 0 of the wavefront's tile row j; a
+// tile is 2 KB bf16 (sub-step s at + 1024 s) or 1 KB int8 or E4M3, so every
+// load of the wavefront reads one contiguous 1 KB. A K-step is one tile (bf16,
+// int8) or two (E4M3: tiles 2 kt and 2 kt + 1; the second repeats the first
+// past the last tile of an odd count, where the A codes are zero).
 template <int WQ>
-__device__ __forceinline__ void b_load(const char* const (&bp)[2], int kt, BStep<WQ>& r) {
-    if (WQ) {
+__device__ __forceinline__ void b_load(const char* const (&bp)[2], int kt, int nkt, BStep<WQ>& r) {
+    if (WQ == 2) {
+        const int64_t o0 = (int64_t)(2 * kt) * 1024, o1 = (int64_t)min(2 * kt + 1, nkt - 1) * 1024;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            r.q[2 * j] = *reinterpret_cast<const v4u*>(bp[j] + o0);
+            r.q[2 * j + 1] = *reinterpret_cast<const v4u*>(bp[j] + o1);
+        }
+    } else if (WQ == 1) {
         const int64_t off = (int64_t)kt * 1024;
 #pragma unroll
         for (int j = 0; j < 2; ++j) r.q[j] = *reinterpret_cast<const v4u*>(bp[j] + off);
@@ -163,18 +178,13 @@ __device__ __forceinline__ void b_load(const char* const (&bp)[2], int kt, BStep
 template <int WQ>
 __device__ __forceinline__ bf16x8_t b_frag(const BStep<WQ>& r, int j, int s) {
     v4u v;
-    if (WQ) {
+    if (WQ == 1) {
         // the piece made opaque here, so that each fragment is widened where it
         // is used rather than all of them ahead (registers the loop lacks)
         v4u w = r.q[j & 1];
         asm volatile("" : "+v"(w));
         const unsigned w0 = s ? w.z : w.x, w1 = s ? w.w : w.y;
-        if (WQ == 2)  // E4M3 codes: half carriers (value * 2^-8), bit placement only
-            v = v4u{fp8pair_to_f16(w0, 0), fp8pair_to_f16(w0, 16), fp8pair_to_f16(w1, 0),
-                    fp8pair_to_f16(w1, 16)};
-        else
-            v = v4u{i8pair_to_bf16(w0, 0), i8pair_to_bf16(w0, 16), i8pair_to_bf16(w1, 0),
-                    i8pair_to_bf16(w1, 16)};
+        v = v4u{i8pair_to_bf16(w0, 0), i8pair_to_bf16(w0, 16), i8pair_to_bf16(w1, 0), i8pair_to_bf16(w1, 16)};
     } else {
         v = r.q[(2 * j + s) & 3];
     }
@@ -204,6 +214,38 @@ __device__ __forceinline__ void a_dma(const char* const (&ap)[kADma], int kt, ui
 template <int WQ, int NSL>
 __device__ __forceinline__ void mma_step(const uint16_t* As, const BStep<WQ>& rb, int lane,
                                          f32x4_t (&acc)[kSlabs][2]) {
+    if (WQ == 2) {
+        // E4M3: one 16x16x128 MFMA per slab and column tile. Lane l gives the
+        // 32 codes at k = 16 (l / 16) .. + 15 of each 64-wide half of the
+        // K-step, for A (chunks l / 16 and 4 + l / 16 of the row) and B (its
+        // piece of tiles 2 kt and 2 kt + 1) alike, so the products pair the same k.
+        const v8i b0 = cat8(rb.q[0], rb.q[1]), b1 = cat8(rb.q[2], rb.q[3]);
+        const int c0 = lane >> 4, c1 = 4 + (lane >> 4);
+        // slabs in pairs: an A fragment is twice a bf16 one, so a pair holds
+        // the registers a group of four does there
+#pragma unroll
+        for (int g = 0; g < NSL; g += 2) {
+            v4u a0[2], a1[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = (g + i) * 16 + (lane & 15);
+                a0[i] = *reinterpret_cast<const v4u*>(As + swz(r, c0));
+                a1[i] = *reinterpret_cast<const v4u*>(As + swz(r, c1));
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const v8i a = cat8(a0[i], a1[i]);
+                // operand formats 0 (E4M3) and unit E8M0 scales (127 = 2^0)
+                acc[g + i][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b0, acc[g + i][0], 0, 0, 0,
+                                                                                 127, 0, 127);
+                acc[g + i][1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b1, acc[g + i][1], 0, 0, 0,
+                                                                                 127, 0, 127);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
+        return;
+    }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
         const bf16x8_t b0 = b_frag<WQ>(rb, 0, s), b1 = b_frag<WQ>(rb, 1, s);
@@ -216,17 +258,8 @@ __device__ __forceinline__ void mma_step(const uint16_t* As, const BStep<WQ>& rb
                 af[i] = *reinterpret_cast<const bf16x8_t*>(As + swz((g + i) * 16 + (lane & 15), c));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                if (WQ == 2) {  // E4M3: half carriers in A and B, f16 MFMAs (exact products)
-                    acc[g + i][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, af[i]),
-                                                                           __builtin_bit_cast(f16x8_t, b0),
-                                                                           acc[g + i][0], 0, 0, 0);
-                    acc[g + i][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, af[i]),
-                                                                           __builtin_bit_cast(f16x8_t, b1),
-                                                                           acc[g + i][1], 0, 0, 0);
-                } else {
-                    acc[g + i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], b0, acc[g + i][0], 0, 0, 0);
-                    acc[g + i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], b1, acc[g + i][1], 0, 0, 0);
-                }
+                acc[g + i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], b0, acc[g + i][0], 0, 0, 0);
+                acc[g + i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], b1, acc[g + i][1], 0, 0, 0);
             }
             // DS reads first, then the MFMAs, in one scheduling group each
             __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -259,7 +292,7 @@ constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 
 // loads against compiler scheduling; loads past the last K-step repeat the
 // last one, so every step issues the same loads.
 template <int WQ, int NSL, bool ADMA>
-__device__ __forceinline__ void k_loop(const char* const (&ap)[kADma], const char* const (&bp)[2], int nk,
+__device__ __forceinline__ void k_loop(const char* const (&ap)[kADma], const char* const (&bp)[2], int nk, int nkt,
                                        const Lds& L, int wave, int lane, f32x4_t (&acc)[kSlabs][2]) {
     constexpr int kA = ADMA ? kADma : 0;
     constexpr int kB = NSL > 0 ? kBLoads<WQ> : 0;
@@ -273,17 +306,17 @@ __device__ __forceinline__ void k_loop(const char* const (&ap)[kADma], const cha
     uint16_t* const S2 = L.a[2];
     uint16_t* const S3 = L.a[3];
     if (ADMA) a_dma(ap, 0, S0, wave);
-    if (NSL > 0) b_load<WQ>(bp, 0, rb0);
+    if (NSL > 0) b_load<WQ>(bp, 0, nkt, rb0);
     if (ADMA) a_dma(ap, min(1, last), S1, wave);
-    if (NSL > 0) b_load<WQ>(bp, min(1, last), rb1);
+    if (NSL > 0) b_load<WQ>(bp, min(1, last), nkt, rb1);
     if (ADMA) a_dma(ap, min(2, last), S2, wave);
-    if (NSL > 0) b_load<WQ>(bp, min(2, last), rb2);
+    if (NSL > 0) b_load<WQ>(bp, min(2, last), nkt, rb2);
 #define MOE_GEMM_STEP(U, SA, RB, SN, RN)                                    \
     __builtin_amdgcn_s_waitcnt(kWait);                                      \
     raw_barrier();                                                          \
     if (ADMA) a_dma(ap, min(kt + (U) + kDepth - 1, last), SN, wave);        \
     if (NSL > 0) {                                                          \
-        b_load<WQ>(bp, min(kt + (U) + kDepth - 1, last), RN);             \
+        b_load<WQ>(bp, min(kt + (U) + kDepth - 1, last), nkt, RN);        \
         if (kt + (U) < nk) mma_step<WQ, NSL>(SA, RB, lane, acc);          \
     }
     for (int kt = 0; kt < nk; kt += kDepth) {
@@ -338,7 +371,9 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
     const int n_slabs = min(kSlabs, (rows_valid + 15) / 16);
     int nsl = (n_slabs + 3) / 4 * 4;
     if (MODE == MODE_GATEUP && nt * kHalfN + wn * 16 >= p.n_out) nsl = 0;
-    const int nk = p.K / BK;
+    // K-steps: 64 values (bf16, int8), or 128 E4M3 codes; B tiles are 64 wide
+    const int nkt = p.K / BK;
+    const int nk = WQ == 2 ? (nkt + 1) / 2 : nkt;
 
     // sources: B fragments of this lane (column l % 16 of tiles 0 and 1, k from
     // 16 (l / 16)) in the tiled layout; A rows of this wavefront's DMA share
@@ -348,7 +383,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
         const char* B = (const char*)p.B + (int64_t)group * p.b_group_stride * esz;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
-            bp[jj] = B + (int64_t)b_tile<MODE>(p, nt, wn, jj) * nk * (esz * 1024) + lane * 16;
+            bp[jj] = B + (int64_t)b_tile<MODE>(p, nt, wn, jj) * nkt * (esz * 1024) + lane * 16;
     }
     const char* ap[kADma];
 #pragma unroll
@@ -357,7 +392,8 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
         const int c = (lane & 7) ^ a_swz(r);
         const int rr = min(r, rows_valid - 1);  // rows past the tile end repeat a valid row
         const int64_t arow = p.a_rows ? p.a_rows[row0 + rr] : (int64_t)(row0 + rr);
-        ap[q] = reinterpret_cast<const char*>(p.A + arow * p.lda + c * 8);
+        // a row: lda bf16 values, or lda bytes of E4M3 codes; its 16-byte chunk c of a K-step
+        ap[q] = reinterpret_cast<const char*>(p.A) + arow * p.lda * (WQ == 2 ? 1 : 2) + c * 16;
     }
     // epilogue operands, loaded now so that their latency hides behind the K
     // loop: 1-byte formats' column scales of this lane's columns, router weight of row tid
@@ -376,12 +412,11 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
     }
     if (MODE == MODE_DOWN && !p.Cf && tid < BM)
         row_wt = tid >= rows_valid ? 0.f : p.row_w ? p.row_w[row0 + tid] : 1.f;
-    // fp8 gate/up: the per-token scale of each A row, times 2^16 (the 2^-8 of
-    // each operand's half carrier)
+    // E4M3 gate/up: the per-token scale of each A row
     if (MODE == MODE_GATEUP && WQ == 2 && tid < BM) {
         const int rr = min(tid, rows_valid - 1);
         const int64_t arow = p.a_rows ? p.a_rows[row0 + rr] : (int64_t)(row0 + rr);
-        row_wt = p.a_scale[arow] * 65536.f;
+        row_wt = p.a_scale[arow];
     }
     // A rows the MFMAs read: the valid slabs rounded up to groups of four (the
     // same for every wavefront); a wavefront whose 32 DMA rows all lie past them
@@ -390,8 +425,8 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, const Lds& 
     const bool adma = wave * kADma * 8 < rows_read;
 #define MOE_K_LOOP(N)                                                      \
     do {                                                                   \
-        if (adma) k_loop<WQ, N, true>(ap, bp, nk, L, wave, lane, acc);     \
-        else k_loop<WQ, N, false>(ap, bp, nk, L, wave, lane, acc);         \
+        if (adma) k_loop<WQ, N, true>(ap, bp, nk, nkt, L, wave, lane, acc); \
+        else k_loop<WQ, N, false>(ap, bp, nk, nkt, L, wave, lane, acc);     \
     } while (0)
     switch (nsl) {  // uniform per wavefront
         case 0: MOE_K_LOOP(0); break;

@@ -161,12 +161,15 @@ hipError_t launch_tile_weights(const void* src, int64_t rows, int cols, bool int
                                hipStream_t stream);
 hipError_t launch_quantize_int8(const uint16_t* w, int64_t rows, int cols, int8_t* q, float* scale,
                                 hipStream_t stream);
-// E4M3 per row: weights -> codes + scales; activations -> half carriers of
-// value * 2^-8 + scales (+ mul_out = mul_in * scale * 2^16 when mul_out is set)
+// E4M3 per row: weights -> codes + scales
 hipError_t launch_quantize_fp8(const uint16_t* w, int64_t rows, int cols, uint8_t* q, float* scale,
                                hipStream_t stream);
-hipError_t launch_act_quant_fp8(const uint16_t* x, int64_t rows, int cols, uint16_t* xq, float* scale,
-                                const float* mul_in, float* mul_out, hipStream_t stream);
+// activations -> per-row E4M3 code bytes for the E4M3 MFMAs: rows of ldq bytes
+// (ldq a multiple of 128, >= cols, the tail zero), + scale, + mul_out = mul_in * scale
+hipError_t launch_act_quant_fp8_bytes(const uint16_t* x, int64_t rows, int cols, uint8_t* q, int ldq, float* scale,
+                                      const float* mul_in, float* mul_out, hipStream_t stream);
+// row length in bytes of E4M3 activation codes of `cols` values (a whole number of 128-code K-steps)
+inline int fp8_row_bytes(int cols) { return (cols + 127) / 128 * 128; }
 
 // ---- the layer's feed-forward norms around the block (ffn.hip) ----------------
 // x_d = bf16(N_gd(h)), x_m = bf16(N_gm(h)) per token (only those whose gain is given)

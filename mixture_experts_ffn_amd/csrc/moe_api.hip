@@ -56,7 +56,7 @@ constexpr int32_t kSlidingWindow = 1024;
 struct Layout {
     size_t logits, partial, topk_idx, topk_w, pair_rank, tile_counts, counts, offsets, active, n_active;
     size_t perm_token, perm_w, inv_row, mtile_group, mtile_row0, n_mtiles, gemm_tiles[2], h, hd, rows;
-    size_t dout, part, dpart, dgu_part, lpart, ss_part, hpart, xq, xscale, hscale, wrow, total;
+    size_t dout, part, dpart, dgu_part, lpart, ss_part, hpart, xq, xscale, hq, hscale, wrow, total;
     int max_mtiles;
 };
 
@@ -104,10 +104,13 @@ Layout make_layout(const moe_dims& d, int64_t T) {
     L.lpart = take(Ts * moe::kFrontSplit * E * 4);
     L.ss_part = take(Ts * moe::kFrontSplit * 4);
     L.hpart = take(2 * Ts * K * 2 * d.expert_inter * 4);
-    // E4M3 experts: x quantised per token and its scales; h's per-row scales and
-    // the down projection's row factors (router weight x scale x 2^16)
+    // E4M3 experts: x quantised per token (half carriers on the streaming path,
+    // code bytes on the grouped one) and its scales; h's codes (grouped path,
+    // rows padded to whole 128-code K-steps), per-row scales and the down
+    // projection's row factors (router weight x scale, x 2^16 for carriers)
     L.xq = take(T * d.hidden * 2);
     L.xscale = take(T * 4);
+    L.hq = take(TK * moe::fp8_row_bytes(d.expert_inter));
     L.hscale = take(TK * 4);
     L.wrow = take(TK * 4);
     L.total = off;
@@ -414,12 +417,13 @@ int block_impl(const moe_dims* d, const moe_weights* w, const void* x, const voi
         // experts gate/up + GELU: gathered rows of x (E4M3 experts: of x
         // quantised per token, with the token scales applied before the GELU)
         g.A = xb; g.lda = H; g.a_rows = po.perm_token;
-        if (wq == 2) {
+        if (wq == 2) {  // E4M3 code bytes for the fp8 MFMAs (H is a multiple of 256)
             HIP_TRY(st.begin("act_quant"), "event record");
-            HIP_TRY(moe::launch_act_quant_fp8(xb, T, H, at<uint16_t>(ws, L.xq), at<float>(ws, L.xscale), nullptr,
-                                              nullptr, stream),
+            HIP_TRY(moe::launch_act_quant_fp8_bytes(xb, T, H, at<uint8_t>(ws, L.xq), H, at<float>(ws, L.xscale),
+                                                    nullptr, nullptr, stream),
                     "act_quant launch");
             g.A = at<uint16_t>(ws, L.xq);
+            g.lda = H;
             g.a_scale = at<float>(ws, L.xscale);
         }
         g.B = w->expert_gate_up; g.b_group_stride = (int64_t)2 * I * H; g.ldb = H;
@@ -443,12 +447,16 @@ int block_impl(const moe_dims* d, const moe_weights* w, const void* x, const voi
         gw.group_end = po.offsets; gw.max_mtiles = L.max_mtiles; gw.tiles = po.tiles[1];
         gw.C = rows; gw.ldc = H; gw.row_w = po.perm_w;
         if (wq == 2) {
-            // h quantised per row in place; each row's factor becomes router
-            // weight x scale x 2^16
+            // h quantised per row to code bytes (rows padded with zero codes to
+            // whole K-steps); each row's factor becomes router weight x scale
+            const int ldh = moe::fp8_row_bytes(I);
             HIP_TRY(st.begin("h_quant"), "event record");
-            HIP_TRY(moe::launch_act_quant_fp8(h, (int64_t)T * K, I, h, at<float>(ws, L.hscale), po.perm_w,
-                                              at<float>(ws, L.wrow), stream),
+            HIP_TRY(moe::launch_act_quant_fp8_bytes(h, (int64_t)T * K, I, at<uint8_t>(ws, L.hq), ldh,
+                                                    at<float>(ws, L.hscale), po.perm_w, at<float>(ws, L.wrow),
+                                                    stream),
                     "h_quant launch");
+            gw.A = at<uint16_t>(ws, L.hq);
+            gw.lda = ldh;
             gw.row_w = at<float>(ws, L.wrow);
         }
         // dense down (fp32), in the same launch
