@@ -181,7 +181,7 @@ int moe_block(const moe_dims* d, const moe_weights* w, const void* x, int32_t T,
  * bit. A batch whose workspace (moe_workspace_bytes) exceeds the array is
  * refused with MOE_ERR_WORKSPACE before anything is launched: at the real
  * shape that admits every decode-sized batch (T <= 64) and grouped batches of
- * about 400 tokens. Every call on one device shares its array and leaves its
+ * up to 374 tokens. Every call on one device shares its array and leaves its
  * intermediates there (no kernel relies on what an earlier call left): calls
  * that overlap on one device, from several streams or threads, race and must
  * be serialised by the caller. */

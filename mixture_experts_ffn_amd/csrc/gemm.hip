@@ -580,21 +580,16 @@ hipError_t launch_gemm_gateup(const GemmArgs& experts, const GemmArgs* dense, in
 }
 hipError_t launch_gemm_down(const GemmArgs& experts, const GemmArgs* dense, int wq,
                             hipStream_t stream) {
-    // the dense problem first: its blocks run a longer reduction. With 1-byte
-    // expert weights the two run as two launches (one kernel holding both loops
-    // would need more registers than a wavefront has).
+    // the dense problem first: its blocks run a longer reduction (alone, its
+    // few 256-row tiles would leave most of the chip idle)
     if (!dense) {
         if (wq == 2) return launch<MODE_DOWN, 2, 2>(experts, nullptr, stream);
         return wq ? launch<MODE_DOWN, 1, 1>(experts, nullptr, stream)
                   : launch<MODE_DOWN, 0, 0>(experts, nullptr, stream);
     }
-    if (wq) {
-        const hipError_t e = launch<MODE_DOWN, 0, 0>(*dense, nullptr, stream);
-        if (e != hipSuccess) return e;
-        return wq == 2 ? launch<MODE_DOWN, 2, 2>(experts, nullptr, stream)
-                       : launch<MODE_DOWN, 1, 1>(experts, nullptr, stream);
-    }
-    return launch<MODE_DOWN, 0, 0>(*dense, &experts, stream);
+    if (wq == 2) return launch<MODE_DOWN, 0, 2>(*dense, &experts, stream);
+    return wq ? launch<MODE_DOWN, 0, 1>(*dense, &experts, stream)
+              : launch<MODE_DOWN, 0, 0>(*dense, &experts, stream);
 }
 hipError_t launch_combine(const float* dense_out, const uint16_t* rows, const int32_t* inv_row,
                           int T, int H, int K, uint16_t* y, hipStream_t stream) {
