@@ -97,26 +97,28 @@ __device__ __forceinline__ void lds_barrier() {
 // finite value is 448. The kernels carry E4M3 values as bf16 holding value *
 // 2^-8 (half carriers) and fold 2^8 per operand into the scales.
 
-// nearest E4M3 code of an fp32 value, ties to the even code, saturating at 448
+// nearest E4M3 code of an fp32 value, ties to the even code, saturating at 448.
+// Without branches: at or above 2^-6 the code is the float's exponent and top 3
+// mantissa bits after a round-half-even add at bit 20 (a mantissa carry moves
+// into the exponent field by itself), rebased from bias 127 to 7 and capped at
+// code 0x7E (448); below 2^-6 it is the nearest multiple of 2^-9 (rint rounds
+// half to even), code 8 being 2^-6 itself.
 __device__ __forceinline__ uint32_t fp8_e4m3_code(float v) {
     const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
     const float a = fabsf(v);
-    uint32_t c;
-    if (a < 0.015625f) {  // below 2^-6: multiples of 2^-9 (code 8 is 2^-6 itself)
-        c = (uint32_t)rintf(a * 512.f);
-    } else {
-        const uint32_t au = __float_as_uint(a);
-        int e = (int)(au >> 23) - 127;
-        uint32_t m = (au >> 20) & 7u;
-        const uint32_t rest = au & 0xFFFFFu;  // the 20 bits below the kept mantissa
-        if (rest > 0x80000u || (rest == 0x80000u && (m & 1u))) ++m;
-        if (m == 8u) {
-            m = 0u;
-            ++e;
-        }
-        c = min(((uint32_t)(e + 7) << 3) | m, 0x7Eu);
-    }
-    return c | sign;
+    const uint32_t au = __float_as_uint(a);
+    const uint32_t t = au + 0x7FFFFu + ((au >> 20) & 1u);
+    const uint32_t cn = min((t >> 20) - (120u << 3), 0x7Eu);
+    const uint32_t cs = (uint32_t)rintf(a * 512.f);
+    return (a < 0.015625f ? cs : cn) | sign;
+}
+
+// the code of v / s (the division in fp32, as the quantisers define it), or 0
+// when the row scale s is 0 (an all-zero row); without branches
+__device__ __forceinline__ uint32_t fp8_e4m3_code_div(float v, float s) {
+    const bool pos = s > 0.f;
+    const uint32_t c = fp8_e4m3_code(v / (pos ? s : 1.f));
+    return pos ? c : 0u;
 }
 
 // an E4M3 code's bits placed at the top of a half (sign to bit 15, exponent
@@ -161,8 +163,8 @@ __device__ __forceinline__ float fp8_quantize_row(const uint16_t* x, uint16_t* x
             uint32_t o[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint32_t c0 = s > 0.f ? fp8_e4m3_code(f[2 * i] / s) : 0u;
-                const uint32_t c1 = s > 0.f ? fp8_e4m3_code(f[2 * i + 1] / s) : 0u;
+                const uint32_t c0 = fp8_e4m3_code_div(f[2 * i], s);
+                const uint32_t c1 = fp8_e4m3_code_div(f[2 * i + 1], s);
                 o[i] = fp8_as_f16_bits(c0) | (fp8_as_f16_bits(c1) << 16);
             }
             dst[c] = make_uint4(o[0], o[1], o[2], o[3]);

@@ -464,8 +464,8 @@ __device__ __forceinline__ void quantize_token_fp8(const StreamArgs& a, int t, f
             uint32_t o[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint32_t c0 = s > 0.f ? fp8_e4m3_code(f[2 * i] / s) : 0u;
-                const uint32_t c1 = s > 0.f ? fp8_e4m3_code(f[2 * i + 1] / s) : 0u;
+                const uint32_t c0 = fp8_e4m3_code_div(f[2 * i], s);
+                const uint32_t c1 = fp8_e4m3_code_div(f[2 * i + 1], s);
                 o[i] = fp8_as_f16_bits(c0) | (fp8_as_f16_bits(c1) << 16);
             }
             dst[c] = make_uint4(o[0], o[1], o[2], o[3]);
@@ -777,8 +777,8 @@ __global__ __launch_bounds__(kThreads) void decode_hquant_kernel(StreamArgs a) {
                 uint32_t o[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const uint32_t c0 = s > 0.f ? fp8_e4m3_code(hv[j][2 * i] / s) : 0u;
-                    const uint32_t c1 = s > 0.f ? fp8_e4m3_code(hv[j][2 * i + 1] / s) : 0u;
+                    const uint32_t c0 = fp8_e4m3_code_div(hv[j][2 * i], s);
+                    const uint32_t c1 = fp8_e4m3_code_div(hv[j][2 * i + 1], s);
                     o[i] = fp8_as_f16_bits(c0) | (fp8_as_f16_bits(c1) << 16);
                 }
                 reinterpret_cast<uint4*>(a.h + (int64_t)p * I)[cc] = make_uint4(o[0], o[1], o[2], o[3]);

@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t* __res
         unpack8(src[c], f);
         uint32_t b[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) b[i] = s > 0.f ? fp8_e4m3_code(f[i] / s) : 0u;
+        for (int i = 0; i < 8; ++i) b[i] = fp8_e4m3_code_div(f[i], s);
         dst[c] = make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
                             b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
     }
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256) void act_quant_fp8_bytes_kernel(const uint16_t
                 unpack8(v[j], f);
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
-                    o[i >> 2] |= (s > 0.f ? fp8_e4m3_code(f[i] / s) : 0u) << (8 * (i & 3));
+                    o[i >> 2] |= fp8_e4m3_code_div(f[i], s) << (8 * (i & 3));
             }
             dst[c] = make_uint2(o[0], o[1]);
         }
