@@ -17,8 +17,8 @@ namespace moe {
 
 namespace {
 
-// A workgroup of NT threads per token row holds the row in registers, kFR
-// four-value pieces a thread: hidden sizes up to 4 kFR NT. Small batches take
+// A workgroup of NT threads per token row holds the row in registers, up to
+// kFR four-value pieces a thread: hidden sizes up to 4 kFR NT. Small batches take
 // 1024 threads a row (more loads in flight for few rows), larger ones 256 (more
 // rows resident per CU).
 constexpr int kFR = 4;
@@ -58,12 +58,24 @@ __global__ __launch_bounds__(NT) void ffn_prenorm_kernel(const uint16_t* __restr
     const int64_t base = (int64_t)blockIdx.x * H;
     const uint2* row = reinterpret_cast<const uint2*>(h + base);
     const int n4 = H >> 2;
-    uint2 v[kFR];
+    // the row's pieces, and both gains' (with few rows, 1024 threads a row,
+    // loaded before the reduction; with many where they are used)
+    constexpr bool kEarly = NT >= 1024;
+    uint2 v[kFR], gv[kFR][2];
+    auto load_gains = [&](int q) {
+        const int c = threadIdx.x + q * NT;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const uint16_t* g = b ? gm : gd;
+            gv[q][b] = (g && c < n4) ? reinterpret_cast<const uint2*>(g)[c] : make_uint2(0u, 0u);
+        }
+    };
     float ss = 0.f;
 #pragma unroll
     for (int q = 0; q < kFR; ++q) {
         const int c = threadIdx.x + q * NT;
         v[q] = c < n4 ? row[c] : make_uint2(0u, 0u);
+        if (kEarly) load_gains(q);
         const float f0 = bf16_lo(v[q].x), f1 = bf16_hi(v[q].x), f2 = bf16_lo(v[q].y), f3 = bf16_hi(v[q].y);
         ss += f0 * f0 + f1 * f1 + f2 * f2 + f3 * f3;
     }
@@ -72,16 +84,17 @@ __global__ __launch_bounds__(NT) void ffn_prenorm_kernel(const uint16_t* __restr
     for (int q = 0; q < kFR; ++q) {
         const int c = threadIdx.x + q * NT;
         if (c >= n4) continue;
+        if (!kEarly) load_gains(q);
         const float f0 = bf16_lo(v[q].x), f1 = bf16_hi(v[q].x), f2 = bf16_lo(v[q].y), f3 = bf16_hi(v[q].y);
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const uint16_t* g = b ? gm : gd;
             uint16_t* dst = b ? xm : xd;
             if (!g) continue;  // uniform
-            const uint2 gv = reinterpret_cast<const uint2*>(g)[c];
+            const uint2 gq = gv[q][b];
             reinterpret_cast<uint2*>(dst + base)[c] =
-                make_uint2(pack_bf16x2(f0 * rn * bf16_lo(gv.x), f1 * rn * bf16_hi(gv.x)),
-                           pack_bf16x2(f2 * rn * bf16_lo(gv.y), f3 * rn * bf16_hi(gv.y)));
+                make_uint2(pack_bf16x2(f0 * rn * bf16_lo(gq.x), f1 * rn * bf16_hi(gq.x)),
+                           pack_bf16x2(f2 * rn * bf16_lo(gq.y), f3 * rn * bf16_hi(gq.y)));
         }
     }
 }
@@ -89,9 +102,9 @@ __global__ __launch_bounds__(NT) void ffn_prenorm_kernel(const uint16_t* __restr
 // out for token t = blockIdx.x. The MoE branch of the token is the sum over
 // k (in k order) of its rows rows[inv_row[t K + k]]: fp32 rows times topk_w
 // (F32ROWS) or bf16 rows already weighted. Each thread keeps its (at most
-// kFR) four-value pieces of the dense and MoE rows in registers; the two
+// FR) four-value pieces of the dense and MoE rows in registers; the two
 // branches' sums of squares are one reduction, their normed sum's another.
-template <int NT, bool F32ROWS>
+template <int NT, int FR, bool F32ROWS>
 __global__ __launch_bounds__(NT) void ffn_post_kernel(const uint16_t* __restrict__ h,
                                                        const float* __restrict__ dense,
                                                        const void* __restrict__ rows,
@@ -112,10 +125,34 @@ __global__ __launch_bounds__(NT) void ffn_post_kernel(const uint16_t* __restrict
         p[k] = inv_row[(int64_t)t * K + min(k, K - 1)];
         wk[k] = F32ROWS ? topk_w[(int64_t)t * K + min(k, K - 1)] : 1.f;
     }
-    float d[kFR][4], m[kFR][4];
+    // the gains and the residual row: with few rows (1024 threads a row) loaded
+    // here, beside the branch rows, so that nothing after the reductions waits
+    // on memory; with many rows where they are used (fewer registers, more
+    // rows resident)
+    constexpr bool kEarly = NT >= 1024;
+    constexpr uint32_t kOne = 0x3F803F80u;  // two bf16 ones
+    uint2 gdv[FR], gmv[FR], gv[FR], hv[FR];
+    auto load_norm_gains = [&](int q) {
+        const int c = min((int)threadIdx.x + q * NT, n4 - 1) * 4;
+        gdv[q] = gpd ? *reinterpret_cast<const uint2*>(gpd + c) : make_uint2(kOne, kOne);
+        gmv[q] = gpm ? *reinterpret_cast<const uint2*>(gpm + c) : make_uint2(kOne, kOne);
+    };
+    auto load_out_operands = [&](int q) {
+        const int c = min((int)threadIdx.x + q * NT, n4 - 1) * 4;
+        gv[q] = gp ? *reinterpret_cast<const uint2*>(gp + c) : make_uint2(kOne, kOne);
+        hv[q] = *reinterpret_cast<const uint2*>(h + base + c);
+    };
+    if (kEarly) {
+#pragma unroll
+        for (int q = 0; q < FR; ++q) {
+            load_norm_gains(q);
+            load_out_operands(q);
+        }
+    }
+    float d[FR][4], m[FR][4];
     float ssd = 0.f, ssm = 0.f;
 #pragma unroll
-    for (int q = 0; q < kFR; ++q) {
+    for (int q = 0; q < FR; ++q) {
         const int c4 = threadIdx.x + q * NT;
         const int c = min(c4, n4 - 1) * 4;  // past the row: a repeat of its last piece, never stored
         const float4 dv = *reinterpret_cast<const float4*>(dense + base + c);
@@ -156,13 +193,11 @@ __global__ __launch_bounds__(NT) void ffn_post_kernel(const uint16_t* __restrict
     }
     float sss = 0.f;
 #pragma unroll
-    for (int q = 0; q < kFR; ++q) {
+    for (int q = 0; q < FR; ++q) {
         const int c4 = threadIdx.x + q * NT;
-        const int c = min(c4, n4 - 1) * 4;
-        const uint2 gdv = gpd ? *reinterpret_cast<const uint2*>(gpd + c) : make_uint2(0x3F803F80u, 0x3F803F80u);
-        const uint2 gmv = gpm ? *reinterpret_cast<const uint2*>(gpm + c) : make_uint2(0x3F803F80u, 0x3F803F80u);
-        const float gdf[4] = {bf16_lo(gdv.x), bf16_hi(gdv.x), bf16_lo(gdv.y), bf16_hi(gdv.y)};
-        const float gmf[4] = {bf16_lo(gmv.x), bf16_hi(gmv.x), bf16_lo(gmv.y), bf16_hi(gmv.y)};
+        if (!kEarly) load_norm_gains(q);
+        const float gdf[4] = {bf16_lo(gdv[q].x), bf16_hi(gdv[q].x), bf16_lo(gdv[q].y), bf16_hi(gdv[q].y)};
+        const float gmf[4] = {bf16_lo(gmv[q].x), bf16_hi(gmv[q].x), bf16_lo(gmv[q].y), bf16_hi(gmv[q].y)};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             d[q][i] = d[q][i] * rnd * gdf[i] + m[q][i] * rnm * gmf[i];  // the branches' sum
@@ -171,14 +206,13 @@ __global__ __launch_bounds__(NT) void ffn_post_kernel(const uint16_t* __restrict
     }
     const float rns = gp ? inv_rms(row_sum2<NT>(sss, 0.f, red).x, H, eps) : 1.f;
 #pragma unroll
-    for (int q = 0; q < kFR; ++q) {
+    for (int q = 0; q < FR; ++q) {
         const int c4 = threadIdx.x + q * NT;
         if (c4 >= n4) continue;
         const int c = c4 * 4;
-        const uint2 gv = gp ? *reinterpret_cast<const uint2*>(gp + c) : make_uint2(0x3F803F80u, 0x3F803F80u);
-        const uint2 hv = *reinterpret_cast<const uint2*>(h + base + c);
-        const float g[4] = {bf16_lo(gv.x), bf16_hi(gv.x), bf16_lo(gv.y), bf16_hi(gv.y)};
-        const float hf[4] = {bf16_lo(hv.x), bf16_hi(hv.x), bf16_lo(hv.y), bf16_hi(hv.y)};
+        if (!kEarly) load_out_operands(q);
+        const float g[4] = {bf16_lo(gv[q].x), bf16_hi(gv[q].x), bf16_lo(gv[q].y), bf16_hi(gv[q].y)};
+        const float hf[4] = {bf16_lo(hv[q].x), bf16_hi(hv[q].x), bf16_lo(hv[q].y), bf16_hi(hv[q].y)};
         *reinterpret_cast<uint2*>(out + base + c) =
             make_uint2(pack_bf16x2(hf[0] + d[q][0] * rns * g[0], hf[1] + d[q][1] * rns * g[1]),
                        pack_bf16x2(hf[2] + d[q][2] * rns * g[2], hf[3] + d[q][3] * rns * g[3]));
@@ -209,17 +243,27 @@ hipError_t launch_ffn_post(const uint16_t* h, const float* dense, const void* ro
                            hipStream_t stream) {
     if (T <= 0) return hipSuccess;
     if (H > kFMaxH) return hipErrorInvalidValue;
-#define MOE_FFN_POST(NT, F32)                                                                              \
-    hipLaunchKernelGGL((ffn_post_kernel<NT, F32>), dim3(T), dim3(NT), 0, stream, h, dense, rows, inv_row, \
+    // pieces a thread: the fewest that cover the row
+#define MOE_FFN_POST(NT, FR, F32)                                                                              \
+    hipLaunchKernelGGL((ffn_post_kernel<NT, FR, F32>), dim3(T), dim3(NT), 0, stream, h, dense, rows, inv_row, \
                        topk_w, H, K, gpd, gpm, gp, eps, out)
+#define MOE_FFN_POST_FR(NT, F32)                            \
+    do {                                                    \
+        const int fr = (H + 4 * NT - 1) / (4 * NT);         \
+        if (fr <= 1) MOE_FFN_POST(NT, 1, F32);              \
+        else if (fr <= 2) MOE_FFN_POST(NT, 2, F32);         \
+        else if (fr <= 3) MOE_FFN_POST(NT, 3, F32);         \
+        else MOE_FFN_POST(NT, 4, F32);                      \
+    } while (0)
     const bool small = ffn_threads(T, H) == 256;
     if (f32_rows) {
-        if (small) MOE_FFN_POST(256, true);
-        else MOE_FFN_POST(1024, true);
+        if (small) MOE_FFN_POST_FR(256, true);
+        else MOE_FFN_POST_FR(1024, true);
     } else {
-        if (small) MOE_FFN_POST(256, false);
-        else MOE_FFN_POST(1024, false);
+        if (small) MOE_FFN_POST_FR(256, false);
+        else MOE_FFN_POST_FR(1024, false);
     }
+#undef MOE_FFN_POST_FR
 #undef MOE_FFN_POST
     return hipGetLastError();
 }
