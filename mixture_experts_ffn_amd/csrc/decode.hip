@@ -428,47 +428,103 @@ __device__ __forceinline__ void router_part(const uint16_t* __restrict__ x, int 
 // Router items first (ceil(E / 16) x kFrontSplit), then the dense gate/up
 // items (Id / 16 x kFrontSplit) if with_dense and front_dense (else the
 // routing launch runs them).
-// E4M3 experts: token t's row of x quantised per row (max |x| / 448, codes
-// round half to even) into a.xq as half carriers, its scale into a.x_scale[t].
-// The whole workgroup takes the row: lane l of wavefront w holds 8-value
-// chunks l + 64 (w + 4 j) (hidden <= 3072: two a lane), the maximum goes
-// through DPP and then LDS.
-__device__ __forceinline__ void quantize_token_fp8(const StreamArgs& a, int t, float* red) {
+// Token items (one workgroup per token, first in the grid: the longest of the
+// launch, so they start first) do what the token's row needs before the
+// experts read it. The whole workgroup takes the row: lane l of wavefront w
+// holds 8-value chunks l + 64 (w + 4 j) (hidden <= 4096), and its reductions
+// go through DPP and then LDS in wavefront order.
+//  - The layer's pre-norms (INF2 card, "The architecture (a dual-path FFN)"):
+//    x_d = bf16(N_gd(h)) and x_m = bf16(N_gm(h)), N_g(v) = v / sqrt(mean(v^2)
+//    + eps) * g, each where its gain is given. The router reads h itself, so
+//    its items in this launch do not wait for them.
+//  - E4M3 experts: the experts' input row (x_m, or x) quantised per row (max
+//    |x| / 448, codes round half to even) into a.xq as half carriers, its
+//    scale into a.x_scale[t].
+__device__ __forceinline__ void front_token(const StreamArgs& a, int t, float* red) {
     constexpr int NC = 2;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nc = a.H >> 3;
-    const uint4* src = reinterpret_cast<const uint4*>(a.x + (int64_t)t * a.H);
-    uint4* dst = reinterpret_cast<uint4*>(a.xq + (int64_t)t * a.H);
+    const uint16_t* row = a.pre_src ? a.pre_src : a.x;
+    const uint4* src = reinterpret_cast<const uint4*>(row + (int64_t)t * a.H);
     uint4 v[NC];
-#pragma unroll
-    for (int j = 0; j < NC; ++j) v[j] = src[min(lane + kWave * (wave + kWaves * j), nc - 1)];  // clamped: same max
-    float amax = 0.f;
+    int cj[NC];
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
-        float f[8];
-        unpack8(v[j], f);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+        cj[j] = lane + kWave * (wave + kWaves * j);
+        v[j] = src[min(cj[j], nc - 1)];  // clamped: a repeat of the last chunk
     }
+    float f[NC][8];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) unpack8(v[j], f[j]);
+    if (a.pre_src) {
+        uint4 gd[NC], gm[NC];
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+            const int c = min(cj[j], nc - 1);
+            gd[j] = a.pre_gd ? reinterpret_cast<const uint4*>(a.pre_gd)[c] : make_uint4(0u, 0u, 0u, 0u);
+            gm[j] = a.pre_gm ? reinterpret_cast<const uint4*>(a.pre_gm)[c] : make_uint4(0u, 0u, 0u, 0u);
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < NC; ++j)
+            if (cj[j] < nc) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ss += f[j][i] * f[j][i];
+            }
+        ss = wave_sum<kWave>(ss);
+        if (lane == 0) red[wave] = ss;
+        __syncthreads();
+        float tot = red[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) tot += red[w];
+        const float rn = 1.0f / sqrtf(tot / (float)a.H + a.pre_eps);
+        __syncthreads();  // red is reused below
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+            float g[8], o[8];
+            if (a.pre_gd) {
+                unpack8(gd[j], g);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) o[i] = f[j][i] * rn * g[i];
+                if (cj[j] < nc)
+                    reinterpret_cast<uint4*>(a.pre_xd + (int64_t)t * a.H)[cj[j]] =
+                        make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                                   pack_bf16x2(o[6], o[7]));
+            }
+            if (a.pre_gm) {
+                unpack8(gm[j], g);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) o[i] = f[j][i] * rn * g[i];
+                const uint4 xm = make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                                            pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
+                if (cj[j] < nc) reinterpret_cast<uint4*>(a.pre_xm + (int64_t)t * a.H)[cj[j]] = xm;
+                unpack8(xm, f[j]);  // the experts' input: x_m as rounded to bf16
+            }
+        }
+    }
+    if (!a.xq) return;
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < NC; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[j][i]));  // repeats: the same maximum
     amax = wave_max<kWave>(amax);
     if (lane == 0) red[wave] = amax;
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) amax = fmaxf(amax, red[w]);
     const float s = amax / 448.0f;
+    uint4* dst = reinterpret_cast<uint4*>(a.xq + (int64_t)t * a.H);
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
-        const int c = lane + kWave * (wave + kWaves * j);
-        if (c < nc) {
-            float f[8];
-            unpack8(v[j], f);
+        if (cj[j] < nc) {
             uint32_t o[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint32_t c0 = fp8_e4m3_code_div(f[2 * i], s);
-                const uint32_t c1 = fp8_e4m3_code_div(f[2 * i + 1], s);
+                const uint32_t c0 = fp8_e4m3_code_div(f[j][2 * i], s);
+                const uint32_t c1 = fp8_e4m3_code_div(f[j][2 * i + 1], s);
                 o[i] = fp8_as_f16_bits(c0) | (fp8_as_f16_bits(c1) << 16);
             }
-            dst[c] = make_uint4(o[0], o[1], o[2], o[3]);
+            dst[cj[j]] = make_uint4(o[0], o[1], o[2], o[3]);
         }
     }
     if (threadIdx.x == 0) a.x_scale[t] = s;
@@ -481,12 +537,10 @@ __global__ __launch_bounds__(kThreads) void decode_front_kernel(StreamArgs a, co
     __shared__ float red[kWaves * 512 + kWaves * 16];
     const int n_router = wr ? ((a.E + 15) / 16) * kFrontSplit : 0;
     const int n_dense = a.with_dense && a.front_dense ? (a.Id / 16) * kFrontSplit : 0;
-    // E4M3 experts: the workgroups that quantise x per token come first (the
-    // longest of the launch, so they start first), one a token
-    const int n_quant = a.xq ? a.T : 0;
-    const int b = (int)blockIdx.x - n_quant;
+    const int n_tok = (a.xq || a.pre_src) ? a.T : 0;  // token items first
+    const int b = (int)blockIdx.x - n_tok;
     if (b < 0) {
-        quantize_token_fp8(a, (int)blockIdx.x, red);
+        front_token(a, (int)blockIdx.x, red);
     } else if (b < n_router) {
         const int nt = b / kFrontSplit, ks = b - nt * kFrontSplit;
         router_part<NS>(a.xr, a.H, scale, wr, a.E, nt, ks, a.T, lpart, ss_part, red);
@@ -916,8 +970,8 @@ template <int NS>
 hipError_t launch_front_ns(const StreamArgs& a, const uint16_t* scale, const uint16_t* wr, float* lpart,
                            float* ss_part, hipStream_t stream) {
     const int n_router = wr ? ((a.E + 15) / 16) * kFrontSplit : 0;
-    const int n_quant = a.xq ? a.T : 0;  // E4M3 experts: x quantised per token, a workgroup each
-    const int blocks = n_router + (a.with_dense && a.front_dense ? (a.Id / 16) * kFrontSplit : 0) + n_quant;
+    const int n_tok = (a.xq || a.pre_src) ? a.T : 0;  // token items: pre-norms, E4M3 quantisation
+    const int blocks = n_router + (a.with_dense && a.front_dense ? (a.Id / 16) * kFrontSplit : 0) + n_tok;
     if (blocks <= 0) return hipSuccess;
     hipLaunchKernelGGL(decode_front_kernel<NS>, dim3(blocks), dim3(kThreads), 0, stream, a, scale, wr, lpart,
                        ss_part);

@@ -108,7 +108,12 @@ struct StreamArgs {
     const uint16_t* xr;                       // router input
     const uint16_t* xd;                       // dense MLP input
     // E4M3 experts: x quantised per token (half carriers of value * 2^-8) and its per-token scales
-    uint16_t* xq; float* x_scale;  // written by decode_front's last workgroups
+    uint16_t* xq; float* x_scale;  // written by decode_front's first workgroups
+    // the layer's pre-norms, folded into decode_front (null pre_src: none): the
+    // residual stream, the dense and MoE branches' gains (either may be null),
+    // eps, and the branch inputs they write (x_d = bf16(N_gd(h)), x_m = bf16(N_gm(h)))
+    const uint16_t* pre_src; const uint16_t* pre_gd; const uint16_t* pre_gm; float pre_eps;
+    uint16_t* pre_xd; uint16_t* pre_xm;
     // experts
     const void* gu; const float* gu_scale;   // [E][2I][H]
     const void* dw; const float* dw_scale;   // [E][H][I]

@@ -343,15 +343,21 @@ int block_impl(const moe_dims* d, const moe_weights* w, const void* x, const voi
     const uint16_t* g_p = norms ? (const uint16_t*)norms->post : nullptr;
 
     Stages st{dbg, stream};
-    if (norms && (norms->pre_dense || norms->pre_moe)) {
+    const bool pre = norms && (norms->pre_dense || norms->pre_moe);
+    uint16_t* xn_d = nullptr;
+    uint16_t* xn_m = nullptr;
+    const uint16_t* hb = xb;  // the residual stream the pre-norms read
+    if (pre) {
         // the branches' normalised inputs, after the block's own workspace
         const size_t xoff = L.total;
-        uint16_t* xn_d = norms->pre_dense ? at<uint16_t>(ws, xoff) : nullptr;
-        uint16_t* xn_m = norms->pre_moe ? at<uint16_t>(ws, xoff + up256((size_t)T * H * 2)) : nullptr;
-        HIP_TRY(st.begin("ffn_prenorm"), "event record");
-        HIP_TRY(moe::launch_ffn_prenorm(xb, T, H, (const uint16_t*)norms->pre_dense, (const uint16_t*)norms->pre_moe,
-                                        norms->eps, xn_d, xn_m, stream),
-                "ffn_prenorm launch");
+        xn_d = norms->pre_dense ? at<uint16_t>(ws, xoff) : nullptr;
+        xn_m = norms->pre_moe ? at<uint16_t>(ws, xoff + up256((size_t)T * H * 2)) : nullptr;
+        if (path != MOE_PATH_STREAM) {  // the streaming path forms them in its first launch
+            HIP_TRY(st.begin("ffn_prenorm"), "event record");
+            HIP_TRY(moe::launch_ffn_prenorm(xb, T, H, (const uint16_t*)norms->pre_dense,
+                                            (const uint16_t*)norms->pre_moe, norms->eps, xn_d, xn_m, stream),
+                    "ffn_prenorm launch");
+        }
         if (xn_d) xdb = xn_d;
         if (xn_m) xb = xn_m;
     }
@@ -359,6 +365,14 @@ int block_impl(const moe_dims* d, const moe_weights* w, const void* x, const voi
         moe::StreamArgs sa{};
         sa.T = T; sa.H = H; sa.I = I; sa.Id = Id; sa.K = K; sa.E = E;
         sa.x = xb; sa.xr = xr; sa.xd = xdb;
+        if (pre) {
+            sa.pre_src = hb;
+            sa.pre_gd = (const uint16_t*)norms->pre_dense;
+            sa.pre_gm = (const uint16_t*)norms->pre_moe;
+            sa.pre_eps = norms->eps;
+            sa.pre_xd = xn_d;
+            sa.pre_xm = xn_m;
+        }
         sa.gu = w->expert_gate_up; sa.gu_scale = w->gate_up_scale;
         sa.dw = w->expert_down; sa.dw_scale = w->down_scale;
         sa.counts = po.counts; sa.offsets = po.offsets; sa.active = po.active; sa.n_active = po.n_active;

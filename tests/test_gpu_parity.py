@@ -426,7 +426,8 @@ def test_graph_replay(dev, name, path):
 
 
 # ---------------------------------------------------------------- the layer's FFN around the block
-FFN_SETS = {"all": oracle.FFN_NORMS, "post_only": ("post",), "pre_moe": ("pre_moe", "post_moe"), "none": ()}
+FFN_SETS = {"all": oracle.FFN_NORMS, "post_only": ("post",), "pre_moe": ("pre_moe", "post_moe"),
+            "pre_dense": ("pre_dense", "post_dense"), "none": ()}
 
 
 def ffn_gains(H, which, dev, eps=1e-5):
@@ -447,7 +448,9 @@ def ffn_gains(H, which, dev, eps=1e-5):
     ("decode", MOE_PATH_STREAM, "all"), ("decode", MOE_PATH_STREAM, "post_only"),
     ("decode", MOE_PATH_GROUPED, "pre_moe"), ("prefill", MOE_PATH_GROUPED, "all"),
     ("int8_decode", MOE_PATH_STREAM, "all"), ("fp8_decode", MOE_PATH_STREAM, "all"),
-    ("fp8_decode", MOE_PATH_GROUPED, "pre_moe")])
+    ("fp8_decode", MOE_PATH_GROUPED, "pre_moe"), ("decode", MOE_PATH_STREAM, "pre_moe"),
+    ("fp8_decode", MOE_PATH_STREAM, "pre_moe"), ("int8_decode", MOE_PATH_STREAM, "pre_dense"),
+    ("fp8_decode", MOE_PATH_STREAM, "pre_dense")])
 def test_ffn_layer(dev, name, path, which):
     """moe_ffn_layer against the oracle's ffn_layer. Routing as in the block
     tests (on the residual h); the output compared whole and, since
