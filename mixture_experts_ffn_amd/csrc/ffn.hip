@@ -17,6 +17,9 @@ namespace moe {
 
 namespace {
 
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+
 // A workgroup of NT threads per token row holds the row in registers, up to
 // kFR four-value pieces a thread: hidden sizes up to 4 kFR NT. Small batches take
 // 1024 threads a row (more loads in flight for few rows), larger ones 256 (more
@@ -155,7 +158,8 @@ __global__ __launch_bounds__(NT) void ffn_post_kernel(const uint16_t* __restrict
     for (int q = 0; q < FR; ++q) {
         const int c4 = threadIdx.x + q * NT;
         const int c = min(c4, n4 - 1) * 4;  // past the row: a repeat of its last piece, never stored
-        const float4 dv = *reinterpret_cast<const float4*>(dense + base + c);
+        // the dense output and the expert rows are read once: non-temporal loads
+        const f4v dv = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(dense + base + c));
         d[q][0] = dv.x; d[q][1] = dv.y; d[q][2] = dv.z; d[q][3] = dv.w;
 #pragma unroll
         for (int i = 0; i < 4; ++i) m[q][i] = 0.f;
@@ -164,12 +168,12 @@ __global__ __launch_bounds__(NT) void ffn_post_kernel(const uint16_t* __restrict
             if (k < K) {
                 float r[4];
                 if (F32ROWS) {
-                    const float4 v = *reinterpret_cast<const float4*>(
-                        reinterpret_cast<const float*>(rows) + (int64_t)p[k] * H + c);
+                    const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(
+                        reinterpret_cast<const float*>(rows) + (int64_t)p[k] * H + c));
                     r[0] = v.x; r[1] = v.y; r[2] = v.z; r[3] = v.w;
                 } else {
-                    const uint2 v = *reinterpret_cast<const uint2*>(
-                        reinterpret_cast<const uint16_t*>(rows) + (int64_t)p[k] * H + c);
+                    const u2v v = __builtin_nontemporal_load(reinterpret_cast<const u2v*>(
+                        reinterpret_cast<const uint16_t*>(rows) + (int64_t)p[k] * H + c));
                     r[0] = bf16_lo(v.x); r[1] = bf16_hi(v.x);
                     r[2] = bf16_lo(v.y); r[3] = bf16_hi(v.y);
                 }

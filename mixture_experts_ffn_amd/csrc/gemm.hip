@@ -542,12 +542,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     int q[kMaxTopKGemm];
 #pragma unroll
     for (int k = 0; k < kMaxTopKGemm; ++k) q[k] = inv_row[t * K + min(k, K - 1)];
+    // the rows and the dense output are read once: non-temporal loads (at the
+    // skewed T=16384, 1 GB a launch, they measured 15% faster than plain ones)
+    typedef float f4v __attribute__((ext_vector_type(4)));
     uint4 rv[kMaxTopKGemm];
 #pragma unroll
-    for (int k = 0; k < kMaxTopKGemm; ++k)
-        rv[k] = *reinterpret_cast<const uint4*>(rows + (int64_t)q[k] * H + c);
-    const float4 d0 = *reinterpret_cast<const float4*>(dense + t * H + c);
-    const float4 d1 = *reinterpret_cast<const float4*>(dense + t * H + c + 4);
+    for (int k = 0; k < kMaxTopKGemm; ++k) {
+        const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(rows + (int64_t)q[k] * H + c));
+        rv[k] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+    const f4v e0 = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(dense + t * H + c));
+    const f4v e1 = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(dense + t * H + c + 4));
+    const float4 d0 = make_float4(e0.x, e0.y, e0.z, e0.w), d1 = make_float4(e1.x, e1.y, e1.z, e1.w);
     float o[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
 #pragma unroll
     for (int k = 0; k < kMaxTopKGemm; ++k) {
