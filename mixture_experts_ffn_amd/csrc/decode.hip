@@ -123,32 +123,37 @@ __device__ __forceinline__ float dot8_f16(const uint4& a, const uint4& b, float 
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a.w), __builtin_bit_cast(f16x2_t, b.w), acc, false);
 }
 
-// One K-step of a lane's piece of a tile (bf16: two 16-byte halves, 8 k each;
-// int8 or E4M3: one 16-byte piece, 16 k) dotted with the 16 matching x values
-// (for E4M3 the half carriers of x).
-// OPAQUE (1-byte weights): the piece is made opaque before it is widened, so that the
-// compiler widens it where it is used instead of hoisting every step's widened
-// copy (twice the registers) out of the caller's loop over tokens.
-template <int WQ, bool OPAQUE = false>
-__device__ __forceinline__ float piece_dot(const uint4 (&w)[WQ ? 1 : 2], const uint16_t* xp,
-                                           float acc) {
+// 1-byte weights are widened ahead of their use: a lane's piece of a K-step
+// (16 k in one 16-byte load) becomes two groups of 8 bf16 (int8, exact) or
+// half carriers (E4M3), the layout of a bf16 piece (two 16-byte halves, 8 k
+// each), and its dot product with the 16 matching x values (for E4M3 the half
+// carriers of x) needs no further conversion.
+template <int WQ>
+__device__ __forceinline__ void widen_piece(const uint4& v, uint4 (&o)[2]) {
+    if (WQ == 2) f8x16_to_f16(v, o[0], o[1]);
+    else i8x16_to_bf16(v, o[0], o[1]);
+}
+// one K-step of a lane's bf16 (or widened) piece dotted with the 16 matching x values
+template <int WQ>
+__device__ __forceinline__ float wide_dot(const uint4 (&w)[2], const uint16_t* xp, float acc) {
     const uint4 x0 = *reinterpret_cast<const uint4*>(xp);
     const uint4 x1 = *reinterpret_cast<const uint4*>(xp + 8);
-    if (WQ) {
-        uint4 v = w[0];
-        if (OPAQUE) asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
-        uint4 lo, hi;
-        if (WQ == 2) {  // E4M3: half carriers on both sides
-            f8x16_to_f16(v, lo, hi);
-            acc = dot8_f16(lo, x0, acc);
-            return dot8_f16(hi, x1, acc);
-        }
-        i8x16_to_bf16(v, lo, hi);
-        acc = dot8_bf16(lo, x0, acc);
-        return dot8_bf16(hi, x1, acc);
+    if (WQ == 2) return dot8_f16(w[1], x1, dot8_f16(w[0], x0, acc));
+    return dot8_bf16(w[1], x1, dot8_bf16(w[0], x0, acc));
+}
+// Widens every step's piece as soon as it lands, in load order. The register
+// pin after each piece keeps the compiler from sinking the conversion to its
+// first use, which comes after the activations are staged (their loads, issued
+// after the weights', complete after all of them): the conversion then overlaps
+// the weights still in flight instead of following the last of them.
+template <int NS, int WQ>
+__device__ __forceinline__ void widen_steps(const uint4 (&w)[NS][1], uint4 (&o)[NS][2]) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        widen_piece<WQ>(w[s][0], o[s]);
+        asm volatile("" : "+v"(o[s][0].x), "+v"(o[s][0].y), "+v"(o[s][0].z), "+v"(o[s][0].w),
+                     "+v"(o[s][1].x), "+v"(o[s][1].y), "+v"(o[s][1].z), "+v"(o[s][1].w));
     }
-    acc = dot8_bf16(w[0], x0, acc);
-    return dot8_bf16(w[WQ ? 0 : 1], x1, acc);
 }
 
 // sum of the four lanes holding one row of a tile (lanes r, r+16, r+32, r+48)
@@ -211,6 +216,12 @@ __device__ __forceinline__ void gateup_half_item(const uint16_t* __restrict__ x,
     // loads clamped to the half's last step
     tile_load<NS, WQ>(Wb + (int64_t)hc * nk * kTileBytes<WQ>, kt0, ke, lane, wg);
     tile_load<NS, WQ>(Wb + (int64_t)(inter / 16 + hc) * nk * kTileBytes<WQ>, kt0, ke, lane, wu);
+    // 1-byte weights: widened as they land (the gate tile's steps first, in load order)
+    uint4 wgw[NS][2], wuw[NS][2];
+    if constexpr (WQ != 0) {
+        widen_steps<NS, WQ>(wg, wgw);
+        widen_steps<NS, WQ>(wu, wuw);
+    }
     const int len8 = hk * 8;  // 16-byte chunks of x per token in the half
     constexpr int kPer = (kPass * 4 * NS * 8 + kThreads - 1) / kThreads;
     for (int pass = 0; pass < n_rows; pass += kPass) {
@@ -239,8 +250,13 @@ __device__ __forceinline__ void gateup_half_item(const uint16_t* __restrict__ x,
 #pragma unroll
             for (int st = 0; st < NS; ++st)
                 if (st < n_steps) {
-                    ag = piece_dot<WQ>(wg[st], xr + st * 64, ag);
-                    au = piece_dot<WQ>(wu[st], xr + st * 64, au);
+                    if constexpr (WQ != 0) {
+                        ag = wide_dot<WQ>(wgw[st], xr + st * 64, ag);
+                        au = wide_dot<WQ>(wuw[st], xr + st * 64, au);
+                    } else {
+                        ag = wide_dot<0>(wg[st], xr + st * 64, ag);
+                        au = wide_dot<0>(wu[st], xr + st * 64, au);
+                    }
                 }
             ag = tile_row_sum(ag);
             au = tile_row_sum(au);
@@ -847,14 +863,15 @@ __global__ __launch_bounds__(kThreads) void decode_hquant_kernel(StreamArgs a) {
 // NS) of one 16-row tile of a tiled [H, inter] matrix and dots them with the
 // token rows of h (or hd) staged in LDS; returns, in lanes 0..15, the partial
 // sum of row lane of the tile for token n of the pass.
+// (bf16 pieces, or 1-byte ones widened beforehand by widen_steps)
 template <int NS, int WQ>
-__device__ __forceinline__ float down_dot(const uint4 (&w)[NS][WQ ? 1 : 2], const uint16_t* hrow,
-                                          int kt0, int n_steps, int lane) {
+__device__ __forceinline__ float down_dot(const uint4 (&w)[NS][2], const uint16_t* hrow, int kt0, int n_steps,
+                                          int lane) {
     const uint16_t* hp = hrow + kt0 * 64 + (lane >> 4) * 16;
     float acc = 0.f;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-        if (s < n_steps) acc = piece_dot<WQ, true>(w[s], hp + s * 64, acc);
+        if (s < n_steps) acc = wide_dot<WQ>(w[s], hp + s * 64, acc);
     return tile_row_sum(acc);
 }
 
@@ -879,6 +896,8 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(StreamArgs a) {
         const int nk = a.I >> 6, tile = g * kWaves + wave;
         uint4 w[NS][WQ ? 1 : 2];
         tile_load<NS, WQ>(W + (int64_t)tile * nk * kTileBytes<WQ>, 0, nk, lane, w);
+        uint4 ww[NS][2];  // 1-byte weights: widened as they land, before h is staged
+        if constexpr (WQ != 0) widen_steps<NS, WQ>(w, ww);
         const float sc = WQ ? a.dw_scale[(int64_t)e * a.H + tile * 16 + (lane & 15)] : 1.f;
         const int hc8 = a.I >> 3;
         const float* gs = WQ ? a.gu_scale + (int64_t)e * 2 * a.I : nullptr;
@@ -893,8 +912,10 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(StreamArgs a) {
             __syncthreads();
 #pragma unroll 1
             for (int n = 0; n < nt; ++n) {
-                const float v = down_dot<NS, WQ>(w, reinterpret_cast<const uint16_t*>(hs + n * hc8), 0,
-                                                   nk, lane);
+                const uint16_t* hrow = reinterpret_cast<const uint16_t*>(hs + n * hc8);
+                float v;
+                if constexpr (WQ != 0) v = down_dot<NS, WQ>(ww, hrow, 0, nk, lane);
+                else v = down_dot<NS, 0>(w, hrow, 0, nk, lane);
                 const float hsc = WQ == 2 ? a.h_scale[p0 + pass + n] : 1.f;
                 if (lane < 16) a.part[(int64_t)(p0 + pass + n) * a.H + tile * 16 + lane] = v * sc * hsc;
             }
@@ -916,7 +937,7 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(StreamArgs a) {
             __syncthreads();
 #pragma unroll 1
             for (int n = 0; n < nt; ++n) {
-                const float v = down_dot<NS, false>(w, reinterpret_cast<const uint16_t*>(hs + n * hc8),
+                const float v = down_dot<NS, 0>(w, reinterpret_cast<const uint16_t*>(hs + n * hc8),
                                                     kt0, n_steps, lane);
                 if (lane < 16) red[(wave * kPass + n) * 16 + lane] = v;
             }
