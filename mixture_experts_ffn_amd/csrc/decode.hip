@@ -38,6 +38,8 @@
 // bit placement and dotted with x quantised per token (decode_front's last
 // workgroups); h is formed and quantised per routed row by decode_hquant.
 // The template parameter WQ names the experts' format: 0 bf16, 1 int8, 2 E4M3.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 #include "topk.h"
@@ -101,6 +103,63 @@ __device__ __forceinline__ void stage_rows(const uint4* __restrict__ src, int n,
     }
 }
 
+// Four per-row values of a pass (rows past nt repeat row nt - 1), as four
+// uniform scalars: pick(r) is a chain of selects, never an indexed array or a
+// load through a selected address (readfirstlane keeps the compiler from
+// folding the selects into the loads).
+template <class T>
+struct QuadOf {
+    T v0, v1, v2, v3;
+    __device__ __forceinline__ T pick(int r) const { return r == 3 ? v3 : r == 2 ? v2 : r == 1 ? v1 : v0; }
+    __device__ __forceinline__ static T uni(T v) {
+        return __builtin_bit_cast(T, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+    }
+    __device__ __forceinline__ static QuadOf load(const T* __restrict__ p, int nt) {
+        return {uni(p[0]), uni(p[min(1, nt - 1)]), uni(p[min(2, nt - 1)]), uni(p[min(3, nt - 1)])};
+    }
+};
+typedef QuadOf<int32_t> Quad;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// The activations a workgroup stages (x rows, h partial sums, h rows) go
+// straight from global memory into LDS (buffer_load_dwordx4 ... lds): no
+// registers hold them and nothing waits for them until the caller's dma_wait,
+// so they are issued right behind the weights and land right behind them.
+// Chunk j (16 bytes) of n is read at byte offset off(j) of a buffer of `bytes`
+// bytes from `base` (reads past it return zero) and lands at dst[j];
+// wavefront w's load q moves chunks (q kWaves + w) 64 .. + 64. Every
+// wavefront issues all KQ loads (a load under a branch makes the compiler's
+// wait counts after the join wait for every load in flight, the weights
+// included); chunks past n fetch chunk n - 1, so the caller reserves KQ kWaves
+// 64 chunks of LDS from dst. (A buffer load, unlike global_load_lds, leaves
+// the compiler's counts for the weights' own waits exact.) The compiler must
+// not move loads across these (the waits count loads in issue order), nor
+// schedule work on the loads in flight ahead of them: compiler memory and
+// scheduling barriers on both sides.
+template <int KQ, class Off>
+__device__ __forceinline__ void dma_chunks(uint4* dst, int n, const void* base, int64_t bytes, Off off) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)min(bytes, (int64_t)INT32_MAX),
+                                          0x00020000);  // raw 32-bit data format
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), lane = threadIdx.x & 63;
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < KQ; ++q) {
+        const int b = (q * kWaves + wave) * 64;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + b), 16, (int)off(min(b + lane, n - 1)), 0, 0,
+                                                 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+}
+// Every load of the wavefront done (its DMA chunks in LDS); a barrier then
+// makes all wavefronts' chunks visible.
+__device__ __forceinline__ void dma_wait() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // 16 int8 (one tiled-layout piece) -> two groups of 8 bf16 (exact)
 __device__ __forceinline__ void i8x16_to_bf16(const uint4& v, uint4& lo, uint4& hi) {
     lo = i8x8_to_bf16(make_uint4(v.x, v.y, 0u, 0u));
@@ -141,16 +200,20 @@ __device__ __forceinline__ float wide_dot(const uint4 (&w)[2], const uint16_t* x
     if (WQ == 2) return dot8_f16(w[1], x1, dot8_f16(w[0], x0, acc));
     return dot8_bf16(w[1], x1, dot8_bf16(w[0], x0, acc));
 }
-// Widens every step's piece as soon as it lands, in load order. The register
-// pin after each piece keeps the compiler from sinking the conversion to its
-// first use, which comes after the activations are staged (their loads, issued
-// after the weights', complete after all of them): the conversion then overlaps
-// the weights still in flight instead of following the last of them.
+// Widens every step's piece as soon as it lands, in load order. The pin
+// before each piece keeps its conversion after the activations' copies issued
+// ahead of it (the scheduler would otherwise start converting, and so wait for
+// the weights, before issuing them); the pin after it keeps the compiler from
+// sinking the conversion to its first use (after the activations are staged).
+// The conversion then overlaps the weights still in flight instead of
+// following the last of them.
 template <int NS, int WQ>
-__device__ __forceinline__ void widen_steps(const uint4 (&w)[NS][1], uint4 (&o)[NS][2]) {
+__device__ __forceinline__ void widen_steps(uint4 (&w)[NS][1], uint4 (&o)[NS][2]) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        widen_piece<WQ>(w[s][0], o[s]);
+        u32x4 v{w[s][0].x, w[s][0].y, w[s][0].z, w[s][0].w};  // one 128-bit operand: no copies
+        asm volatile("" : "+v"(v));
+        widen_piece<WQ>(make_uint4(v.x, v.y, v.z, v.w), o[s]);
         asm volatile("" : "+v"(o[s][0].x), "+v"(o[s][0].y), "+v"(o[s][0].z), "+v"(o[s][0].w),
                      "+v"(o[s][1].x), "+v"(o[s][1].y), "+v"(o[s][1].z), "+v"(o[s][1].w));
     }
@@ -203,8 +266,9 @@ __device__ __forceinline__ void tile_load2(const char* ta, const char* tb, int k
 // kb + w NS (steps past the half contribute 0); only the half's columns of x
 // are staged.
 template <int NS, int WQ>
-__device__ __forceinline__ void gateup_half_item(const uint16_t* __restrict__ x, int H, const void* W, int inter,
-                                                 int hc, int half, const int32_t* toks, int n_rows,
+__device__ __forceinline__ void gateup_half_item(const uint16_t* __restrict__ x, int64_t x_bytes, int H, const void* W,
+                                                 int inter,
+                                                 int hc, int half, const int32_t* __restrict__ toks, int n_rows,
                                                  int64_t half_stride, float* __restrict__ part, uint4* xs,
                                                  float* red) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -212,35 +276,40 @@ __device__ __forceinline__ void gateup_half_item(const uint16_t* __restrict__ x,
     const int kb = half * hk, kt0 = kb + wave * NS, ke = kb + hk;
     const int n_steps = max(0, min(NS, ke - kt0));
     const char* Wb = reinterpret_cast<const char*>(W);
+    const int len8 = hk * 8;  // 16-byte chunks of x per token in the half
+    // x rows of a pass's tokens -> LDS, chunk i of token i / len8. The token
+    // indices are uniform loads (the scalar path, beside the weights' vector
+    // loads), kept as four values rather than an array, which the compiler
+    // would index through memory.
+    static_assert(kPass == 4, "four token values a pass");
+    Quad tk;
+    constexpr int kXQ = (kPass * 32 * NS + kThreads - 1) / kThreads;  // DMA loads a wavefront issues
+    auto stage_x = [&](int nt) {
+        dma_chunks<kXQ>(xs, nt * len8, x, x_bytes, [&](int i) {
+            const int r = i / len8;
+            return (tk.pick(r) * H + kb * 64) * 2 + (i - r * len8) * 16;
+        });
+    };
+    tk = Quad::load(toks, min(kPass, n_rows));
     uint4 wg[NS][WQ ? 1 : 2], wu[NS][WQ ? 1 : 2];
     // loads clamped to the half's last step
     tile_load<NS, WQ>(Wb + (int64_t)hc * nk * kTileBytes<WQ>, kt0, ke, lane, wg);
     tile_load<NS, WQ>(Wb + (int64_t)(inter / 16 + hc) * nk * kTileBytes<WQ>, kt0, ke, lane, wu);
+    stage_x(min(kPass, n_rows));  // the first pass's x, right behind the weights
     // 1-byte weights: widened as they land (the gate tile's steps first, in load order)
     uint4 wgw[NS][2], wuw[NS][2];
     if constexpr (WQ != 0) {
         widen_steps<NS, WQ>(wg, wgw);
         widen_steps<NS, WQ>(wu, wuw);
     }
-    const int len8 = hk * 8;  // 16-byte chunks of x per token in the half
-    constexpr int kPer = (kPass * 4 * NS * 8 + kThreads - 1) / kThreads;
     for (int pass = 0; pass < n_rows; pass += kPass) {
-        const int nt = min(kPass, n_rows - pass), n = nt * len8;
-        __syncthreads();  // previous pass done with xs and red
-        {
-            uint4 v[kPer];
-#pragma unroll
-            for (int q = 0; q < kPer; ++q) {
-                const int i = min((int)threadIdx.x + q * kThreads, n - 1);
-                const int r = i / len8;
-                v[q] = reinterpret_cast<const uint4*>(x + (int64_t)toks[pass + r] * H + kb * 64)[i - r * len8];
-            }
-#pragma unroll
-            for (int q = 0; q < kPer; ++q) {
-                const int i = (int)threadIdx.x + q * kThreads;
-                if (i < n) xs[i] = v[q];
-            }
+        const int nt = min(kPass, n_rows - pass);
+        if (pass > 0) {
+            __syncthreads();  // previous pass done with xs and red
+            tk = Quad::load(toks + pass, nt);
+            stage_x(nt);
         }
+        dma_wait();
         __syncthreads();
 #pragma unroll 1
         for (int t = 0; t < nt; ++t) {
@@ -608,11 +677,12 @@ __global__ __launch_bounds__(kThreads) void decode_experts_gateup_kernel(StreamA
     if (slot >= *a.n_active) return;
     const int e = a.active[slot];
     const int p0 = a.offsets[e], n = a.offsets[e + 1] - p0;
+    if (n <= 0) return;  // (an active expert has rows)
     const int64_t wstride = (int64_t)2 * a.I * a.H;
     const void* W = WQ ? (const void*)((const int8_t*)a.gu + e * wstride)
                          : (const void*)((const uint16_t*)a.gu + e * wstride);
     // E4M3 experts read x quantised per token (half carriers of value * 2^-8)
-    gateup_half_item<NS, WQ>(WQ == 2 ? a.xq : a.x, a.H, W, a.I, hc, half, a.perm_token + p0, n,
+    gateup_half_item<NS, WQ>(WQ == 2 ? a.xq : a.x, (int64_t)a.T * a.H * 2, a.H, W, a.I, hc, half, a.perm_token + p0, n,
                                (int64_t)a.T * a.K * 2 * a.I, a.hpart + (int64_t)p0 * 2 * a.I, xs, red);
 }
 
@@ -875,9 +945,19 @@ __device__ __forceinline__ float down_dot(const uint4 (&w)[NS][2], const uint16_
     return tile_row_sum(acc);
 }
 
+// DMA loads a wavefront issues per pass: the E4M3 h rows of a pass, the dense
+// rows of a pass (I <= 64 NS, Id <= 256 NS). (bf16 and int8 experts form h
+// from the two K halves' partial sums as they stage it: their loads, issued
+// right behind the weights, land right behind them without a copy to LDS
+// first.)
+template <int NS>
+constexpr int kDownRowQ = (kPass * 8 * NS + kThreads - 1) / kThreads;
+template <int NS>
+constexpr int kDenseRowQ = (kPass * 32 * NS + kThreads - 1) / kThreads;
+
 template <int NS, int WQ>
 __global__ __launch_bounds__(kThreads) void decode_down_kernel(StreamArgs a) {
-    extern __shared__ uint4 hs[];  // [kPass][max(I, Id)] bf16
+    extern __shared__ uint4 hs[];  // [kPass][max(I, Id)] bf16 (rounded up to whole DMA loads)
     __shared__ float red[kWaves * kPass * 16];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int ipe = a.H / 64;  // expert items: 4 tiles (one per wavefront) of 16 rows
@@ -890,34 +970,52 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(StreamArgs a) {
         if (slot >= *a.n_active) return;
         const int e = a.active[slot];
         const int p0 = a.offsets[e], n_rows = a.offsets[e + 1] - p0;
+        if (n_rows <= 0) return;  // (an active expert has rows)
         const int64_t wstride = (int64_t)a.H * a.I;
         const char* W = WQ ? (const char*)((const int8_t*)a.dw + e * wstride)
                              : (const char*)((const uint16_t*)a.dw + e * wstride);
         const int nk = a.I >> 6, tile = g * kWaves + wave;
+        const int hc8 = a.I >> 3;
+        // E4M3: the pass's rows' activation scales (the first pass's read
+        // ahead of everything, on the scalar path), and its rows of h -> LDS,
+        // issued right behind the weights
+        QuadOf<float> hsc{1.f, 1.f, 1.f, 1.f};
+        if constexpr (WQ == 2) hsc = QuadOf<float>::load(a.h_scale + p0, min(kPass, n_rows));
+        const int pairs = a.T * a.K;  // grouped rows
+        auto stage = [&](int pass, int nt) {
+            const int o0 = (p0 + pass) * a.I * 2;
+            dma_chunks<kDownRowQ<NS>>(hs, nt * hc8, a.h, (int64_t)pairs * a.I * 2, [&](int j) { return o0 + j * 16; });
+        };
         uint4 w[NS][WQ ? 1 : 2];
         tile_load<NS, WQ>(W + (int64_t)tile * nk * kTileBytes<WQ>, 0, nk, lane, w);
-        uint4 ww[NS][2];  // 1-byte weights: widened as they land, before h is staged
+        if constexpr (WQ == 2) stage(0, min(kPass, n_rows));
+        uint4 ww[NS][2];  // 1-byte weights: widened as they land
         if constexpr (WQ != 0) widen_steps<NS, WQ>(w, ww);
         const float sc = WQ ? a.dw_scale[(int64_t)e * a.H + tile * 16 + (lane & 15)] : 1.f;
-        const int hc8 = a.I >> 3;
         const float* gs = WQ ? a.gu_scale + (int64_t)e * 2 * a.I : nullptr;
         for (int pass = 0; pass < n_rows; pass += kPass) {
             const int nt = min(kPass, n_rows - pass);
-            __syncthreads();
-            if (WQ == 2)  // E4M3: rows of h already formed and quantised (decode_hquant_kernel)
-                stage_rows<(kPass * 128 + kThreads - 1) / kThreads>(
-                    reinterpret_cast<const uint4*>(a.h + (int64_t)(p0 + pass) * a.I), nt * hc8, hs);
-            else
+            if constexpr (WQ == 2) {
+                if (pass > 0) {
+                    __syncthreads();  // previous pass done with hs
+                    stage(pass, nt);
+                    hsc = QuadOf<float>::load(a.h_scale + p0 + pass, nt);
+                }
+                dma_wait();
+                __syncthreads();
+            } else {
+                __syncthreads();
                 stage_h<(kPass * 128 + kThreads - 1) / kThreads, WQ>(a, p0 + pass, nt * hc8, gs, hs);
-            __syncthreads();
+                __syncthreads();
+            }
 #pragma unroll 1
             for (int n = 0; n < nt; ++n) {
                 const uint16_t* hrow = reinterpret_cast<const uint16_t*>(hs + n * hc8);
                 float v;
                 if constexpr (WQ != 0) v = down_dot<NS, WQ>(ww, hrow, 0, nk, lane);
                 else v = down_dot<NS, 0>(w, hrow, 0, nk, lane);
-                const float hsc = WQ == 2 ? a.h_scale[p0 + pass + n] : 1.f;
-                if (lane < 16) a.part[(int64_t)(p0 + pass + n) * a.H + tile * 16 + lane] = v * sc * hsc;
+                const float hv = WQ == 2 ? hsc.pick(n) : 1.f;
+                if (lane < 16) a.part[(int64_t)(p0 + pass + n) * a.H + tile * 16 + lane] = v * sc * hv;
             }
         }
     } else {
@@ -925,15 +1023,22 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(StreamArgs a) {
         const int tile = (int)blockIdx.x;
         const int nk = a.Id >> 6, kd = (nk + kWaves - 1) / kWaves;
         const int kt0 = wave * kd, n_steps = max(0, min(kd, nk - kt0));
+        const int hc8 = a.Id >> 3;
+        auto stage = [&](int pass, int nt) {
+            const int o0 = pass * a.Id * 2;
+            dma_chunks<kDenseRowQ<NS>>(hs, nt * hc8, a.hd, (int64_t)a.T * a.Id * 2, [&](int j) { return o0 + j * 16; });
+        };
         uint4 w[NS][2];
         tile_load<NS, false>(reinterpret_cast<const char*>(a.ddw) + (int64_t)tile * nk * kTileBytes<false>,
                              kt0, nk, lane, w);
-        const int hc8 = a.Id >> 3;
+        stage(0, min(kPass, a.T));
         for (int pass = 0; pass < a.T; pass += kPass) {
             const int nt = min(kPass, a.T - pass);
-            __syncthreads();
-            stage_rows<(kPass * 512 + kThreads - 1) / kThreads>(
-                reinterpret_cast<const uint4*>(a.hd + (int64_t)pass * a.Id), nt * hc8, hs);
+            if (pass > 0) {
+                __syncthreads();  // previous pass done with hs and red
+                stage(pass, nt);
+            }
+            dma_wait();
             __syncthreads();
 #pragma unroll 1
             for (int n = 0; n < nt; ++n) {
@@ -1004,7 +1109,10 @@ hipError_t launch_experts_nj(const StreamArgs& a, int wq, hipStream_t stream) {
     const int n_fin = a.with_dense ? (a.T * a.Id + kThreads - 1) / kThreads : 0;
     const int blocks = n_fin + a.max_active * (a.I / 16) * 2;
     if (blocks <= 0) return hipSuccess;
-    const size_t lds = (size_t)kPass * (a.H / 2) * sizeof(uint16_t);
+    // a pass's x rows (half the hidden size each), rounded up to whole DMA loads
+    const size_t kq = (kPass * 32 * NJ + kThreads - 1) / kThreads;
+    const size_t x_bytes = (size_t)kPass * (a.H / 2) * sizeof(uint16_t), dma_bytes = kq * kThreads * sizeof(uint4);
+    const size_t lds = x_bytes > dma_bytes ? x_bytes : dma_bytes;
     if (wq == 2)
         hipLaunchKernelGGL((decode_experts_gateup_kernel<NJ, 2>), dim3(blocks), dim3(kThreads), lds, stream, a);
     else if (wq == 1)
@@ -1071,16 +1179,27 @@ hipError_t launch_decode_experts_gateup(const StreamArgs& a, int wq, hipStream_t
 #undef CALL
 }
 
+// LDS of a down workgroup: the larger of an expert item's (h rows; E4M3
+// rounded up to whole DMA loads) and a dense item's (its rows, rounded up
+// likewise)
+template <int NS>
+size_t down_lds_bytes(const StreamArgs& a, int wq) {
+    const size_t rows = (size_t)kPass * (a.I / 8);
+    size_t chunks = wq == 2 ? std::max(rows, (size_t)kDownRowQ<NS> * kThreads) : rows;
+    if (a.with_dense) chunks = std::max(chunks, std::max((size_t)kPass * (a.Id / 8), (size_t)kDenseRowQ<NS> * kThreads));
+    return chunks * sizeof(uint4);
+}
+
 hipError_t launch_decode_down(const StreamArgs& a, int wq, hipStream_t stream) {
     // K-steps a wavefront holds: a whole expert tile (I / 64) or a quarter of
     // a dense tile (Id / 256, rounded up)
     const int need = max(a.I / 64, (a.Id / 64 + kWaves - 1) / kWaves);
     const int blocks = a.max_active * (a.H / 64) + (a.with_dense ? a.H / 16 : 0);
     if (blocks <= 0) return hipSuccess;
-    const size_t lds = (size_t)kPass * (a.I > a.Id ? a.I : a.Id) * sizeof(uint16_t);
     const dim3 grid(blocks), block(kThreads);
 #define LAUNCH(N)                                                                                   \
     do {                                                                                            \
+        const size_t lds = down_lds_bytes<N>(a, wq);                                                \
         if (wq == 2) hipLaunchKernelGGL((decode_down_kernel<N, 2>), grid, block, lds, stream, a);   \
         else if (wq == 1) hipLaunchKernelGGL((decode_down_kernel<N, 1>), grid, block, lds, stream, a); \
         else hipLaunchKernelGGL((decode_down_kernel<N, 0>), grid, block, lds, stream, a);            \
