@@ -586,3 +586,28 @@ def test_random_shapes(dev, case):
         y_ref, _ = oracle.moe_block(x, ow, shape.top_k, shape.rms_eps, expert_dtype=ofmt, routing=r)
         cos, rel = compare_y(y_f64(y), y_ref, REL_BF16 if ofmt == "bf16" else REL_INT8)
         say(f"  path {path}: cos {cos:.7f}  rel-L2 {rel:.3e}")
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "int8", "fp8"])
+@pytest.mark.parametrize("T", [5, 64])
+def test_stream_many_rows(dev, fmt, T):
+    """The streaming path with many rows per expert (8 experts, top-8: every
+    expert takes every token), so that its staging of x, of h and of the
+    dense rows runs over several passes of four rows, in each expert format,
+    against the oracle on every token."""
+    shape = EDGE["k_eq_e"]
+    say(f"case: streaming, every expert takes all {T} tokens, experts {fmt}")
+    w = moe_synth.make_weights(shape, 77)
+    x = moe_synth.make_tokens(shape, 77, T)
+    lw = upload(w, dev, int8=fmt == "int8", fp8=fmt == "fp8")
+    wl = moe_synth.Workload("many_rows", shape, T, 77, int8=fmt == "int8", fp8=fmt == "fp8")
+    ref_r = oracle_route(wl, w, x)
+    ow, ofmt = oracle_weights(wl, w)
+    y, dbg = run_block(wl, lw, bf16_dev(x, dev), MOE_PATH_STREAM)
+    check_routing(dbg["topk_idx"], dbg["topk_w"], ref_r, w["per_expert_scale"])
+    assert (dbg["counts"] == T).all()
+    r = routing_for(dbg["topk_idx"], ref_r, w["per_expert_scale"])
+    y_ref, _ = oracle.moe_block(x, ow, shape.top_k, shape.rms_eps, expert_dtype=ofmt, routing=r)
+    rel_bar = REL_BF16 if ofmt == "bf16" else REL_INT8
+    compare_y(y_f64(y), y_ref, rel_bar)
+    compare_per_token(y_f64(y), y_ref, rel_bar)
