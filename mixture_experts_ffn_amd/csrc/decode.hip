@@ -874,6 +874,32 @@ __device__ __forceinline__ void stage_h(const StreamArgs& a, int p0, int n, cons
     }
 }
 
+// stage_h for int8 experts, four columns a thread and one 256-chunk round at
+// a time: the down item keeps its widened weights in registers meanwhile, and
+// this keeps the kernel within 128 registers (four wavefronts a SIMD).
+// n4: chunks of 4 columns (rows p0 .. p0 + n4 / (I / 4)); same arithmetic as
+// stage_h.
+__device__ __forceinline__ void stage_h4_int8(const StreamArgs& a, int p0, int n4, const float* gs, uint4* hs) {
+    const int I = a.I, hc4 = I >> 2;
+    const int64_t half = (int64_t)a.T * a.K * 2 * I;
+    uint2* hs2 = reinterpret_cast<uint2*>(hs);
+#pragma unroll 1
+    for (int i0 = 0; i0 < n4; i0 += kThreads) {
+        const int i = min(i0 + (int)threadIdx.x, n4 - 1);
+        const int r = i / hc4, c = (i - r * hc4) * 4;
+        const float* g0 = a.hpart + (int64_t)(p0 + r) * 2 * I + c;
+        const float4 ga = *reinterpret_cast<const float4*>(g0), gb = *reinterpret_cast<const float4*>(g0 + half);
+        const float4 ua = *reinterpret_cast<const float4*>(g0 + I);
+        const float4 ub = *reinterpret_cast<const float4*>(g0 + half + I);
+        const float4 sg = *reinterpret_cast<const float4*>(gs + c), su = *reinterpret_cast<const float4*>(gs + I + c);
+        const float g[4] = {(ga.x + gb.x) * sg.x, (ga.y + gb.y) * sg.y, (ga.z + gb.z) * sg.z, (ga.w + gb.w) * sg.w};
+        const float u[4] = {(ua.x + ub.x) * su.x, (ua.y + ub.y) * su.y, (ua.z + ub.z) * su.z, (ua.w + ub.w) * su.w};
+        if (i0 + (int)threadIdx.x < n4)
+            hs2[i] = make_uint2(pack_bf16x2(gelu_tanh(g[0]) * u[0], gelu_tanh(g[1]) * u[1]),
+                                pack_bf16x2(gelu_tanh(g[2]) * u[2], gelu_tanh(g[3]) * u[3]));
+    }
+}
+
 // ---------------------------------------------------------------- K3b
 // E4M3 experts: h of each routed pair (grouped row p) from the two K halves'
 // partial sums, times the gate/up column scales and the token's activation
@@ -1005,7 +1031,8 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(StreamArgs a) {
                 __syncthreads();
             } else {
                 __syncthreads();
-                stage_h<(kPass * 128 + kThreads - 1) / kThreads, WQ>(a, p0 + pass, nt * hc8, gs, hs);
+                if constexpr (WQ == 1) stage_h4_int8(a, p0 + pass, nt * (a.I >> 2), gs, hs);
+                else stage_h<(kPass * 128 + kThreads - 1) / kThreads, WQ>(a, p0 + pass, nt * hc8, gs, hs);
                 __syncthreads();
             }
 #pragma unroll 1
