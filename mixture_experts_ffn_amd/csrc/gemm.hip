@@ -288,8 +288,12 @@ constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 
 // steps are pending: then its A(k) and B(k) have landed. A barrier then
 // publishes every wavefront's A share and frees the stage read at step k-1.
 // (A shallower A distance would drain the B ring too: waiting for an A load
-// also waits for every B load issued before it.) a_dma pins the order of the
-// loads against compiler scheduling; loads past the last K-step repeat the
+// also waits for every B load issued before it.) a_dma and a compiler memory
+// barrier after b_load pin the order of the loads against compiler
+// scheduling: a B load sunk below the MFMAs (to reuse the registers they
+// read) leaves the compiler unsure, across the loop's back edge, which loads
+// a register still waits for, and it then waits for all of them once per
+// unrolled group, draining the ring. Loads past the last K-step repeat the
 // last one, so every step issues the same loads.
 template <int WQ, int NSL, bool ADMA>
 __device__ __forceinline__ void k_loop(const char* const (&ap)[kADma], const char* const (&bp)[2], int nk, int nkt,
@@ -305,18 +309,25 @@ __device__ __forceinline__ void k_loop(const char* const (&ap)[kADma], const cha
     uint16_t* const S1 = L.a[1];
     uint16_t* const S2 = L.a[2];
     uint16_t* const S3 = L.a[3];
+    // (the prologue's B loads in step order too: with rb0 issued last, the
+    // compiler's wait for it at the first step of every unrolled group would
+    // drain the ring)
     if (ADMA) a_dma(ap, 0, S0, wave);
     if (NSL > 0) b_load<WQ>(bp, 0, nkt, rb0);
+    asm volatile("" ::: "memory");
     if (ADMA) a_dma(ap, min(1, last), S1, wave);
     if (NSL > 0) b_load<WQ>(bp, min(1, last), nkt, rb1);
+    asm volatile("" ::: "memory");
     if (ADMA) a_dma(ap, min(2, last), S2, wave);
     if (NSL > 0) b_load<WQ>(bp, min(2, last), nkt, rb2);
+    asm volatile("" ::: "memory");
 #define MOE_GEMM_STEP(U, SA, RB, SN, RN)                                    \
     __builtin_amdgcn_s_waitcnt(kWait);                                      \
     raw_barrier();                                                          \
     if (ADMA) a_dma(ap, min(kt + (U) + kDepth - 1, last), SN, wave);        \
     if (NSL > 0) {                                                          \
         b_load<WQ>(bp, min(kt + (U) + kDepth - 1, last), nkt, RN);        \
+        asm volatile("" ::: "memory");                                      \
         if (kt + (U) < nk) mma_step<WQ, NSL>(SA, RB, lane, acc);          \
     }
     for (int kt = 0; kt < nk; kt += kDepth) {
