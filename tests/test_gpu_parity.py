@@ -611,3 +611,27 @@ def test_stream_many_rows(dev, fmt, T):
     rel_bar = REL_BF16 if ofmt == "bf16" else REL_INT8
     compare_y(y_f64(y), y_ref, rel_bar)
     compare_per_token(y_f64(y), y_ref, rel_bar)
+
+
+@pytest.mark.parametrize("name", ["decode", "int8_decode", "fp8_decode"])
+def test_stream_largest_batch_real_shape(dev, name):
+    """The streaming path at its largest batch (T = 64) at the real shape, in
+    each expert format: several rows per expert for most experts, so its
+    staging runs over more than one pass, against the oracle on every token."""
+    wl, w, x, lw, xd = inputs(name, dev, tokens=64)
+    s = wl.shape
+    say(f"case: streaming path, real shape, {name} weights, T=64")
+    y, dbg = run_block(wl, lw, xd, MOE_PATH_STREAM)
+    ref = oracle_route(wl, w, x)
+    check_routing(dbg["topk_idx"], dbg["topk_w"], ref, w["per_expert_scale"])
+    p = oracle.permute_pairs(dbg["topk_idx"], s.num_experts)
+    for k in ("counts", "offsets", "perm_token", "inv_row"):
+        np.testing.assert_array_equal(dbg[k], p[k], err_msg=k)
+    assert int(dbg["counts"].max()) > 4  # at least one expert takes two passes
+    r = routing_for(dbg["topk_idx"], ref, w["per_expert_scale"])
+    ow, fmt = oracle_weights(wl, w)
+    y_ref, _ = oracle.moe_block(x, ow, s.top_k, s.rms_eps, expert_dtype=fmt, routing=r)
+    bar = REL_BF16 if fmt == "bf16" else REL_INT8
+    cos, rel = compare_y(y_f64(y), y_ref, bar)
+    worst = compare_per_token(y_f64(y), y_ref, bar)
+    say(f"  cos {cos:.7f}  rel-L2 {rel:.3e}  worst token rel-L2 {worst:.3e}")
